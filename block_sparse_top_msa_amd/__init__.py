@@ -1,0 +1,365 @@
+"""Python binding of libmsa.so, the MI355X MiniMax Sparse Attention library.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI declared in include/msa.h.  PyTorch provides device memory and the
+current stream.  There is no fallback: if libmsa.so is missing or fails to
+load, importing this package raises.
+
+    proxy_score(q, k, cu_seqlens_q, ...)          msa_proxy_score page
+    topk_select(max_score, topk, num_kv_heads)    the top-K block select
+    sparse_attention(q, k, v, q2k_indices, ...)   msa_sparse_attention page
+    tile_union(q2k, cu_seqlens_q, lengths_k, ...) the per-tile union builder
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "MsaError", "lib", "library_path", "sparse_attention", "proxy_score", "topk_select",
+    "tile_union", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3", "KV_E2M1X2",
+    "REDUCE_NONE", "REDUCE_ALL", "REDUCE_GROUP", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libmsa.so")
+
+KV_BF16, KV_FP8_E4M3, KV_E2M1X2 = 0, 1, 2
+REDUCE_NONE, REDUCE_ALL, REDUCE_GROUP = 0, 1, 2
+BLOCK = 128
+
+EXPORTED_SYMBOLS = (
+    "msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
+    "msa_topk_select", "msa_tile_union", "msa_status_string", "msa_last_error", "msa_version",
+)
+
+_STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_DTYPE",
+           4: "MSA_ERR_CONFLICT", 5: "MSA_ERR_UNSUPPORTED", 6: "MSA_ERR_WORKSPACE",
+           7: "MSA_ERR_HIP"}
+
+
+class MsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = _STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class Strides(ctypes.Structure):
+    _fields_ = [("page", ctypes.c_int64), ("head", ctypes.c_int64), ("token", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_I32P = ctypes.c_void_p
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("total_q", ctypes.c_int32),
+        ("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("topk", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32), ("max_k_tiles", ctypes.c_int32),
+        ("page_table_width", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float), ("k_global_scale", ctypes.c_float),
+        ("v_global_scale", ctypes.c_float), ("kv_dtype", ctypes.c_int32),
+        ("splits", ctypes.c_int32),
+        ("q", _P), ("k", _P), ("v", _P), ("k_scale", _P), ("v_scale", _P),
+        ("k_strides", Strides), ("v_strides", Strides),
+        ("k_scale_strides", Strides), ("v_scale_strides", Strides),
+        ("q2k", _I32P), ("cu_seqlens_q", _I32P), ("cu_seqlens_k", _I32P),
+        ("page_table", _I32P), ("seqused_k", _I32P),
+        ("out", _P), ("lse", _P),
+    ]
+
+
+class ProxyArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("total_q", ctypes.c_int32),
+        ("num_qo_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("max_seqlen_q", ctypes.c_int32),
+        ("max_k_tiles", ctypes.c_int32), ("page_table_width", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("reduce_heads", ctypes.c_int32),
+        ("q", _P), ("k", _P), ("k_strides", Strides),
+        ("cu_seqlens_q", _I32P), ("cu_seqlens_k", _I32P), ("page_table", _I32P),
+        ("seqused_k", _I32P), ("out", _P),
+    ]
+
+
+def _load():
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with `python -m block_sparse_top_msa_amd.build` "
+            "(the MSA path runs only in its HIP kernels; there is no fallback)")
+    L = ctypes.CDLL(library_path)
+    L.msa_sparse_attention_workspace_size.argtypes = [ctypes.POINTER(AttnArgs),
+                                                      ctypes.POINTER(ctypes.c_size_t)]
+    L.msa_sparse_attention.argtypes = [ctypes.POINTER(AttnArgs), _P, ctypes.c_size_t, _P]
+    L.msa_proxy_score.argtypes = [ctypes.POINTER(ProxyArgs), _P]
+    L.msa_topk_select.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
+    L.msa_tile_union.argtypes = [_P, _P, _P] + [ctypes.c_int32] * 8 + [_P, _P, _P, _P]
+    for fn in ("msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
+               "msa_topk_select", "msa_tile_union"):
+        getattr(L, fn).restype = ctypes.c_int
+    L.msa_status_string.argtypes = [ctypes.c_int]
+    L.msa_status_string.restype = ctypes.c_char_p
+    L.msa_last_error.argtypes = []
+    L.msa_last_error.restype = ctypes.c_char_p
+    L.msa_version.argtypes = []
+    L.msa_version.restype = ctypes.c_char_p
+    return L
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != 0:
+        raise MsaError(status, lib.msa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _kv_format(k: torch.Tensor, k_scale) -> int:
+    if k.dtype == torch.bfloat16:
+        return KV_BF16
+    if k.dtype == torch.float8_e4m3fn:
+        return KV_FP8_E4M3
+    if k.dtype == torch.uint8:
+        if k_scale is None:
+            raise ValueError("uint8 K/V is packed E2M1 and needs k_scale / v_scale")
+        return KV_E2M1X2
+    raise ValueError(f"unsupported K/V dtype {k.dtype} (bf16, float8_e4m3fn, or uint8 packed E2M1)")
+
+
+def _strides(t: Optional[torch.Tensor], paged: bool) -> Strides:
+    if t is None:
+        return Strides(0, 0, 0)
+    es = t.element_size()
+    if t.stride(-1) != 1:
+        raise MsaError(5, "the last dimension must be contiguous (views are never copied)")
+    if paged:
+        if t.dim() != 4 or t.shape[2] != BLOCK:
+            raise ValueError(f"paged K/V must be (num_pages, num_kv_heads, 128, d'), got {tuple(t.shape)}")
+        return Strides(t.stride(0) * es, t.stride(1) * es, t.stride(2) * es)
+    if t.dim() != 3:
+        raise ValueError(f"flat K/V must be (total_k, num_kv_heads, d'), got {tuple(t.shape)}")
+    return Strides(0, t.stride(1) * es, t.stride(0) * es)
+
+
+def _host_max_seqlen(cu: torch.Tensor) -> int:
+    c = cu.to("cpu", torch.int64)
+    return int((c[1:] - c[:-1]).max()) if c.numel() > 1 else 0
+
+
+def _host_max_tiles(cu_k, seqused_k) -> int:
+    if seqused_k is not None:
+        L = int(seqused_k.max().item()) if seqused_k.numel() else 0
+    else:
+        L = _host_max_seqlen(cu_k)
+    return (L + BLOCK - 1) // BLOCK
+
+
+class Workspace:
+    """Caller-owned split-KV workspace (partials + completion counters).
+
+    Zeroed once at creation; each launch leaves its counters at zero, so it is
+    reused across launches on one stream.  Launches that may overlap need
+    separate workspaces."""
+
+    def __init__(self, nbytes: int, device):
+        self.nbytes = int(nbytes)
+        self.buffer = torch.zeros(max(self.nbytes, 256) + 256, dtype=torch.uint8, device=device)
+        off = (-self.buffer.data_ptr()) % 256
+        self.view = self.buffer[off:off + max(self.nbytes, 256)]
+
+    def ensure(self, nbytes: int) -> "Workspace":
+        return self if nbytes <= self.nbytes else Workspace(nbytes, self.buffer.device)
+
+
+_ws_cache: dict = {}
+
+
+def _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, causal, softmax_scale,
+               page_table, seqused_k, k_scale, v_scale, k_global_scale, v_global_scale,
+               max_seqlen_q, max_k_tiles, out, lse, splits):
+    paged = page_table is not None
+    fmt = _kv_format(k, k_scale)
+    a = AttnArgs()
+    a.batch = cu_seqlens_q.numel() - 1
+    a.total_q = q.shape[0]
+    a.num_qo_heads = q.shape[1]
+    a.num_kv_heads = k.shape[1]
+    a.head_dim = q.shape[2]
+    a.topk = q2k_indices.shape[2]
+    a.max_seqlen_q = _host_max_seqlen(cu_seqlens_q) if max_seqlen_q is None else int(max_seqlen_q)
+    a.max_k_tiles = _host_max_tiles(cu_seqlens_k, seqused_k) if max_k_tiles is None else int(max_k_tiles)
+    a.page_table_width = page_table.shape[1] if paged else 0
+    a.causal = 1 if causal else 0
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.k_global_scale = 0.0 if k_global_scale is None else float(k_global_scale)
+    a.v_global_scale = 0.0 if v_global_scale is None else float(v_global_scale)
+    a.kv_dtype = fmt
+    a.splits = int(splits)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.k_scale, a.v_scale = _ptr(k_scale), _ptr(v_scale)
+    a.k_strides = _strides(k, paged)
+    a.v_strides = _strides(v, paged)
+    a.k_scale_strides = _strides(k_scale, paged) if k_scale is not None else Strides(0, 0, 0)
+    a.v_scale_strides = _strides(v_scale, paged) if v_scale is not None else Strides(0, 0, 0)
+    a.q2k = _ptr(q2k_indices)
+    a.cu_seqlens_q = _ptr(cu_seqlens_q)
+    a.cu_seqlens_k = _ptr(cu_seqlens_k)
+    a.page_table = _ptr(page_table)
+    a.seqused_k = _ptr(seqused_k)
+    a.out = _ptr(out)
+    a.lse = _ptr(lse)
+    return a
+
+
+def _check_i32(name, t):
+    if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous int32 tensor")
+
+
+def workspace_size(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None,
+                   seqused_k=None, k_scale=None, v_scale=None, max_seqlen_q=None,
+                   max_k_tiles=None, splits=0) -> int:
+    a = _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, False, None, page_table,
+                   seqused_k, k_scale, v_scale, None, None, max_seqlen_q, max_k_tiles, None,
+                   None, splits)
+    n = ctypes.c_size_t(0)
+    _check(lib.msa_sparse_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)))
+    return int(n.value)
+
+
+def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, causal=False,
+                     softmax_scale=None, page_table=None, seqused_k=None,
+                     return_softmax_lse=False, k_scale=None, v_scale=None,
+                     k_global_scale=None, v_global_scale=None, *, max_seqlen_q=None,
+                     max_k_tiles=None, workspace: Optional[Workspace] = None, out=None,
+                     lse=None, splits=0):
+    """MSA forward (msa_sparse_attention page).  Returns out, or (out, lse)."""
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 tensor (total_q, num_qo_heads, 128)")
+    for name, t in (("q2k_indices", q2k_indices), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k), ("page_table", page_table),
+                    ("seqused_k", seqused_k)):
+        _check_i32(name, t)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_softmax_lse:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    a = _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, causal, softmax_scale,
+                   page_table, seqused_k, k_scale, v_scale, k_global_scale, v_global_scale,
+                   max_seqlen_q, max_k_tiles, out, lse, splits)
+    need = ctypes.c_size_t(0)
+    _check(lib.msa_sparse_attention_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    ws_ptr, ws_bytes = None, 0
+    if need.value:
+        if workspace is None:
+            key = (q.device, torch.cuda.current_stream().cuda_stream)
+            ws = _ws_cache.get(key)
+            ws = Workspace(need.value, q.device) if ws is None else ws.ensure(need.value)
+            _ws_cache[key] = ws
+            workspace = ws
+        elif workspace.nbytes < need.value:
+            raise MsaError(6, f"workspace of {need.value} bytes needed, got {workspace.nbytes}")
+        ws_ptr, ws_bytes = _ptr(workspace.view), workspace.nbytes
+    _check(lib.msa_sparse_attention(ctypes.byref(a), ws_ptr, ws_bytes, _stream()))
+    return (out, lse) if return_softmax_lse else out
+
+
+def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, seqused_k=None,
+                causal=True, max_seqlen_q=None, max_k_tiles=None, output=None,
+                reduce_heads=False):
+    """Stage-1 block max of unscaled masked QK^T (msa_proxy_score page).
+    Returns fp32 (num_qo_heads or 1, max_k_tiles, total_q)."""
+    if q.dtype != torch.bfloat16 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 tensor (total_q, num_qo_heads, 128)")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
+                    ("page_table", page_table), ("seqused_k", seqused_k)):
+        _check_i32(name, t)
+    paged = page_table is not None
+    if k.dtype == torch.bfloat16:
+        fmt = KV_BF16
+    elif k.dtype == torch.float8_e4m3fn:
+        fmt = KV_FP8_E4M3
+    else:
+        raise ValueError(f"proxy K must be bf16 or float8_e4m3fn, got {k.dtype}")
+    T = _host_max_tiles(cu_seqlens_k, seqused_k) if max_k_tiles is None else int(max_k_tiles)
+    H = 1 if reduce_heads else q.shape[1]
+    if output is None:
+        output = torch.empty(H, T, q.shape[0], dtype=torch.float32, device=q.device)
+    elif (output.shape != (H, T, q.shape[0]) or output.dtype != torch.float32
+          or not output.is_contiguous()):
+        raise ValueError(f"output must be contiguous fp32 {(H, T, q.shape[0])}")
+    a = ProxyArgs()
+    a.batch = cu_seqlens_q.numel() - 1
+    a.total_q = q.shape[0]
+    a.num_qo_heads = q.shape[1]
+    a.num_kv_heads = k.shape[1]
+    a.head_dim = q.shape[2]
+    a.max_seqlen_q = _host_max_seqlen(cu_seqlens_q) if max_seqlen_q is None else int(max_seqlen_q)
+    a.max_k_tiles = T
+    a.page_table_width = page_table.shape[1] if paged else 0
+    a.causal = 1 if causal else 0
+    a.kv_dtype = fmt
+    a.reduce_heads = 1 if reduce_heads else 0
+    a.q, a.k = _ptr(q), _ptr(k)
+    a.k_strides = _strides(k, paged)
+    a.cu_seqlens_q = _ptr(cu_seqlens_q)
+    a.cu_seqlens_k = _ptr(cu_seqlens_k)
+    a.page_table = _ptr(page_table)
+    a.seqused_k = _ptr(seqused_k)
+    a.out = _ptr(output)
+    _check(lib.msa_proxy_score(ctypes.byref(a), _stream()))
+    return output
+
+
+def topk_select(max_score, topk, num_kv_heads, mode=None, out=None):
+    """Top-K block select: fp32 (H_s, T, total_q) -> int32 q2k (Hkv, total_q, topk).
+    mode None picks ALL for H_s == 1 and NONE for H_s == num_kv_heads."""
+    if max_score.dtype != torch.float32 or not max_score.is_contiguous():
+        raise ValueError("max_score must be a contiguous fp32 tensor")
+    hs, T, total_q = max_score.shape
+    if mode is None:
+        mode = REDUCE_ALL if hs == 1 else (REDUCE_NONE if hs == num_kv_heads else REDUCE_GROUP)
+    if out is None:
+        out = torch.empty(num_kv_heads, total_q, topk, dtype=torch.int32, device=max_score.device)
+    _check(lib.msa_topk_select(_ptr(max_score), hs, T, total_q, int(topk), int(num_kv_heads),
+                               int(mode), _ptr(out), _stream()))
+    return out
+
+
+def tile_union(q2k, cu_seqlens_q, lengths_k, tile_tokens, max_k_tiles, max_seqlen_q=None,
+               max_union=None):
+    """The attention kernel's per-tile union, exported for checking.  Returns
+    (blocks int32, masks uint64-as-int64, counts int32) shaped
+    (Hkv, B, tiles_per_req, max_union) / (Hkv, B, tiles_per_req)."""
+    _check_i32("q2k", q2k)
+    _check_i32("cu_seqlens_q", cu_seqlens_q)
+    _check_i32("lengths_k", lengths_k)
+    hkv, total_q, topk = q2k.shape
+    B = cu_seqlens_q.numel() - 1
+    mq = _host_max_seqlen(cu_seqlens_q) if max_seqlen_q is None else int(max_seqlen_q)
+    tiles = (mq + tile_tokens - 1) // tile_tokens
+    mu = min(tile_tokens * topk, max_k_tiles) if max_union is None else int(max_union)
+    mu = max(mu, 1)
+    blocks = torch.empty(hkv, B, tiles, mu, dtype=torch.int32, device=q2k.device)
+    masks = torch.empty(hkv, B, tiles, mu, dtype=torch.int64, device=q2k.device)
+    counts = torch.empty(hkv, B, tiles, dtype=torch.int32, device=q2k.device)
+    _check(lib.msa_tile_union(_ptr(q2k), _ptr(cu_seqlens_q), _ptr(lengths_k), B, total_q, hkv,
+                              topk, mq, int(max_k_tiles), int(tile_tokens), mu, _ptr(blocks),
+                              _ptr(masks), _ptr(counts), _stream()))
+    return blocks, masks, counts

@@ -1,0 +1,390 @@
+// C ABI of the MSA library: host-side validation, launch planning and
+// dispatch.  No device memory is allocated and the host never waits on the
+// device; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/msa.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+msa_status_t fail(msa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+msa_status_t ok() {
+  g_last_error[0] = '\0';
+  return MSA_OK;
+}
+
+msa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Resolve a stride triple for a tensor with `row_bytes` contiguous bytes per
+// token row.  Dense layout for zeros.  Rejects unaligned views.
+msa_status_t resolve_strides(const char* name, const msa_strides_t& in, bool paged, int hkv,
+                             int64_t row_bytes, int64_t align, msa::Strides* out) {
+  msa::Strides s;
+  s.token = in.token ? in.token : row_bytes;
+  if (paged) {
+    s.head = in.head ? in.head : (int64_t)128 * s.token;
+    s.page = in.page ? in.page : (int64_t)hkv * s.head;
+  } else {
+    s.head = in.head ? in.head : row_bytes;
+    s.token = in.token ? in.token : (int64_t)hkv * row_bytes;
+    s.page = 0;
+  }
+  if (s.token < row_bytes || s.token % align || s.head % align || s.page % align || s.head < 0 ||
+      s.page < 0)
+    return fail(MSA_ERR_UNSUPPORTED,
+                "%s: strides (page %lld, head %lld, token %lld bytes) are not a readable view "
+                "(rows of %lld contiguous bytes, %lld-byte aligned); views are never copied",
+                name, (long long)s.page, (long long)s.head, (long long)s.token,
+                (long long)row_bytes, (long long)align);
+  *out = s;
+  return MSA_OK;
+}
+
+int kv_row_bytes(int fmt) { return fmt == MSA_KV_BF16 ? 256 : (fmt == MSA_KV_FP8_E4M3 ? 128 : 64); }
+
+struct Resolved {
+  msa::AttnParams p;
+  msa::AttnPlan plan;
+  size_t ws_bytes;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r) {
+  if (!a) return fail(MSA_ERR_NULL, "args is NULL");
+  if (a->batch < 0 || a->total_q < 0)
+    return fail(MSA_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", a->batch, a->total_q);
+  if (a->head_dim != 128) return fail(MSA_ERR_SHAPE, "head_dim must be 128 (got %d)", a->head_dim);
+  if (a->num_qo_heads <= 0 || a->num_kv_heads <= 0 || a->num_qo_heads % a->num_kv_heads)
+    return fail(MSA_ERR_SHAPE, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_qo_heads, a->num_kv_heads);
+  if (a->topk < 1 || a->topk > msa::kMaxTopk)
+    return fail(MSA_ERR_SHAPE, "topk must be in [1, %d] (got %d)", msa::kMaxTopk, a->topk);
+  if (a->max_seqlen_q < 0 || a->max_k_tiles < 0)
+    return fail(MSA_ERR_SHAPE, "max_seqlen_q and max_k_tiles must be >= 0");
+  if (a->max_k_tiles > msa::kMaxBitmapWords * 32)
+    return fail(MSA_ERR_SHAPE, "max_k_tiles %d exceeds %d blocks", a->max_k_tiles,
+                msa::kMaxBitmapWords * 32);
+  if (a->kv_dtype < MSA_KV_BF16 || a->kv_dtype > MSA_KV_E2M1X2)
+    return fail(MSA_ERR_DTYPE, "unknown kv_dtype %d", a->kv_dtype);
+  const bool paged = a->page_table != nullptr;
+  if (paged) {
+    if (a->cu_seqlens_k && a->seqused_k)
+      return fail(MSA_ERR_CONFLICT,
+                  "paged route: both cu_seqlens_k and seqused_k were given; seqused_k is the "
+                  "only source of KV lengths and the call is declined rather than choosing one");
+    if (!a->seqused_k) return fail(MSA_ERR_NULL, "paged route needs seqused_k");
+    if (a->page_table_width < a->max_k_tiles || a->page_table_width <= 0)
+      return fail(MSA_ERR_SHAPE, "page_table_width (%d) must be >= max_k_tiles (%d) and > 0",
+                  a->page_table_width, a->max_k_tiles);
+  } else {
+    if (!a->cu_seqlens_k) return fail(MSA_ERR_NULL, "flat route needs cu_seqlens_k");
+    if (a->kv_dtype == MSA_KV_E2M1X2)
+      return fail(MSA_ERR_UNSUPPORTED, "packed E2M1 K/V is read from the paged layout only");
+  }
+  if (a->kv_dtype == MSA_KV_E2M1X2 && (!a->k_scale || !a->v_scale))
+    return fail(MSA_ERR_NULL, "packed E2M1 K/V needs k_scale and v_scale");
+  if (a->kv_dtype != MSA_KV_E2M1X2 && (a->k_scale || a->v_scale))
+    return fail(MSA_ERR_UNSUPPORTED, "k_scale/v_scale are only read with packed E2M1 K/V");
+  if (a->total_q > 0 && a->batch > 0) {
+    if (!a->q || !a->k || !a->v || !a->q2k || !a->cu_seqlens_q || !a->out)
+      return fail(MSA_ERR_NULL, "q, k, v, q2k, cu_seqlens_q and out must be non-NULL");
+    if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->k, 16) || !aligned(a->v, 16))
+      return fail(MSA_ERR_UNSUPPORTED, "q, k, v and out must be 16-byte aligned");
+  }
+
+  msa::AttnParams& p = r->p;
+  std::memset(&p, 0, sizeof(p));
+  const int fmt = a->kv_dtype;
+  const int rb = kv_row_bytes(fmt);
+  msa_status_t st;
+  if ((st = resolve_strides("k", a->k_strides, paged, a->num_kv_heads, rb, 16, &p.k_st))) return st;
+  if ((st = resolve_strides("v", a->v_strides, paged, a->num_kv_heads, rb, 16, &p.v_st))) return st;
+  if (fmt == MSA_KV_E2M1X2) {
+    if ((st = resolve_strides("k_scale", a->k_scale_strides, paged, a->num_kv_heads, 8, 8, &p.ks_st)))
+      return st;
+    if ((st = resolve_strides("v_scale", a->v_scale_strides, paged, a->num_kv_heads, 8, 8, &p.vs_st)))
+      return st;
+    if (!aligned(a->k_scale, 8) || !aligned(a->v_scale, 8))
+      return fail(MSA_ERR_UNSUPPORTED, "k_scale/v_scale must be 8-byte aligned");
+  }
+
+  const int G = a->num_qo_heads / a->num_kv_heads;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint8_t*>(a->k);
+  p.v = static_cast<const uint8_t*>(a->v);
+  p.ks = static_cast<const uint8_t*>(a->k_scale);
+  p.vs = static_cast<const uint8_t*>(a->v_scale);
+  p.q2k = a->q2k;
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.page_table = a->page_table;
+  p.seqused_k = a->seqused_k;
+  p.pt_width = a->page_table_width;
+  p.paged = paged;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.lse = a->lse;
+  p.batch = a->batch;
+  p.total_q = a->total_q;
+  p.hq = a->num_qo_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = G;
+  p.topk = a->topk;
+  p.causal = a->causal ? 1 : 0;
+  p.max_k_tiles = a->max_k_tiles;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / std::sqrt(128.0f);
+  const float kgs = a->k_global_scale > 0.f ? a->k_global_scale : 1.0f;
+  p.scale_log2 = scale * kgs * 1.4426950408889634f;
+  p.v_gs = a->v_global_scale > 0.f ? a->v_global_scale : 1.0f;
+
+  // ---- plan ----
+  msa::AttnPlan& plan = r->plan;
+  const int lqmax = std::max(1, a->max_seqlen_q);
+  const int rows_req = lqmax * G;
+  if (rows_req <= 64) {
+    // decode shape: one tile per request, 4 waves split every block's keys
+    plan.decode = 1;
+    plan.tok_per_tile = lqmax;
+    const int slots = (rows_req + 15) / 16;
+    plan.spw = slots <= 1 ? 1 : (slots <= 2 ? 2 : 4);
+    const int units = std::max(1, a->batch * a->num_kv_heads);
+    const int union_max = std::min(lqmax * a->topk, std::max(1, a->max_k_tiles));
+    int splits;
+    if (a->splits > 0) {
+      splits = a->splits;
+    } else {
+      // fill ~2 workgroups per CU (256 CUs) with at least 2 blocks per split
+      splits = std::max(1, std::min((512 + units - 1) / units, union_max / 2));
+      splits = std::min(splits, 16);
+    }
+    plan.splits = std::max(1, std::min(splits, 64));
+  } else {
+    plan.decode = 0;
+    plan.spw = 2;
+    // 4 waves x 2 slots x 16 rows = 128 rows per tile
+    plan.tok_per_tile = std::max(1, std::min(64, 128 / G));
+    plan.splits = 1;
+  }
+  if (plan.tok_per_tile * a->topk > msa::kMaxUnion) {
+    if (plan.decode)
+      return fail(MSA_ERR_SHAPE, "seqlen_q (%d) x topk (%d) exceeds the %d-entry tile union",
+                  lqmax, a->topk, msa::kMaxUnion);
+    plan.tok_per_tile = std::max(1, msa::kMaxUnion / a->topk);
+  }
+  p.tok_per_tile = plan.tok_per_tile;
+  p.tiles_per_req = (lqmax + plan.tok_per_tile - 1) / plan.tok_per_tile;
+  p.splits = plan.splits;
+
+  r->ws_bytes = 0;
+  if (plan.splits > 1) {
+    const int rows = plan.tok_per_tile * G;
+    const int rows_pad = (rows + 31) / 32 * 32;
+    const size_t units = (size_t)a->batch * a->num_kv_heads * p.tiles_per_req;
+    const size_t o_bytes = units * plan.splits * rows * 128 * sizeof(float);
+    const size_t l_bytes = units * plan.splits * rows_pad * sizeof(float);
+    const size_t c_bytes = units * sizeof(uint32_t);
+    p.ws_rows = rows;
+    p.ws_lse_rows = rows_pad;
+    r->ws_bytes = round_up(o_bytes, 256) + round_up(l_bytes, 256) + round_up(c_bytes, 256);
+  }
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* msa_status_string(msa_status_t s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_NULL: return "MSA_ERR_NULL";
+    case MSA_ERR_SHAPE: return "MSA_ERR_SHAPE";
+    case MSA_ERR_DTYPE: return "MSA_ERR_DTYPE";
+    case MSA_ERR_CONFLICT: return "MSA_ERR_CONFLICT";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error(void) { return g_last_error; }
+
+const char* msa_version(void) { return "0.1.0"; }
+
+msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args, size_t* bytes) {
+  if (!bytes) return fail(MSA_ERR_NULL, "bytes is NULL");
+  Resolved r;
+  msa_status_t st = resolve_attention(args, &r);
+  if (st) return st;
+  *bytes = r.ws_bytes;
+  return ok();
+}
+
+msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Resolved r;
+  msa_status_t st = resolve_attention(args, &r);
+  if (st) return st;
+  if (r.ws_bytes) {
+    if (!workspace || workspace_bytes < r.ws_bytes)
+      return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", r.ws_bytes,
+                  workspace_bytes, workspace);
+    if (!aligned(workspace, 256)) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const int rows = r.p.ws_rows;
+    const size_t units = (size_t)args->batch * args->num_kv_heads * r.p.tiles_per_req;
+    const size_t o_bytes = round_up(units * r.plan.splits * rows * 128 * sizeof(float), 256);
+    const size_t l_bytes = round_up(units * r.plan.splits * r.p.ws_lse_rows * sizeof(float), 256);
+    char* base = static_cast<char*>(workspace);
+    r.p.ws_o = reinterpret_cast<float*>(base);
+    r.p.ws_lse = reinterpret_cast<float*>(base + o_bytes);
+    r.p.ws_cnt = reinterpret_cast<uint32_t*>(base + o_bytes + l_bytes);
+  }
+  if (args->total_q == 0 || args->batch == 0) return ok();
+  return hip_status(msa::launch_attention(r.p, args->kv_dtype, r.plan,
+                                          static_cast<hipStream_t>(stream)),
+                    "msa_sparse_attention launch");
+}
+
+msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
+  if (!a) return fail(MSA_ERR_NULL, "args is NULL");
+  if (a->head_dim != 128) return fail(MSA_ERR_SHAPE, "head_dim must be 128 (got %d)", a->head_dim);
+  if (a->batch < 0 || a->total_q < 0 || a->max_k_tiles < 0 || a->max_seqlen_q < 0)
+    return fail(MSA_ERR_SHAPE, "sizes must be >= 0");
+  if (a->num_qo_heads <= 0 || a->num_kv_heads <= 0 || a->num_qo_heads % a->num_kv_heads)
+    return fail(MSA_ERR_SHAPE, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_qo_heads, a->num_kv_heads);
+  if (a->kv_dtype != MSA_KV_BF16 && a->kv_dtype != MSA_KV_FP8_E4M3)
+    return fail(MSA_ERR_DTYPE, "proxy K must be bf16 or fp8 E4M3 (got kv_dtype %d)", a->kv_dtype);
+  const bool paged = a->page_table != nullptr;
+  if (paged) {
+    if (!a->seqused_k) return fail(MSA_ERR_NULL, "paged K needs page_table and seqused_k together");
+    if (a->cu_seqlens_k)
+      return fail(MSA_ERR_CONFLICT, "paged K takes seqused_k; cu_seqlens_k must be NULL");
+    if (a->page_table_width < a->max_k_tiles || a->page_table_width <= 0)
+      return fail(MSA_ERR_SHAPE, "page_table_width (%d) must be >= max_k_tiles (%d) and > 0",
+                  a->page_table_width, a->max_k_tiles);
+  } else if (!a->cu_seqlens_k) {
+    return fail(MSA_ERR_NULL, "flat K needs cu_seqlens_k");
+  } else if (a->seqused_k) {
+    return fail(MSA_ERR_UNSUPPORTED, "seqused_k is read only with a page_table");
+  }
+  if (a->total_q == 0 || a->batch == 0 || a->max_k_tiles == 0) return ok();
+  if (!a->q || !a->k || !a->cu_seqlens_q || !a->out)
+    return fail(MSA_ERR_NULL, "q, k, cu_seqlens_q and out must be non-NULL");
+  if (!aligned(a->q, 16) || !aligned(a->k, 16))
+    return fail(MSA_ERR_UNSUPPORTED, "q and k must be 16-byte aligned");
+  msa::ProxyParams p;
+  std::memset(&p, 0, sizeof(p));
+  msa_status_t st;
+  const int rb = kv_row_bytes(a->kv_dtype);
+  if ((st = resolve_strides("k", a->k_strides, paged, a->num_kv_heads, rb, 16, &p.k_st))) return st;
+  const int G = a->num_qo_heads / a->num_kv_heads;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint8_t*>(a->k);
+  p.cu_q = a->cu_seqlens_q;
+  p.cu_k = a->cu_seqlens_k;
+  p.page_table = a->page_table;
+  p.seqused_k = a->seqused_k;
+  p.pt_width = a->page_table_width;
+  p.paged = paged;
+  p.out = a->out;
+  p.batch = a->batch;
+  p.total_q = a->total_q;
+  p.hq = a->num_qo_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = G;
+  p.causal = a->causal ? 1 : 0;
+  p.reduce = a->reduce_heads ? 1 : 0;
+  p.max_k_tiles = a->max_k_tiles;
+  const int lqmax = std::max(1, a->max_seqlen_q);
+  const int rows = lqmax * G;
+  const int wide = rows > 64;
+  p.rows_per_tile = wide ? 256 : 64;
+  p.row_tiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
+  // aim for >= ~2048 workgroups; at least 4 blocks per workgroup
+  const int base = std::max(1, a->batch * a->num_kv_heads * p.row_tiles);
+  int chunks = std::max(1, (2048 + base - 1) / base);
+  int bpw = std::max(4, (a->max_k_tiles + chunks - 1) / chunks);
+  p.blocks_per_wg = bpw;
+  p.block_chunks = (a->max_k_tiles + bpw - 1) / bpw;
+  return hip_status(msa::launch_proxy(p, a->kv_dtype == MSA_KV_FP8_E4M3 ? msa::kFmtFp8 : msa::kFmtBf16,
+                                      wide, static_cast<hipStream_t>(stream)),
+                    "msa_proxy_score launch");
+}
+
+msa_status_t msa_topk_select(const float* scores, int32_t score_heads, int32_t max_k_tiles,
+                             int32_t total_q, int32_t topk, int32_t num_kv_heads, int32_t mode,
+                             int32_t* q2k, void* stream) {
+  if (topk < 1 || topk > msa::kMaxTopk)
+    return fail(MSA_ERR_SHAPE, "topk must be in [1, %d] (got %d)", msa::kMaxTopk, topk);
+  if (score_heads <= 0 || num_kv_heads <= 0 || total_q < 0 || max_k_tiles < 0)
+    return fail(MSA_ERR_SHAPE, "bad sizes (score_heads %d, num_kv_heads %d, total_q %d, T %d)",
+                score_heads, num_kv_heads, total_q, max_k_tiles);
+  if (max_k_tiles > 4096)
+    return fail(MSA_ERR_UNSUPPORTED, "top-K select reads at most 4096 blocks per row (got %d)",
+                max_k_tiles);
+  if (mode == MSA_REDUCE_NONE && score_heads != num_kv_heads)
+    return fail(MSA_ERR_SHAPE, "mode NONE needs score_heads == num_kv_heads (%d vs %d)",
+                score_heads, num_kv_heads);
+  if (mode == MSA_REDUCE_GROUP && score_heads % num_kv_heads)
+    return fail(MSA_ERR_SHAPE, "mode GROUP needs score_heads %% num_kv_heads == 0");
+  if (mode < MSA_REDUCE_NONE || mode > MSA_REDUCE_GROUP)
+    return fail(MSA_ERR_UNSUPPORTED, "unknown reduce mode %d", mode);
+  if (total_q == 0) return ok();
+  if (!scores || !q2k) return fail(MSA_ERR_NULL, "scores and q2k must be non-NULL");
+  return hip_status(msa::launch_topk(scores, score_heads, max_k_tiles, total_q, topk, num_kv_heads,
+                                     mode, q2k, static_cast<hipStream_t>(stream)),
+                    "msa_topk_select launch");
+}
+
+msa_status_t msa_tile_union(const int32_t* q2k, const int32_t* cu_seqlens_q,
+                            const int32_t* lengths_k, int32_t batch, int32_t total_q,
+                            int32_t num_kv_heads, int32_t topk, int32_t max_seqlen_q,
+                            int32_t max_k_tiles, int32_t tile_tokens, int32_t max_union,
+                            int32_t* union_blocks, uint64_t* union_masks, int32_t* union_count,
+                            void* stream) {
+  if (tile_tokens < 1 || tile_tokens > 64)
+    return fail(MSA_ERR_SHAPE, "tile_tokens must be in [1, 64] (got %d)", tile_tokens);
+  if (topk < 1 || topk > msa::kMaxTopk) return fail(MSA_ERR_SHAPE, "topk must be in [1, 64]");
+  if (max_k_tiles < 0 || max_k_tiles > msa::kMaxBitmapWords * 32)
+    return fail(MSA_ERR_SHAPE, "max_k_tiles must be in [0, %d]", msa::kMaxBitmapWords * 32);
+  if (tile_tokens * topk > msa::kMaxUnion)
+    return fail(MSA_ERR_SHAPE, "tile_tokens x topk must be <= %d", msa::kMaxUnion);
+  if (max_union < std::min(tile_tokens * topk, max_k_tiles) || max_union > 1024)
+    return fail(MSA_ERR_SHAPE, "max_union (%d) must be >= min(tile_tokens*topk, max_k_tiles) and <= 1024",
+                max_union);
+  if (batch < 0 || total_q < 0 || num_kv_heads <= 0 || max_seqlen_q < 0)
+    return fail(MSA_ERR_SHAPE, "bad sizes");
+  if (batch == 0 || max_seqlen_q == 0) return ok();
+  if (!q2k || !cu_seqlens_q || !lengths_k || !union_blocks || !union_masks || !union_count)
+    return fail(MSA_ERR_NULL, "all pointers must be non-NULL");
+  return hip_status(msa::launch_tile_union(q2k, cu_seqlens_q, lengths_k, batch, total_q,
+                                           num_kv_heads, topk, max_seqlen_q, max_k_tiles,
+                                           tile_tokens, max_union, union_blocks, union_masks,
+                                           union_count, static_cast<hipStream_t>(stream)),
+                    "msa_tile_union launch");
+}
+
+}  // extern "C"

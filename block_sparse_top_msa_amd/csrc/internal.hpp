@@ -1,0 +1,91 @@
+// Internal launch interfaces between the C ABI layer (api.cpp) and the HIP
+// kernels.  Not installed; the public surface is include/msa.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+enum KvFmt : int { kFmtBf16 = 0, kFmtFp8 = 1, kFmtE2m1 = 2 };
+
+// Largest union a tile may hold (entries), and largest block-id bitmap.
+constexpr int kMaxUnion = 512;
+constexpr int kMaxBitmapWords = 512;   // block ids < 16384 (2M tokens)
+constexpr int kMaxTopk = 64;
+
+struct Strides {
+  int64_t page, head, token;  // bytes
+};
+
+struct AttnParams {
+  const uint16_t* q;          // bf16 [total_q, Hq, 128]
+  const uint8_t* k;
+  const uint8_t* v;
+  const uint8_t* ks;          // E2M1 block scales
+  const uint8_t* vs;
+  Strides k_st, v_st, ks_st, vs_st;
+  const int32_t* q2k;
+  const int32_t* cu_q;
+  const int32_t* cu_k;        // flat route
+  const int32_t* page_table;  // paged route
+  const int32_t* seqused_k;
+  int pt_width;
+  int paged;
+  uint16_t* out;
+  float* lse;                 // may be null
+  int batch, total_q, hq, hkv, group, topk, causal;
+  int max_k_tiles;            // bound on ceil(Lk / 128)
+  int tok_per_tile;           // query tokens per tile
+  int tiles_per_req;          // ceil(max_seqlen_q / tok_per_tile)
+  int splits;                 // split-KV partials per tile (1 = none)
+  float scale_log2;           // softmax_scale * k_global_scale * log2(e)
+  float v_gs;
+  float* ws_o;                // [units, splits, rows, 128] fp32
+  float* ws_lse;              // [units, splits, rows_pad]
+  uint32_t* ws_cnt;           // [units]
+  int ws_rows;                // rows per unit (tok_per_tile * group)
+  int ws_lse_rows;            // rows_pad: rows rounded up to 32
+};
+
+// Kernel family selection for one attention call.
+struct AttnPlan {
+  int decode;       // 1: key-split decode kernel; 0: slot-per-wave prefill kernel
+  int spw;          // 16-row slots per wave
+  int tok_per_tile;
+  int splits;
+};
+
+hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
+                            hipStream_t stream);
+
+struct ProxyParams {
+  const uint16_t* q;
+  const uint8_t* k;
+  Strides k_st;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* page_table;
+  const int32_t* seqused_k;
+  int pt_width, paged;
+  float* out;
+  int batch, total_q, hq, hkv, group, causal, reduce;
+  int max_k_tiles;
+  int rows_per_tile;          // query rows (token x head) per workgroup
+  int row_tiles;              // ceil(max_seqlen_q * group / rows_per_tile)
+  int blocks_per_wg;          // KV blocks per workgroup
+  int block_chunks;           // ceil(max_k_tiles / blocks_per_wg)
+};
+
+hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, int score_heads, int T, int total_q, int topk,
+                       int hkv, int mode, int32_t* q2k, hipStream_t stream);
+
+hipError_t launch_tile_union(const int32_t* q2k, const int32_t* cu_q, const int32_t* len_k,
+                             int batch, int total_q, int hkv, int topk, int max_seqlen_q,
+                             int max_k_tiles, int tile_tokens, int max_union,
+                             int32_t* ublocks, uint64_t* umasks, int32_t* ucount,
+                             hipStream_t stream);
+
+}  // namespace msa

@@ -1,0 +1,226 @@
+/*
+ * msa.h — C ABI of the MI355X (gfx950) MiniMax Sparse Attention hot path.
+ *
+ * The operations follow the MSA documentation pages:
+ *   msa_proxy_score       msa_proxy_score page (summary, Parameters, Returns)
+ *   msa_topk_select       the top-K block select that feeds q2k_indices
+ *                         (msa_proxy_score page, summary: "feeds directly into
+ *                         msa_topk_select"; msa_sparse_attention page,
+ *                         Parameters: q2k_indices)
+ *   msa_sparse_attention  msa_sparse_attention page (summary, Parameters,
+ *                         Returns); the paged decode route of
+ *                         prepare_msa_nvfp4_sparse_decode page (Parameters)
+ *   msa_tile_union        the per-tile union the attention builds internally
+ *                         (msa_sparse_attention page, summary), exported so it
+ *                         can be checked on its own
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is a DEVICE pointer.  The argument structs and the
+ *     integers in them are HOST memory, read during the call only.
+ *   - All buffers are caller-owned.  The library never allocates or frees
+ *     device memory and never synchronises with the host; it only enqueues
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream).
+ *   - Host-side validation runs before any HIP call.  A non-OK return
+ *     enqueues nothing; msa_last_error() then holds a message for the calling
+ *     thread.  MSA_ERR_HIP means a launch was rejected by the runtime.
+ *   - Device-side contents (sequence boundaries, indices, page ids) are
+ *     caller contracts and are not copied to the host for checking.
+ *   - head_dim is 128 and the KV block / page size is 128 tokens.
+ *   - Strides are in BYTES; a stride of 0 selects the dense layout.  The last
+ *     (head_dim) dimension must be contiguous and every row 16-byte aligned
+ *     (8-byte for E4M3 block-scale rows); other views are rejected with
+ *     MSA_ERR_UNSUPPORTED, never copied.
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_NULL = 1,        /* a required pointer is NULL                     */
+  MSA_ERR_SHAPE = 2,       /* sizes inconsistent or outside the envelope     */
+  MSA_ERR_DTYPE = 3,       /* unknown or unsupported storage format          */
+  MSA_ERR_CONFLICT = 4,    /* both cu_seqlens_k and seqused_k on the paged route */
+  MSA_ERR_UNSUPPORTED = 5, /* a view or option this library does not read   */
+  MSA_ERR_WORKSPACE = 6,   /* workspace missing or too small                 */
+  MSA_ERR_HIP = 7          /* the HIP runtime rejected a launch              */
+} msa_status_t;
+
+/* K/V storage formats (msa_sparse_attention page, Parameters: k). */
+typedef enum {
+  MSA_KV_BF16 = 0,      /* bf16 values                                        */
+  MSA_KV_FP8_E4M3 = 1,  /* OCP float8 E4M3FN bytes, upconverted in-kernel     */
+  MSA_KV_E2M1X2 = 2     /* packed E2M1, two per byte (element 2i = low nibble),
+                           with E4M3 block scales, one per 16 values          */
+} msa_kv_dtype_t;
+
+/* How score heads map to the per-KV-head selections of q2k_indices. */
+typedef enum {
+  MSA_REDUCE_NONE = 0,  /* one score head per KV head                         */
+  MSA_REDUCE_ALL = 1,   /* max over every score head; the one shared selection
+                           is written for every KV head (msa_proxy_score page,
+                           Parameters: reduce_heads)                          */
+  MSA_REDUCE_GROUP = 2  /* per-query-head scores; max over the G = Hq/Hkv heads
+                           of each KV head (per-group analogue of reduce_heads) */
+} msa_reduce_t;
+
+/* Byte strides of a K/V (or block-scale) tensor.  Flat layout
+ * (total_k, Hkv, d'): `token` and `head` are used, `page` is ignored.  Paged
+ * layout (num_pages, Hkv, 128, d'): all three are used.  0 = dense. */
+typedef struct {
+  int64_t page;
+  int64_t head;
+  int64_t token;
+} msa_strides_t;
+
+/* ------------------------------------------------------------------------ */
+/* Sparse attention                                                          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  /* host integers */
+  int32_t batch;          /* B                                                */
+  int32_t total_q;        /* rows of q                                        */
+  int32_t num_qo_heads;   /* Hq                                               */
+  int32_t num_kv_heads;   /* Hkv; Hq % Hkv == 0 (query head h reads KV head
+                             h / (Hq / Hkv))                                   */
+  int32_t head_dim;       /* must be 128                                      */
+  int32_t topk;           /* width of q2k_indices rows, 1..64                 */
+  int32_t max_seqlen_q;   /* >= every per-request query length               */
+  int32_t max_k_tiles;    /* >= every ceil(Lk / 128); paged: <= page_table_width */
+  int32_t page_table_width; /* paged: columns of page_table                   */
+  int32_t causal;         /* 1: right-aligned causal mask, query i of a request
+                             sits at KV position Lk - Lq + i                  */
+  float softmax_scale;    /* <= 0 selects head_dim^-0.5                       */
+  float k_global_scale;   /* <= 0 selects 1; folds into the softmax scale     */
+  float v_global_scale;   /* <= 0 selects 1; multiplies the output            */
+  int32_t kv_dtype;       /* msa_kv_dtype_t                                   */
+  int32_t splits;         /* 0: library choice; > 0 forces that many split-KV
+                             partials per (request, KV head) on the decode
+                             route; ignored on the prefill route              */
+  /* device tensors */
+  const void* q;          /* bf16 [total_q, Hq, 128], contiguous              */
+  const void* k;          /* flat [total_k, Hkv, d'] or paged [pages, Hkv, 128, d'];
+                             d' = 128 (bf16, fp8) or 64 bytes (E2M1)          */
+  const void* v;          /* same layout rules as k                           */
+  const void* k_scale;    /* E2M1 only: E4M3 bytes [pages, Hkv, 128, 8]       */
+  const void* v_scale;    /* E2M1 only: same, stored linearly                 */
+  msa_strides_t k_strides, v_strides, k_scale_strides, v_scale_strides;
+  const int32_t* q2k;     /* [Hkv, total_q, topk] block ids, ascending, -1 padded */
+  const int32_t* cu_seqlens_q; /* [B + 1]                                     */
+  const int32_t* cu_seqlens_k; /* flat route: [B + 1]; must be NULL when paged */
+  const int32_t* page_table;   /* paged route: [B, page_table_width]          */
+  const int32_t* seqused_k;    /* paged route: [B] valid KV tokens per request */
+  void* out;              /* bf16 [total_q, Hq, 128], written                 */
+  float* lse;             /* NULL or fp32 [total_q, Hq], natural log, written;
+                             -inf for a row with no attended key (out = 0)    */
+} msa_attn_args_t;
+
+/* Bytes of workspace msa_sparse_attention needs for these arguments (split-KV
+ * partials and completion counters; prepare_msa_nvfp4_sparse_decode page,
+ * Parameters: workspace_buffer).  0 when the call runs without splitting.
+ * The workspace must be zeroed once before first use; each launch leaves its
+ * counters at zero again, so it can be reused by later launches on the same
+ * stream but must not be shared by launches that may run concurrently. */
+msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args,
+                                                 size_t* bytes);
+
+/* Forward sparse attention (msa_sparse_attention page).  Each query token,
+ * per KV head, attends only to the 128-token KV blocks listed in its q2k row;
+ * query tiles run one online softmax over the union of their tokens' blocks
+ * and write out (and lse) directly, or through split-KV partials merged by
+ * LSE on the decode route.  q2k entries outside [0, ceil(Lk/128)) and -1 are
+ * ignored; rows must be ascending without duplicates (caller contract).
+ * `workspace` may be NULL when the size query returned 0. */
+msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Proxy score (stage 1)                                                     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t batch, total_q, num_qo_heads, num_kv_heads, head_dim;
+  int32_t max_seqlen_q;   /* >= every per-request query length               */
+  int32_t max_k_tiles;    /* columns t of the output                          */
+  int32_t page_table_width;
+  int32_t causal;         /* right-aligned, applied before the block max      */
+  int32_t kv_dtype;       /* MSA_KV_BF16 or MSA_KV_FP8_E4M3                   */
+  int32_t reduce_heads;   /* 1: max over query heads, output (1, T, total_q)  */
+  const void* q;          /* bf16 [total_q, Hq, 128] (the proxy Q)            */
+  const void* k;          /* flat [total_k, Hkv, 128] or paged [pages, Hkv, 128, 128] */
+  msa_strides_t k_strides;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;   /* flat route                               */
+  const int32_t* page_table;     /* paged route, with seqused_k              */
+  const int32_t* seqused_k;
+  float* out;             /* fp32 [Hq or 1, max_k_tiles, total_q], written in full */
+} msa_proxy_args_t;
+
+/* max_score[h, t, i]: the max over the keys of block t of the UNSCALED dot
+ * products q[i, h] . k[j, h / G], after the causal mask; -inf where no key of
+ * the block is visible or the block is past the sequence (msa_proxy_score
+ * page, summary).  With reduce_heads the max over h is taken in-kernel. */
+msa_status_t msa_proxy_score(const msa_proxy_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Top-K block select                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* scores: fp32 [score_heads, max_k_tiles, total_q].  Writes q2k int32
+ * [num_kv_heads, total_q, topk]: per (KV head, query) the `topk` blocks with
+ * the largest finite score (equal scores, with -0 == +0, go to the lower block
+ * id), ascending, -1 padded.  -inf and NaN scores are never selected.
+ * mode: MSA_REDUCE_NONE needs score_heads == num_kv_heads; MSA_REDUCE_ALL
+ * takes the max over all score heads and writes the shared selection to every
+ * KV head; MSA_REDUCE_GROUP needs score_heads % num_kv_heads == 0. */
+msa_status_t msa_topk_select(const float* scores, int32_t score_heads,
+                             int32_t max_k_tiles, int32_t total_q, int32_t topk,
+                             int32_t num_kv_heads, int32_t mode, int32_t* q2k,
+                             void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Tile union (the attention kernel's own builder, exported for checking)    */
+/* ------------------------------------------------------------------------ */
+
+/* For every tile of `tile_tokens` consecutive query tokens of one request and
+ * one KV head (tiles never cross requests; tile j of request b covers local
+ * queries [j * tile_tokens, ...)), writes the ascending union of the valid
+ * selected blocks (0 <= id < n_blocks_b, n_blocks_b = ceil(Lk_b / 128)) and,
+ * per union entry, the bit mask of tile tokens that selected it.
+ *   q2k          [Hkv, total_q, topk]
+ *   cu_seqlens_q [B + 1]; lengths_k [B] KV tokens per request
+ *   union_blocks int32  [Hkv, B, tiles_per_req, max_union], -1 padded
+ *   union_masks  uint64 [Hkv, B, tiles_per_req, max_union], 0 padded
+ *   union_count  int32  [Hkv, B, tiles_per_req]
+ * tiles_per_req = ceil(max_seqlen_q / tile_tokens); tile_tokens in 1..64;
+ * max_union >= min(tile_tokens * topk, max_k_tiles) and <= 1024. */
+msa_status_t msa_tile_union(const int32_t* q2k, const int32_t* cu_seqlens_q,
+                            const int32_t* lengths_k, int32_t batch,
+                            int32_t total_q, int32_t num_kv_heads, int32_t topk,
+                            int32_t max_seqlen_q, int32_t max_k_tiles,
+                            int32_t tile_tokens, int32_t max_union,
+                            int32_t* union_blocks, uint64_t* union_masks,
+                            int32_t* union_count, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+
+const char* msa_status_string(msa_status_t status);
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* msa_last_error(void);
+/* Library version, e.g. "0.1.0". */
+const char* msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H_ */

@@ -1,0 +1,151 @@
+"""C-ABI boundary checks that run without a GPU.
+
+The library must load, export every function include/msa.h declares, and
+reject bad arguments on the host before any HIP call (every case below stops
+in validation, so no device is touched).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_top_msa_amd as msa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # never dereferenced: validation fails before any launch
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "msa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared_functions()
+    assert len(names) == 8, names
+    assert set(names) == set(msa.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(msa.lib, n), n
+
+
+def test_status_strings_and_version():
+    assert msa.lib.msa_status_string(0) == b"MSA_OK"
+    assert msa.lib.msa_status_string(4) == b"MSA_ERR_CONFLICT"
+    assert msa.lib.msa_version().decode().count(".") == 2
+
+
+def _attn(**kw):
+    a = msa.AttnArgs()
+    a.batch, a.total_q, a.num_qo_heads, a.num_kv_heads = 2, 8, 8, 2
+    a.head_dim, a.topk, a.max_seqlen_q, a.max_k_tiles = 128, 4, 4, 4
+    a.q = a.k = a.v = a.out = a.q2k = a.cu_seqlens_q = a.cu_seqlens_k = FAKE
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _call(a, ws=None, nbytes=0):
+    st = msa.lib.msa_sparse_attention(ctypes.byref(a), ws, nbytes, None)
+    return st, msa.lib.msa_last_error().decode()
+
+
+def _size(a):
+    n = ctypes.c_size_t(0)
+    st = msa.lib.msa_sparse_attention_workspace_size(ctypes.byref(a), ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, 2),
+    ("num_kv_heads", 3, 2),
+    ("topk", 0, 2),
+    ("topk", 65, 2),
+    ("kv_dtype", 7, 3),
+    ("max_k_tiles", 1 << 20, 2),
+])
+def test_attention_rejects_bad_shapes(field, value, status):
+    st, msg = _call(_attn(**{field: value}))
+    assert st == status and msg
+
+
+def test_attention_paged_conflict_and_missing_lengths():
+    a = _attn(page_table=FAKE, seqused_k=FAKE, page_table_width=4)  # cu_seqlens_k still set
+    st, msg = _call(a)
+    assert st == 4 and "seqused_k" in msg
+    b = _attn(page_table=FAKE, page_table_width=4)
+    b.cu_seqlens_k = None
+    st, _ = _call(b)
+    assert st == 1
+    c = _attn(page_table=FAKE, seqused_k=FAKE, page_table_width=2)
+    c.cu_seqlens_k = None
+    st, msg = _call(c)
+    assert st == 2 and "page_table_width" in msg
+
+
+def test_attention_rejects_unreadable_views():
+    a = _attn()
+    a.k_strides = msa.Strides(0, 256, 100)  # token stride not 16-byte aligned
+    st, msg = _call(a)
+    assert st == 5 and "never copied" in msg
+    b = _attn(q=FAKE + 8)
+    st, _ = _call(b)
+    assert st == 5
+
+
+def test_attention_e2m1_needs_scales_and_paging():
+    st, _ = _call(_attn(kv_dtype=2))  # flat E2M1
+    assert st == 5
+    a = _attn(kv_dtype=2, page_table=FAKE, seqused_k=FAKE, page_table_width=4)
+    a.cu_seqlens_k = None
+    st, _ = _call(a)
+    assert st == 1  # no scales
+    st, _ = _call(_attn(k_scale=FAKE))  # scales with bf16
+    assert st == 5
+
+
+def test_workspace_sizing_and_enforcement():
+    # decode shape (1 query x 16 heads per KV head): splits > 1 need a workspace
+    a = _attn(num_qo_heads=32, num_kv_heads=2, total_q=4, batch=4, max_seqlen_q=1,
+              max_k_tiles=64, topk=16, page_table=FAKE, seqused_k=FAKE, page_table_width=64)
+    a.cu_seqlens_k = None
+    st, n = _size(a)
+    assert st == 0 and n > 0
+    st, msg = _call(a, None, 0)
+    assert st == 6 and "workspace" in msg
+    st, _ = _call(a, FAKE, n - 1)
+    assert st == 6
+    st, _ = _call(a, FAKE + 4, n + 8)  # misaligned
+    assert st == 6
+    # forcing one split needs no workspace
+    a.splits = 1
+    assert _size(a) == (0, 0)
+    # prefill shape never splits
+    assert _size(_attn(max_seqlen_q=512, num_qo_heads=16, num_kv_heads=2)) == (0, 0)
+
+
+def test_proxy_and_topk_validation():
+    p = msa.ProxyArgs()
+    p.batch, p.total_q, p.num_qo_heads, p.num_kv_heads = 1, 4, 4, 2
+    p.head_dim, p.max_seqlen_q, p.max_k_tiles, p.kv_dtype = 128, 4, 2, 0
+    p.q = p.k = p.out = p.cu_seqlens_q = FAKE
+    assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 1  # no cu_seqlens_k
+    p.cu_seqlens_k = FAKE
+    p.kv_dtype = 2
+    assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 3  # E2M1 proxy K
+    p.kv_dtype = 0
+    p.page_table, p.seqused_k, p.page_table_width = FAKE, FAKE, 2
+    assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 4  # both lengths
+    p.head_dim = 64
+    assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 2
+    f = msa.lib.msa_topk_select
+    assert f(FAKE, 2, 64, 8, 0, 2, 0, FAKE, None) == 2          # topk 0
+    assert f(FAKE, 3, 64, 8, 4, 2, 0, FAKE, None) == 2          # NONE with 3 != 2 heads
+    assert f(FAKE, 3, 64, 8, 4, 2, 2, FAKE, None) == 2          # GROUP 3 % 2
+    assert f(FAKE, 2, 5000, 8, 4, 2, 0, FAKE, None) == 5        # too many blocks
+    assert f(FAKE, 2, 64, 8, 4, 2, 9, FAKE, None) == 5          # unknown mode
+    assert f(FAKE, 2, 64, 0, 4, 2, 0, FAKE, None) == 0          # empty: no launch
+    u = msa.lib.msa_tile_union
+    assert u(FAKE, FAKE, FAKE, 1, 8, 1, 4, 8, 8, 65, 8, FAKE, FAKE, FAKE, None) == 2
+    assert u(FAKE, FAKE, FAKE, 1, 8, 1, 4, 8, 8, 4, 3, FAKE, FAKE, FAKE, None) == 2

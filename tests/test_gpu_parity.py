@@ -1,0 +1,275 @@
+"""HIP path vs the fp64 oracle on small seeded problems (GPU).
+
+Sizes are chosen so the oracle finishes in seconds while the kernels still
+see several tiles, several KV blocks, ragged tails (partial last block, a
+partial last query tile), empty selections and blocks above the causal
+limit.  Every call goes through the C ABI (via the ctypes binding).
+"""
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import (assert_attention_close, assert_proxy_close, gpu_attention,
+                         oracle_attention)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_sparse_top_msa_amd as m
+    return m
+
+
+def _dev(p):
+    return p.to("cuda")
+
+
+# ---------------------------------------------------------------------------
+# sparse attention, prefill shape
+# ---------------------------------------------------------------------------
+
+PREFILL_CASES = [
+    # q_lens, k_lens, Hq, Hkv, topk, causal
+    ([1024], [1024], 4, 1, 4, True),
+    ([300, 77], [300, 500], 16, 2, 5, True),      # ragged tiles, Lq != Lk
+    ([200], [700], 8, 1, 6, False),               # non-causal
+    ([129, 64, 1], [129, 640, 200], 32, 2, 3, True),  # G = 16
+    ([90], [400], 2, 2, 4, True),                 # MHA, G = 1
+    ([150, 40], [150, 300], 6, 3, 4, True),       # G = 2
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_prefill_bf16_matches_oracle(msa, case):
+    ql, kl, hq, hkv, topk, causal = PREFILL_CASES[case]
+    p = synth.make_problem("prefill", q_lens=ql, k_lens=kl, num_qo_heads=hq, num_kv_heads=hkv,
+                           topk=topk, causal=causal, seed=100 + case, selection="general")
+    print(f"prefill case {case}: q {ql} k {kl} Hq {hq} Hkv {hkv} topk {topk}", flush=True)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, f"prefill case {case}")
+
+
+def test_prefill_fp8_and_scales(msa):
+    p = synth.make_problem("prefill_fp8", q_lens=[260, 33], k_lens=[400, 33], num_qo_heads=8,
+                           num_kv_heads=2, topk=3, kv_dtype=synth.KV_FP8, seed=7,
+                           selection="general", softmax_scale=0.05, v_global_scale=1.5)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "prefill fp8")
+
+
+def test_prefill_without_lse_and_diagonal_selection(msa):
+    p = synth.make_problem("prefill_diag", q_lens=[640], k_lens=[640], num_qo_heads=8,
+                           num_kv_heads=1, topk=4, seed=8, selection="diagonal")
+    out = gpu_attention(msa, _dev(p), lse=False)
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, None, ref_out, ref_lse, "prefill no lse")
+
+
+def test_full_selection_is_dense_causal(msa):
+    # every causally valid block selected: equals dense causal attention
+    ql = kl = [384, 200]
+    p = synth.make_problem("dense", q_lens=ql, k_lens=kl, num_qo_heads=8, num_kv_heads=2,
+                           topk=3, seed=9, selection="proxy")
+    rows = []
+    for L in ql:
+        for i in range(L):
+            n = i // 128 + 1
+            rows.append(list(range(n)) + [-1] * (3 - n))
+    p.q2k = torch.tensor(rows, dtype=torch.int32).unsqueeze(0).repeat(2, 1, 1)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "dense")
+    assert torch.isfinite(lse).all()
+
+
+def test_empty_and_out_of_range_rows(msa):
+    p = synth.make_problem("empty", q_lens=[64, 10], k_lens=[300, 10], num_qo_heads=4,
+                           num_kv_heads=1, topk=4, seed=10, selection="general")
+    q2k = p.q2k.clone()
+    q2k[:, :20] = -1                 # nothing selected
+    q2k[:, 20:30, 0] = 2             # block 2 holds keys 256..299; queries at
+    q2k[:, 20:30, 1:] = -1           # positions 256..265 see some of it
+    q2k[:, 30:40, 0] = 9             # past the sequence: ignored
+    q2k[:, 30:40, 1:] = -1
+    p.q2k = q2k
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "empty rows")
+    assert (out[:20].float() == 0).all() and torch.isneginf(lse[:20]).all()
+    assert (out[30:40].float() == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# sparse attention, decode shape (paged, split-KV + LSE merge)
+# ---------------------------------------------------------------------------
+
+DECODE_CASES = [
+    # batch, seqlen_q, Hq, Hkv, fmt, splits, kgs, vgs
+    (5, 1, 64, 4, synth.KV_BF16, 0, None, None),
+    (5, 1, 64, 4, synth.KV_BF16, 1, None, None),
+    (3, 4, 32, 2, synth.KV_FP8, 0, None, None),
+    (3, 4, 32, 2, synth.KV_FP8, 3, None, None),
+    (6, 1, 16, 1, synth.KV_E2M1, 0, 0.5, 2.0),
+    (6, 1, 16, 1, synth.KV_E2M1, 5, 0.5, 2.0),
+    (4, 2, 8, 1, synth.KV_BF16, 2, None, None),     # 16 rows: 2 tokens x 8 heads
+    (2, 3, 12, 1, synth.KV_FP8, 4, None, 1.25),     # 36 rows, 3 slots
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+def test_decode_paged_matches_oracle(msa, case):
+    B, sq, hq, hkv, fmt, splits, kgs, vgs = DECODE_CASES[case]
+    g = torch.Generator().manual_seed(200 + case)
+    lens = [int(x) for x in torch.randint(200, 3000, (B,), generator=g)]
+    lens[0] = 129  # a two-page request whose last page holds one key
+    p = synth.make_problem("decode", q_lens=[sq] * B, k_lens=lens, num_qo_heads=hq,
+                           num_kv_heads=hkv, topk=8, paged=True, kv_dtype=fmt, seed=300 + case,
+                           selection="general", k_global_scale=kgs, v_global_scale=vgs,
+                           extra_pages=3)
+    print(f"decode case {case}: B {B} sq {sq} Hq {hq} Hkv {hkv} fmt {fmt} splits {splits}", flush=True)
+    out, lse = gpu_attention(msa, _dev(p), splits=splits)
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, f"decode case {case}")
+
+
+def test_decode_is_deterministic_and_counters_reset(msa):
+    p = _dev(synth.make_problem("det", q_lens=[4] * 6, k_lens=[5000, 3000, 900, 4000, 128, 2000],
+                                num_qo_heads=32, num_kv_heads=2, topk=16, paged=True,
+                                kv_dtype=synth.KV_FP8, seed=11, selection="decode"))
+    ws = msa.Workspace(msa.workspace_size(p.q, p.k, p.v, p.q2k, p.cu_seqlens_q, page_table=p.page_table,
+                                          seqused_k=p.seqused_k, max_seqlen_q=4,
+                                          max_k_tiles=p.max_k_tiles, splits=4), "cuda")
+    a = gpu_attention(msa, p, splits=4, workspace=ws)
+    b = gpu_attention(msa, p, splits=4, workspace=ws)
+    c = gpu_attention(msa, p, splits=4, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[0], c[0])
+    assert torch.equal(a[1], b[1]) and torch.equal(a[1], c[1])
+    # split factors agree with each other within tolerance
+    one = gpu_attention(msa, p, splits=1)
+    assert float((one[0].float() - a[0].float()).abs().max()) <= 2e-2
+    # counters are back at zero: the workspace tail (counter words) reads 0
+    assert int(ws.view[-256:].count_nonzero()) == 0
+
+
+def test_fp8_subnormals_and_e2m1_halves_decode_exactly(msa):
+    # V made of E4M3 subnormal codes only, amplified through v_global_scale:
+    # a flushed subnormal would move the output by ~100 x 2^-9
+    p = synth.make_problem("sub", q_lens=[1, 1], k_lens=[256, 256], num_qo_heads=16,
+                           num_kv_heads=1, topk=2, paged=True, kv_dtype=synth.KV_FP8, seed=12,
+                           selection="decode", v_global_scale=100.0)
+    codes = torch.tensor([1, 2, 3, 4, 5, 6, 7, 0x81, 0x82, 0x87], dtype=torch.uint8)
+    idx = torch.randint(0, len(codes), p.v.shape, generator=torch.Generator().manual_seed(1))
+    p.v = codes[idx].view(torch.float8_e4m3fn)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "fp8 subnormal V")
+    # E2M1 with every nibble and subnormal E4M3 block scales
+    pe = synth.make_problem("e2", q_lens=[1, 1], k_lens=[256, 200], num_qo_heads=16,
+                            num_kv_heads=1, topk=2, paged=True, kv_dtype=synth.KV_E2M1, seed=13,
+                            selection="decode", v_global_scale=64.0, k_global_scale=0.5)
+    gen = torch.Generator().manual_seed(2)
+    pe.v = torch.randint(0, 256, pe.v.shape, generator=gen, dtype=torch.int64).to(torch.uint8)
+    pe.v_scale = torch.randint(1, 8, pe.v_scale.shape, generator=gen, dtype=torch.int64).to(torch.uint8)
+    out, lse = gpu_attention(msa, _dev(pe))
+    ref_out, ref_lse = oracle_attention(pe)
+    assert_attention_close(out, lse, ref_out, ref_lse, "e2m1 all nibbles")
+
+
+# ---------------------------------------------------------------------------
+# proxy score
+# ---------------------------------------------------------------------------
+
+PROXY_CASES = [
+    # q_lens, k_lens, Hq, Hkv, paged, fmt, causal, reduce
+    ([300, 77], [300, 500], 2, 2, False, synth.KV_BF16, True, False),
+    ([513], [513], 1, 1, False, synth.KV_BF16, True, False),
+    ([200], [700], 4, 2, False, synth.KV_BF16, False, False),
+    ([4, 4, 4], [3000, 129, 1000], 32, 2, True, synth.KV_FP8, True, True),
+    ([4, 4], [700, 1300], 32, 2, True, synth.KV_FP8, True, False),
+    ([1, 1, 1], [900, 128, 2000], 16, 1, True, synth.KV_BF16, True, True),
+    ([3, 2], [1000, 500], 6, 2, True, synth.KV_BF16, True, True),  # G = 3 (atomic path)
+]
+
+
+@pytest.mark.parametrize("case", range(len(PROXY_CASES)))
+def test_proxy_matches_oracle(msa, case):
+    ql, kl, hq, hkv, paged, fmt, causal, reduce = PROXY_CASES[case]
+    p = synth.make_problem("proxy", q_lens=ql, k_lens=kl, num_qo_heads=hq, num_kv_heads=hkv,
+                           paged=paged, kv_dtype=fmt, causal=causal, seed=400 + case,
+                           selection="proxy", reduce_heads=reduce)
+    print(f"proxy case {case}", flush=True)
+    d = _dev(p)
+    T = p.max_k_tiles + 2  # extra columns past every sequence must be -inf
+    got = msa.proxy_score(d.q, d.k, d.cu_seqlens_q, d.cu_seqlens_k, page_table=d.page_table,
+                          seqused_k=d.seqused_k, causal=causal, max_seqlen_q=max(ql),
+                          max_k_tiles=T, reduce_heads=reduce)
+    ref = oracle.proxy_score(p.q, p.k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k,
+                             page_table=p.page_table, seqused_k=p.seqused_k, causal=causal,
+                             max_k_tiles=T, reduce_heads=reduce, kv_format=fmt)
+    assert_proxy_close(got, ref, f"proxy case {case}")
+
+
+# ---------------------------------------------------------------------------
+# top-K select
+# ---------------------------------------------------------------------------
+
+def _adversarial_scores(hs, T, n, seed):
+    g = torch.Generator().manual_seed(seed)
+    s = torch.randn(hs, T, n, generator=g)
+    k = n // 5
+    s[:, :, :k] = torch.randint(-2, 3, (hs, T, k), generator=g).float()   # heavy ties
+    s[:, :, k:2 * k] = 0.0
+    s[:, ::2, k:2 * k] = -0.0                                              # +-0 ties
+    s[:, 3:, 2 * k:3 * k] = float("-inf")                                  # few finite
+    s[:, :, 3 * k] = float("-inf")                                         # none finite
+    return s
+
+
+@pytest.mark.parametrize("T,topk,hs,hkv,mode", [
+    (64, 16, 2, 2, 0), (7, 16, 2, 2, 0), (1024, 16, 1, 2, 1), (130, 4, 8, 2, 2),
+    (300, 33, 3, 1, 1), (64, 64, 1, 1, 0), (4096, 16, 1, 1, 0),
+])
+def test_topk_bit_exact(msa, T, topk, hs, hkv, mode):
+    s = _adversarial_scores(hs, T, 257, seed=T + topk)
+    got = msa.topk_select(s.cuda(), topk, hkv, mode=mode)
+    mode_name = {0: "none", 1: "all", 2: "group"}[mode]
+    ref = oracle.topk_select(s, topk, hkv, mode=mode_name)
+    assert torch.equal(got.cpu(), ref)
+
+
+# ---------------------------------------------------------------------------
+# tile union
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tile_tokens", [1, 4, 16, 64])
+def test_tile_union_bit_exact(msa, tile_tokens):
+    p = synth.make_problem("union", q_lens=[300, 5, 64], k_lens=[2000, 900, 64 * 128],
+                           num_qo_heads=2, num_kv_heads=2, topk=8, seed=tile_tokens,
+                           selection="general")
+    lens = torch.tensor(p.k_lens, dtype=torch.int32)
+    T = p.max_k_tiles
+    blocks, masks, counts = msa.tile_union(p.q2k.cuda(), p.cu_seqlens_q.cuda(), lens.cuda(),
+                                           tile_tokens, T)
+    blocks, masks, counts = blocks.cpu(), masks.cpu(), counts.cpu()
+    cu = p.cu_seqlens_q.tolist()
+    for g in range(2):
+        for b in range(3):
+            nblk = (p.k_lens[b] + 127) // 128
+            for j in range(blocks.shape[2]):
+                i0 = cu[b] + j * tile_tokens
+                i1 = min(cu[b + 1], i0 + tile_tokens)
+                if i0 >= cu[b + 1]:
+                    assert int(counts[g, b, j]) == 0
+                    continue
+                ref_b, ref_m = oracle.tile_union(p.q2k[g, i0:i1], nblk)
+                n = int(counts[g, b, j])
+                assert blocks[g, b, j, :n].tolist() == ref_b
+                assert [m % (1 << 64) for m in masks[g, b, j, :n].tolist()] == ref_m
+                assert (blocks[g, b, j, n:] == -1).all()
