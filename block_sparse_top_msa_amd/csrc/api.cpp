@@ -71,7 +71,7 @@ struct Resolved {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r) {
+msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_ptrs) {
   if (!a) return fail(MSA_ERR_NULL, "args is NULL");
   if (a->batch < 0 || a->total_q < 0)
     return fail(MSA_ERR_SHAPE, "batch (%d) and total_q (%d) must be >= 0", a->batch, a->total_q);
@@ -103,11 +103,11 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r) {
     if (a->kv_dtype == MSA_KV_E2M1X2)
       return fail(MSA_ERR_UNSUPPORTED, "packed E2M1 K/V is read from the paged layout only");
   }
-  if (a->kv_dtype == MSA_KV_E2M1X2 && (!a->k_scale || !a->v_scale))
+  if (need_ptrs && a->kv_dtype == MSA_KV_E2M1X2 && (!a->k_scale || !a->v_scale))
     return fail(MSA_ERR_NULL, "packed E2M1 K/V needs k_scale and v_scale");
   if (a->kv_dtype != MSA_KV_E2M1X2 && (a->k_scale || a->v_scale))
     return fail(MSA_ERR_UNSUPPORTED, "k_scale/v_scale are only read with packed E2M1 K/V");
-  if (a->total_q > 0 && a->batch > 0) {
+  if (need_ptrs && a->total_q > 0 && a->batch > 0) {
     if (!a->q || !a->k || !a->v || !a->q2k || !a->cu_seqlens_q || !a->out)
       return fail(MSA_ERR_NULL, "q, k, v, q2k, cu_seqlens_q and out must be non-NULL");
     if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->k, 16) || !aligned(a->v, 16))
@@ -126,7 +126,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r) {
       return st;
     if ((st = resolve_strides("v_scale", a->v_scale_strides, paged, a->num_kv_heads, 8, 8, &p.vs_st)))
       return st;
-    if (!aligned(a->k_scale, 8) || !aligned(a->v_scale, 8))
+    if (need_ptrs && (!aligned(a->k_scale, 8) || !aligned(a->v_scale, 8)))
       return fail(MSA_ERR_UNSUPPORTED, "k_scale/v_scale must be 8-byte aligned");
   }
 
@@ -236,7 +236,7 @@ const char* msa_version(void) { return "0.1.0"; }
 msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args, size_t* bytes) {
   if (!bytes) return fail(MSA_ERR_NULL, "bytes is NULL");
   Resolved r;
-  msa_status_t st = resolve_attention(args, &r);
+  msa_status_t st = resolve_attention(args, &r, false);
   if (st) return st;
   *bytes = r.ws_bytes;
   return ok();
@@ -245,21 +245,24 @@ msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args, si
 msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   Resolved r;
-  msa_status_t st = resolve_attention(args, &r);
+  msa_status_t st = resolve_attention(args, &r, true);
   if (st) return st;
   if (r.ws_bytes) {
     if (!workspace || workspace_bytes < r.ws_bytes)
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", r.ws_bytes,
                   workspace_bytes, workspace);
     if (!aligned(workspace, 256)) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    // layout: [completion counters][partial LSE][partial O]; the counter
+    // prefix sits at offset 0 for every shape
     const int rows = r.p.ws_rows;
     const size_t units = (size_t)args->batch * args->num_kv_heads * r.p.tiles_per_req;
-    const size_t o_bytes = round_up(units * r.plan.splits * rows * 128 * sizeof(float), 256);
+    const size_t c_bytes = round_up(units * sizeof(uint32_t), 256);
     const size_t l_bytes = round_up(units * r.plan.splits * r.p.ws_lse_rows * sizeof(float), 256);
+    (void)rows;
     char* base = static_cast<char*>(workspace);
-    r.p.ws_o = reinterpret_cast<float*>(base);
-    r.p.ws_lse = reinterpret_cast<float*>(base + o_bytes);
-    r.p.ws_cnt = reinterpret_cast<uint32_t*>(base + o_bytes + l_bytes);
+    r.p.ws_cnt = reinterpret_cast<uint32_t*>(base);
+    r.p.ws_lse = reinterpret_cast<float*>(base + c_bytes);
+    r.p.ws_o = reinterpret_cast<float*>(base + c_bytes + l_bytes);
   }
   if (args->total_q == 0 || args->batch == 0) return ok();
   return hip_status(msa::launch_attention(r.p, args->kv_dtype, r.plan,
@@ -282,9 +285,8 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
     if (!a->seqused_k) return fail(MSA_ERR_NULL, "paged K needs page_table and seqused_k together");
     if (a->cu_seqlens_k)
       return fail(MSA_ERR_CONFLICT, "paged K takes seqused_k; cu_seqlens_k must be NULL");
-    if (a->page_table_width < a->max_k_tiles || a->page_table_width <= 0)
-      return fail(MSA_ERR_SHAPE, "page_table_width (%d) must be >= max_k_tiles (%d) and > 0",
-                  a->page_table_width, a->max_k_tiles);
+    if (a->page_table_width <= 0)
+      return fail(MSA_ERR_SHAPE, "page_table_width must be > 0 (got %d)", a->page_table_width);
   } else if (!a->cu_seqlens_k) {
     return fail(MSA_ERR_NULL, "flat K needs cu_seqlens_k");
   } else if (a->seqused_k) {

@@ -321,7 +321,6 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
   bf16x8 qf[SPW][4];
   int tk_[SPW], pos_[SPW];
   unsigned long long slot_tokmask[SPW];
-  int slot_pos_min[SPW];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const int slot = sg * SPW + s;
@@ -332,7 +331,6 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
     pos_[s] = lk - lq + i0 + tk;
     const int tfirst = (16 * slot) / G;
     const int tlast = min((16 * slot + 15) / G, ntok - 1);
-    slot_pos_min[s] = lk - lq + i0 + tfirst;
     unsigned long long m = 0;
     for (int t = tfirst; t <= tlast && t < 64; ++t) m |= 1ull << t;
     slot_tokmask[s] = (tfirst < ntok) ? m : 0ull;
@@ -385,22 +383,20 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
           acc[kt] = mfma16(a, qf[s][ds], acc[kt]);
         }
       }
-      // scale into the log2 domain and mask
+      // scale into the log2 domain and mask: a key is visible to this lane's
+      // row iff key <= lim (lim = -1 when the row's token did not select t).
+      // Branch-free on purpose: one compare + select per accumulator value.
       const bool sel = (tk_[s] < ntok) && ((umask >> tk_[s]) & 1ull);
-      const bool full = (!p.causal || kBlock * t + kbase + KP - 1 <= slot_pos_min[s]) &&
-                        (kbase + KP <= nvalid);
+      int lim = nvalid - 1;
+      if (p.causal) lim = min(lim, pos_[s] - kBlock * t);
+      lim = sel ? lim : -1;
       float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = acc[kt][r] * p.scale_log2;
-          bool ok = sel;
-          if (!full) {
-            const int key = kbase + 16 * kt + 4 * lg + r;
-            ok = ok && key < nvalid && (!p.causal || kBlock * t + key <= pos_[s]);
-          }
-          x = ok ? x : -INFINITY;
+          const int key = kbase + 16 * kt + 4 * lg + r;
+          const float x = key <= lim ? acc[kt][r] * p.scale_log2 : -INFINITY;
           acc[kt][r] = x;
           mx = fmaxf(mx, x);
         }

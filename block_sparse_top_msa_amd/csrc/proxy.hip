@@ -116,6 +116,7 @@ __global__ __launch_bounds__(256) void msa_proxy_kernel(ProxyParams p) {
   const int pos_max = lk - lq + r_last / G;
   // blocks with at least one visible key for some row of the tile
   int t_act = min(t_end, nblk);
+  if (p.paged) t_act = min(t_act, p.pt_width);
   if (p.causal) t_act = min(t_act, pos_max < 0 ? 0 : pos_max / kBlock + 1);
   t_act = max(t_act, t_beg);
 
@@ -190,16 +191,19 @@ __global__ __launch_bounds__(256) void msa_proxy_kernel(ProxyParams p) {
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma32(a, qf[nt][s], acc[nt]);
       }
-      const bool full = (32 * kt + 32 <= nvalid) &&
-                        (!p.causal || kBlock * t + 32 * kt + 31 <= lk - lq + r0 / G);
+      // Visible keys of this block for a row: key <= lim.  Written without
+      // short-circuit logic so the select stays a plain compare + cndmask on
+      // the accumulator values.
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
+        int lim = nvalid - 1;
+        if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
         float m = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool ok = full || (key < nvalid && (!p.causal || kBlock * t + key <= pos_[nt]));
-          m = fmaxf(m, ok ? acc[nt][r] : -INFINITY);
+          const float v = acc[nt][r];
+          m = fmaxf(m, key <= lim ? v : -INFINITY);
         }
         m = xor_max(m, 32);
         cm[nt] = fmaxf(cm[nt], m);

@@ -125,9 +125,14 @@ typedef struct {
 /* Bytes of workspace msa_sparse_attention needs for these arguments (split-KV
  * partials and completion counters; prepare_msa_nvfp4_sparse_decode page,
  * Parameters: workspace_buffer).  0 when the call runs without splitting.
- * The workspace must be zeroed once before first use; each launch leaves its
- * counters at zero again, so it can be reused by later launches on the same
- * stream but must not be shared by launches that may run concurrently. */
+ * Layout: the completion counters come first, one uint32 per (request, KV
+ * head), in the first round_up(4 * batch * num_kv_heads, 256) bytes; the
+ * partials follow.  Those counter bytes must be zero when a launch starts;
+ * every launch leaves them zero again, so one workspace serves any number of
+ * back-to-back launches on a stream.  Zero the counter prefix again before a
+ * launch whose counter prefix is longer than the one known to be zero (the
+ * partials of an earlier, different-shaped launch may sit there).  Launches
+ * that may run concurrently need separate workspaces. */
 msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args,
                                                  size_t* bytes);
 

@@ -276,9 +276,10 @@ def selection_scores(scores: torch.Tensor, num_kv_heads: int, mode: str = "auto"
     """Scores used by each KV head's selection: (Hkv, T, total_q).
 
     mode "none": one score head per KV head (H_s == Hkv).
-    mode "all":  a single shared score (H_s == 1) copied to every KV head —
-                 reading of the pages' "one shared block selection per query"
-                 for reduce_heads output feeding a per-KV-head q2k.
+    mode "all":  the max over every score head (a reduce_heads output has
+                 H_s == 1 already), copied to every KV head — reading of the
+                 pages' "one shared block selection per query" for a
+                 reduce_heads score feeding a per-KV-head q2k.
     mode "group": per-query-head scores (H_s == G * Hkv), max over the G
                  query heads of each KV head.  Not on the pages; the
                  per-group analogue of reduce_heads.
@@ -289,8 +290,7 @@ def selection_scores(scores: torch.Tensor, num_kv_heads: int, mode: str = "auto"
     if mode == "auto":
         mode = "all" if hs == 1 else ("none" if hs == num_kv_heads else "group")
     if mode == "all":
-        assert hs == 1
-        return s.expand(num_kv_heads, *s.shape[1:])
+        return s.max(dim=0, keepdim=True).values.expand(num_kv_heads, *s.shape[1:])
     if mode == "none":
         assert hs == num_kv_heads
         return s
