@@ -1,0 +1,293 @@
+"""Benchmark of the MSA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Default workload: flat causal prefill, 2 x 8192 tokens, 16 q heads / 2 KV
+heads, head_dim 128, topk 16, with the full pipeline per step: proxy score
+(2 indexer heads) -> top-K block select -> sparse attention with LSE.  The
+metric is selected-block attention TFLOP/s: FLOPs counted over the keys each
+query actually attends (4 * head_dim per key and query head), divided by the
+step time.  Inputs are seeded synthetic tensors resident in HBM before timing.
+
+The decode workloads (--workload paged_decode_...) report KV GB/s over the
+K/V blocks actually gathered, timed cold: a 1 GiB scrub runs before every
+step, outside the timed events.
+
+Per-stage times come from HIP events recorded on the stream the kernels run
+on.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+DEFAULT_WORKLOAD = "flat_prefill_2x8192_h16kv2_top16_pipeline"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    return ap.parse_args()
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _traffic_for(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel)
+    if not ent:
+        return None
+    src = os.path.join(ROOT, "block_sparse_top_msa_amd", "csrc", ent["source"])
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    return ent["bytes_per_launch"] if h == ent.get("source_sha256_16") else None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the same workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline_prefill(p, rows_n):
+    import torch
+    import oracle
+    from block_sparse_top_msa_amd import accounting
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    pc = p.to("cpu")
+    total = pc.total_q
+    step = max(1, total // rows_n)
+    rows = list(range(step - 1, total, step))[:rows_n]
+    t0 = time.perf_counter()
+    s = oracle.proxy_score(pc.proxy_q, pc.k, pc.cu_seqlens_q, cu_seqlens_k=pc.cu_seqlens_k,
+                           causal=True, max_k_tiles=pc.max_k_tiles, rows=rows)
+    q2k = oracle.topk_select(s.float(), pc.topk, pc.num_kv_heads, rows=rows)
+    oracle.sparse_attention(pc.q, pc.k, pc.v, q2k, pc.cu_seqlens_q,
+                            cu_seqlens_k=pc.cu_seqlens_k, causal=True, rows=rows)
+    dt = time.perf_counter() - t0
+    lens = pc.cu_seqlens_k[1:] - pc.cu_seqlens_k[:-1]
+    keys = accounting.attended_keys(q2k, pc.cu_seqlens_q, lens, causal=True)[:, rows]
+    flops = int(keys.sum()) * (pc.num_qo_heads // pc.num_kv_heads) * 4 * pc.head_dim
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {total} query rows (every {step}th), all 16 heads: "
+                      f"fp64 proxy + top-K + attention, {dt:.1f} s"}
+
+
+def cpu_baseline_decode(p, rows_n, fmt):
+    import torch
+    import oracle
+    from block_sparse_top_msa_amd import accounting
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    q2k = p.q2k.cpu()
+    per = p.total_q // p.batch
+    reqs = list(range(0, p.batch, max(1, p.batch // max(1, rows_n // per))))[:max(1, rows_n // per)]
+    rows = [b * per + t for b in reqs for t in range(per)]
+    t0 = time.perf_counter()
+    oracle.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q.cpu(), page_table=p.page_table.cpu(),
+                            seqused_k=p.seqused_k.cpu(), causal=True, kv_format=fmt,
+                            k_scale=p.k_scale, v_scale=p.v_scale,
+                            k_global_scale=p.k_global_scale, v_global_scale=p.v_global_scale,
+                            rows=rows)
+    dt = time.perf_counter() - t0
+    sub = torch.zeros_like(q2k).fill_(-1)
+    sub[:, rows] = q2k[:, rows]
+    nbytes = accounting.decode_kv_bytes(sub, p.cu_seqlens_q.cpu(), p.seqused_k.cpu(), fmt,
+                                        p.max_k_tiles)
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(reqs)} of {p.batch} requests ({len(rows)} query rows): fp64 "
+                      f"attention over their selected pages, {dt:.1f} s"}
+
+
+# ---------------------------------------------------------------------------
+# GPU runs
+# ---------------------------------------------------------------------------
+
+def bench_prefill_pipeline(args, msa, synth, torch):
+    from block_sparse_top_msa_amd import accounting
+    p = synth.workload(args.workload, device="cuda")
+    T, B = p.max_k_tiles, p.batch
+    mq = max(p.q_lens)
+    scores = torch.empty(p.proxy_q.shape[1], T, p.total_q, dtype=torch.float32, device="cuda")
+    q2k = torch.empty(p.num_kv_heads, p.total_q, p.topk, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(p.q)
+    lse = torch.empty(p.total_q, p.num_qo_heads, dtype=torch.float32, device="cuda")
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        msa.proxy_score(p.proxy_q, p.k, p.cu_seqlens_q, p.cu_seqlens_k, causal=True,
+                        max_seqlen_q=mq, max_k_tiles=T, output=scores)
+        if ev: ev[1].record()
+        msa.topk_select(scores, p.topk, p.num_kv_heads, out=q2k)
+        if ev: ev[2].record()
+        msa.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q, p.cu_seqlens_k, causal=True,
+                             return_softmax_lse=True, max_seqlen_q=mq, max_k_tiles=T,
+                             out=out, lse=lse)
+        if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    lens = p.cu_seqlens_k[1:] - p.cu_seqlens_k[:-1]
+    flops = accounting.attention_flops(q2k, p.cu_seqlens_q, lens, p.num_qo_heads)
+    pflops = accounting.proxy_flops(p.cu_seqlens_q, lens, p.proxy_q.shape[1])
+
+    evs = [_events(4) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
+    ms_step = wall * 1e3 / args.steps
+    attn_ms = st[2]
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    res = {
+        "metric": "selected-block attention TFLOP/s",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(ms_step, 4),
+        "dtype": "bf16",
+        "config": {"workload": p.name, "batch": B, "seq_len": mq, "num_qo_heads": p.num_qo_heads,
+                   "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "topk": p.topk,
+                   "proxy_heads": p.proxy_q.shape[1], "causal": True},
+        "stages_ms": {"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
+                      "sparse_attention": round(st[2], 4)},
+        "work": {"attention_flops": flops, "proxy_flops": pflops,
+                 "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3)},
+        "roofline": {"kernel": "msa_attention_kernel (prefill)", "bound": "mfma",
+                     "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": _traffic_for("msa_attention_kernel_prefill")},
+    }
+    return res, p
+
+
+def bench_decode(args, msa, synth, torch):
+    from block_sparse_top_msa_amd import accounting
+    p = synth.workload(args.workload, device="cuda")
+    fmt = p.kv_dtype
+    T, B = p.max_k_tiles, p.batch
+    mq = max(p.q_lens)
+    out = torch.empty_like(p.q)
+    lse = torch.empty(p.total_q, p.num_qo_heads, dtype=torch.float32, device="cuda")
+    pipeline = p.q2k is None
+    scores = q2k = None
+    if pipeline:
+        scores = torch.empty(1 if p.reduce_heads else p.num_qo_heads, T, p.total_q,
+                             dtype=torch.float32, device="cuda")
+        q2k = torch.empty(p.num_kv_heads, p.total_q, p.topk, dtype=torch.int32, device="cuda")
+    else:
+        q2k = p.q2k
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        if pipeline:
+            msa.proxy_score(p.q, p.k, p.cu_seqlens_q, page_table=p.page_table,
+                            seqused_k=p.seqused_k, causal=True, max_seqlen_q=mq, max_k_tiles=T,
+                            output=scores, reduce_heads=p.reduce_heads)
+        if ev: ev[1].record()
+        if pipeline:
+            msa.topk_select(scores, p.topk, p.num_kv_heads, out=q2k)
+        if ev: ev[2].record()
+        msa.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q, causal=True,
+                             page_table=p.page_table, seqused_k=p.seqused_k,
+                             return_softmax_lse=True, k_scale=p.k_scale, v_scale=p.v_scale,
+                             k_global_scale=p.k_global_scale, v_global_scale=p.v_global_scale,
+                             max_seqlen_q=mq, max_k_tiles=T, out=out, lse=lse)
+        if ev: ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    nbytes = accounting.decode_kv_bytes(q2k, p.cu_seqlens_q, p.seqused_k, fmt, T)
+    evs = [_events(4) for _ in range(args.steps)]
+    for k in range(args.steps):
+        scrub.fill_(k & 0xFF)          # evict L2 / MALL: cold K/V every step
+        step(evs[k])
+    torch.cuda.synchronize()
+    st = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
+    ms_step = sum(st)
+    gbs = nbytes / (st[2] * 1e-3) / 1e9
+    res = {
+        "metric": "KV GB/s",
+        "value": round(gbs, 3),
+        "unit": "GB/s",
+        "ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(p.total_q / (ms_step * 1e-3), 1),
+        "dtype": {"bf16": "bf16", "fp8_e4m3": "fp8_e4m3->bf16", "e2m1x2": "e2m1->bf16"}[fmt],
+        "config": {"workload": p.name, "batch": B, "seqlen_q": mq, "num_qo_heads": p.num_qo_heads,
+                   "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "topk": p.topk,
+                   "kv_format": fmt, "cold_cache": True},
+        "stages_ms": {"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
+                      "sparse_attention": round(st[2], 4)},
+        "work": {"kv_bytes": nbytes},
+        "roofline": {"kernel": "msa_attention_kernel (decode)", "bound": "hbm",
+                     "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": _traffic_for("msa_attention_kernel_decode_" + fmt)},
+    }
+    return res, p
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the MSA hot path here runs on a single MI355X and "
+              f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_top_msa_amd as msa
+    import synth
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    if args.workload == DEFAULT_WORKLOAD or args.workload.startswith("flat_prefill"):
+        res, p = bench_prefill_pipeline(args, msa, synth, torch)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(p, args.cpu_sample_rows)
+    else:
+        res, p = bench_decode(args, msa, synth, torch)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_decode(p, p.total_q, p.kv_dtype)
+    line = {
+        "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": res["dtype"], "data": "synthetic (seeded, generated on the GPU)",
+        "config": res["config"],
+    }
+    for k in ("tokens_per_s", "stages_ms", "work"):
+        if k in res:
+            line[k] = res[k]
+    line["roofline"] = res["roofline"]
+    line["cpu_baseline"] = cpu
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

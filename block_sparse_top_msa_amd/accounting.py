@@ -1,0 +1,91 @@
+"""Algorithmic work of an MSA call, for throughput and roofline reporting.
+
+Counts only what the method must do:
+  attention FLOPs = sum over (query, query head) of 4 * head_dim * |A(g, i)|,
+      A(g, i) the keys of the query's selected blocks that exist (j < Lk) and
+      are causally visible (2 * d for QK^T, 2 * d for PV per attended key);
+      work on blocks a tile computes but a token did not select is not counted.
+  decode KV bytes = sum over (request, KV head) of the valid tokens of every
+      block in the union of the request's selections, times both sides, times
+      the stored bytes per token per side (bf16 256, fp8 128, E2M1 64 + 8
+      scale bytes); each block counts once per (request, KV head).
+  proxy FLOPs = 2 * head_dim per (query head, visible key) pair.
+
+torch ops on index tensors only; none of the attention arithmetic.
+"""
+from __future__ import annotations
+
+import torch
+
+BLOCK = 128
+BYTES_PER_TOKEN_SIDE = {"bf16": 256, "fp8_e4m3": 128, "e2m1x2": 72}
+
+
+def _row_geometry(cu_seqlens_q, lengths_k, total_q, device):
+    cu = cu_seqlens_q.to(device=device, dtype=torch.int64)
+    i = torch.arange(total_q, device=device)
+    b = torch.searchsorted(cu[1:], i, right=True)
+    lq = (cu[1:] - cu[:-1])[b]
+    iq = i - cu[b]
+    lk = lengths_k.to(device=device, dtype=torch.int64)[b]
+    return b, lq, iq, lk
+
+
+def attended_keys(q2k, cu_seqlens_q, lengths_k, causal=True):
+    """|A(g, i)| as an int64 tensor (Hkv, total_q)."""
+    hkv, total_q, topk = q2k.shape
+    dev = q2k.device
+    _, lq, iq, lk = _row_geometry(cu_seqlens_q, lengths_k, total_q, dev)
+    t = q2k.to(torch.int64)
+    start = BLOCK * t
+    end = torch.minimum(start + BLOCK, lk.view(1, -1, 1))
+    if causal:
+        pos = (lk - lq + iq).view(1, -1, 1)
+        end = torch.minimum(end, pos + 1)
+    nblk = (lk + BLOCK - 1) // BLOCK
+    valid = (t >= 0) & (t < nblk.view(1, -1, 1))
+    n = torch.clamp(end - start, min=0) * valid
+    return n.sum(-1)
+
+
+def attention_flops(q2k, cu_seqlens_q, lengths_k, num_qo_heads, head_dim=128, causal=True):
+    hkv = q2k.shape[0]
+    G = num_qo_heads // hkv
+    return int(attended_keys(q2k, cu_seqlens_q, lengths_k, causal).sum()) * G * 4 * head_dim
+
+
+def decode_kv_bytes(q2k, cu_seqlens_q, lengths_k, kv_format, max_k_tiles):
+    """Bytes of K and V the decode must read: union of selected blocks per
+    (request, KV head), valid tokens only, both sides."""
+    hkv, total_q, topk = q2k.shape
+    dev = q2k.device
+    b, _, _, lk = _row_geometry(cu_seqlens_q, lengths_k, total_q, dev)
+    B = cu_seqlens_q.numel() - 1
+    used = torch.zeros(hkv, B, max_k_tiles + 1, dtype=torch.bool, device=dev)
+    t = q2k.to(torch.int64)
+    nblk = ((lk + BLOCK - 1) // BLOCK).view(1, -1, 1)
+    ok = (t >= 0) & (t < nblk)
+    tt = torch.where(ok, t, torch.full_like(t, max_k_tiles))
+    bb = b.view(1, -1, 1).expand_as(tt)
+    gg = torch.arange(hkv, device=dev).view(-1, 1, 1).expand_as(tt)
+    used[gg, bb, tt] = True
+    used = used[:, :, :max_k_tiles]
+    lkb = lengths_k.to(device=dev, dtype=torch.int64).view(1, -1, 1)
+    starts = BLOCK * torch.arange(max_k_tiles, device=dev).view(1, 1, -1)
+    tokens = torch.clamp(torch.minimum(starts + BLOCK, lkb) - starts, min=0)
+    return int((used * tokens).sum()) * 2 * BYTES_PER_TOKEN_SIDE[kv_format]
+
+
+def proxy_flops(cu_seqlens_q, lengths_k, num_qo_heads, head_dim=128, causal=True):
+    cq = cu_seqlens_q.cpu().tolist()
+    lks = lengths_k.cpu().tolist()
+    pairs = 0
+    for b in range(len(cq) - 1):
+        lq, lk = cq[b + 1] - cq[b], int(lks[b])
+        if causal:
+            # query iq sees keys 0..lk-lq+iq
+            first = lk - lq + 1
+            pairs += sum(max(0, min(lk, first + iq)) for iq in range(lq))
+        else:
+            pairs += lq * lk
+    return pairs * num_qo_heads * 2 * head_dim

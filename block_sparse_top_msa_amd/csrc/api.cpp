@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/msa.h"
@@ -160,6 +161,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
 
   // ---- plan ----
   msa::AttnPlan& plan = r->plan;
+  plan = msa::AttnPlan{};
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows_req = lqmax * G;
   if (rows_req <= 64) {
@@ -181,9 +183,19 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     plan.splits = std::max(1, std::min(splits, 64));
   } else {
     plan.decode = 0;
-    plan.spw = 2;
-    // 4 waves x 2 slots x 16 rows = 128 rows per tile
-    plan.tok_per_tile = std::max(1, std::min(64, 128 / G));
+    plan.async_bf16 = (a->kv_dtype == MSA_KV_BF16);
+    // bf16: 4 waves x spw slots x 32 rows per tile; other formats: 4 x 2 x 16
+    int rows;
+    if (plan.async_bf16) {
+      int spw = 2;
+      if (const char* e = std::getenv("MSA_PREFILL_SPW")) spw = std::atoi(e) == 1 ? 1 : 2;
+      plan.spw = spw;
+      rows = 128 * spw;
+    } else {
+      plan.spw = 2;
+      rows = 128;
+    }
+    plan.tok_per_tile = std::max(1, std::min(64, rows / G));
     plan.splits = 1;
   }
   if (plan.tok_per_tile * a->topk > msa::kMaxUnion) {

@@ -582,6 +582,7 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
 
 template <int FMT>
 static hipError_t launch_fmt(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
+  if (!plan.decode && plan.async_bf16 && FMT == kFmtBf16) return launch_prefill_bf16(p, plan.spw, stream);
   if (!plan.decode) return launch_one<4, 2, 1, FMT, false>(p, stream);
   const bool split = plan.splits > 1;
   switch (plan.spw) {

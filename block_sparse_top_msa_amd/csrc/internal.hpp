@@ -51,6 +51,7 @@ struct AttnParams {
 // Kernel family selection for one attention call.
 struct AttnPlan {
   int decode;       // 1: key-split decode kernel; 0: slot-per-wave prefill kernel
+  int async_bf16;   // prefill with bf16 K/V: asynchronous LDS staging kernel
   int spw;          // 16-row slots per wave
   int tok_per_tile;
   int splits;
@@ -58,6 +59,9 @@ struct AttnPlan {
 
 hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
                             hipStream_t stream);
+
+// bf16 prefill tiles of 4 waves x spw slots x 16 rows (spw = 2 or 4)
+hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream);
 
 struct ProxyParams {
   const uint16_t* q;

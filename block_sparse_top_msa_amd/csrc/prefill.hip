@@ -1,0 +1,451 @@
+// MSA sparse attention, prefill shape, bf16 K/V (msa_sparse_attention page,
+// summary: query tiles, each running one online softmax over the union of
+// the blocks its tokens selected, writing the output directly).
+//
+// gfx950 design:
+//  * Tile = TOK query tokens of one request x the G query heads of one KV
+//    head, as token-major rows cut into 32-row slots; each of NW waves owns
+//    SPW slots.  32-row slots because v_mfma_f32_32x32x16_bf16 runs at twice
+//    the FLOP rate of the 16x16x32 shape on this chip (measured: ~2.4 vs
+//    ~1.3 PFLOP/s) and reads half the LDS bytes per FLOP.
+//  * The tile's block union is built in LDS (tile_union.hpp).  Each union
+//    block (128 keys of K and V, 64 KiB) is staged global -> LDS with
+//    global_load_lds (16 B per lane, no VGPR staging), double buffered: block
+//    u+1 streams in while block u is computed.  Rows are XOR-swizzled in
+//    16-byte chunks so every operand read is bank-conflict free with an
+//    unpadded 256-byte row pitch.
+//  * Per 32-key chunk: S^T = K Q^T (keys on the MFMA M axis, query rows on
+//    N), the softmax update, and O^T += V^T P^T with P taken straight from
+//    the S^T registers.  The chunk's K and V^T fragments are read into
+//    registers once and reused by every active slot of the wave; V^T comes
+//    from row-major V through the transposing ds_read_b64_tr_b16.
+//  * Softmax: p = exp2(s * c - m) is one FMA + one exp per score against a
+//    per-row reference max m set by the row's first scores and moved again
+//    (rescaling O and l) only if a score exceeds it by more than 2^64, which
+//    the fp32 accumulators absorb; row sums stay per lane until the end.  A slot none of whose tokens chose a
+//    block skips it (one scalar branch per slot and chunk).
+#include "common.hpp"
+#include "internal.hpp"
+#include "tile_union.hpp"
+
+namespace msa {
+
+namespace {
+
+constexpr int kTileBytes = kBlock * kHeadDim * 2;   // 32 KiB of bf16 per side
+constexpr float kLn2f = 0.69314718055994530942f;
+// log2 units: p = 2^(s - m) <= 2^64.  Safe in bf16 (P operand) and in the
+// fp32 O / l accumulators (sums stay far below 2^128), and precision does not
+// depend on magnitude, so O is rescaled only if a row's max jumps by more
+// than 64 (in log2 units) after its first block.
+constexpr float kRescaleSlack = 64.0f;
+
+struct PrefillLds {
+  uint8_t kv[2][2 * kTileBytes];   // [buffer][K | V]
+  UnionLds un;
+  int64_t kbase[kMaxUnion];        // byte offset of each union block's row 0 in K
+  int64_t vbase[kMaxUnion];        // ... and in V
+};
+
+// 16-byte chunk swizzles (chunk index 0..15 within a 256-byte row).  K: the
+// 16 consecutive rows one MFMA operand fetch reads per pass land on distinct
+// chunks.  V: the four rows a 16-lane transposed read touches land on
+// distinct chunk quads.
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 2); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// global -> LDS, 16 bytes per lane, lane l writing at lds_base + 16 l.
+// Issued from inline asm so that the compiler does not treat the in-flight
+// LDS writes as pending on every later LDS read (it would wait for the whole
+// prefetch); completion is awaited explicitly with vmcnt.
+__device__ __forceinline__ void g2lds16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\t"
+               "s_nop 0\n\t"
+               "global_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Workgroup barrier that does not drain outstanding global loads (unlike
+// __syncthreads, whose release fence waits for every in-flight load,
+// including the next block's prefetch).  Callers first wait on exactly the
+// counters they need; the asm statements keep memory accesses in place.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Transposed reads of the V^T operand of one 32-key chunk, for the four
+// 32-column head-dim tiles dt and the two 16-key k-steps: rows r, r + 8
+// (first k-step) and r + 16, r + 24 (second), i.e. byte offsets 0, 2048,
+// 4096, 6144.  In each group of 16 lanes, lane j receives element j % 4 of
+// the 8 bytes at lane 4e + j / 4's address, for e = 0..3: four consecutive
+// keys of one head-dim column.
+__device__ __forceinline__ void vtr_issue(u32x2 (&v)[16], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %3, %16 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %4, %17\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %8, %18\n\t"
+      "ds_read_b64_tr_b16 %9, %18 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %11, %18 offset:6144\n\t"
+      "ds_read_b64_tr_b16 %12, %19\n\t"
+      "ds_read_b64_tr_b16 %13, %19 offset:2048\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:6144"
+      : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]),
+        "=v"(v[7]), "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]),
+        "=v"(v[14]), "=v"(v[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+// Waits for the reads above; naming the registers orders their uses after it.
+__device__ __forceinline__ void vtr_wait(u32x2 (&v)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                 "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+}
+
+__device__ __forceinline__ float swap32_max(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ unsigned long long uniform64(unsigned long long x) {
+  return ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+}
+
+}  // namespace
+
+template <int NW, int SPW>
+__global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
+  constexpr int NT = NW * kWave;
+  constexpr int LOADS = 64 / NW;   // 1 KiB load instructions per wave per block
+  constexpr int KLOADS = LOADS / 2;
+  static_assert(64 % NW == 0 && LOADS <= 63, "64 KiB per block split evenly over waves");
+  static_assert((4 * NW) % 16 == 0, "a lane's staged rows keep one swizzle phase");
+  __shared__ PrefillLds lds;
+
+  const int n_units = p.batch * p.hkv * p.tiles_per_req;
+  const int lid = xcd_remap(blockIdx.x, n_units);
+  if (lid < 0) return;
+  const int jr = lid % p.tiles_per_req;
+  int rest = lid / p.tiles_per_req;
+  const int g = rest % p.hkv;
+  const int b = rest / p.hkv;
+  const int j = p.tiles_per_req - 1 - jr;  // later tiles (more visible blocks) first
+
+  const int q0 = p.cu_q[b];
+  const int lq = p.cu_q[b + 1] - q0;
+  const int i0 = j * p.tok_per_tile;
+  if (i0 >= lq) return;
+  const int ntok = min(p.tok_per_tile, lq - i0);
+  const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
+  const int nblk = max(0, min((lk + kBlock - 1) / kBlock, p.max_k_tiles));
+
+  const int tid = threadIdx.x;
+  // wave-uniform values live in scalar registers, so per-slot decisions are
+  // scalar branches rather than exec-masked selects
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int l32 = lane & 31;
+  const int hf = lane >> 5;
+  const int G = p.group;
+
+  const int32_t* rows = p.q2k + ((int64_t)g * p.total_q + q0 + i0) * p.topk;
+  const int ucount = __builtin_amdgcn_readfirstlane(
+      build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk));
+
+  const int64_t kst = p.k_st.token, vst = p.v_st.token;
+  for (int u = tid; u < ucount; u += NT) {  // page lookups, once per block
+    const int t = lds.un.list[u];
+    if (p.paged) {
+      const int64_t page = p.page_table[(int64_t)b * p.pt_width + t];
+      lds.kbase[u] = page * p.k_st.page + g * p.k_st.head;
+      lds.vbase[u] = page * p.v_st.page + g * p.v_st.head;
+    } else {
+      const int64_t row0 = (int64_t)p.cu_k[b] + kBlock * t;
+      lds.kbase[u] = row0 * kst + g * p.k_st.head;
+      lds.vbase[u] = row0 * vst + g * p.v_st.head;
+    }
+  }
+
+  // ---- per-slot lane data: lane l owns query row 32 * slot + l % 32
+  bf16x8 qf[SPW][8];
+  int tk_[SPW], pos_[SPW];
+  unsigned long long tokmask[SPW];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const int slot = wave * SPW + s;
+    const int r = 32 * slot + l32;
+    const int tk = r / G;
+    const int hh = r % G;
+    tk_[s] = tk;
+    pos_[s] = lk - lq + i0 + tk;
+    const int tfirst = (32 * slot) / G;
+    const int tlast = min((32 * slot + 31) / G, ntok - 1);
+    unsigned long long m = 0;
+    for (int t = tfirst; t <= tlast && t < 64; ++t) m |= 1ull << t;
+    tokmask[s] = uniform64((tfirst < ntok) ? m : 0ull);
+    if (tk < ntok) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(
+          p.q + ((int64_t)(q0 + i0 + tk) * p.hq + g * G + hh) * kHeadDim);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        qf[s][ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 2 * (16 * ks + 8 * hf)));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf[s][ks] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+  }
+
+  float m_[SPW], l_[SPW];
+  f32x16 o_[SPW][4];
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    m_[s] = -INFINITY;
+    l_[s] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o_[s][dt][r] = 0.f;
+  }
+  __syncthreads();  // kbase / vbase visible; q loads done
+
+  // Staging: lane l of wave w loads the 16-byte chunk (row r_i, logical
+  // chunk c) for physical position (r_i, l % 16), r_i = 4 w + l / 16 + 16 i.
+  const int lr0 = 4 * wave + (lane >> 4);
+  const int64_t koff0 = lr0 * kst + 16 * swz_k(lr0, lane & 15);
+  const int64_t voff0 = lr0 * vst + 16 * swz_v(lr0, lane & 15);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds.kv[0])) + wave * 1024;
+
+  auto issue = [&](int u, int buf) {
+    const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    const uint8_t* kb = p.k + lds.kbase[u];
+    const uint8_t* vb = p.v + lds.vbase[u];
+    const uint32_t dst = lds0 + buf * (2 * kTileBytes);
+    if (nvalid == kBlock) {
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i)
+        g2lds16(kb + koff0 + (int64_t)(4 * NW * i) * kst, dst + i * NW * 1024);
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i)
+        g2lds16(vb + voff0 + (int64_t)(4 * NW * i) * vst, dst + kTileBytes + i * NW * 1024);
+    } else {
+      // partial last block: rows past Lk read the block's row 0 instead
+      // (finite values; those keys are masked and their P is 0)
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i) {
+        const bool in = lr0 + 4 * NW * i < nvalid;
+        g2lds16(kb + (in ? koff0 + (int64_t)(4 * NW * i) * kst : koff0 - lr0 * kst),
+                dst + i * NW * 1024);
+      }
+#pragma unroll
+      for (int i = 0; i < KLOADS; ++i) {
+        const bool in = lr0 + 4 * NW * i < nvalid;
+        g2lds16(vb + (in ? voff0 + (int64_t)(4 * NW * i) * vst : voff0 - lr0 * vst),
+                dst + kTileBytes + i * NW * 1024);
+      }
+    }
+  };
+
+  const float C = p.scale_log2;
+  if (ucount > 0) issue(0, 0);
+
+  // per-lane constant parts of the transposed V reads: 16-lane group q16
+  // covers key half q16 / 2 and head-dim columns 16 * (q16 % 2) + 0..15 of a
+  // 32-column tile; its lane 4e + q reads row 4 * half + e, columns 4q..4q+3
+  const int q16 = lane >> 4;
+  const int vrow = 4 * (q16 >> 1) + ((lane & 15) >> 2);
+  const int vchunk = 2 * (q16 & 1) + ((lane & 3) >> 1);
+  const int vbyte = 8 * (lane & 1);
+
+  for (int u = 0; u < ucount; ++u) {
+    const int buf = u & 1;
+    const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
+    const unsigned long long umask = uniform64(lds.un.mask[u]);
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    // this wave's loads of block u done (block u+1's stay in flight), then
+    // every wave's
+    if (u + 1 < ucount) {
+      issue(u + 1, buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    block_barrier();
+
+    const uint8_t* kt_base = lds.kv[buf];
+    const uint32_t vt_lds = lds_addr(lds.kv[buf] + kTileBytes);
+
+    bool act[SPW], rowsel[SPW];
+    int lim[SPW];
+    bool any = false;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      act[s] = (umask & tokmask[s]) != 0ull;
+      any |= act[s];
+      rowsel[s] = (tk_[s] < ntok) && ((umask >> tk_[s]) & 1ull);
+      int lm = nvalid - 1;
+      if (p.causal) lm = min(lm, pos_[s] - kBlock * t);
+      lim[s] = lm;
+    }
+    if (any) {
+#pragma unroll 1
+      for (int c = 0; c < 4; ++c) {  // 32-key chunks of the block
+        // K fragments: lane l holds key 32c + l % 32, head dims 16 ks + 8 hf ..
+        bf16x8 kf[8];
+        {
+          const int r = 32 * c + l32;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks)
+            kf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+                kt_base + r * 256 + 16 * swz_k(r, 2 * ks + hf)));
+        }
+        // V^T fragments (transposed reads), waited for before the first PV
+        u32x2 vv[16];
+        {
+          const int r = 32 * c + vrow;
+          uint32_t a[4];
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+            a[dt] = vt_lds + r * 256 + 16 * swz_v(r, 4 * dt + vchunk) + vbyte;
+          vtr_issue(vv, a);
+        }
+        bool waited = false;
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+          if (!act[s]) continue;
+          // ---- S^T chunk: 32 keys x 32 query rows
+          f32x16 acc;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[ks], qf[s][ks], acc);
+          // ---- mask (diagonal / partial block only)
+          if (__ballot(rowsel[s] && lim[s] < 32 * c + 31) != 0ull) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
+              acc[r] = key <= lim[s] ? acc[r] : -INFINITY;
+            }
+          }
+          float mx = fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
+                           fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7])));
+          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
+                               fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
+          mx = rowsel[s] ? mx * C : -INFINITY;
+          // first scores of a row: take the max as the reference (O and l are
+          // still zero); afterwards move it only when it grows past the slack
+          if (__ballot(mx > m_[s] + kRescaleSlack) != 0ull) {
+            const float mr = swap32_max(mx);
+            if (__ballot(mr > m_[s] + kRescaleSlack && m_[s] > -INFINITY) != 0ull) {
+              const float alpha =
+                  mr > m_[s] + kRescaleSlack ? __builtin_amdgcn_exp2f(m_[s] - mr) : 1.0f;
+              l_[s] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) o_[s][dt] *= alpha;
+            }
+            m_[s] = mr > m_[s] + kRescaleSlack ? mr : m_[s];
+          }
+          const float mu = (rowsel[s] && m_[s] > -INFINITY) ? m_[s] : INFINITY;
+          float e[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], C, -mu));
+          l_[s] += (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
+                   (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
+          u32x4 pw0, pw1;  // P^T for the two 16-key k-steps
+          pw0[0] = cvt_pk_bf16(e[0], e[1]);
+          pw0[1] = cvt_pk_bf16(e[2], e[3]);
+          pw0[2] = cvt_pk_bf16(e[4], e[5]);
+          pw0[3] = cvt_pk_bf16(e[6], e[7]);
+          pw1[0] = cvt_pk_bf16(e[8], e[9]);
+          pw1[1] = cvt_pk_bf16(e[10], e[11]);
+          pw1[2] = cvt_pk_bf16(e[12], e[13]);
+          pw1[3] = cvt_pk_bf16(e[14], e[15]);
+          if (!waited) {
+            vtr_wait(vv);
+            waited = true;
+          }
+          // ---- O^T += V^T P^T
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const u32x4 w0 = {vv[4 * dt][0], vv[4 * dt][1], vv[4 * dt + 1][0], vv[4 * dt + 1][1]};
+            const u32x4 w1 = {vv[4 * dt + 2][0], vv[4 * dt + 2][1], vv[4 * dt + 3][0],
+                              vv[4 * dt + 3][1]};
+            o_[s][dt] = mfma32(as_bf16x8(w0), as_bf16x8(pw0), o_[s][dt]);
+            o_[s][dt] = mfma32(as_bf16x8(w1), as_bf16x8(pw1), o_[s][dt]);
+          }
+        }
+        if (!waited) vtr_wait(vv);
+      }
+    }
+    // every wave's LDS reads of buffer `buf` are done before it is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+  }
+
+  // ---- epilogue: out = O / l * v_gs (bf16), lse = (m + log2 l) * ln 2
+  const int out_row0 = q0 + i0;
+#pragma unroll
+  for (int s = 0; s < SPW; ++s) {
+    const float lsum = swap32_sum(l_[s]);
+    const int slot = wave * SPW + s;
+    const int tk = tk_[s];
+    if (tk >= ntok) continue;
+    const int hh = (32 * slot + l32) % G;
+    const int64_t row = (int64_t)(out_row0 + tk) * p.hq + g * G + hh;
+    const float inv = lsum > 0.f ? p.v_gs / lsum : 0.f;
+    uint16_t* op = p.out + row * kHeadDim + 4 * hf;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q) =
+            u32x2{pack_bf16x2(o_[s][dt][4 * q] * inv, o_[s][dt][4 * q + 1] * inv),
+                  pack_bf16x2(o_[s][dt][4 * q + 2] * inv, o_[s][dt][4 * q + 3] * inv)};
+    if (p.lse && hf == 0)
+      p.lse[row] = lsum > 0.f ? (m_[s] + __log2f(lsum)) * kLn2f : -INFINITY;
+  }
+}
+
+template <int NW, int SPW>
+static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
+  const int n = p.batch * p.hkv * p.tiles_per_req;
+  if (n <= 0) return hipSuccess;
+  const int grid = 8 * ((n + 7) / 8);
+  hipLaunchKernelGGL((msa_prefill_kernel<NW, SPW>), dim3(grid), dim3(NW * kWave), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Tiles of 4 waves x spw slots x 32 rows.
+hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream) {
+  return spw == 1 ? launch_prefill_t<4, 1>(p, stream) : launch_prefill_t<4, 2>(p, stream);
+}
+
+}  // namespace msa
