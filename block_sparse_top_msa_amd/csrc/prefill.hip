@@ -81,7 +81,8 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Transposed reads of the V^T operand of one 32-key chunk, for the four
+// Transposed reads (outputs early-clobber, see kfrag_load) of the V^T operand
+// of one 32-key chunk, for the four
 // 32-column head-dim tiles dt and the two 16-key k-steps: rows r, r + 8
 // (first k-step) and r + 16, r + 24 (second), i.e. byte offsets 0, 2048,
 // 4096, 6144.  In each group of 16 lanes, lane j receives element j % 4 of
@@ -105,10 +106,30 @@ __device__ __forceinline__ void vtr_issue(u32x2 (&v)[16], const uint32_t (&a)[4]
       "ds_read_b64_tr_b16 %13, %19 offset:2048\n\t"
       "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
       "ds_read_b64_tr_b16 %15, %19 offset:6144"
-      : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]),
-        "=v"(v[7]), "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]),
-        "=v"(v[14]), "=v"(v[15])
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+        "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]),
+        "=&v"(v[14]), "=&v"(v[15])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+// The eight K operand fragments of one 32-key chunk (ds_read_b128 each),
+// issued back to back and waited for once.  Outputs are early-clobber: a
+// load may return while later loads of the block still read their address
+// registers.
+__device__ __forceinline__ void kfrag_load(u32x4 (&k)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+        "=&v"(k[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
 }
 
 // Waits for the reads above; naming the registers orders their uses after it.
@@ -150,15 +171,27 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
   static_assert((4 * NW) % 16 == 0, "a lane's staged rows keep one swizzle phase");
   __shared__ PrefillLds lds;
 
-  const int n_units = p.batch * p.hkv * p.tiles_per_req;
-  const int lid = xcd_remap(blockIdx.x, n_units);
-  if (lid < 0) return;
-  const int jr = lid % p.tiles_per_req;
-  int rest = lid / p.tiles_per_req;
-  const int g = rest % p.hkv;
-  const int b = rest / p.hkv;
+  // Workgroup -> (request, KV head, tile).  Workgroups reach the 8 XCDs
+  // round-robin by id.  Each (request, KV head) unit keeps to its own XCDs so
+  // its K/V stays in their L2, and its tiles are dealt to those XCDs
+  // alternately, later (heavier) tiles first, so every XCD gets the same mix.
+  const int units = p.batch * p.hkv;
+  int unit, jr;
+  if (units <= 8 && 8 % units == 0) {
+    const int xpu = 8 / units;
+    const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+    unit = x / xpu;
+    jr = k * xpu + x % xpu;
+    if (jr >= p.tiles_per_req) return;
+  } else {
+    const int lid = xcd_remap(blockIdx.x, units * p.tiles_per_req);
+    if (lid < 0) return;
+    unit = lid / p.tiles_per_req;
+    jr = lid % p.tiles_per_req;
+  }
+  const int g = unit % p.hkv;
+  const int b = unit / p.hkv;
   const int j = p.tiles_per_req - 1 - jr;  // later tiles (more visible blocks) first
-
   const int q0 = p.cu_q[b];
   const int lq = p.cu_q[b + 1] - q0;
   const int i0 = j * p.tok_per_tile;
@@ -223,6 +256,19 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
     }
   }
 
+  // Settle the Q fragments once: the empty asm takes them as in/out operands,
+  // so the loads are waited for here and the loop does not see them as
+  // pending (it would otherwise wait on vmcnt inside the loop, where the
+  // counter also holds the prefetch of the next block).
+#pragma unroll
+  for (int s = 0; s < SPW; ++s)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      u32x4 w = __builtin_bit_cast(u32x4, qf[s][ks]);
+      asm volatile("" : "+v"(w));
+      qf[s][ks] = as_bf16x8(w);
+    }
+
   float m_[SPW], l_[SPW];
   f32x16 o_[SPW][4];
 #pragma unroll
@@ -280,6 +326,9 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
   // per-lane constant parts of the transposed V reads: 16-lane group q16
   // covers key half q16 / 2 and head-dim columns 16 * (q16 % 2) + 0..15 of a
   // 32-column tile; its lane 4e + q reads row 4 * half + e, columns 4q..4q+3
+  uint32_t koffs[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) koffs[ks] = l32 * 256 + 16 * swz_k(l32, 2 * ks + hf);
   const int q16 = lane >> 4;
   const int vrow = 4 * (q16 >> 1) + ((lane & 15) >> 2);
   const int vchunk = 2 * (q16 & 1) + ((lane & 3) >> 1);
@@ -300,8 +349,8 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
     }
     block_barrier();
 
-    const uint8_t* kt_base = lds.kv[buf];
-    const uint32_t vt_lds = lds_addr(lds.kv[buf] + kTileBytes);
+    const uint32_t kt_lds = lds_addr(lds.kv[buf]);
+    const uint32_t vt_lds = kt_lds + kTileBytes;
 
     bool act[SPW], rowsel[SPW];
     int lim[SPW];
@@ -319,13 +368,13 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
 #pragma unroll 1
       for (int c = 0; c < 4; ++c) {  // 32-key chunks of the block
         // K fragments: lane l holds key 32c + l % 32, head dims 16 ks + 8 hf ..
-        bf16x8 kf[8];
+        u32x4 kw[8];
         {
-          const int r = 32 * c + l32;
+          const uint32_t kbase_c = kt_lds + 32 * c * 256;
+          uint32_t a[8];
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks)
-            kf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-                kt_base + r * 256 + 16 * swz_k(r, 2 * ks + hf)));
+          for (int ks = 0; ks < 8; ++ks) a[ks] = kbase_c + koffs[ks];
+          kfrag_load(kw, a);
         }
         // V^T fragments (transposed reads), waited for before the first PV
         u32x2 vv[16];
@@ -346,7 +395,7 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) acc = mfma32(kf[ks], qf[s][ks], acc);
+          for (int ks = 0; ks < 8; ++ks) acc = mfma32(as_bf16x8(kw[ks]), qf[s][ks], acc);
           // ---- mask (diagonal / partial block only)
           if (__ballot(rowsel[s] && lim[s] < 32 * c + 31) != 0ull) {
 #pragma unroll
@@ -436,16 +485,24 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
 
 template <int NW, int SPW>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
-  const int n = p.batch * p.hkv * p.tiles_per_req;
-  if (n <= 0) return hipSuccess;
-  const int grid = 8 * ((n + 7) / 8);
+  const int units = p.batch * p.hkv;
+  if (units <= 0 || p.tiles_per_req <= 0) return hipSuccess;
+  int grid;
+  if (units <= 8 && 8 % units == 0) {
+    const int xpu = 8 / units;
+    grid = 8 * ((p.tiles_per_req + xpu - 1) / xpu);
+  } else {
+    const int n = units * p.tiles_per_req;
+    grid = 8 * ((n + 7) / 8);
+  }
   hipLaunchKernelGGL((msa_prefill_kernel<NW, SPW>), dim3(grid), dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
-// Tiles of 4 waves x spw slots x 32 rows.
+// Tiles of 256 rows: 8 waves x 1 slot or 4 waves x 2 slots of 32 rows.
 hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream) {
-  return spw == 1 ? launch_prefill_t<4, 1>(p, stream) : launch_prefill_t<4, 2>(p, stream);
+  if (spw == 1) return launch_prefill_t<8, 1>(p, stream);   // 8 waves x 1 slot
+  return launch_prefill_t<4, 2>(p, stream);                  // 4 waves x 2 slots
 }
 
 }  // namespace msa
