@@ -40,7 +40,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    ap.add_argument("--cpu-sample-rows", type=int, default=16384)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run plain copies of BYTES bytes (profiler counter scaling)")
     return ap.parse_args()
 
 
@@ -61,9 +63,24 @@ def _traffic_for(kernel: str):
     ent = data.get(kernel)
     if not ent:
         return None
-    src = os.path.join(ROOT, "block_sparse_top_msa_amd", "csrc", ent["source"])
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    return ent["bytes_per_launch"] if h == ent.get("source_sha256_16") else None
+    h = hashlib.sha256()
+    for name in ent["sources"]:
+        with open(os.path.join(ROOT, "block_sparse_top_msa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return ent["bytes_per_launch"] if h.hexdigest()[:16] == ent.get("sources_sha256_16") else None
+
+
+def calibrate_copy(nbytes: int, reps: int):
+    """Plain device-to-device copies of a known size, for scaling the HBM
+    byte counters of a profiler run (each copy reads and writes nbytes)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -102,11 +119,21 @@ def cpu_baseline_decode(p, rows_n, fmt):
     from block_sparse_top_msa_amd import accounting
     cores = len(os.sched_getaffinity(0))
     torch.set_num_threads(cores)
-    q2k = p.q2k.cpu()
     per = p.total_q // p.batch
     reqs = list(range(0, p.batch, max(1, p.batch // max(1, rows_n // per))))[:max(1, rows_n // per)]
     rows = [b * per + t for b in reqs for t in range(per)]
     t0 = time.perf_counter()
+    if p.q2k is None:
+        # full pipeline: the oracle selects the blocks for the sampled rows itself
+        s = oracle.proxy_score(p.q, p.k, p.cu_seqlens_q.cpu(), page_table=p.page_table.cpu(),
+                               seqused_k=p.seqused_k.cpu(), causal=True,
+                               max_k_tiles=p.max_k_tiles, reduce_heads=p.reduce_heads,
+                               kv_format=fmt, rows=rows)
+        q2k = oracle.topk_select(s.float(), p.topk, p.num_kv_heads, rows=rows)
+        what = "fp64 proxy + top-K + attention"
+    else:
+        q2k = p.q2k.cpu()
+        what = "fp64 attention over their selected pages"
     oracle.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q.cpu(), page_table=p.page_table.cpu(),
                             seqused_k=p.seqused_k.cpu(), causal=True, kv_format=fmt,
                             k_scale=p.k_scale, v_scale=p.v_scale,
@@ -119,8 +146,8 @@ def cpu_baseline_decode(p, rows_n, fmt):
                                         p.max_k_tiles)
     return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{len(reqs)} of {p.batch} requests ({len(rows)} query rows): fp64 "
-                      f"attention over their selected pages, {dt:.1f} s"}
+            "sample": f"{len(reqs)} of {p.batch} requests ({len(rows)} query rows): "
+                      f"{what}, {dt:.1f} s"}
 
 
 # ---------------------------------------------------------------------------
@@ -180,10 +207,10 @@ def bench_prefill_pipeline(args, msa, synth, torch):
                       "sparse_attention": round(st[2], 4)},
         "work": {"attention_flops": flops, "proxy_flops": pflops,
                  "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3)},
-        "roofline": {"kernel": "msa_attention_kernel (prefill)", "bound": "mfma",
+        "roofline": {"kernel": "msa_prefill_kernel<8,1>", "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": _traffic_for("msa_attention_kernel_prefill")},
+                     "traffic": _traffic_for("msa_prefill_kernel:" + p.name)},
     }
     return res, p
 
@@ -251,7 +278,7 @@ def bench_decode(args, msa, synth, torch):
         "roofline": {"kernel": "msa_attention_kernel (decode)", "bound": "hbm",
                      "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic_for("msa_attention_kernel_decode_" + fmt)},
+                     "traffic": _traffic_for("msa_attention_kernel:" + p.name)},
     }
     return res, p
 
@@ -268,6 +295,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, args.steps)
+        return
     if args.workload == DEFAULT_WORKLOAD or args.workload.startswith("flat_prefill"):
         res, p = bench_prefill_pipeline(args, msa, synth, torch)
         cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(p, args.cpu_sample_rows)
