@@ -171,33 +171,18 @@ def _host_max_tiles(cu_k, seqused_k) -> int:
 
 
 class Workspace:
-    """Caller-owned split-KV workspace (completion counters + partials).
-
-    The counters sit at the front; a launch needs its counter prefix zero on
-    entry and leaves it zero.  The buffer is zeroed at creation and the
-    length of the prefix known to be zero is tracked, so a later launch with
-    more (request, KV head) units re-zeroes the prefix first.  Launches that
-    may overlap need separate workspaces."""
+    """Caller-owned split-KV workspace (the fp32 partials of every split and
+    their LSE; no state survives a launch).  Launches that may overlap need
+    separate workspaces."""
 
     def __init__(self, nbytes: int, device):
         self.nbytes = int(nbytes)
-        self.buffer = torch.zeros(max(self.nbytes, 256) + 256, dtype=torch.uint8, device=device)
+        self.buffer = torch.empty(max(self.nbytes, 256) + 256, dtype=torch.uint8, device=device)
         off = (-self.buffer.data_ptr()) % 256
         self.view = self.buffer[off:off + max(self.nbytes, 256)]
-        self.clean_prefix = self.view.numel()
 
     def ensure(self, nbytes: int) -> "Workspace":
         return self if nbytes <= self.nbytes else Workspace(nbytes, self.buffer.device)
-
-    def prepare(self, counter_bytes: int):
-        if counter_bytes > self.clean_prefix:
-            self.view[:counter_bytes].zero_()
-        self.clean_prefix = counter_bytes
-
-
-def counter_bytes(batch: int, num_kv_heads: int) -> int:
-    """Bytes of the completion-counter prefix of a workspace."""
-    return (4 * batch * num_kv_heads + 255) // 256 * 256
 
 
 _ws_cache: dict = {}
@@ -288,7 +273,6 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
             workspace = ws
         elif workspace.nbytes < need.value:
             raise MsaError(6, f"workspace of {need.value} bytes needed, got {workspace.nbytes}")
-        workspace.prepare(counter_bytes(a.batch, a.num_kv_heads))
         ws_ptr, ws_bytes = _ptr(workspace.view), workspace.nbytes
     _check(lib.msa_sparse_attention(ctypes.byref(a), ws_ptr, ws_bytes, _stream()))
     return (out, lse) if return_softmax_lse else out

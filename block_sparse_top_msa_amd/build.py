@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 
-SOURCES = ["api.cpp", "attention.hip", "prefill.hip", "proxy.hip", "topk.hip"]
+SOURCES = ["api.cpp", "attention.hip", "decode.hip", "prefill.hip", "proxy.hip", "topk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -127,8 +127,14 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
       return st;
     if ((st = resolve_strides("v_scale", a->v_scale_strides, paged, a->num_kv_heads, 8, 8, &p.vs_st)))
       return st;
-    if (need_ptrs && (!aligned(a->k_scale, 8) || !aligned(a->v_scale, 8)))
-      return fail(MSA_ERR_UNSUPPORTED, "k_scale/v_scale must be 8-byte aligned");
+    // scale rows are staged two at a time (16 bytes)
+    if (p.ks_st.token != 8 || p.vs_st.token != 8 || p.ks_st.page % 16 || p.vs_st.page % 16 ||
+        p.ks_st.head % 16 || p.vs_st.head % 16)
+      return fail(MSA_ERR_UNSUPPORTED,
+                  "k_scale/v_scale: token rows must be contiguous (8 bytes) and page/head "
+                  "strides multiples of 16 bytes");
+    if (need_ptrs && (!aligned(a->k_scale, 16) || !aligned(a->v_scale, 16)))
+      return fail(MSA_ERR_UNSUPPORTED, "k_scale/v_scale must be 16-byte aligned");
   }
 
   const int G = a->num_qo_heads / a->num_kv_heads;
@@ -165,19 +171,20 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows_req = lqmax * G;
   if (rows_req <= 64) {
-    // decode shape: one tile per request, 4 waves split every block's keys
+    // decode shape: one workgroup per (request, KV head, split); its 4 waves
+    // split every page's keys
     plan.decode = 1;
     plan.tok_per_tile = lqmax;
-    const int slots = (rows_req + 15) / 16;
-    plan.spw = slots <= 1 ? 1 : (slots <= 2 ? 2 : 4);
     const int units = std::max(1, a->batch * a->num_kv_heads);
     const int union_max = std::min(lqmax * a->topk, std::max(1, a->max_k_tiles));
     int splits;
     if (a->splits > 0) {
       splits = a->splits;
     } else {
-      // fill ~2 workgroups per CU (256 CUs) with at least 2 blocks per split
-      splits = std::max(1, std::min((512 + units - 1) / units, union_max / 2));
+      // fill every CU (256) with as many workgroups as its LDS holds, with at
+      // least 4 pages per split
+      const int target = 256 * msa::decode_workgroups_per_cu(a->kv_dtype, rows_req);
+      splits = std::max(1, std::min((target + units - 1) / units, union_max / 4));
       splits = std::min(splits, 16);
     }
     plan.splits = std::max(1, std::min(splits, 64));
@@ -214,13 +221,11 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   if (plan.splits > 1) {
     const int rows = plan.tok_per_tile * G;
     const int rows_pad = (rows + 31) / 32 * 32;
-    const size_t units = (size_t)a->batch * a->num_kv_heads * p.tiles_per_req;
-    const size_t o_bytes = units * plan.splits * rows * 128 * sizeof(float);
-    const size_t l_bytes = units * plan.splits * rows_pad * sizeof(float);
-    const size_t c_bytes = units * sizeof(uint32_t);
+    const size_t units = (size_t)a->batch * a->num_kv_heads;
     p.ws_rows = rows;
     p.ws_lse_rows = rows_pad;
-    r->ws_bytes = round_up(o_bytes, 256) + round_up(l_bytes, 256) + round_up(c_bytes, 256);
+    r->ws_bytes = round_up(units * plan.splits * rows_pad * sizeof(float), 256) +
+                  round_up(units * plan.splits * rows * 128 * sizeof(float), 256);
   }
   return MSA_OK;
 }
@@ -266,17 +271,12 @@ msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", r.ws_bytes,
                   workspace_bytes, workspace);
     if (!aligned(workspace, 256)) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    // layout: [completion counters][partial LSE][partial O]; the counter
-    // prefix sits at offset 0 for every shape
-    const int rows = r.p.ws_rows;
-    const size_t units = (size_t)args->batch * args->num_kv_heads * r.p.tiles_per_req;
-    const size_t c_bytes = round_up(units * sizeof(uint32_t), 256);
+    // layout: [partial LSE][partial O]
+    const size_t units = (size_t)args->batch * args->num_kv_heads;
     const size_t l_bytes = round_up(units * r.plan.splits * r.p.ws_lse_rows * sizeof(float), 256);
-    (void)rows;
     char* base = static_cast<char*>(workspace);
-    r.p.ws_cnt = reinterpret_cast<uint32_t*>(base);
-    r.p.ws_lse = reinterpret_cast<float*>(base + c_bytes);
-    r.p.ws_o = reinterpret_cast<float*>(base + c_bytes + l_bytes);
+    r.p.ws_lse = reinterpret_cast<float*>(base);
+    r.p.ws_o = reinterpret_cast<float*>(base + l_bytes);
   }
   if (args->total_q == 0 || args->batch == 0) return ok();
   return hip_status(msa::launch_attention(r.p, args->kv_dtype, r.plan,

@@ -3,17 +3,12 @@
 // summary), with K/V blocks gathered by index into LDS, QK^T and PV on bf16
 // MFMA, and in-register fp8 / E2M1 dequantisation while staging.
 //
-// Two kernel shapes share the code:
-//  * prefill (KSPLIT = 1): each wave owns SPW 16-row slots (token x head
-//    rows of one KV head) and runs every union block over all 128 keys.  A
-//    slot whose tokens did not select a block skips it; rows of tokens that
-//    did not select it are masked.
-//  * decode (KSPLIT = 4): one tile per request; the four waves share the
-//    slots and each takes 32 keys of every block, keeping its own softmax
-//    state; the states are merged through LDS.  With splits > 1 the union is
-//    divided among workgroups that write fp32 partials, and the last one to
-//    finish (completion counter) merges them by LSE and resets the counter
-//    (prepare_msa_nvfp4_sparse_decode page, Parameters: workspace_buffer).
+// This kernel serves prefill-shaped calls with fp8 / E2M1 K/V (bf16 prefill
+// runs the asynchronous kernel in prefill.hip, decode shapes the kernel in
+// decode.hip): each wave owns SPW 16-row slots (token x head rows of one KV
+// head) and runs every union block over all 128 keys.  A slot whose tokens
+// did not select a block skips it; rows of tokens that did not select it are
+// masked.
 //
 // Orientation: S^T = K Q^T puts keys on the MFMA M axis and query rows on N,
 // so a query's scores sit in one lane group and row max / sum need only two
@@ -34,19 +29,9 @@ struct KvTile {
   uint16_t vt[kHeadDim * kVPitch];
 };
 
-struct MergeScratch {
-  float o[4][16][kHeadDim];
-  float m[4][16];
-  float l[4][16];
-};
-
 struct AttnLds {
-  union {
-    KvTile kv;
-    MergeScratch mg;
-  };
+  KvTile kv;
   UnionLds un;
-  int last;
 };
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
@@ -270,22 +255,18 @@ __device__ __forceinline__ BlockAddr block_addr(const AttnParams& p, int b, int 
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
-template <int NW, int SPW, int KSPLIT, int FMT, bool SPLIT>
+template <int NW, int SPW, int FMT>
 __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p) {
   constexpr int NT = NW * kWave;
-  constexpr int KP = kBlock / KSPLIT;   // keys per wave per block
-  constexpr int NKT = KP / 16;          // 16-key S^T subtiles
-  constexpr int NKS = KP / 32;          // 32-key PV steps
-  static_assert(KSPLIT == 1 || KSPLIT == NW, "key split spans the whole workgroup");
-  static_assert(!SPLIT || KSPLIT > 1, "split-KV runs on the decode shape");
+  constexpr int NKT = kBlock / 16;      // 16-key S^T subtiles
+  constexpr int NKS = kBlock / 32;      // 32-key PV steps
 
   __shared__ AttnLds lds;
 
-  const int n_units = p.batch * p.hkv * p.tiles_per_req * p.splits;
+  const int n_units = p.batch * p.hkv * p.tiles_per_req;
   const int lid = xcd_remap(blockIdx.x, n_units);
   if (lid < 0) return;
-  const int split = lid % p.splits;
-  int rest = lid / p.splits;
+  int rest = lid;
   const int jr = rest % p.tiles_per_req;
   rest /= p.tiles_per_req;
   const int g = rest % p.hkv;
@@ -305,17 +286,12 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
   const int lane = tid & (kWave - 1);
   const int lq16 = lane & 15;
   const int lg = lane >> 4;
-  const int sg = wave / KSPLIT;   // slot group
-  const int kq = wave % KSPLIT;   // key part
+  const int sg = wave;            // slot group
   const int G = p.group;
 
   const int32_t* rows = p.q2k + ((int64_t)g * p.total_q + q0 + i0) * p.topk;
   const int ucount = build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk);
-  int u0 = 0, u1 = ucount;
-  if (SPLIT) {
-    u0 = (int)(((int64_t)ucount * split) / p.splits);
-    u1 = (int)(((int64_t)ucount * (split + 1)) / p.splits);
-  }
+  const int u0 = 0, u1 = ucount;
 
   // Per-slot, per-lane row data.  Row r of the tile = token r / G, head r % G.
   bf16x8 qf[SPW][4];
@@ -358,7 +334,7 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
   Stage<FMT, NT> stage;
   if (u0 < u1) stage.issue(block_addr(p, b, g, lds.un.list[u0], lk), p);
 
-  const int kbase = kq * KP;
+  const int kbase = 0;
   for (int u = u0; u < u1; ++u) {
     const int t = lds.un.list[u];
     const unsigned long long umask = lds.un.mask[u];
@@ -443,164 +419,47 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
     }
   }
 
+  // epilogue: each wave writes its own rows
   const int out_row0 = q0 + i0;
-  if constexpr (KSPLIT == 1) {
-    // prefill epilogue: each wave writes its own rows
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      const int slot = sg * SPW + s;
-      const int tk = tk_[s];
-      if (tk >= ntok) continue;
-      const int hh = (16 * slot + lq16) % G;
-      const int64_t row = (int64_t)(out_row0 + tk) * p.hq + g * G + hh;
-      const float inv = l_[s] > 0.f ? p.v_gs / l_[s] : 0.f;
-      uint16_t* op = p.out + row * kHeadDim + 4 * lg;
+  for (int s = 0; s < SPW; ++s) {
+    const int slot = sg * SPW + s;
+    const int tk = tk_[s];
+    if (tk >= ntok) continue;
+    const int hh = (16 * slot + lq16) % G;
+    const int64_t row = (int64_t)(out_row0 + tk) * p.hq + g * G + hh;
+    const float inv = l_[s] > 0.f ? p.v_gs / l_[s] : 0.f;
+    uint16_t* op = p.out + row * kHeadDim + 4 * lg;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        *reinterpret_cast<u32x2*>(op + 16 * dt) =
-            u32x2{pack_bf16x2(o_[s][dt][0] * inv, o_[s][dt][1] * inv),
-                  pack_bf16x2(o_[s][dt][2] * inv, o_[s][dt][3] * inv)};
-      }
-      if (p.lse && lg == 0)
-        p.lse[row] = l_[s] > 0.f ? (m_[s] + __log2f(l_[s])) * kLn2 : -INFINITY;
+    for (int dt = 0; dt < 8; ++dt) {
+      *reinterpret_cast<u32x2*>(op + 16 * dt) =
+          u32x2{pack_bf16x2(o_[s][dt][0] * inv, o_[s][dt][1] * inv),
+                pack_bf16x2(o_[s][dt][2] * inv, o_[s][dt][3] * inv)};
     }
-  } else {
-    // decode epilogue: merge the KSPLIT key parts slot by slot through LDS,
-    // then write the output (no split) or this split's partial.
-    const int rows_tile = ntok * G;
-    const int unit = ((b * p.hkv + g) * p.tiles_per_req + j);
-#pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      __syncthreads();  // K/V tile (or previous round) no longer read
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) lds.mg.o[kq][lq16][16 * dt + 4 * lg + r] = o_[s][dt][r];
-      if (lg == 0) {
-        lds.mg.m[kq][lq16] = m_[s];
-        lds.mg.l[kq][lq16] = l_[s];
-      }
-      __syncthreads();
-      // 16 rows x 128 d, 8 consecutive d per thread
-      const int rrow = tid >> 4;
-      const int d0 = 8 * (tid & 15);
-      const int trow = 16 * s + rrow;   // row within the tile (all waves share slots)
-      if (trow < rows_tile) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int k = 0; k < KSPLIT; ++k) M = fmaxf(M, lds.mg.m[k][rrow]);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        float wk[KSPLIT], L = 0.f;
-#pragma unroll
-        for (int k = 0; k < KSPLIT; ++k) {
-          wk[k] = __builtin_amdgcn_exp2f(lds.mg.m[k][rrow] - Mu);
-          L += lds.mg.l[k][rrow] * wk[k];
-        }
-        const float invL = L > 0.f ? 1.f / L : 0.f;
-        float acc8[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float x = 0.f;
-#pragma unroll
-          for (int k = 0; k < KSPLIT; ++k) x += lds.mg.o[k][rrow][d0 + e] * wk[k];
-          acc8[e] = x * invL;
-        }
-        const float lse_nat = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-        const int tk = trow / G, hh = trow % G;
-        if (!SPLIT) {
-          const int64_t row = (int64_t)(out_row0 + tk) * p.hq + g * G + hh;
-          u32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            w[e] = pack_bf16x2(acc8[2 * e] * p.v_gs, acc8[2 * e + 1] * p.v_gs);
-          *reinterpret_cast<u32x4*>(p.out + row * kHeadDim + d0) = w;
-          if (p.lse && d0 == 0) p.lse[row] = lse_nat;
-        } else {
-          float* po = p.ws_o + (((int64_t)unit * p.splits + split) * p.ws_rows + trow) * kHeadDim + d0;
-          *reinterpret_cast<f32x4*>(po) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
-          *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
-          if (d0 == 0) p.ws_lse[((int64_t)unit * p.splits + split) * p.ws_lse_rows + trow] = lse_nat;
-        }
-      }
-    }
-    if constexpr (SPLIT) {
-      // completion counter: the last split to arrive merges by LSE
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) {
-        const uint32_t prev = atomicAdd(&p.ws_cnt[unit], 1u);
-        lds.last = (prev == (uint32_t)(p.splits - 1));
-      }
-      __syncthreads();
-      if (!lds.last) return;
-      __threadfence();
-      const int nsp = p.splits;
-      for (int task = tid; task < rows_tile * 16; task += NT) {
-        const int trow = task >> 4;
-        const int d0 = 8 * (task & 15);
-        const float* lsep = p.ws_lse + (int64_t)unit * nsp * p.ws_lse_rows + trow;
-        float M = -INFINITY;
-        for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, lsep[(int64_t)sp * p.ws_lse_rows]);
-        const float Mu = (M == -INFINITY) ? 0.f : M;
-        float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float W = 0.f;
-        for (int sp = 0; sp < nsp; ++sp) {
-          const float w = __expf(lsep[(int64_t)sp * p.ws_lse_rows] - Mu);
-          W += w;
-          const float* po = p.ws_o + (((int64_t)unit * nsp + sp) * p.ws_rows + trow) * kHeadDim + d0;
-          const f32x4 a0 = *reinterpret_cast<const f32x4*>(po);
-          const f32x4 a1 = *reinterpret_cast<const f32x4*>(po + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc8[e] += w * a0[e];
-            acc8[4 + e] += w * a1[e];
-          }
-        }
-        const float sc = W > 0.f ? p.v_gs / W : 0.f;
-        const int tk = trow / G, hh = trow % G;
-        const int64_t row = (int64_t)(out_row0 + tk) * p.hq + g * G + hh;
-        u32x4 w4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w4[e] = pack_bf16x2(acc8[2 * e] * sc, acc8[2 * e + 1] * sc);
-        *reinterpret_cast<u32x4*>(p.out + row * kHeadDim + d0) = w4;
-        if (p.lse && d0 == 0) p.lse[row] = W > 0.f ? M + __logf(W) : -INFINITY;
-      }
-      if (tid == 0) p.ws_cnt[unit] = 0u;  // ready for the next launch
-    }
+    if (p.lse && lg == 0)
+      p.lse[row] = l_[s] > 0.f ? (m_[s] + __log2f(l_[s])) * kLn2 : -INFINITY;
   }
 }
 
-template <int NW, int SPW, int KSPLIT, int FMT, bool SPLIT>
+template <int NW, int SPW, int FMT>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
-  const int n = p.batch * p.hkv * p.tiles_per_req * p.splits;
+  const int n = p.batch * p.hkv * p.tiles_per_req;
   if (n <= 0) return hipSuccess;
   const int grid = 8 * ((n + 7) / 8);
-  hipLaunchKernelGGL((msa_attention_kernel<NW, SPW, KSPLIT, FMT, SPLIT>), dim3(grid),
-                     dim3(NW * kWave), 0, stream, p);
+  hipLaunchKernelGGL((msa_attention_kernel<NW, SPW, FMT>), dim3(grid), dim3(NW * kWave), 0, stream,
+                     p);
   return hipGetLastError();
-}
-
-template <int FMT>
-static hipError_t launch_fmt(const AttnParams& p, const AttnPlan& plan, hipStream_t stream) {
-  if (!plan.decode && plan.async_bf16 && FMT == kFmtBf16) return launch_prefill_bf16(p, plan.spw, stream);
-  if (!plan.decode) return launch_one<4, 2, 1, FMT, false>(p, stream);
-  const bool split = plan.splits > 1;
-  switch (plan.spw) {
-    case 1: return split ? launch_one<4, 1, 4, FMT, true>(p, stream)
-                         : launch_one<4, 1, 4, FMT, false>(p, stream);
-    case 2: return split ? launch_one<4, 2, 4, FMT, true>(p, stream)
-                         : launch_one<4, 2, 4, FMT, false>(p, stream);
-    default: return split ? launch_one<4, 4, 4, FMT, true>(p, stream)
-                          : launch_one<4, 4, 4, FMT, false>(p, stream);
-  }
 }
 
 hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
                             hipStream_t stream) {
+  if (plan.decode) return launch_decode(p, fmt, stream);
   switch (fmt) {
-    case kFmtBf16: return launch_fmt<kFmtBf16>(p, plan, stream);
-    case kFmtFp8: return launch_fmt<kFmtFp8>(p, plan, stream);
-    default: return launch_fmt<kFmtE2m1>(p, plan, stream);
+    case kFmtBf16:
+      if (plan.async_bf16) return launch_prefill_bf16(p, plan.spw, stream);
+      return launch_one<4, 2, kFmtBf16>(p, stream);
+    case kFmtFp8: return launch_one<4, 2, kFmtFp8>(p, stream);
+    default: return launch_one<4, 2, kFmtE2m1>(p, stream);
   }
 }
 

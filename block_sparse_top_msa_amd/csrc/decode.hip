@@ -1,0 +1,755 @@
+// MSA sparse attention, decode shape: few query rows per (request, KV head)
+// (seqlen_q x G <= 64), K/V read from a paged (or flat) cache, bf16, fp8
+// E4M3 or packed E2M1 with E4M3 block scales (prepare_msa_nvfp4_sparse_decode
+// page, summary and Parameters: q, k, v, k_scale, v_scale, page_table,
+// seqused_k; msa_sparse_attention page, Parameters: k, k_scale,
+// k_global_scale, v_global_scale).
+//
+// gfx950 design (HBM-bound: every selected page is read once):
+//  * One workgroup of 4 waves per (request, KV head, split).  The union of
+//    the request's tokens' selected pages is built in LDS; a split takes a
+//    contiguous share of it.  Page ids for the share are looked up once.
+//  * Pages stream global -> LDS with global_load_lds (16 B per lane, no
+//    register staging) through a ring of NST stages, raw bytes as stored.
+//    Every wave issues the same number of 1 KiB loads per page, so waiting
+//    for a page is one vmcnt immediate.  Rows past the sequence end are
+//    filled from the page's row 0 (finite; those keys are masked).
+//  * Wave w owns keys 32w..32w+31 of every page.  K fragments are read from
+//    LDS and dequantised in registers (fp8: cvt_scalef32_pk_bf16_fp8; E2M1:
+//    nibbles -> f32 -> x block scale -> bf16); V^T fragments come from the
+//    transposing LDS reads (ds_read_b64_tr_b16 / _b8 / _b4) on row-major V,
+//    E2M1 codes scaled per key.  S^T = K Q^T and O^T += V^T P^T on
+//    v_mfma_f32_16x16x32_bf16, 16-row tiles (one tile per token at G = 16).
+//  * The four waves' softmax states are merged through LDS at the end.  With
+//    one split the output is written directly; otherwise each split writes
+//    an fp32 partial (O / l and its LSE) and msa_decode_merge_kernel combines
+//    them by LSE (prepare_msa_nvfp4_sparse_decode page, Parameters:
+//    workspace_buffer).  A separate launch orders the partial writes before
+//    the merge without device-scope fences inside the kernel (each such
+//    fence writes back and invalidates the whole L2).
+#include "async_lds.hpp"
+#include "common.hpp"
+#include "internal.hpp"
+#include "tile_union.hpp"
+
+namespace msa {
+
+namespace {
+
+constexpr float kLn2d = 0.69314718055994530942f;
+
+template <int FMT>
+struct DecGeom;
+
+template <>
+struct DecGeom<kFmtBf16> {
+  static constexpr int kRow = 256;                 // bytes per K / V row
+  static constexpr int kSide = kBlock * kRow;      // 32 KiB
+  static constexpr int kStage = 2 * kSide;         // K | V
+  static constexpr int kStages = 2;
+  static constexpr int kLoads = kStage / 4096;     // 1 KiB loads per wave per page
+};
+
+template <>
+struct DecGeom<kFmtFp8> {
+  static constexpr int kRow = 128;
+  static constexpr int kSide = kBlock * kRow;      // 16 KiB
+  static constexpr int kStage = 2 * kSide;
+  static constexpr int kStages = 2;
+  static constexpr int kLoads = kStage / 4096;
+};
+
+template <>
+struct DecGeom<kFmtE2m1> {
+  static constexpr int kRow = 64;                  // 128 nibbles
+  static constexpr int kSide = kBlock * kRow;      // 8 KiB
+  static constexpr int kScale = kBlock * 8;        // 1 KiB of E4M3 scales per side
+  // K | V | K scales | V scales | 2 KiB target of two padding loads
+  static constexpr int kStage = 2 * kSide + 2 * kScale + 2048;
+  static constexpr int kStages = 3;
+  static constexpr int kLoads = kStage / 4096;     // 5
+};
+
+template <int FMT>
+struct DecodeLds {
+  static constexpr int kRing = DecGeom<FMT>::kStages * DecGeom<FMT>::kStage;
+  uint8_t ring[kRing];
+  UnionLds un;
+  int32_t page[kMaxUnion];   // page id (paged) or first row (flat) of each entry of the share
+};
+
+struct MergeLds {
+  float o[4][16][kHeadDim];
+  float m[4][16];
+  float l[4][16];
+};
+
+__device__ __forceinline__ float xsum16_32(float x) {
+  x += __shfl_xor(x, 16, kWave);
+  return x + __shfl_xor(x, 32, kWave);
+}
+__device__ __forceinline__ float xmax16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, kWave));
+  return fmaxf(x, __shfl_xor(x, 32, kWave));
+}
+
+// ---- LDS fragment reads (asm, so that in-flight LDS-DMA writes of other
+// stages do not make the compiler wait for every outstanding load).
+__device__ __forceinline__ void lds_b128x4(u32x4 (&k)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+__device__ __forceinline__ void lds_b128x2_u16x2(u32x4 (&k)[2], uint32_t (&s)[2],
+                                                 const uint32_t (&a)[2], const uint32_t (&as)[2]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_u16 %2, %6\n\t"
+      "ds_read_u16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(s[0]), "=&v"(s[1])
+      : "v"(a[0]), "v"(a[1]), "v"(as[0]), "v"(as[1]));
+}
+
+// bf16 V^T: for head-dim tile dt, reads at a[dt] (keys 4q..4q+3) and
+// a[dt] + 4096 (keys 16 + 4q..): lane j of a 16-lane group receives element
+// j % 4 of the 8 bytes at lane 4e + j / 4's address for e = 0..3.
+__device__ __forceinline__ void vtr16_issue(u32x2 (&v)[16], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %2, %17\n\t"
+      "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %4, %18\n\t"
+      "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %6, %19\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %8, %20\n\t"
+      "ds_read_b64_tr_b16 %9, %20 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %10, %21\n\t"
+      "ds_read_b64_tr_b16 %11, %21 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %12, %22\n\t"
+      "ds_read_b64_tr_b16 %13, %22 offset:4096\n\t"
+      "ds_read_b64_tr_b16 %14, %23\n\t"
+      "ds_read_b64_tr_b16 %15, %23 offset:4096"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
+        "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]),
+        "=&v"(v[13]), "=&v"(v[14]), "=&v"(v[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+__device__ __forceinline__ void wait16(u32x2 (&v)[16]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
+                 "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+}
+
+// fp8 V^T (ds_read_b64_tr_b8): lane j of a 16-lane group receives byte
+// j % 8 of the 8 bytes at lane 2e + j / 8's address for e = 0..7.
+// E2M1 V^T (ds_read_b64_tr_b4): lane j receives nibble j of the 8 bytes at
+// lane e's address, for e = 0..15 (nibble e of the result).
+template <bool B4>
+__device__ __forceinline__ void vtr8_issue(u32x2 (&v)[8], const uint32_t (&a)[8]) {
+  if constexpr (B4) {
+    asm volatile(
+        "ds_read_b64_tr_b4 %0, %8\n\t"
+        "ds_read_b64_tr_b4 %1, %9\n\t"
+        "ds_read_b64_tr_b4 %2, %10\n\t"
+        "ds_read_b64_tr_b4 %3, %11\n\t"
+        "ds_read_b64_tr_b4 %4, %12\n\t"
+        "ds_read_b64_tr_b4 %5, %13\n\t"
+        "ds_read_b64_tr_b4 %6, %14\n\t"
+        "ds_read_b64_tr_b4 %7, %15"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b8 %0, %8\n\t"
+        "ds_read_b64_tr_b8 %1, %9\n\t"
+        "ds_read_b64_tr_b8 %2, %10\n\t"
+        "ds_read_b64_tr_b8 %3, %11\n\t"
+        "ds_read_b64_tr_b8 %4, %12\n\t"
+        "ds_read_b64_tr_b8 %5, %13\n\t"
+        "ds_read_b64_tr_b8 %6, %14\n\t"
+        "ds_read_b64_tr_b8 %7, %15"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+  }
+}
+__device__ __forceinline__ void wait8(u32x2 (&v)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
+                 "+v"(v[6]), "+v"(v[7]));
+}
+
+// The eight E4M3 V-scale rows (8 bytes each) of this lane's keys.
+__device__ __forceinline__ void lds_b64x8(u32x2 (&v)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b64 %0, %8\n\t"
+      "ds_read_b64 %1, %9\n\t"
+      "ds_read_b64 %2, %10\n\t"
+      "ds_read_b64 %3, %11\n\t"
+      "ds_read_b64 %4, %12\n\t"
+      "ds_read_b64 %5, %13\n\t"
+      "ds_read_b64 %6, %14\n\t"
+      "ds_read_b64 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+
+// ---- in-register dequantisation (exact: E4M3 and E2M1 values and their
+// products with E4M3 scales fit bf16 / fp32 without rounding, except a
+// product of two E4M3-range numbers, rounded once to bf16)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// 8 fp8 E4M3 bytes (two dwords) -> 8 bf16
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return u32x4{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+}
+
+// 8 E2M1 nibbles (one dword, low nibble = even element) x scale -> 8 bf16
+__device__ __forceinline__ u32x4 e2m1x8_scaled(uint32_t w, float s) {
+  u32x4 r;
+  f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  r[0] = cvt_pk_bf16(a[0] * s, a[1] * s);
+  a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  r[1] = cvt_pk_bf16(a[0] * s, a[1] * s);
+  a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  r[2] = cvt_pk_bf16(a[0] * s, a[1] * s);
+  a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  r[3] = cvt_pk_bf16(a[0] * s, a[1] * s);
+  return r;
+}
+
+// 8 E2M1 nibbles of 8 different keys x each key's scale -> 8 bf16
+__device__ __forceinline__ u32x4 e2m1x8_keyscaled(uint32_t w, const float (&s)[8]) {
+  u32x4 r;
+  f32x2_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  r[0] = cvt_pk_bf16(a[0] * s[0], a[1] * s[1]);
+  a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  r[1] = cvt_pk_bf16(a[0] * s[2], a[1] * s[3]);
+  a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  r[2] = cvt_pk_bf16(a[0] * s[4], a[1] * s[5]);
+  a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  r[3] = cvt_pk_bf16(a[0] * s[6], a[1] * s[7]);
+  return r;
+}
+
+// byte `sel` (0..3) of each of four dwords packed into one dword
+__device__ __forceinline__ uint32_t gather_byte(uint32_t a, uint32_t b, uint32_t c, uint32_t d,
+                                                int sel) {
+  const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u + 0x0101u * (uint32_t)sel);
+  const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x04000c0cu + 0x01010000u * (uint32_t)sel);
+  return ab | cd;
+}
+
+}  // namespace
+
+template <int FMT, int RT>
+__global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
+  using Geo = DecGeom<FMT>;
+  constexpr int NST = Geo::kStages;
+  constexpr int LOADS = Geo::kLoads;
+  __shared__ __attribute__((aligned(16))) DecodeLds<FMT> lds;
+
+  const int lid = blockIdx.x;
+  const int split = lid % p.splits;
+  const int unit = lid / p.splits;
+  const int g = unit % p.hkv;
+  const int b = unit / p.hkv;
+  if (b >= p.batch) return;
+  const int q0 = p.cu_q[b];
+  const int lq = p.cu_q[b + 1] - q0;
+  if (lq <= 0) return;
+  const int ntok = min(lq, p.tok_per_tile);
+  const int G = p.group;
+  const int R = ntok * G;
+  const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
+  const int nblk = max(0, min((lk + kBlock - 1) / kBlock, p.max_k_tiles));
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int l16 = lane & 15;
+  const int q = lane >> 4;
+
+  const int32_t* rows = p.q2k + ((int64_t)g * p.total_q + q0) * p.topk;
+  const int ucount = __builtin_amdgcn_readfirstlane(
+      build_tile_union<256>(lds.un, rows, ntok, p.topk, nblk));
+  const int u0 = (int)(((int64_t)ucount * split) / p.splits);
+  const int u1 = (int)(((int64_t)ucount * (split + 1)) / p.splits);
+  const int n = u1 - u0;
+  for (int i = tid; i < n; i += 256) {
+    const int t = lds.un.list[u0 + i];
+    lds.page[i] = p.paged ? p.page_table[(int64_t)b * p.pt_width + t] : p.cu_k[b] + kBlock * t;
+  }
+
+  // ---- per row tile: lane l holds query row 16 rt + l % 16 (token r / G, head r % G)
+  bf16x8 qf[RT][4];
+  int tk_[RT], pos_[RT];
+  unsigned long long tokmask[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int r = 16 * rt + l16;
+    const int tk = r < R ? r / G : 64;
+    tk_[rt] = tk;
+    pos_[rt] = lk - lq + tk;
+    const int tfirst = (16 * rt) / G;
+    const int tlast = min((16 * rt + 15) / G, ntok - 1);
+    unsigned long long m = 0;
+    for (int t = tfirst; t <= tlast && t < 64; ++t) m |= 1ull << t;
+    tokmask[rt] = uniform64((16 * rt < R) ? m : 0ull);
+    if (r < R) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(
+          p.q + ((int64_t)(q0 + tk) * p.hq + g * G + r % G) * kHeadDim) + 64 * q;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+        qf[rt][ds] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ds));
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) qf[rt][ds] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+  }
+  // settle the Q loads before the loop (see the prefill kernel)
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) {
+      u32x4 w = __builtin_bit_cast(u32x4, qf[rt][ds]);
+      asm volatile("" : "+v"(w));
+      qf[rt][ds] = as_bf16x8(w);
+    }
+
+  float m_[RT], l_[RT];
+  f32x4 o_[RT][8];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m_[rt] = -INFINITY;
+    l_[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();  // page ids visible
+
+  // ---- staging: load n = wave + 4 i (i < LOADS) fills LDS bytes
+  // [1024 n, 1024 n + 1024) of the stage; lane l writes 16 bytes at 16 l.
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr(lds.ring));
+  const int64_t kst = p.k_st.token, vst = p.v_st.token;
+  auto issue = [&](int i, int stage) {
+    const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u0 + i]);
+    const int pg = __builtin_amdgcn_readfirstlane(lds.page[i]);
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    const uint8_t* kb;
+    const uint8_t* vb;
+    if (p.paged) {
+      kb = p.k + (int64_t)pg * p.k_st.page + g * p.k_st.head;
+      vb = p.v + (int64_t)pg * p.v_st.page + g * p.v_st.head;
+    } else {
+      kb = p.k + (int64_t)pg * kst + g * p.k_st.head;
+      vb = p.v + (int64_t)pg * vst + g * p.v_st.head;
+    }
+    const uint32_t dst = ring0 + stage * Geo::kStage;
+#pragma unroll
+    for (int li = 0; li < LOADS; ++li) {
+      const int nn = wave + 4 * li;
+      const uint8_t* src;
+      if constexpr (FMT == kFmtBf16) {
+        // rows of 256 B: 4 rows per load
+        const bool isv = nn >= 32;
+        const int row = 4 * (nn & 31) + (lane >> 4);
+        const int rr = row < nvalid ? row : 0;
+        const int c = isv ? ((lane & 15) ^ ((row & 3) << 1)) : ((lane & 15) ^ (row & 15));
+        src = (isv ? vb + rr * vst : kb + rr * kst) + 16 * c;
+      } else if constexpr (FMT == kFmtFp8) {
+        // rows of 128 B: 8 rows per load
+        const bool isv = nn >= 16;
+        const int row = 8 * (nn & 15) + (lane >> 3);
+        const int rr = row < nvalid ? row : 0;
+        const int gv = (row & 3) | (((row >> 4) & 1) << 2);
+        const int c = isv ? ((lane & 7) ^ gv) : ((lane & 7) ^ (row & 7));
+        src = (isv ? vb + rr * vst : kb + rr * kst) + 16 * c;
+      } else {
+        if (nn < 16) {
+          // data rows of 64 B: 16 rows per load
+          const bool isv = nn >= 8;
+          const int row = 16 * (nn & 7) + (lane >> 2);
+          const int rr = row < nvalid ? row : 0;
+          const int gv = ((row >> 1) & 1) | (((row >> 4) & 1) << 1);
+          const int c = isv ? ((lane & 3) ^ gv) : ((lane & 3) ^ ((row >> 1) & 3));
+          src = (isv ? vb + rr * vst : kb + rr * kst) + 16 * c;
+        } else {
+          // scale rows of 8 B, two per lane; loads 18 and 19 only pad the
+          // count (they rewrite K scales into the spare 2 KiB)
+          const bool isv = nn == 17;
+          const int row = 2 * lane;
+          const int rr = row < nvalid ? row : 0;
+          const uint8_t* sb;
+          if (p.paged) {
+            sb = isv ? p.vs + (int64_t)pg * p.vs_st.page + g * p.vs_st.head
+                     : p.ks + (int64_t)pg * p.ks_st.page + g * p.ks_st.head;
+          } else {
+            sb = isv ? p.vs + (int64_t)pg * p.vs_st.token + g * p.vs_st.head
+                     : p.ks + (int64_t)pg * p.ks_st.token + g * p.ks_st.head;
+          }
+          src = sb + rr * (isv ? p.vs_st.token : p.ks_st.token);
+        }
+      }
+      g2lds16(src, dst + 1024 * nn);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < n) issue(s, s);
+
+  const float C = p.scale_log2;
+  const int kw0 = 32 * wave;  // this wave's first key of every page
+
+  for (int i = 0; i < n; ++i) {
+    const int stage = i % NST;
+    // this page's loads done (NST - 2 later pages may stay in flight), then
+    // every wave's; the barrier also frees stage (i - 1) % NST for reuse
+    if constexpr (NST == 3) {
+      if (i + 1 < n) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    block_barrier();
+    if (i + NST - 1 < n) issue(i + NST - 1, (i + NST - 1) % NST);
+
+    const int u = u0 + i;
+    const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
+    const unsigned long long umask = uniform64(lds.un.mask[u]);
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    bool any = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) any |= (umask & tokmask[rt]) != 0ull;
+    if (!any) continue;
+
+    const uint32_t sb = ring0 + stage * Geo::kStage;
+
+    // ---- K fragments (A operand of S^T): key kw0 + 16 kt + l % 16,
+    // head dims 32 q + 8 ds .. + 7 for k-step ds
+    bf16x8 kf[2][4];
+    if constexpr (FMT == kFmtBf16) {
+      u32x4 kw[8];
+      uint32_t a[8];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = kw0 + 16 * kt + l16;
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) a[4 * kt + ds] = sb + row * 256 + 16 * ((4 * q + ds) ^ (row & 15));
+      }
+      kfrag_load(kw, a);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = as_bf16x8(kw[4 * kt + ds]);
+    } else if constexpr (FMT == kFmtFp8) {
+      u32x4 kw[4];
+      uint32_t a[4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = kw0 + 16 * kt + l16;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) a[2 * kt + j] = sb + row * 128 + 16 * ((2 * q + j) ^ (row & 7));
+      }
+      lds_b128x4(kw, a);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 w = kw[2 * kt + j];
+          kf[kt][2 * j] = as_bf16x8(fp8x8_to_bf16(w[0], w[1]));
+          kf[kt][2 * j + 1] = as_bf16x8(fp8x8_to_bf16(w[2], w[3]));
+        }
+    } else {
+      u32x4 kw[2];
+      uint32_t ks[2];
+      uint32_t a[2], as[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = kw0 + 16 * kt + l16;
+        a[kt] = sb + row * 64 + 16 * (q ^ ((row >> 1) & 3));
+        as[kt] = sb + 2 * Geo::kSide + row * 8 + 2 * q;
+      }
+      lds_b128x2_u16x2(kw, ks, a, as);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ks[kt], 1.0f, false);
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) kf[kt][ds] = as_bf16x8(e2m1x8_scaled(kw[kt][ds], ds < 2 ? sc[0] : sc[1]));
+      }
+    }
+
+    // ---- V^T fragments (A operand of O^T): head dim 16 dt + l % 16, keys
+    // kw0 + {4q..4q+3, 16+4q..16+4q+3} (the order of P in the S^T registers)
+    bf16x8 vf[8];
+    if constexpr (FMT == kFmtBf16) {
+      u32x2 vv[16];
+      uint32_t a[8];
+      const int e = l16 >> 2, aa = lane & 3;
+      const int row = kw0 + 4 * q + e;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) a[dt] = sb + Geo::kSide + row * 256 + 32 * (dt ^ e) + 8 * aa;
+      vtr16_issue(vv, a);
+      wait16(vv);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        vf[dt] = as_bf16x8(u32x4{vv[2 * dt][0], vv[2 * dt][1], vv[2 * dt + 1][0], vv[2 * dt + 1][1]});
+    } else if constexpr (FMT == kFmtFp8) {
+      u32x2 vv[8];
+      uint32_t a[8];
+      const int e = l16 >> 1, aa = lane & 1;
+      const int row = kw0 + (e < 4 ? 4 * q + e : 16 + 4 * q + e - 4);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) a[dt] = sb + Geo::kSide + row * 128 + 16 * (dt ^ e) + 8 * aa;
+      vtr8_issue<false>(vv, a);
+      wait8(vv);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        vf[dt] = as_bf16x8(fp8x8_to_bf16(vv[dt][0], vv[dt][1]));
+      }
+    } else {
+      u32x2 vv[8], vsr[8];
+      uint32_t a[8], asr[8];
+      const int e = l16 & 7;
+      const int row = kw0 + (e < 4 ? 4 * q + e : 16 + 4 * q + e - 4);
+      const int gv = ((row >> 1) & 1) | (((row >> 4) & 1) << 1);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        a[dt] = sb + Geo::kSide + row * 64 + 16 * ((dt >> 1) ^ gv) + 8 * (dt & 1);
+      vtr8_issue<true>(vv, a);
+      // scale rows of this lane's eight keys
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int rk = kw0 + (k < 4 ? 4 * q + k : 16 + 4 * q + k - 4);
+        asr[k] = sb + 2 * Geo::kSide + Geo::kScale + rk * 8;
+      }
+      lds_b64x8(vsr, asr);
+      wait8(vv);   // orders the uses of the transposed reads after their wait
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int rk = kw0 + (k < 4 ? 4 * q + k : 16 + 4 * q + k - 4);
+        if (rk >= nvalid) vsr[k] = u32x2{0u, 0u};   // no scale of a row past the end
+      }
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const int w = dt >> 2, sel = dt & 3;
+        const uint32_t s03 = gather_byte(vsr[0][w], vsr[1][w], vsr[2][w], vsr[3][w], sel);
+        const uint32_t s47 = gather_byte(vsr[4][w], vsr[5][w], vsr[6][w], vsr[7][w], sel);
+        float s[8];
+        f32x2_t x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s03, 1.0f, false);
+        s[0] = x[0]; s[1] = x[1];
+        x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s03, 1.0f, true);
+        s[2] = x[0]; s[3] = x[1];
+        x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s47, 1.0f, false);
+        s[4] = x[0]; s[5] = x[1];
+        x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s47, 1.0f, true);
+        s[6] = x[0]; s[7] = x[1];
+        vf[dt] = as_bf16x8(e2m1x8_keyscaled(vv[dt][0], s));
+      }
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if ((umask & tokmask[rt]) == 0ull) continue;
+      f32x4 acc[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) acc[kt] = mfma16(kf[kt][ds], qf[rt][ds], acc[kt]);
+      }
+      const bool sel = (tk_[rt] < ntok) && ((umask >> tk_[rt]) & 1ull);
+      int lim = nvalid - 1;
+      if (p.causal) lim = min(lim, pos_[rt] - kBlock * t);
+      lim = sel ? lim : -1;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kw0 + 16 * kt + 4 * q + r;
+          const float x = key <= lim ? acc[kt][r] * C : -INFINITY;
+          acc[kt][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = xmax16_32(mx);
+      const float m_new = fmaxf(m_[rt], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_[rt] - m_use);
+      float e[8];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[4 * kt + r] = __builtin_amdgcn_exp2f(acc[kt][r] - m_use);
+      l_[rt] = l_[rt] * alpha + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+      m_[rt] = m_new;
+      const bf16x8 pf = as_bf16x8(u32x4{cvt_pk_bf16(e[0], e[1]), cvt_pk_bf16(e[2], e[3]),
+                                        cvt_pk_bf16(e[4], e[5]), cvt_pk_bf16(e[6], e[7])});
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = mfma16(vf[dt], pf, o_[rt][dt] * alpha);
+    }
+  }
+
+  // ---- merge the four waves' states row tile by row tile through LDS
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+  MergeLds& mg = *reinterpret_cast<MergeLds*>(lds.ring);
+  const int unit_split = unit * p.splits + split;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    if (16 * rt >= R) break;
+    const float lsum = xsum16_32(l_[rt]);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *reinterpret_cast<f32x4*>(&mg.o[wave][l16][16 * dt + 4 * q]) = o_[rt][dt];
+    if (q == 0) {
+      mg.m[wave][l16] = m_[rt];
+      mg.l[wave][l16] = lsum;
+    }
+    __syncthreads();
+    const int rr = tid >> 4;          // row within the tile
+    const int d0 = 8 * (tid & 15);
+    const int row = 16 * rt + rr;
+    if (row < R) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, mg.m[w][rr]);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      float wk[4], L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        wk[w] = __builtin_amdgcn_exp2f(mg.m[w][rr] - Mu);
+        L += mg.l[w][rr] * wk[w];
+      }
+      const float invL = L > 0.f ? 1.f / L : 0.f;
+      float acc8[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        float x = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x += mg.o[w][rr][d0 + k] * wk[w];
+        acc8[k] = x * invL;
+      }
+      const float lse_nat = L > 0.f ? (M + __log2f(L)) * kLn2d : -INFINITY;
+      if (p.splits == 1) {
+        const int64_t orow = (int64_t)(q0 + row / G) * p.hq + g * G + row % G;
+        u32x4 w4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) w4[k] = pack_bf16x2(acc8[2 * k] * p.v_gs, acc8[2 * k + 1] * p.v_gs);
+        *reinterpret_cast<u32x4*>(p.out + orow * kHeadDim + d0) = w4;
+        if (p.lse && d0 == 0) p.lse[orow] = lse_nat;
+      } else {
+        float* po = p.ws_o + ((int64_t)unit_split * p.ws_rows + row) * kHeadDim + d0;
+        *reinterpret_cast<f32x4*>(po) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
+        *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
+        if (d0 == 0) p.ws_lse[(int64_t)unit_split * p.ws_lse_rows + row] = lse_nat;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Combine the split partials of every (request, KV head) by their LSE:
+// lse = ln sum_s exp(lse_s), out = v_gs * sum_s exp(lse_s - lse) O_s.
+// Thread: one row, 8 head dims.
+__global__ __launch_bounds__(256) void msa_decode_merge_kernel(AttnParams p) {
+  const int per_unit = p.ws_rows * 16;
+  const int64_t task = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int unit = (int)(task / per_unit);
+  const int rem = (int)(task % per_unit);
+  if (unit >= p.batch * p.hkv) return;
+  const int g = unit % p.hkv, b = unit / p.hkv;
+  const int q0 = p.cu_q[b];
+  const int lq = min(p.cu_q[b + 1] - q0, p.tok_per_tile);
+  const int row = rem >> 4, d0 = 8 * (rem & 15);
+  if (row >= lq * p.group) return;
+  const int nsp = p.splits;
+  const float* lsep = p.ws_lse + (int64_t)unit * nsp * p.ws_lse_rows + row;
+  float M = -INFINITY;
+  for (int s = 0; s < nsp; ++s) M = fmaxf(M, lsep[(int64_t)s * p.ws_lse_rows]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float W = 0.f;
+  for (int s = 0; s < nsp; ++s) {
+    const float w = __expf(lsep[(int64_t)s * p.ws_lse_rows] - Mu);
+    W += w;
+    const float* po = p.ws_o + (((int64_t)unit * nsp + s) * p.ws_rows + row) * kHeadDim + d0;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(po);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(po + 4);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[k] += w * a0[k];
+      acc[4 + k] += w * a1[k];
+    }
+  }
+  const float sc = W > 0.f ? p.v_gs / W : 0.f;
+  const int64_t orow = (int64_t)(q0 + row / p.group) * p.hq + g * p.group + row % p.group;
+  u32x4 w4;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w4[k] = pack_bf16x2(acc[2 * k] * sc, acc[2 * k + 1] * sc);
+  *reinterpret_cast<u32x4*>(p.out + orow * kHeadDim + d0) = w4;
+  if (p.lse && d0 == 0) p.lse[orow] = W > 0.f ? M + __logf(W) : -INFINITY;
+}
+
+template <int FMT, int RT>
+static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
+  const int n = p.batch * p.hkv * p.splits;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((msa_decode_kernel<FMT, RT>), dim3(n), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t tasks = (int64_t)p.batch * p.hkv * p.ws_rows * 16;
+  hipLaunchKernelGGL(msa_decode_merge_kernel, dim3((unsigned)((tasks + 255) / 256)), dim3(256), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_decode_fmt(const AttnParams& p, hipStream_t stream) {
+  const int rows = p.tok_per_tile * p.group;
+  if (rows <= 16) return launch_decode_t<FMT, 1>(p, stream);
+  if (rows <= 32) return launch_decode_t<FMT, 2>(p, stream);
+  if (rows <= 48) return launch_decode_t<FMT, 3>(p, stream);
+  return launch_decode_t<FMT, 4>(p, stream);
+}
+
+hipError_t launch_decode(const AttnParams& p, int fmt, hipStream_t stream) {
+  switch (fmt) {
+    case kFmtBf16: return launch_decode_fmt<kFmtBf16>(p, stream);
+    case kFmtFp8: return launch_decode_fmt<kFmtFp8>(p, stream);
+    default: return launch_decode_fmt<kFmtE2m1>(p, stream);
+  }
+}
+
+int decode_workgroups_per_cu(int fmt, int rows) {
+  // more than one row tile takes over half the register file
+  if (rows > 16) return 1;
+  auto per = [](int bytes) { return (160 * 1024) / bytes; };
+  switch (fmt) {
+    case kFmtBf16: return per(sizeof(DecodeLds<kFmtBf16>));
+    case kFmtFp8: return per(sizeof(DecodeLds<kFmtFp8>));
+    default: return per(sizeof(DecodeLds<kFmtE2m1>));
+  }
+}
+
+}  // namespace msa

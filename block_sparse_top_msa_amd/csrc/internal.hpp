@@ -41,18 +41,17 @@ struct AttnParams {
   int splits;                 // split-KV partials per tile (1 = none)
   float scale_log2;           // softmax_scale * k_global_scale * log2(e)
   float v_gs;
-  float* ws_o;                // [units, splits, rows, 128] fp32
-  float* ws_lse;              // [units, splits, rows_pad]
-  uint32_t* ws_cnt;           // [units]
+  float* ws_o;                // [units, splits, rows, 128] fp32 split partials (O / l)
+  float* ws_lse;              // [units, splits, rows_pad] their natural-log LSE
   int ws_rows;                // rows per unit (tok_per_tile * group)
   int ws_lse_rows;            // rows_pad: rows rounded up to 32
 };
 
 // Kernel family selection for one attention call.
 struct AttnPlan {
-  int decode;       // 1: key-split decode kernel; 0: slot-per-wave prefill kernel
+  int decode;       // 1: decode kernel (<= 64 rows per request and KV head)
   int async_bf16;   // prefill with bf16 K/V: asynchronous LDS staging kernel
-  int spw;          // 16-row slots per wave
+  int spw;          // prefill slots per wave
   int tok_per_tile;
   int splits;
 };
@@ -60,8 +59,12 @@ struct AttnPlan {
 hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
                             hipStream_t stream);
 
-// bf16 prefill tiles of 4 waves x spw slots x 16 rows (spw = 2 or 4)
+// bf16 prefill tiles of 256 rows: 8 waves x 1 slot (spw 1) or 4 x 2 (spw 2)
 hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream);
+
+// decode kernel (+ split merge when p.splits > 1); workgroups one CU holds
+hipError_t launch_decode(const AttnParams& p, int fmt, hipStream_t stream);
+int decode_workgroups_per_cu(int fmt, int rows);
 
 struct ProxyParams {
   const uint16_t* q;

@@ -24,6 +24,7 @@
 //    (rescaling O and l) only if a score exceeds it by more than 2^64, which
 //    the fp32 accumulators absorb; row sums stay per lane until the end.  A slot none of whose tokens chose a
 //    block skips it (one scalar branch per slot and chunk).
+#include "async_lds.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 #include "tile_union.hpp"
@@ -53,33 +54,6 @@ struct PrefillLds {
 // distinct chunk quads.
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 2); }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// global -> LDS, 16 bytes per lane, lane l writing at lds_base + 16 l.
-// Issued from inline asm so that the compiler does not treat the in-flight
-// LDS writes as pending on every later LDS read (it would wait for the whole
-// prefetch); completion is awaited explicitly with vmcnt.
-__device__ __forceinline__ void g2lds16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\t"
-               "s_nop 0\n\t"
-               "global_load_lds_dwordx4 %0, off"
-               :
-               : "v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// Workgroup barrier that does not drain outstanding global loads (unlike
-// __syncthreads, whose release fence waits for every in-flight load,
-// including the next block's prefetch).  Callers first wait on exactly the
-// counters they need; the asm statements keep memory accesses in place.
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // Transposed reads (outputs early-clobber, see kfrag_load) of the V^T operand
 // of one 32-key chunk, for the four
@@ -112,26 +86,6 @@ __device__ __forceinline__ void vtr_issue(u32x2 (&v)[16], const uint32_t (&a)[4]
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
 
-// The eight K operand fragments of one 32-key chunk (ds_read_b128 each),
-// issued back to back and waited for once.  Outputs are early-clobber: a
-// load may return while later loads of the block still read their address
-// registers.
-__device__ __forceinline__ void kfrag_load(u32x4 (&k)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %9\n\t"
-      "ds_read_b128 %2, %10\n\t"
-      "ds_read_b128 %3, %11\n\t"
-      "ds_read_b128 %4, %12\n\t"
-      "ds_read_b128 %5, %13\n\t"
-      "ds_read_b128 %6, %14\n\t"
-      "ds_read_b128 %7, %15\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
-        "=&v"(k[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
-}
-
 // Waits for the reads above; naming the registers orders their uses after it.
 __device__ __forceinline__ void vtr_wait(u32x2 (&v)[16]) {
   asm volatile("s_waitcnt lgkmcnt(0)"
@@ -147,17 +101,6 @@ __device__ __forceinline__ float swap32_max(float x) {
 __device__ __forceinline__ float swap32_sum(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
-}
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  bf16x2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-
-__device__ __forceinline__ unsigned long long uniform64(unsigned long long x) {
-  return ((unsigned long long)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
-         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
 }
 
 }  // namespace

@@ -109,7 +109,9 @@ typedef struct {
   const void* k;          /* flat [total_k, Hkv, d'] or paged [pages, Hkv, 128, d'];
                              d' = 128 (bf16, fp8) or 64 bytes (E2M1)          */
   const void* v;          /* same layout rules as k                           */
-  const void* k_scale;    /* E2M1 only: E4M3 bytes [pages, Hkv, 128, 8]       */
+  const void* k_scale;    /* E2M1 only: E4M3 bytes [pages, Hkv, 128, 8], one per
+                             16 values of a row; rows contiguous (8 bytes),
+                             16-byte aligned page/head strides and base       */
   const void* v_scale;    /* E2M1 only: same, stored linearly                 */
   msa_strides_t k_strides, v_strides, k_scale_strides, v_scale_strides;
   const int32_t* q2k;     /* [Hkv, total_q, topk] block ids, ascending, -1 padded */
@@ -122,17 +124,15 @@ typedef struct {
                              -inf for a row with no attended key (out = 0)    */
 } msa_attn_args_t;
 
-/* Bytes of workspace msa_sparse_attention needs for these arguments (split-KV
- * partials and completion counters; prepare_msa_nvfp4_sparse_decode page,
- * Parameters: workspace_buffer).  0 when the call runs without splitting.
- * Layout: the completion counters come first, one uint32 per (request, KV
- * head), in the first round_up(4 * batch * num_kv_heads, 256) bytes; the
- * partials follow.  Those counter bytes must be zero when a launch starts;
- * every launch leaves them zero again, so one workspace serves any number of
- * back-to-back launches on a stream.  Zero the counter prefix again before a
- * launch whose counter prefix is longer than the one known to be zero (the
- * partials of an earlier, different-shaped launch may sit there).  Launches
- * that may run concurrently need separate workspaces. */
+/* Bytes of workspace msa_sparse_attention needs for these arguments: the
+ * fp32 split-KV partials (O / l per row) and their LSE
+ * (prepare_msa_nvfp4_sparse_decode page, Parameters: workspace_buffer).  0
+ * when the call runs without splitting (prefill shapes; decode shapes whose
+ * plan uses one split).  The buffer is 256-byte aligned, owned by the
+ * caller, needs no initialisation and carries no state between launches:
+ * every launch writes the partials before a second kernel on the same
+ * stream merges them.  Launches that may run concurrently need separate
+ * workspaces. */
 msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args,
                                                  size_t* bytes);
 
