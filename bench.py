@@ -10,8 +10,8 @@ query actually attends (4 * head_dim per key and query head), divided by the
 step time.  Inputs are seeded synthetic tensors resident in HBM before timing.
 
 The decode workloads (--workload paged_decode_...) report KV GB/s over the
-K/V blocks actually gathered, timed cold: a 1 GiB scrub runs before every
-step, outside the timed events.
+K/V blocks actually gathered, timed cold: a 1 GiB read evicts L2 and MALL
+before every step, outside the timed events.
 
 Per-stage times come from HIP events recorded on the stream the kernels run
 on.  One JSON line is printed.
@@ -231,7 +231,7 @@ def bench_decode(args, msa, synth, torch):
         q2k = torch.empty(p.num_kv_heads, p.total_q, p.topk, dtype=torch.int32, device="cuda")
     else:
         q2k = p.q2k
-    scrub = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    scrub32 = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
 
     def step(ev=None):
         if ev: ev[0].record()
@@ -255,8 +255,12 @@ def bench_decode(args, msa, synth, torch):
     torch.cuda.synchronize()
     nbytes = accounting.decode_kv_bytes(q2k, p.cu_seqlens_q, p.seqused_k, fmt, T)
     evs = [_events(4) for _ in range(args.steps)]
+    sink = torch.empty((), dtype=torch.int64, device="cuda")
     for k in range(args.steps):
-        scrub.fill_(k & 0xFF)          # evict L2 / MALL: cold K/V every step
+        # evict L2 and MALL before every step (cold K/V): a 1 GiB read leaves
+        # the caches full of clean lines, so the step pays no writeback of a
+        # previous kernel's dirty data
+        torch.sum(scrub32, dim=0, out=sink)
         step(evs[k])
     torch.cuda.synchronize()
     st = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]

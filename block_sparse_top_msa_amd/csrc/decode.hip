@@ -37,45 +37,49 @@ namespace msa {
 namespace {
 
 constexpr float kLn2d = 0.69314718055994530942f;
+constexpr int kPtCache = 1024;   // page-table entries read ahead into LDS
 
+// Per-wave staging geometry: wave w stages (and alone reads) key rows
+// 32w..32w+31 of K and V of every page, so waves pipeline independently.
 template <int FMT>
 struct DecGeom;
 
 template <>
 struct DecGeom<kFmtBf16> {
   static constexpr int kRow = 256;                 // bytes per K / V row
-  static constexpr int kSide = kBlock * kRow;      // 32 KiB
+  static constexpr int kSide = 32 * kRow;          // 8 KiB per wave and side
   static constexpr int kStage = 2 * kSide;         // K | V
-  static constexpr int kStages = 2;
-  static constexpr int kLoads = kStage / 4096;     // 1 KiB loads per wave per page
+  static constexpr int kStages = 2;                // pages in flight per wave
+  static constexpr int kLoads = kStage / 1024;     // 1 KiB loads per wave per page
 };
 
 template <>
 struct DecGeom<kFmtFp8> {
   static constexpr int kRow = 128;
-  static constexpr int kSide = kBlock * kRow;      // 16 KiB
+  static constexpr int kSide = 32 * kRow;          // 4 KiB
   static constexpr int kStage = 2 * kSide;
-  static constexpr int kStages = 2;
-  static constexpr int kLoads = kStage / 4096;
+  static constexpr int kStages = 3;
+  static constexpr int kLoads = kStage / 1024;
 };
 
 template <>
 struct DecGeom<kFmtE2m1> {
   static constexpr int kRow = 64;                  // 128 nibbles
-  static constexpr int kSide = kBlock * kRow;      // 8 KiB
-  static constexpr int kScale = kBlock * 8;        // 1 KiB of E4M3 scales per side
-  // K | V | K scales | V scales | 2 KiB target of two padding loads
-  static constexpr int kStage = 2 * kSide + 2 * kScale + 2048;
+  static constexpr int kSide = 32 * kRow;          // 2 KiB
+  static constexpr int kScale = 32 * 8;            // 256 B of E4M3 scales per side
+  // K | V | K scales | V scales | 512 B target of the scale load's idle lanes
+  static constexpr int kStage = 2 * kSide + 2 * kScale + 512;
   static constexpr int kStages = 3;
-  static constexpr int kLoads = kStage / 4096;     // 5
+  static constexpr int kLoads = kStage / 1024;     // 5
 };
 
 template <int FMT>
 struct DecodeLds {
-  static constexpr int kRing = DecGeom<FMT>::kStages * DecGeom<FMT>::kStage;
-  uint8_t ring[kRing];
+  static constexpr int kRing = 4 * DecGeom<FMT>::kStages * DecGeom<FMT>::kStage;
+  uint8_t ring[kRing];       // [wave][stage][K | V | (scales)]
   UnionLds un;
   int32_t page[kMaxUnion];   // page id (paged) or first row (flat) of each entry of the share
+  int32_t ptrow[kPtCache];   // the request's page-table row, when it is this short
 };
 
 struct MergeLds {
@@ -289,18 +293,10 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
   const int l16 = lane & 15;
   const int q = lane >> 4;
 
-  const int32_t* rows = p.q2k + ((int64_t)g * p.total_q + q0) * p.topk;
-  const int ucount = __builtin_amdgcn_readfirstlane(
-      build_tile_union<256>(lds.un, rows, ntok, p.topk, nblk));
-  const int u0 = (int)(((int64_t)ucount * split) / p.splits);
-  const int u1 = (int)(((int64_t)ucount * (split + 1)) / p.splits);
-  const int n = u1 - u0;
-  for (int i = tid; i < n; i += 256) {
-    const int t = lds.un.list[u0 + i];
-    lds.page[i] = p.paged ? p.page_table[(int64_t)b * p.pt_width + t] : p.cu_k[b] + kBlock * t;
-  }
-
-  // ---- per row tile: lane l holds query row 16 rt + l % 16 (token r / G, head r % G)
+  // ---- prologue.  Three independent reads start together: the query rows,
+  // the request's q2k rows and (short enough) its page-table row; the page
+  // ids of the union then come from LDS instead of a dependent global read.
+  // Per row tile: lane l holds query row 16 rt + l % 16 (token r / G, head r % G).
   bf16x8 qf[RT][4];
   int tk_[RT], pos_[RT];
   unsigned long long tokmask[RT];
@@ -326,6 +322,64 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       for (int ds = 0; ds < 4; ++ds) qf[rt][ds] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
   }
+  const bool ptc = p.paged && nblk <= kPtCache;
+  int32_t ptr_[kPtCache / 256];
+  if (ptc) {
+    const int32_t* prow = p.page_table + (int64_t)b * p.pt_width;
+#pragma unroll
+    for (int k = 0; k < kPtCache / 256; ++k) {
+      const int t = tid + 256 * k;
+      ptr_[k] = t < nblk ? prow[t] : 0;
+    }
+  }
+
+  const int32_t* rows = p.q2k + ((int64_t)g * p.total_q + q0) * p.topk;
+  int ucount;
+  if (ntok == 1) {
+    // one token: its row is the union when ascending without repeats (the
+    // q2k contract); checked, with the general builder as the fallback
+    int id = -1;
+    if (tid < p.topk) id = rows[tid];
+    const bool in = tid < p.topk && id >= 0 && id < nblk;
+    int bad = 0;
+    if (wave == 0) {
+      const unsigned long long bal = __ballot(in);
+      const unsigned long long below = bal & ((1ull << lane) - 1ull);
+      const int pos = __popcll(below);
+      // each in-range id must exceed the previous in-range id
+      const int pl = below ? 63 - __clzll(below) : lane;
+      const int pid = __shfl(id, pl, kWave);
+      bad = __ballot(in && below != 0ull && pid >= id) != 0ull;
+      if (in) {
+        lds.un.list[pos] = id;
+        lds.un.mask[pos] = 1ull;
+      }
+      if (lane == 0) lds.un.count = bad ? -1 : (int)__popcll(bal);
+    }
+    __syncthreads();
+    ucount = lds.un.count;
+    if (ucount < 0) ucount = build_tile_union<256>(lds.un, rows, ntok, p.topk, nblk);
+  } else {
+    ucount = build_tile_union<256>(lds.un, rows, ntok, p.topk, nblk);
+  }
+  ucount = __builtin_amdgcn_readfirstlane(ucount);
+  const int u0 = (int)(((int64_t)ucount * split) / p.splits);
+  const int u1 = (int)(((int64_t)ucount * (split + 1)) / p.splits);
+  const int n = u1 - u0;
+  if (ptc) {
+#pragma unroll
+    for (int k = 0; k < kPtCache / 256; ++k) {
+      const int t = tid + 256 * k;
+      if (t < nblk) lds.ptrow[t] = ptr_[k];
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < n; i += 256) {
+    const int t = lds.un.list[u0 + i];
+    lds.page[i] = ptc ? lds.ptrow[t]
+                      : (p.paged ? p.page_table[(int64_t)b * p.pt_width + t] : p.cu_k[b] + kBlock * t);
+  }
+
   // settle the Q loads before the loop (see the prefill kernel)
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
@@ -347,14 +401,17 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
   }
   __syncthreads();  // page ids visible
 
-  // ---- staging: load n = wave + 4 i (i < LOADS) fills LDS bytes
-  // [1024 n, 1024 n + 1024) of the stage; lane l writes 16 bytes at 16 l.
-  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr(lds.ring));
+  // ---- staging: wave w's load nn (< LOADS) of a page fills bytes
+  // [1024 nn, 1024 nn + 1024) of its stage; lane l writes 16 bytes at 16 l.
+  // Rows are the wave's local key rows 0..31 (key 32 w + row).
+  const uint32_t wring = __builtin_amdgcn_readfirstlane(lds_addr(lds.ring)) +
+                         wave * NST * Geo::kStage;
   const int64_t kst = p.k_st.token, vst = p.v_st.token;
+  const int kw0 = 32 * wave;  // this wave's first key of every page
   auto issue = [&](int i, int stage) {
     const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u0 + i]);
     const int pg = __builtin_amdgcn_readfirstlane(lds.page[i]);
-    const int nvalid = min(kBlock, lk - kBlock * t);
+    const int nvalid = min(kBlock, lk - kBlock * t) - kw0;  // valid local rows
     const uint8_t* kb;
     const uint8_t* vb;
     if (p.paged) {
@@ -364,50 +421,47 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       kb = p.k + (int64_t)pg * kst + g * p.k_st.head;
       vb = p.v + (int64_t)pg * vst + g * p.v_st.head;
     }
-    const uint32_t dst = ring0 + stage * Geo::kStage;
+    kb += kw0 * kst;
+    vb += kw0 * vst;
+    const uint32_t dst = wring + stage * Geo::kStage;
 #pragma unroll
-    for (int li = 0; li < LOADS; ++li) {
-      const int nn = wave + 4 * li;
+    for (int nn = 0; nn < LOADS; ++nn) {
       const uint8_t* src;
       if constexpr (FMT == kFmtBf16) {
         // rows of 256 B: 4 rows per load
-        const bool isv = nn >= 32;
-        const int row = 4 * (nn & 31) + (lane >> 4);
-        const int rr = row < nvalid ? row : 0;
+        constexpr int kHalf = LOADS / 2;
+        const bool isv = nn >= kHalf;
+        const int row = 4 * (isv ? nn - kHalf : nn) + (lane >> 4);
+        const int rr = row < nvalid ? row : -kw0;   // past the end: the page's row 0
         const int c = isv ? ((lane & 15) ^ ((row & 3) << 1)) : ((lane & 15) ^ (row & 15));
         src = (isv ? vb + rr * vst : kb + rr * kst) + 16 * c;
       } else if constexpr (FMT == kFmtFp8) {
         // rows of 128 B: 8 rows per load
-        const bool isv = nn >= 16;
-        const int row = 8 * (nn & 15) + (lane >> 3);
-        const int rr = row < nvalid ? row : 0;
+        constexpr int kHalf = LOADS / 2;
+        const bool isv = nn >= kHalf;
+        const int row = 8 * (isv ? nn - kHalf : nn) + (lane >> 3);
+        const int rr = row < nvalid ? row : -kw0;
         const int gv = (row & 3) | (((row >> 4) & 1) << 2);
         const int c = isv ? ((lane & 7) ^ gv) : ((lane & 7) ^ (row & 7));
         src = (isv ? vb + rr * vst : kb + rr * kst) + 16 * c;
       } else {
-        if (nn < 16) {
-          // data rows of 64 B: 16 rows per load
-          const bool isv = nn >= 8;
-          const int row = 16 * (nn & 7) + (lane >> 2);
-          const int rr = row < nvalid ? row : 0;
+        if (nn < 4) {
+          // data rows of 64 B: 16 rows per load (K: loads 0-1, V: 2-3)
+          const bool isv = nn >= 2;
+          const int row = 16 * (nn & 1) + (lane >> 2);
+          const int rr = row < nvalid ? row : -kw0;
           const int gv = ((row >> 1) & 1) | (((row >> 4) & 1) << 1);
           const int c = isv ? ((lane & 3) ^ gv) : ((lane & 3) ^ ((row >> 1) & 3));
           src = (isv ? vb + rr * vst : kb + rr * kst) + 16 * c;
         } else {
-          // scale rows of 8 B, two per lane; loads 18 and 19 only pad the
-          // count (they rewrite K scales into the spare 2 KiB)
-          const bool isv = nn == 17;
-          const int row = 2 * lane;
-          const int rr = row < nvalid ? row : 0;
-          const uint8_t* sb;
-          if (p.paged) {
-            sb = isv ? p.vs + (int64_t)pg * p.vs_st.page + g * p.vs_st.head
-                     : p.ks + (int64_t)pg * p.ks_st.page + g * p.ks_st.head;
-          } else {
-            sb = isv ? p.vs + (int64_t)pg * p.vs_st.token + g * p.vs_st.head
-                     : p.ks + (int64_t)pg * p.ks_st.token + g * p.ks_st.head;
-          }
-          src = sb + rr * (isv ? p.vs_st.token : p.ks_st.token);
+          // scale rows of 8 B, two per lane: lanes 0-15 K scales, 16-31 V
+          // scales; lanes 32-63 repeat the K scales into the spare bytes
+          const bool isv = lane >= 16 && lane < 32;
+          const int row = 2 * (lane & 15);
+          const int rr = kw0 + (row < nvalid ? row : -kw0);
+          const uint8_t* sb = isv ? p.vs + (int64_t)pg * p.vs_st.page + g * p.vs_st.head
+                                  : p.ks + (int64_t)pg * p.ks_st.page + g * p.ks_st.head;
+          src = sb + rr * 8;
         }
       }
       g2lds16(src, dst + 1024 * nn);
@@ -415,24 +469,20 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
   };
 
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
+  for (int s = 0; s < NST; ++s)
     if (s < n) issue(s, s);
 
   const float C = p.scale_log2;
-  const int kw0 = 32 * wave;  // this wave's first key of every page
 
   for (int i = 0; i < n; ++i) {
     const int stage = i % NST;
-    // this page's loads done (NST - 2 later pages may stay in flight), then
-    // every wave's; the barrier also frees stage (i - 1) % NST for reuse
-    if constexpr (NST == 3) {
-      if (i + 1 < n) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    block_barrier();
-    if (i + NST - 1 < n) issue(i + NST - 1, (i + NST - 1) % NST);
+    // wait for this page's loads; the wave's later pages (up to NST - 1)
+    // stay in flight
+    const int later = min(NST - 1, n - 1 - i);
+    if (later >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LOADS) : "memory");
+    else if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
+    else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     const int u = u0 + i;
     const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
@@ -441,10 +491,8 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
     bool any = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) any |= (umask & tokmask[rt]) != 0ull;
-    if (!any) continue;
-
-    const uint32_t sb = ring0 + stage * Geo::kStage;
-
+    const uint32_t sb = wring + stage * Geo::kStage;
+    if (any) {
     // ---- K fragments (A operand of S^T): key kw0 + 16 kt + l % 16,
     // head dims 32 q + 8 ds .. + 7 for k-step ds
     bf16x8 kf[2][4];
@@ -453,7 +501,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       uint32_t a[8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int row = kw0 + 16 * kt + l16;
+        const int row = 16 * kt + l16;   // local row
 #pragma unroll
         for (int ds = 0; ds < 4; ++ds) a[4 * kt + ds] = sb + row * 256 + 16 * ((4 * q + ds) ^ (row & 15));
       }
@@ -467,7 +515,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       uint32_t a[4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int row = kw0 + 16 * kt + l16;
+        const int row = 16 * kt + l16;   // local row
 #pragma unroll
         for (int j = 0; j < 2; ++j) a[2 * kt + j] = sb + row * 128 + 16 * ((2 * q + j) ^ (row & 7));
       }
@@ -486,7 +534,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       uint32_t a[2], as[2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int row = kw0 + 16 * kt + l16;
+        const int row = 16 * kt + l16;   // local row
         a[kt] = sb + row * 64 + 16 * (q ^ ((row >> 1) & 3));
         as[kt] = sb + 2 * Geo::kSide + row * 8 + 2 * q;
       }
@@ -506,7 +554,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       u32x2 vv[16];
       uint32_t a[8];
       const int e = l16 >> 2, aa = lane & 3;
-      const int row = kw0 + 4 * q + e;
+      const int row = 4 * q + e;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) a[dt] = sb + Geo::kSide + row * 256 + 32 * (dt ^ e) + 8 * aa;
       vtr16_issue(vv, a);
@@ -518,7 +566,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       u32x2 vv[8];
       uint32_t a[8];
       const int e = l16 >> 1, aa = lane & 1;
-      const int row = kw0 + (e < 4 ? 4 * q + e : 16 + 4 * q + e - 4);
+      const int row = e < 4 ? 4 * q + e : 16 + 4 * q + e - 4;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) a[dt] = sb + Geo::kSide + row * 128 + 16 * (dt ^ e) + 8 * aa;
       vtr8_issue<false>(vv, a);
@@ -531,7 +579,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       u32x2 vv[8], vsr[8];
       uint32_t a[8], asr[8];
       const int e = l16 & 7;
-      const int row = kw0 + (e < 4 ? 4 * q + e : 16 + 4 * q + e - 4);
+      const int row = e < 4 ? 4 * q + e : 16 + 4 * q + e - 4;
       const int gv = ((row >> 1) & 1) | (((row >> 4) & 1) << 1);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
@@ -540,7 +588,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       // scale rows of this lane's eight keys
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int rk = kw0 + (k < 4 ? 4 * q + k : 16 + 4 * q + k - 4);
+        const int rk = k < 4 ? 4 * q + k : 16 + 4 * q + k - 4;
         asr[k] = sb + 2 * Geo::kSide + Geo::kScale + rk * 8;
       }
       lds_b64x8(vsr, asr);
@@ -548,7 +596,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int rk = kw0 + (k < 4 ? 4 * q + k : 16 + 4 * q + k - 4);
-        if (rk >= nvalid) vsr[k] = u32x2{0u, 0u};   // no scale of a row past the end
+        if (rk >= nvalid) vsr[k] = u32x2{0u, 0u};   // no scale of a key past the end
       }
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -608,6 +656,10 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = mfma16(vf[dt], pf, o_[rt][dt] * alpha);
     }
+    }  // any
+    // the stage's reads completed (every fragment read above waited for
+    // its data), so it takes the page NST ahead
+    if (i + NST < n) issue(i + NST, stage);
   }
 
   // ---- merge the four waves' states row tile by row tile through LDS

@@ -138,6 +138,26 @@ def test_decode_paged_matches_oracle(msa, case):
     assert_attention_close(out, lse, ref_out, ref_lse, f"decode case {case}")
 
 
+def test_decode_single_token_rows_out_of_order_and_repeated(msa):
+    # one-token rows are used directly as the union only when ascending
+    # without repeats; other rows go through the general union builder
+    p = synth.make_problem("dec_perm", q_lens=[1] * 5, k_lens=[3000, 900, 4100, 128, 2500],
+                           num_qo_heads=16, num_kv_heads=2, topk=8, paged=True, seed=21,
+                           selection="decode")
+    g = torch.Generator().manual_seed(5)
+    q2k = p.q2k.clone()
+    for h in range(q2k.shape[0]):
+        for i in range(q2k.shape[1]):
+            row = q2k[h, i]
+            q2k[h, i] = row[torch.randperm(row.numel(), generator=g)]
+    q2k[0, 0, 1] = q2k[0, 0, 0]      # a repeated id
+    q2k[1, 2, :] = -1                # an empty row
+    p.q2k = q2k
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "unsorted one-token rows")
+
+
 def test_decode_is_deterministic_and_workspace_carries_no_state(msa):
     p = _dev(synth.make_problem("det", q_lens=[4] * 6, k_lens=[5000, 3000, 900, 4000, 128, 2000],
                                 num_qo_heads=32, num_kv_heads=2, topk=16, paged=True,
