@@ -337,12 +337,14 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows = lqmax * G;
   const int wide = rows > 64;
-  p.rows_per_tile = wide ? 256 : 64;
+  p.rows_per_tile = wide ? 256 : (rows <= 32 ? 32 : 64);
   p.row_tiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
-  // aim for >= ~2048 workgroups; at least 4 blocks per workgroup
+  // aim for >= ~2048 workgroups; at least 4 blocks per workgroup (a multiple
+  // of 4 on the register path, whose 4 waves take every 4th block)
   const int base = std::max(1, a->batch * a->num_kv_heads * p.row_tiles);
   int chunks = std::max(1, (2048 + base - 1) / base);
   int bpw = std::max(4, (a->max_k_tiles + chunks - 1) / chunks);
+  if (!wide) bpw = std::min(64, (bpw + 3) / 4 * 4);
   p.blocks_per_wg = bpw;
   p.block_chunks = (a->max_k_tiles + bpw - 1) / bpw;
   return hip_status(msa::launch_proxy(p, a->kv_dtype == MSA_KV_FP8_E4M3 ? msa::kFmtFp8 : msa::kFmtBf16,

@@ -243,6 +243,358 @@ __global__ __launch_bounds__(256) void msa_proxy_kernel(ProxyParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode-shaped proxy (at most 64 query rows per request and KV head, e.g.
+// a few MTP tokens x G heads): HBM-bound, every K page is read once.  Each
+// wave scores whole blocks (t_beg + wave, + 4, ...) on its own, without
+// barriers: the blocks stream global -> LDS (global_load_lds, raw bytes)
+// through a per-wave ring of NST stages, so NST blocks per wave are in
+// flight.  Lane (key l % 32, half l / 32) then reads its key row's bytes for
+// head dims 64 half .. 64 half + 63; with the same permutation of the head
+// dimension on Q that is exactly the A operand of S^T = K Q^T on 32x32x16
+// MFMA (k-step s covers dims 64 half + 8 s ..).  fp8 K is converted in
+// registers.  Page ids of the workgroup's blocks are looked up once, into LDS.
+// ---------------------------------------------------------------------------
+template <int FMT>
+struct RowsGeom;
+template <>
+struct RowsGeom<kFmtFp8> {
+  static constexpr int kRow = 128;
+  static constexpr int kStage = kBlock * kRow;   // 16 KiB
+  static constexpr int kStages = 2;
+  static constexpr int kLoads = kStage / 1024;
+  static constexpr int kLaneBytes = 64;          // per lane and 32-key chunk
+};
+template <>
+struct RowsGeom<kFmtBf16> {
+  static constexpr int kRow = 256;
+  static constexpr int kStage = kBlock * kRow;   // 32 KiB
+  static constexpr int kStages = 1;
+  static constexpr int kLoads = kStage / 1024;
+  static constexpr int kLaneBytes = 128;
+};
+
+constexpr int kRowsMaxBpw = 64;   // blocks per workgroup on this path
+
+template <int FMT>
+struct RowsLds {
+  uint8_t ring[4 * RowsGeom<FMT>::kStages * RowsGeom<FMT>::kStage];   // [wave][stage]
+  int32_t page[kRowsMaxBpw];
+  // block maxima per wave, block and row: written out after the block loop,
+  // so that no global store or atomic (counted by vmcnt like the staging
+  // loads) is issued between a page's loads and the wait for them
+  float res[4][kRowsMaxBpw / 4][64];
+};
+
+__device__ __forceinline__ bf16x8 fp8x8_bf16(uint32_t w0, uint32_t w1) {
+  return as_bf16x8(u32x4{
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))});
+}
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  return fmaxf(fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+                     fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7]))),
+               fmaxf(fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11])),
+                     fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15]))));
+}
+
+// Four 16-byte LDS reads, waited for (outputs early-clobber).
+__device__ __forceinline__ void lds_rd4(u32x4 (&k)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+__device__ __forceinline__ uint32_t lds_addr32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+__device__ __forceinline__ void g2lds16_px(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\t"
+               "s_nop 0\n\t"
+               "global_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// Same, addressed as scalar base + per-lane 32-bit byte offset (no 64-bit
+// address arithmetic per lane).
+__device__ __forceinline__ void g2lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\t"
+               "s_nop 0\n\t"
+               "global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
+template <int NT, int FMT, bool REDUCE>
+__global__ __launch_bounds__(256) void msa_proxy_rows_kernel(ProxyParams p) {
+  using Geo = RowsGeom<FMT>;
+  constexpr int NST = Geo::kStages;
+  constexpr int LOADS = Geo::kLoads;
+  __shared__ __attribute__((aligned(16))) RowsLds<FMT> lds;
+
+  const int chunk = blockIdx.x % p.block_chunks;
+  const int rest = blockIdx.x / p.block_chunks;
+  const int g = rest % p.hkv;
+  const int b = rest / p.hkv;
+  if (b >= p.batch) return;
+
+  const int G = p.group;
+  const int q0 = p.cu_q[b];
+  const int lq = p.cu_q[b + 1] - q0;
+  const int nrows = lq * G;
+  if (nrows <= 0) return;
+  const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
+  const int nblk = max(0, (lk + kBlock - 1) / kBlock);
+  const int t_beg = chunk * p.blocks_per_wg;
+  const int t_end = min(t_beg + p.blocks_per_wg, p.max_k_tiles);
+  if (t_beg >= t_end) return;
+  const int pos_min = lk - lq;                    // causal position of the first token
+  const int pos_max = lk - lq + (nrows - 1) / G;  // ... and of the last
+  int t_act = min(t_end, nblk);
+  if (p.paged) t_act = min(t_act, p.pt_width);
+  if (p.causal) t_act = min(t_act, pos_max < 0 ? 0 : pos_max / kBlock + 1);
+  t_act = max(t_act, t_beg);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+
+  // page ids (paged) or first rows (flat) of the workgroup's visible blocks
+  for (int i = tid; i < t_act - t_beg; i += 256) {
+    const int t = t_beg + i;
+    lds.page[i] = p.paged ? p.page_table[(int64_t)b * p.pt_width + t] : p.cu_k[b] + kBlock * t;
+  }
+
+  int row_[NT], pos_[NT];
+  bf16x8 qf[NT][8];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int r = 32 * nt + col;
+    row_[nt] = r;
+    const int tk = r / G, hh = r % G;
+    pos_[nt] = lk - lq + tk;
+    if (r < nrows) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(
+          p.q + ((int64_t)(q0 + tk) * p.hq + g * G + hh) * kHeadDim) + 128 * half;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[nt][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[nt][s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+  }
+
+  // blocks of the chunk with no visible key: -inf (pre-filled when reducing)
+  if (!REDUCE && half == 0) {
+    for (int t = t_act + wave; t < t_end; t += 4) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int r = row_[nt];
+        if (r < nrows)
+          p.out[((int64_t)(g * G + r % G) * p.max_k_tiles + t) * p.total_q + q0 + r / G] = -INFINITY;
+      }
+    }
+  }
+  // settle the Q loads; page ids visible
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 w = __builtin_bit_cast(u32x4, qf[nt][s]);
+      asm volatile("" : "+v"(w));
+      qf[nt][s] = as_bf16x8(w);
+    }
+  __syncthreads();
+
+  const int64_t kst = p.k_st.token;
+  const uint32_t wring = __builtin_amdgcn_readfirstlane(lds_addr32(lds.ring)) +
+                         wave * NST * Geo::kStage;
+  // this wave's blocks: t_beg + wave + 4 i, i < nb
+  const int nb = t_act - t_beg > wave ? (t_act - t_beg - wave + 3) / 4 : 0;
+
+  // stage block i of this wave: load nn writes LDS bytes [1024 nn, +1024);
+  // rows XOR-swizzled in 16-byte chunks (conflict-free operand reads)
+  // Per-lane byte offsets within a block of the staged rows: row = RPL nn +
+  // lane / LPR (RPL rows per load, LPR lanes per row); the XOR swizzle of a
+  // row depends on nn only through (RPL nn) mod SW, so VAR offsets suffice
+  // and the rest of the row offset goes into the scalar base.
+  constexpr int LPR = Geo::kRow / 16;          // lanes per row
+  constexpr int RPL = 64 / LPR;                // rows per load
+  constexpr int SW = FMT == kFmtFp8 ? 8 : 16;  // swizzle period (rows)
+  constexpr int VAR = SW / RPL;                // distinct lane offsets
+  uint32_t loff[VAR];
+#pragma unroll
+  for (int v = 0; v < VAR; ++v) {
+    const int row = RPL * v + lane / LPR;
+    loff[v] = (uint32_t)((lane / LPR) * kst) + 16u * (uint32_t)((lane % LPR) ^ (row % SW));
+  }
+  auto issue = [&](int i, int stage) {
+    const int t = t_beg + wave + 4 * i;
+    const int pg = __builtin_amdgcn_readfirstlane(lds.page[t - t_beg]);
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    const uint8_t* base = p.paged ? p.k + (int64_t)pg * p.k_st.page + g * p.k_st.head
+                                  : p.k + (int64_t)pg * kst + g * p.k_st.head;
+    const uint32_t dst = wring + stage * Geo::kStage;
+    if (nvalid == kBlock) {
+#pragma unroll
+      for (int nn = 0; nn < LOADS; ++nn)
+        g2lds16_sv(base + (int64_t)(RPL * nn) * kst, loff[nn % VAR], dst + 1024 * nn);
+    } else {
+#pragma unroll
+      for (int nn = 0; nn < LOADS; ++nn) {
+        const int row = RPL * nn + lane / LPR;
+        const int c = (lane % LPR) ^ (row % SW);
+        const int rr = row < nvalid ? row : 0;   // past the end: row 0 (masked)
+        g2lds16_px(base + rr * kst + 16 * c, dst + 1024 * nn);
+      }
+    }
+  };
+
+  constexpr int LB = Geo::kLaneBytes / 16;   // 16-byte pieces per lane and chunk
+  // lane's key rows 32 c + col of chunks c0, c0 + 1: bytes of head dims
+  // 64 half .. 64 half + 63
+  auto read_pair = [&](uint32_t sb, int c0, u32x4 (&kr)[2][LB]) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int row = 32 * (c0 + cc) + col;
+#pragma unroll
+      for (int j0 = 0; j0 < LB; j0 += 4) {
+        uint32_t a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int lc = LB * half + j0 + j;   // logical 16-byte chunk of the row
+          const int pc = FMT == kFmtFp8 ? (lc ^ (row & 7)) : (lc ^ (row & 15));
+          a[j] = sb + row * Geo::kRow + 16 * pc;
+        }
+        u32x4 w[4];
+        lds_rd4(w, a);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kr[cc][j0 + j] = w[j];
+      }
+    }
+  };
+
+  // block max of chunks c0, c0 + 1 into bm: 2 x NT independent accumulator
+  // chains keep the MFMA pipe busy
+  auto score_pair = [&](int t, int c0, const u32x4 (&kr)[2][LB], float (&bm)[NT]) {
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    const bool full = nvalid == kBlock && (!p.causal || pos_min >= kBlock * t + kBlock - 1);
+    f32x16 acc[2][NT];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        bf16x8 a;
+        if constexpr (FMT == kFmtFp8) {
+          const u32x4 w = kr[cc][s >> 1];
+          a = (s & 1) ? fp8x8_bf16(w[2], w[3]) : fp8x8_bf16(w[0], w[1]);
+        } else {
+          a = as_bf16x8(kr[cc][s]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          if (s == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            acc[cc][nt] = mfma32(a, qf[nt][s], z);
+          } else {
+            acc[cc][nt] = mfma32(a, qf[nt][s], acc[cc][nt]);
+          }
+        }
+      }
+    }
+    if (full) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) bm[nt] = fmaxf(bm[nt], max16(acc[cc][nt]));
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int c = c0 + cc;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          int lim = nvalid - 1;
+          if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * c + 8 * (r >> 2) + 4 * half + (r & 3);
+            acc[cc][nt][r] = key <= lim ? acc[cc][nt][r] : -INFINITY;
+          }
+          bm[nt] = fmaxf(bm[nt], max16(acc[cc][nt]));
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NST; ++s)
+    if (s < nb) issue(s, s);
+  for (int i = 0; i < nb; ++i) {
+    const int stage = i % NST;
+    const int later = min(NST - 1, nb - 1 - i);
+    if (later >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int t = t_beg + wave + 4 * i;
+    const uint32_t sb = wring + stage * Geo::kStage;
+    float bm[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) bm[nt] = -INFINITY;
+    u32x4 kr[2][LB];
+    read_pair(sb, 0, kr);
+    score_pair(t, 0, kr, bm);
+    read_pair(sb, 2, kr);
+    // the stage has been read: it takes the block NST ahead
+    if (i + NST < nb) issue(i + NST, stage);
+    score_pair(t, 2, kr, bm);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float v = xor_max(bm[nt], 32);
+      if (half == 0) lds.res[wave][i][32 * nt + col] = v;
+    }
+  }
+
+  // ---- results of this wave's blocks (its own LDS rows: no barrier)
+  for (int i = 0; i < nb; ++i) {
+    const int t = t_beg + wave + 4 * i;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int r = row_[nt];
+      const int tk = r / G, hh = r % G;
+      float v = lds.res[wave][i][32 * nt + col];
+      if constexpr (!REDUCE) {
+        if (half == 0 && r < nrows)
+          p.out[((int64_t)(g * G + hh) * p.max_k_tiles + t) * p.total_q + q0 + tk] = v;
+      } else {
+        // max over the G heads of a token when they share 32 lanes, then
+        // across KV heads (other workgroups) by atomic max
+        if ((G & (G - 1)) == 0 && G <= 32) {
+          for (int off = 1; off < G; off <<= 1) v = xor_max(v, off);
+          if (half == 0 && r < nrows && hh == 0)
+            atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+        } else if (half == 0 && r < nrows) {
+          atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+        }
+      }
+    }
+  }
+}
+
 __global__ void msa_fill_kernel(float* __restrict__ out, int64_t n, float v) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -267,15 +619,36 @@ static hipError_t launch_proxy_t(const ProxyParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// wide_rows: 1 -> 256 rows per workgroup (4 row groups x 64); 0 -> 64 rows
-// shared by 4 waves that split each block's keys.
+template <int NT, int FMT>
+static hipError_t launch_proxy_rows_t(const ProxyParams& p, hipStream_t stream) {
+  const int n = p.batch * p.hkv * p.block_chunks;
+  if (n <= 0) return hipSuccess;
+  if (p.reduce) {
+    const int64_t total = (int64_t)p.max_k_tiles * p.total_q;
+    if (total > 0) {
+      int fb = (int)std::min<int64_t>((total + 255) / 256, 4096);
+      hipLaunchKernelGGL(msa_fill_kernel, dim3(fb), dim3(256), 0, stream, p.out, total, -INFINITY);
+    }
+    hipLaunchKernelGGL((msa_proxy_rows_kernel<NT, FMT, true>), dim3(n), dim3(256), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((msa_proxy_rows_kernel<NT, FMT, false>), dim3(n), dim3(256), 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+// wide_rows: 1 -> 256 rows per workgroup (4 row groups x 64) with K staged
+// through LDS; 0 -> at most 64 rows per (request, KV head), the register
+// path above (p.rows_per_tile holds the row count rounded up to 32).
 hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream) {
   if (wide_rows) {
     return fmt == kFmtFp8 ? launch_proxy_t<2, 4, kFmtFp8>(p, stream)
                           : launch_proxy_t<2, 4, kFmtBf16>(p, stream);
   }
-  return fmt == kFmtFp8 ? launch_proxy_t<2, 1, kFmtFp8>(p, stream)
-                        : launch_proxy_t<2, 1, kFmtBf16>(p, stream);
+  if (p.rows_per_tile <= 32)
+    return fmt == kFmtFp8 ? launch_proxy_rows_t<1, kFmtFp8>(p, stream)
+                          : launch_proxy_rows_t<1, kFmtBf16>(p, stream);
+  return fmt == kFmtFp8 ? launch_proxy_rows_t<2, kFmtFp8>(p, stream)
+                        : launch_proxy_rows_t<2, kFmtBf16>(p, stream);
 }
 
 }  // namespace msa
