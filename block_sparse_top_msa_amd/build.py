@@ -34,11 +34,20 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 
+# The attention kernels take row maxima of MFMA results that are never NaN
+# for valid inputs (finite bf16 / fp8 / E2M1 operands; masked scores are
+# -inf): without NaN semantics the compiler drops the quieting "max x, x"
+# it would otherwise put in front of every such maximum.
+PER_FILE = {
+    "prefill.hip": ["-fno-honor-nans"],
+    "decode.hip": ["-fno-honor-nans"],
+}
+
 
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *PER_FILE.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", out]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -194,11 +194,9 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     // bf16: 4 waves x spw slots x 32 rows per tile; other formats: 4 x 2 x 16
     int rows;
     if (plan.async_bf16) {
-      // 8 waves x 1 slot (two waves per SIMD overlap MFMA and softmax work);
-      // MSA_PREFILL_SPW=2 selects 4 waves x 2 slots
-      int spw = 1;
-      if (const char* e = std::getenv("MSA_PREFILL_SPW")) spw = std::atoi(e) == 2 ? 2 : 1;
-      plan.spw = spw;
+      // 8 waves x one 32-row slot (two waves per SIMD overlap MFMA and
+      // softmax work)
+      plan.spw = 1;
       rows = 256;
     } else {
       plan.spw = 2;

@@ -86,6 +86,32 @@ __device__ __forceinline__ void vtr_issue(u32x2 (&v)[16], const uint32_t (&a)[4]
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
 
+// The eight K operand fragments of one 32-key chunk (ds_read_b128 each),
+// issued without waiting (outputs early-clobber: a load may return while
+// later loads of the group still read their address registers).
+__device__ __forceinline__ void kfrag_issue(u32x4 (&k)[8], const uint32_t (&a)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
+        "=&v"(k[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+}
+
+// Waits for every outstanding LDS read; naming the K registers orders their
+// uses after it.
+__device__ __forceinline__ void kfrag_wait(u32x4 (&k)[8]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]), "+v"(k[4]), "+v"(k[5]),
+                 "+v"(k[6]), "+v"(k[7]));
+}
+
 // Waits for the reads above; naming the registers orders their uses after it.
 __device__ __forceinline__ void vtr_wait(u32x2 (&v)[16]) {
   asm volatile("s_waitcnt lgkmcnt(0)"
@@ -277,6 +303,11 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
   const int vchunk = 2 * (q16 & 1) + ((lane & 3) >> 1);
   const int vbyte = 8 * (lane & 1);
 
+  static_assert(SPW == 1, "the software-pipelined loop runs one slot per wave");
+  const unsigned long long tokmask0 = tokmask[0];
+  const int tk0 = tk_[0];
+  const int pos0 = pos_[0];
+
   for (int u = 0; u < ucount; ++u) {
     const int buf = u & 1;
     const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
@@ -294,32 +325,34 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
 
     const uint32_t kt_lds = lds_addr(lds.kv[buf]);
     const uint32_t vt_lds = kt_lds + kTileBytes;
+    const bool rowsel = (tk0 < ntok) && ((umask >> tk0) & 1ull);
+    int lim = nvalid - 1;
+    if (p.causal) lim = min(lim, pos0 - kBlock * t);
 
-    bool act[SPW], rowsel[SPW];
-    int lim[SPW];
-    bool any = false;
+    if ((umask & tokmask0) != 0ull) {
+      // Software pipeline over the block's four 32-key chunks: S^T of chunk
+      // c + 1 and O^T += V^T P^T of chunk c are issued back to back, so the
+      // matrix core works through them while the softmax of chunk c + 1 runs
+      // on the vector ALU.
+      u32x4 kw[8];
+      {
+        uint32_t a[8];
 #pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      act[s] = (umask & tokmask[s]) != 0ull;
-      any |= act[s];
-      rowsel[s] = (tk_[s] < ntok) && ((umask >> tk_[s]) & 1ull);
-      int lm = nvalid - 1;
-      if (p.causal) lm = min(lm, pos_[s] - kBlock * t);
-      lim[s] = lm;
-    }
-    if (any) {
-#pragma unroll 1
-      for (int c = 0; c < 4; ++c) {  // 32-key chunks of the block
-        // K fragments: lane l holds key 32c + l % 32, head dims 16 ks + 8 hf ..
-        u32x4 kw[8];
-        {
-          const uint32_t kbase_c = kt_lds + 32 * c * 256;
-          uint32_t a[8];
+        for (int ks = 0; ks < 8; ++ks) a[ks] = kt_lds + koffs[ks];
+        kfrag_issue(kw, a);
+        kfrag_wait(kw);
+      }
+      f32x16 s_next;
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) a[ks] = kbase_c + koffs[ks];
-          kfrag_load(kw, a);
-        }
-        // V^T fragments (transposed reads), waited for before the first PV
+      for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) s_next = mfma32(as_bf16x8(kw[ks]), qf[0][ks], s_next);
+
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        f32x16 acc = s_next;
+        // V^T fragments of chunk c and K fragments of chunk c + 1, in flight
+        // during the softmax
         u32x2 vv[16];
         {
           const int r = 32 * c + vrow;
@@ -329,72 +362,70 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
             a[dt] = vt_lds + r * 256 + 16 * swz_v(r, 4 * dt + vchunk) + vbyte;
           vtr_issue(vv, a);
         }
-        bool waited = false;
+        if (c < 3) {
+          uint32_t a[8];
 #pragma unroll
-        for (int s = 0; s < SPW; ++s) {
-          if (!act[s]) continue;
-          // ---- S^T chunk: 32 keys x 32 query rows
-          f32x16 acc;
+          for (int ks = 0; ks < 8; ++ks) a[ks] = kt_lds + 32 * (c + 1) * 256 + koffs[ks];
+          kfrag_issue(kw, a);
+        }
+        // ---- mask (diagonal / partial block only)
+        if (__ballot(rowsel && lim < 32 * c + 31) != 0ull) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) acc = mfma32(as_bf16x8(kw[ks]), qf[s][ks], acc);
-          // ---- mask (diagonal / partial block only)
-          if (__ballot(rowsel[s] && lim[s] < 32 * c + 31) != 0ull) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
-              acc[r] = key <= lim[s] ? acc[r] : -INFINITY;
-            }
-          }
-          float mx = fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
-                           fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7])));
-          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
-                               fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
-          mx = rowsel[s] ? mx * C : -INFINITY;
-          // first scores of a row: take the max as the reference (O and l are
-          // still zero); afterwards move it only when it grows past the slack
-          if (__ballot(mx > m_[s] + kRescaleSlack) != 0ull) {
-            const float mr = swap32_max(mx);
-            if (__ballot(mr > m_[s] + kRescaleSlack && m_[s] > -INFINITY) != 0ull) {
-              const float alpha =
-                  mr > m_[s] + kRescaleSlack ? __builtin_amdgcn_exp2f(m_[s] - mr) : 1.0f;
-              l_[s] *= alpha;
-#pragma unroll
-              for (int dt = 0; dt < 4; ++dt) o_[s][dt] *= alpha;
-            }
-            m_[s] = mr > m_[s] + kRescaleSlack ? mr : m_[s];
-          }
-          const float mu = (rowsel[s] && m_[s] > -INFINITY) ? m_[s] : INFINITY;
-          float e[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], C, -mu));
-          l_[s] += (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
-                   (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
-          u32x4 pw0, pw1;  // P^T for the two 16-key k-steps
-          pw0[0] = cvt_pk_bf16(e[0], e[1]);
-          pw0[1] = cvt_pk_bf16(e[2], e[3]);
-          pw0[2] = cvt_pk_bf16(e[4], e[5]);
-          pw0[3] = cvt_pk_bf16(e[6], e[7]);
-          pw1[0] = cvt_pk_bf16(e[8], e[9]);
-          pw1[1] = cvt_pk_bf16(e[10], e[11]);
-          pw1[2] = cvt_pk_bf16(e[12], e[13]);
-          pw1[3] = cvt_pk_bf16(e[14], e[15]);
-          if (!waited) {
-            vtr_wait(vv);
-            waited = true;
-          }
-          // ---- O^T += V^T P^T
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const u32x4 w0 = {vv[4 * dt][0], vv[4 * dt][1], vv[4 * dt + 1][0], vv[4 * dt + 1][1]};
-            const u32x4 w1 = {vv[4 * dt + 2][0], vv[4 * dt + 2][1], vv[4 * dt + 3][0],
-                              vv[4 * dt + 3][1]};
-            o_[s][dt] = mfma32(as_bf16x8(w0), as_bf16x8(pw0), o_[s][dt]);
-            o_[s][dt] = mfma32(as_bf16x8(w1), as_bf16x8(pw1), o_[s][dt]);
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
+            acc[r] = key <= lim ? acc[r] : -INFINITY;
           }
         }
-        if (!waited) vtr_wait(vv);
+        float mx = fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
+                         fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
+                             fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
+        mx = rowsel ? mx * C : -INFINITY;
+        // first scores of a row: take the max as the reference (O and l are
+        // still zero); afterwards move it only when it grows past the slack
+        if (__ballot(mx > m_[0] + kRescaleSlack) != 0ull) {
+          const float mr = swap32_max(mx);
+          if (__ballot(mr > m_[0] + kRescaleSlack && m_[0] > -INFINITY) != 0ull) {
+            const float alpha =
+                mr > m_[0] + kRescaleSlack ? __builtin_amdgcn_exp2f(m_[0] - mr) : 1.0f;
+            l_[0] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o_[0][dt] *= alpha;
+          }
+          m_[0] = mr > m_[0] + kRescaleSlack ? mr : m_[0];
+        }
+        const float mu = (rowsel && m_[0] > -INFINITY) ? m_[0] : INFINITY;
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], C, -mu));
+        l_[0] += (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
+                 (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
+        u32x4 pw0, pw1;  // P^T for the two 16-key k-steps
+        pw0[0] = cvt_pk_bf16(e[0], e[1]);
+        pw0[1] = cvt_pk_bf16(e[2], e[3]);
+        pw0[2] = cvt_pk_bf16(e[4], e[5]);
+        pw0[3] = cvt_pk_bf16(e[6], e[7]);
+        pw1[0] = cvt_pk_bf16(e[8], e[9]);
+        pw1[1] = cvt_pk_bf16(e[10], e[11]);
+        pw1[2] = cvt_pk_bf16(e[12], e[13]);
+        pw1[3] = cvt_pk_bf16(e[14], e[15]);
+        vtr_wait(vv);
+        if (c < 3) {
+          kfrag_wait(kw);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) s_next = mfma32(as_bf16x8(kw[ks]), qf[0][ks], s_next);
+        }
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x4 w0 = {vv[4 * dt][0], vv[4 * dt][1], vv[4 * dt + 1][0], vv[4 * dt + 1][1]};
+          const u32x4 w1 = {vv[4 * dt + 2][0], vv[4 * dt + 2][1], vv[4 * dt + 3][0],
+                            vv[4 * dt + 3][1]};
+          o_[0][dt] = mfma32(as_bf16x8(w0), as_bf16x8(pw0), o_[0][dt]);
+          o_[0][dt] = mfma32(as_bf16x8(w1), as_bf16x8(pw1), o_[0][dt]);
+        }
       }
     }
     // every wave's LDS reads of buffer `buf` are done before it is refilled
@@ -442,10 +473,10 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tiles of 256 rows: 8 waves x 1 slot or 4 waves x 2 slots of 32 rows.
+// Tiles of 256 rows: 8 waves x one 32-row slot.
 hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream) {
-  if (spw == 1) return launch_prefill_t<8, 1>(p, stream);   // 8 waves x 1 slot
-  return launch_prefill_t<4, 2>(p, stream);                  // 4 waves x 2 slots
+  (void)spw;
+  return launch_prefill_t<8, 1>(p, stream);
 }
 
 }  // namespace msa
