@@ -16,233 +16,6 @@
 
 namespace msa {
 
-constexpr int kPKPitch = 136;  // bf16 per K row in LDS
-
-template <int FMT>
-struct ProxyStage;
-
-template <>
-struct ProxyStage<kFmtBf16> {
-  static constexpr int KT = 2048 / 256;
-  u32x4 kr[KT];
-  __device__ void issue(const uint8_t* kb, int64_t st, int nvalid) {
-#pragma unroll
-    for (int i = 0; i < KT; ++i) {
-      int task = i * 256 + threadIdx.x, row = task >> 4, c = task & 15;
-      kr[i] = row < nvalid ? *reinterpret_cast<const u32x4*>(kb + row * st + 16 * c)
-                           : u32x4{0, 0, 0, 0};
-    }
-  }
-  __device__ void store(uint16_t* k) const {
-#pragma unroll
-    for (int i = 0; i < KT; ++i) {
-      int task = i * 256 + threadIdx.x, row = task >> 4, c = task & 15;
-      *reinterpret_cast<u32x4*>(&k[row * kPKPitch + 8 * c]) = kr[i];
-    }
-  }
-};
-
-template <>
-struct ProxyStage<kFmtFp8> {
-  static constexpr int KT = 1024 / 256;
-  u32x4 kr[KT];
-  __device__ void issue(const uint8_t* kb, int64_t st, int nvalid) {
-#pragma unroll
-    for (int i = 0; i < KT; ++i) {
-      int task = i * 256 + threadIdx.x, row = task >> 3, c = task & 7;
-      kr[i] = row < nvalid ? *reinterpret_cast<const u32x4*>(kb + row * st + 16 * c)
-                           : u32x4{0, 0, 0, 0};
-    }
-  }
-  __device__ static uint32_t byte_of(const u32x4& v, int e) {
-    return (v[e >> 2] >> (8 * (e & 3))) & 0xFFu;
-  }
-  __device__ void store(uint16_t* k) const {
-#pragma unroll
-    for (int i = 0; i < KT; ++i) {
-      int task = i * 256 + threadIdx.x, row = task >> 3, c = task & 7;
-      u32x4 w0, w1;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16x2(e4m3_to_f32(byte_of(kr[i], 2 * e)), e4m3_to_f32(byte_of(kr[i], 2 * e + 1)));
-        w1[e] = pack_bf16x2(e4m3_to_f32(byte_of(kr[i], 8 + 2 * e)), e4m3_to_f32(byte_of(kr[i], 9 + 2 * e)));
-      }
-      *reinterpret_cast<u32x4*>(&k[row * kPKPitch + 16 * c]) = w0;
-      *reinterpret_cast<u32x4*>(&k[row * kPKPitch + 16 * c + 8]) = w1;
-    }
-  }
-};
-
-// NTW: 32-row N tiles per wave.  KSW: 32-key subtiles per wave (of 4 per block).
-template <int NTW, int KSW, int FMT, bool REDUCE>
-__global__ __launch_bounds__(256) void msa_proxy_kernel(ProxyParams p) {
-  constexpr int KG = 4 / KSW;          // waves sharing the same rows
-  constexpr int RG = 4 / KG;           // row groups
-  constexpr int RW = RG * NTW * 32;    // rows per workgroup
-  __shared__ uint16_t klds[kBlock * kPKPitch];
-  __shared__ float red[KG][RW];
-
-  const int n = p.batch * p.hkv * p.row_tiles * p.block_chunks;
-  const int lid = xcd_remap(blockIdx.x, n);
-  if (lid < 0) return;
-  const int chunk = lid % p.block_chunks;
-  int rest = lid / p.block_chunks;
-  const int rt = rest % p.row_tiles;
-  rest /= p.row_tiles;
-  const int g = rest % p.hkv;
-  const int b = rest / p.hkv;
-
-  const int G = p.group;
-  const int q0 = p.cu_q[b];
-  const int lq = p.cu_q[b + 1] - q0;
-  const int nrows = lq * G;
-  const int r0 = rt * RW;
-  if (r0 >= nrows) return;
-  const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
-  const int nblk = max(0, (lk + kBlock - 1) / kBlock);
-  const int t_beg = chunk * p.blocks_per_wg;
-  const int t_end = min(t_beg + p.blocks_per_wg, p.max_k_tiles);
-  if (t_beg >= t_end) return;
-
-  const int tid = threadIdx.x;
-  const int wave = tid / kWave;
-  const int lane = tid & (kWave - 1);
-  const int col = lane & 31;
-  const int half = lane >> 5;
-  const int rgp = wave / KG;
-  const int kgp = wave % KG;
-
-  const int r_last = min(r0 + RW, nrows) - 1;
-  const int pos_max = lk - lq + r_last / G;
-  // blocks with at least one visible key for some row of the tile
-  int t_act = min(t_end, nblk);
-  if (p.paged) t_act = min(t_act, p.pt_width);
-  if (p.causal) t_act = min(t_act, pos_max < 0 ? 0 : pos_max / kBlock + 1);
-  t_act = max(t_act, t_beg);
-
-  // rows of this wave
-  int row_[NTW], pos_[NTW];
-  bf16x8 qf[NTW][8];
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int r = r0 + (rgp * NTW + nt) * 32 + col;
-    row_[nt] = r;
-    const int tk = r / G, hh = r % G;
-    pos_[nt] = lk - lq + tk;
-    if (r < nrows) {
-      const uint8_t* qp = reinterpret_cast<const uint8_t*>(
-          p.q + ((int64_t)(q0 + tk) * p.hq + g * G + hh) * kHeadDim);
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qf[nt][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 2 * (16 * s + 8 * half)));
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) qf[nt][s] = as_bf16x8(u32x4{0, 0, 0, 0});
-    }
-  }
-
-  // fully masked blocks of the chunk: -inf (pre-filled when reducing)
-  if (!REDUCE && kgp == 0 && half == 0) {
-    for (int t = t_act; t < t_end; ++t) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const int r = row_[nt];
-        if (r < nrows) {
-          const int tk = r / G, hh = r % G;
-          p.out[((int64_t)(g * G + hh) * p.max_k_tiles + t) * p.total_q + q0 + tk] = -INFINITY;
-        }
-      }
-    }
-  }
-
-  auto kbase_of = [&](int t) -> const uint8_t* {
-    if (p.paged) {
-      int64_t page = p.page_table[(int64_t)b * p.pt_width + t];
-      return p.k + page * p.k_st.page + g * p.k_st.head;
-    }
-    return p.k + ((int64_t)p.cu_k[b] + kBlock * t) * p.k_st.token + g * p.k_st.head;
-  };
-
-  ProxyStage<FMT> stage;
-  if (t_beg < t_act) stage.issue(kbase_of(t_beg), p.k_st.token, min(kBlock, lk - kBlock * t_beg));
-
-  for (int t = t_beg; t < t_act; ++t) {
-    const int nvalid = min(kBlock, lk - kBlock * t);
-    __syncthreads();
-    stage.store(klds);
-    __syncthreads();
-    if (t + 1 < t_act) stage.issue(kbase_of(t + 1), p.k_st.token, min(kBlock, lk - kBlock * (t + 1)));
-
-    float cm[NTW];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) cm[nt] = -INFINITY;
-#pragma unroll
-    for (int ktl = 0; ktl < KSW; ++ktl) {
-      const int kt = kgp * KSW + ktl;
-      f32x16 acc[NTW];
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &klds[(32 * kt + col) * kPKPitch + 16 * s + 8 * half]));
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[nt] = mfma32(a, qf[nt][s], acc[nt]);
-      }
-      // Visible keys of this block for a row: key <= lim.  Written without
-      // short-circuit logic so the select stays a plain compare + cndmask on
-      // the accumulator values.
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        int lim = nvalid - 1;
-        if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
-        float m = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float v = acc[nt][r];
-          m = fmaxf(m, key <= lim ? v : -INFINITY);
-        }
-        m = xor_max(m, 32);
-        cm[nt] = fmaxf(cm[nt], m);
-      }
-    }
-    if constexpr (KG > 1) {
-      if (half == 0) {
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) red[kgp][(rgp * NTW + nt) * 32 + col] = cm[nt];
-      }
-      __syncthreads();
-      if (kgp != 0) continue;
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int k = 1; k < KG; ++k) cm[nt] = fmaxf(cm[nt], red[k][(rgp * NTW + nt) * 32 + col]);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int r = row_[nt];
-      const int tk = r / G, hh = r % G;
-      if constexpr (!REDUCE) {
-        if (half == 0 && r < nrows)
-          p.out[((int64_t)(g * G + hh) * p.max_k_tiles + t) * p.total_q + q0 + tk] = cm[nt];
-      } else {
-        float v = cm[nt];
-        // max over the G heads of a token when they share this 32-lane half
-        if ((G & (G - 1)) == 0 && G <= 32) {
-          for (int off = 1; off < G; off <<= 1) v = xor_max(v, off);
-          if (half == 0 && r < nrows && hh == 0)
-            atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
-        } else if (half == 0 && r < nrows) {
-          atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
-        }
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Decode-shaped proxy (at most 64 query rows per request and KV head, e.g.
 // a few MTP tokens x G heads): HBM-bound, every K page is read once.  Each
@@ -311,6 +84,21 @@ __device__ __forceinline__ void lds_rd4(u32x4 (&k)[4], const uint32_t (&a)[4]) {
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+
+// Four 16-byte LDS reads, not waited for (outputs early-clobber); pair with
+// lds_wait4 on the same registers before their use.
+__device__ __forceinline__ void lds_rd4_issue(u32x4 (&k)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
+}
+__device__ __forceinline__ void lds_wait4(u32x4 (&k)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]));
 }
 
 __device__ __forceinline__ uint32_t lds_addr32(const void* p) {
@@ -595,14 +383,251 @@ __global__ __launch_bounds__(256) void msa_proxy_rows_kernel(ProxyParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill-shaped proxy (many query rows): MFMA-bound.  A workgroup owns 256
+// query rows (4 waves x 64, token x head of one KV head) and a range of KV
+// blocks.  Each block's K streams global -> LDS with global_load_lds (raw
+// bytes, XOR-swizzled rows, double buffered, one barrier per block); lane
+// (key l % 32, half l / 32) reads its key row's bytes for head dims
+// 64 half .. 64 half + 63 in the A-operand layout of 32x32x16 MFMA (Q uses
+// the same head-dim permutation), fp8 converted in registers.  Per block and
+// wave: 4 key subtiles x 2 row tiles x 8 k-steps, the two row tiles' chains
+// interleaved; block maxima go out as coalesced rows.
+// ---------------------------------------------------------------------------
+template <int FMT, bool REDUCE>
+__global__ __launch_bounds__(256) void msa_proxy_wide_kernel(ProxyParams p) {
+  using Geo = RowsGeom<FMT>;
+  constexpr int LB = Geo::kLaneBytes / 16;   // 16-byte pieces per lane and key subtile
+  constexpr int LOADS = Geo::kStage / 4096;  // 1 KiB loads per wave per block
+  constexpr int SW = FMT == kFmtFp8 ? 8 : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t ring[2][Geo::kStage];
+  __shared__ int64_t kbase[kRowsMaxBpw];
+
+  const int n = p.batch * p.hkv * p.row_tiles * p.block_chunks;
+  const int lid = xcd_remap(blockIdx.x, n);
+  if (lid < 0) return;
+  const int chunk = lid % p.block_chunks;
+  int rest = lid / p.block_chunks;
+  const int rt = rest % p.row_tiles;
+  rest /= p.row_tiles;
+  const int g = rest % p.hkv;
+  const int b = rest / p.hkv;
+
+  const int G = p.group;
+  const int q0 = p.cu_q[b];
+  const int lq = p.cu_q[b + 1] - q0;
+  const int nrows = lq * G;
+  const int r0 = rt * 256;
+  if (r0 >= nrows) return;
+  const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
+  const int nblk = max(0, (lk + kBlock - 1) / kBlock);
+  const int t_beg = chunk * p.blocks_per_wg;
+  const int t_end = min(t_beg + p.blocks_per_wg, p.max_k_tiles);
+  if (t_beg >= t_end) return;
+  const int r_last = min(r0 + 256, nrows) - 1;
+  const int pos_min = lk - lq + r0 / G;
+  const int pos_max = lk - lq + r_last / G;
+  int t_act = min(t_end, nblk);
+  if (p.paged) t_act = min(t_act, p.pt_width);
+  if (p.causal) t_act = min(t_act, pos_max < 0 ? 0 : pos_max / kBlock + 1);
+  t_act = max(t_act, t_beg);
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int lane = tid & (kWave - 1);
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int64_t kst = p.k_st.token;
+
+  for (int i = tid; i < t_act - t_beg; i += 256) {
+    const int t = t_beg + i;
+    if (p.paged) {
+      const int64_t page = p.page_table[(int64_t)b * p.pt_width + t];
+      kbase[i] = page * p.k_st.page + g * p.k_st.head;
+    } else {
+      kbase[i] = ((int64_t)p.cu_k[b] + kBlock * t) * kst + g * p.k_st.head;
+    }
+  }
+
+  // rows of this wave: r0 + 64 wave + 32 nt + col
+  int row_[2], pos_[2];
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = r0 + 64 * wave + 32 * nt + col;
+    row_[nt] = r;
+    const int tk = r / G, hh = r % G;
+    pos_[nt] = lk - lq + tk;
+    if (r < nrows) {
+      const uint8_t* qp = reinterpret_cast<const uint8_t*>(
+          p.q + ((int64_t)(q0 + tk) * p.hq + g * G + hh) * kHeadDim) + 128 * half;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[nt][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qf[nt][s] = as_bf16x8(u32x4{0, 0, 0, 0});
+    }
+  }
+  // blocks of the chunk with no visible key: -inf (pre-filled when reducing)
+  if (!REDUCE && half == 0) {
+    for (int t = t_act; t < t_end; ++t) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int r = row_[nt];
+        if (r < nrows)
+          p.out[((int64_t)(g * G + r % G) * p.max_k_tiles + t) * p.total_q + q0 + r / G] = -INFINITY;
+      }
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 w = __builtin_bit_cast(u32x4, qf[nt][s]);
+      asm volatile("" : "+v"(w));
+      qf[nt][s] = as_bf16x8(w);
+    }
+  __syncthreads();   // kbase visible; Q loads and stores settled
+
+  // staging: load nn of wave w fills LDS bytes [1024 (4 nn + w), + 1024) of
+  // the buffer; rows of kRow bytes, XOR-swizzled in 16-byte chunks
+  constexpr int LPR = Geo::kRow / 16;   // lanes per row
+  constexpr int RPL = 64 / LPR;         // rows per load
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr32(&ring[0][0]));
+  auto issue = [&](int t, int buf) {
+    const int i = t - t_beg;
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    const uint8_t* base = p.k + kbase[i];
+#pragma unroll
+    for (int nn = 0; nn < LOADS; ++nn) {
+      const int ld = 4 * nn + wave;
+      const int row = RPL * ld + lane / LPR;
+      const int c = (lane % LPR) ^ (row % SW);
+      const int rr = row < nvalid ? row : 0;   // past the end: row 0 (masked)
+      g2lds16_px(base + rr * kst + 16 * c, ring0 + buf * Geo::kStage + 1024 * ld);
+    }
+  };
+
+  if (t_beg < t_act) issue(t_beg, 0);
+  for (int t = t_beg; t < t_act; ++t) {
+    const int buf = (t - t_beg) & 1;
+    if (t + 1 < t_act) {
+      issue(t + 1, buf ^ 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+
+    const int nvalid = min(kBlock, lk - kBlock * t);
+    const bool full = nvalid == kBlock && (!p.causal || pos_min >= kBlock * t + kBlock - 1);
+    const uint32_t sb = ring0 + buf * Geo::kStage;
+    float bm[2] = {-INFINITY, -INFINITY};
+    // Software pipeline over the 4 key subtiles: the LDS reads of subtile
+    // kt + 1 and the row maxima of subtile kt - 1 overlap the MFMAs of kt.
+    u32x4 kr[2][LB];
+    auto kread = [&](int kt, u32x4 (&dst)[LB]) {
+      const int row = 32 * kt + col;
+#pragma unroll
+      for (int j0 = 0; j0 < LB; j0 += 4) {
+        uint32_t a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a[j] = sb + row * Geo::kRow + 16 * ((LB * half + j0 + j) ^ (row % SW));
+        u32x4 w[4];
+        lds_rd4_issue(w, a);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j0 + j] = w[j];
+      }
+    };
+    auto kwait = [&](u32x4 (&dst)[LB]) {
+#pragma unroll
+      for (int j0 = 0; j0 < LB; j0 += 4) {
+        u32x4 w[4] = {dst[j0], dst[j0 + 1], dst[j0 + 2], dst[j0 + 3]};
+        lds_wait4(w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dst[j0 + j] = w[j];
+      }
+    };
+    auto reduce = [&](int kt, f32x16 (&acc)[2]) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        if (!full) {
+          int lim = nvalid - 1;
+          if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+            acc[nt][r] = key <= lim ? acc[nt][r] : -INFINITY;
+          }
+        }
+        bm[nt] = fmaxf(bm[nt], max16(acc[nt]));
+      }
+    };
+    f32x16 acc[2][2];
+    kread(0, kr[0]);
+    kwait(kr[0]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int cur = kt & 1;
+      if (kt < 3) kread(kt + 1, kr[cur ^ 1]);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        bf16x8 a;
+        if constexpr (FMT == kFmtFp8) {
+          const u32x4 w = kr[cur][s >> 1];
+          a = (s & 1) ? fp8x8_bf16(w[2], w[3]) : fp8x8_bf16(w[0], w[1]);
+        } else {
+          a = as_bf16x8(kr[cur][s]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          if (s == 0) {
+            f32x16 z;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) z[r] = 0.f;
+            acc[cur][nt] = mfma32(a, qf[nt][s], z);
+          } else {
+            acc[cur][nt] = mfma32(a, qf[nt][s], acc[cur][nt]);
+          }
+        }
+      }
+      if (kt > 0) reduce(kt - 1, acc[cur ^ 1]);
+      if (kt < 3) kwait(kr[cur ^ 1]);
+    }
+    reduce(3, acc[1]);
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      float v = xor_max(bm[nt], 32);
+      const int r = row_[nt];
+      const int tk = r / G, hh = r % G;
+      if constexpr (!REDUCE) {
+        if (half == 0 && r < nrows)
+          p.out[((int64_t)(g * G + hh) * p.max_k_tiles + t) * p.total_q + q0 + tk] = v;
+      } else {
+        if ((G & (G - 1)) == 0 && G <= 32) {
+          for (int off = 1; off < G; off <<= 1) v = xor_max(v, off);
+          if (half == 0 && r < nrows && hh == 0)
+            atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+        } else if (half == 0 && r < nrows) {
+          atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+        }
+      }
+    }
+    // every wave's reads of this buffer done before it is refilled
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+}
+
 __global__ void msa_fill_kernel(float* __restrict__ out, int64_t n, float v) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (; i < n; i += stride) out[i] = v;
 }
 
-template <int NTW, int KSW, int FMT>
-static hipError_t launch_proxy_t(const ProxyParams& p, hipStream_t stream) {
+template <int FMT>
+static hipError_t launch_proxy_wide_t(const ProxyParams& p, hipStream_t stream) {
   const int n = p.batch * p.hkv * p.row_tiles * p.block_chunks;
   if (n <= 0) return hipSuccess;
   const int grid = 8 * ((n + 7) / 8);
@@ -612,9 +637,9 @@ static hipError_t launch_proxy_t(const ProxyParams& p, hipStream_t stream) {
       int fb = (int)std::min<int64_t>((total + 255) / 256, 4096);
       hipLaunchKernelGGL(msa_fill_kernel, dim3(fb), dim3(256), 0, stream, p.out, total, -INFINITY);
     }
-    hipLaunchKernelGGL((msa_proxy_kernel<NTW, KSW, FMT, true>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((msa_proxy_wide_kernel<FMT, true>), dim3(grid), dim3(256), 0, stream, p);
   } else {
-    hipLaunchKernelGGL((msa_proxy_kernel<NTW, KSW, FMT, false>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((msa_proxy_wide_kernel<FMT, false>), dim3(grid), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }
@@ -636,13 +661,13 @@ static hipError_t launch_proxy_rows_t(const ProxyParams& p, hipStream_t stream) 
   return hipGetLastError();
 }
 
-// wide_rows: 1 -> 256 rows per workgroup (4 row groups x 64) with K staged
-// through LDS; 0 -> at most 64 rows per (request, KV head), the register
-// path above (p.rows_per_tile holds the row count rounded up to 32).
+// wide_rows: 1 -> 256 rows per workgroup (msa_proxy_wide_kernel); 0 -> at
+// most 64 rows per (request, KV head) (msa_proxy_rows_kernel; p.rows_per_tile
+// holds the row count rounded up to 32).
 hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream) {
   if (wide_rows) {
-    return fmt == kFmtFp8 ? launch_proxy_t<2, 4, kFmtFp8>(p, stream)
-                          : launch_proxy_t<2, 4, kFmtBf16>(p, stream);
+    return fmt == kFmtFp8 ? launch_proxy_wide_t<kFmtFp8>(p, stream)
+                          : launch_proxy_wide_t<kFmtBf16>(p, stream);
   }
   if (p.rows_per_tile <= 32)
     return fmt == kFmtFp8 ? launch_proxy_rows_t<1, kFmtFp8>(p, stream)
