@@ -279,10 +279,10 @@ def bench_decode(args, msa, synth, torch):
         "stages_ms": {"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
                       "sparse_attention": round(st[2], 4)},
         "work": {"kv_bytes": nbytes},
-        "roofline": {"kernel": "msa_attention_kernel (decode)", "bound": "hbm",
+        "roofline": {"kernel": "msa_decode_kernel", "bound": "hbm",
                      "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": _traffic_for("msa_attention_kernel:" + p.name)},
+                     "traffic": _traffic_for("msa_decode_kernel:" + p.name)},
     }
     return res, p
 
