@@ -37,6 +37,8 @@ msa_status_t hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+constexpr int64_t kMaxTokenStride = (int64_t)1 << 24;
+
 // Resolve a stride triple for a tensor with `row_bytes` contiguous bytes per
 // token row.  Dense layout for zeros.  Rejects unaligned views.
 msa_status_t resolve_strides(const char* name, const msa_strides_t& in, bool paged, int hkv,
@@ -51,13 +53,15 @@ msa_status_t resolve_strides(const char* name, const msa_strides_t& in, bool pag
     s.token = in.token ? in.token : (int64_t)hkv * row_bytes;
     s.page = 0;
   }
-  if (s.token < row_bytes || s.token % align || s.head % align || s.page % align || s.head < 0 ||
-      s.page < 0)
+  // (kernels address a 128-token block as base + 32-bit per-lane offset)
+  if (s.token < row_bytes || s.token > kMaxTokenStride || s.token % align || s.head % align ||
+      s.page % align || s.head < 0 || s.page < 0)
     return fail(MSA_ERR_UNSUPPORTED,
                 "%s: strides (page %lld, head %lld, token %lld bytes) are not a readable view "
-                "(rows of %lld contiguous bytes, %lld-byte aligned); views are never copied",
+                "(rows of %lld contiguous bytes, %lld-byte aligned, token stride <= %lld); "
+                "views are never copied",
                 name, (long long)s.page, (long long)s.head, (long long)s.token,
-                (long long)row_bytes, (long long)align);
+                (long long)row_bytes, (long long)align, (long long)kMaxTokenStride);
   *out = s;
   return MSA_OK;
 }

@@ -23,6 +23,17 @@ __device__ __forceinline__ void g2lds16(const void* gaddr, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// Same, addressed as scalar base + per-lane 32-bit byte offset (the saddr
+// form: no 64-bit address arithmetic or registers per lane).
+__device__ __forceinline__ void g2lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\t"
+               "s_nop 0\n\t"
+               "global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // Workgroup barrier that does not drain outstanding global loads (unlike
 // __syncthreads, whose release fence waits for every in-flight load,
 // including the next block's prefetch).  Callers first wait on exactly the

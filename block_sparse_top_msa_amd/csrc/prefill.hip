@@ -5,9 +5,10 @@
 // gfx950 design:
 //  * Tile = TOK query tokens of one request x the G query heads of one KV
 //    head, as token-major rows cut into 32-row slots; each of NW waves owns
-//    SPW slots.  32-row slots because v_mfma_f32_32x32x16_bf16 runs at twice
-//    the FLOP rate of the 16x16x32 shape on this chip (measured: ~2.4 vs
-//    ~1.3 PFLOP/s) and reads half the LDS bytes per FLOP.
+//    SPW slots.  32-row slots because v_mfma_f32_32x32x16_bf16 reads half
+//    the LDS operand bytes per FLOP of the 16x16x32 shape and runs ~10%
+//    faster per FLOP on this chip (measured: 32 vs ~17.5 cycles per
+//    instruction for twice the work).
 //  * The tile's block union is built in LDS (tile_union.hpp).  Each union
 //    block (128 keys of K and V, 64 KiB) is staged global -> LDS with
 //    global_load_lds (16 B per lane, no VGPR staging), double buffered: block
@@ -15,15 +16,20 @@
 //    16-byte chunks so every operand read is bank-conflict free with an
 //    unpadded 256-byte row pitch.
 //  * Per 32-key chunk: S^T = K Q^T (keys on the MFMA M axis, query rows on
-//    N), the softmax update, and O^T += V^T P^T with P taken straight from
-//    the S^T registers.  The chunk's K and V^T fragments are read into
-//    registers once and reused by every active slot of the wave; V^T comes
-//    from row-major V through the transposing ds_read_b64_tr_b16.
+//    N), the softmax, and O^T += V^T P^T with P taken straight from the S^T
+//    registers; V^T comes from row-major V through the transposing
+//    ds_read_b64_tr_b16.  The chunks are software pipelined per wave (the
+//    softmax of chunk c runs beside the MFMAs of S^T(c + 1) and of
+//    O^T += V^T P^T for chunk c - 1), written as groups of one MFMA, its LDS
+//    reads and a few vector instructions so that one wave keeps the matrix
+//    core and the vector ALU busy together; O^T += V^T P^T of a block's last
+//    chunk runs in the next block.
 //  * Softmax: p = exp2(s * c - m) is one FMA + one exp per score against a
-//    per-row reference max m set by the row's first scores and moved again
-//    (rescaling O and l) only if a score exceeds it by more than 2^64, which
-//    the fp32 accumulators absorb; row sums stay per lane until the end.  A slot none of whose tokens chose a
-//    block skips it (one scalar branch per slot and chunk).
+//    per-row reference max m, taken from the row's first scores and moved
+//    (rescaling O and l) only when a score passes it by more than 64 in log2
+//    units, which an overflowing partial row sum reveals without a per-chunk
+//    max; row sums stay per lane until the end.  A slot none of whose tokens
+//    chose a block skips it (one scalar branch per slot and block).
 #include "async_lds.hpp"
 #include "common.hpp"
 #include "internal.hpp"
@@ -40,6 +46,9 @@ constexpr float kLn2f = 0.69314718055994530942f;
 // depend on magnitude, so O is rescaled only if a row's max jumps by more
 // than 64 (in log2 units) after its first block.
 constexpr float kRescaleSlack = 64.0f;
+// A lane's 16 exponentials of a chunk sum to at most 16 * 2^64 while every
+// score is within the slack of the reference max.
+constexpr float kSumLimit = 0x1p68f;
 
 struct PrefillLds {
   uint8_t kv[2][2 * kTileBytes];   // [buffer][K | V]
@@ -55,69 +64,19 @@ struct PrefillLds {
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 __device__ __forceinline__ int swz_v(int r, int c) { return c ^ ((r & 3) << 2); }
 
-// Transposed reads (outputs early-clobber, see kfrag_load) of the V^T operand
-// of one 32-key chunk, for the four
-// 32-column head-dim tiles dt and the two 16-key k-steps: rows r, r + 8
-// (first k-step) and r + 16, r + 24 (second), i.e. byte offsets 0, 2048,
-// 4096, 6144.  In each group of 16 lanes, lane j receives element j % 4 of
-// the 8 bytes at lane 4e + j / 4's address, for e = 0..3: four consecutive
-// keys of one head-dim column.
-__device__ __forceinline__ void vtr_issue(u32x2 (&v)[16], const uint32_t (&a)[4]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n\t"
-      "ds_read_b64_tr_b16 %1, %16 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %2, %16 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %3, %16 offset:6144\n\t"
-      "ds_read_b64_tr_b16 %4, %17\n\t"
-      "ds_read_b64_tr_b16 %5, %17 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %6, %17 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %7, %17 offset:6144\n\t"
-      "ds_read_b64_tr_b16 %8, %18\n\t"
-      "ds_read_b64_tr_b16 %9, %18 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %10, %18 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %11, %18 offset:6144\n\t"
-      "ds_read_b64_tr_b16 %12, %19\n\t"
-      "ds_read_b64_tr_b16 %13, %19 offset:2048\n\t"
-      "ds_read_b64_tr_b16 %14, %19 offset:4096\n\t"
-      "ds_read_b64_tr_b16 %15, %19 offset:6144"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]),
-        "=&v"(v[7]), "=&v"(v[8]), "=&v"(v[9]), "=&v"(v[10]), "=&v"(v[11]), "=&v"(v[12]), "=&v"(v[13]),
-        "=&v"(v[14]), "=&v"(v[15])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
-}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// The eight K operand fragments of one 32-key chunk (ds_read_b128 each),
-// issued without waiting (outputs early-clobber: a load may return while
-// later loads of the group still read their address registers).
-__device__ __forceinline__ void kfrag_issue(u32x4 (&k)[8], const uint32_t (&a)[8]) {
-  asm volatile(
-      "ds_read_b128 %0, %8\n\t"
-      "ds_read_b128 %1, %9\n\t"
-      "ds_read_b128 %2, %10\n\t"
-      "ds_read_b128 %3, %11\n\t"
-      "ds_read_b128 %4, %12\n\t"
-      "ds_read_b128 %5, %13\n\t"
-      "ds_read_b128 %6, %14\n\t"
-      "ds_read_b128 %7, %15"
-      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]), "=&v"(k[6]),
-        "=&v"(k[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]));
+// LDS reads through the compiler's builtins: it tracks their completion (LDS
+// reads return in order, so it waits with exact lgkmcnt values) and may place
+// them among the MFMAs of a scheduling region.
+__device__ __forceinline__ u32x4 lds_b128(uint32_t a) {
+  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)a;
 }
-
-// Waits for every outstanding LDS read; naming the K registers orders their
-// uses after it.
-__device__ __forceinline__ void kfrag_wait(u32x4 (&k)[8]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]), "+v"(k[4]), "+v"(k[5]),
-                 "+v"(k[6]), "+v"(k[7]));
-}
-
-// Waits for the reads above; naming the registers orders their uses after it.
-__device__ __forceinline__ void vtr_wait(u32x2 (&v)[16]) {
-  asm volatile("s_waitcnt lgkmcnt(0)"
-               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),
-                 "+v"(v[6]), "+v"(v[7]), "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]),
-                 "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15]));
+// ds_read_b64_tr_b16: in each group of 16 lanes, lane j receives element
+// j % 4 of the 8 bytes at lane 4e + j / 4's address, for e = 0..3.
+__device__ __forceinline__ u32x2 lds_tr16(uint32_t a) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) s16x4*)(uintptr_t)a));
 }
 
 __device__ __forceinline__ float swap32_max(float x) {
@@ -127,6 +86,185 @@ __device__ __forceinline__ float swap32_max(float x) {
 __device__ __forceinline__ float swap32_sum(float x) {
   auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+
+// Per-lane LDS addresses of the current block's operands (the buffer's base
+// included, moved with it from block to block, so that the chunk and row
+// offsets below are instruction immediates).  K fragment ks of 32-key chunk
+// c: k[ks] + 8192 c.  V^T fragments of chunk c for head-dim tile dt:
+// v[dt] + 8192 c + 2048 e, e = 0..3 (rows r, r + 8, r + 16, r + 24).
+struct ChunkAddr {
+  uint32_t k[8];
+  uint32_t v[4];
+};
+
+__device__ __forceinline__ void load_k(u32x4 (&kw)[8], const ChunkAddr& a, int c) {
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) kw[ks] = lds_b128(a.k[ks] + 8192 * c);
+}
+
+// O^T += V^T P^T for one chunk (two 16-key k-steps per head-dim tile).
+__device__ __forceinline__ void pv(f32x16 (&o)[4], const u32x2 (&vv)[16], u32x4 p0, u32x4 p1) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const u32x4 w0 = {vv[4 * dt][0], vv[4 * dt][1], vv[4 * dt + 1][0], vv[4 * dt + 1][1]};
+    const u32x4 w1 = {vv[4 * dt + 2][0], vv[4 * dt + 2][1], vv[4 * dt + 3][0], vv[4 * dt + 3][1]};
+    o[dt] = mfma32(as_bf16x8(w0), as_bf16x8(p0), o[dt]);
+    o[dt] = mfma32(as_bf16x8(w1), as_bf16x8(p1), o[dt]);
+  }
+}
+
+__device__ __forceinline__ float max16(const f32x16& a) {
+  const float x = fmaxf(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3])),
+                        fmaxf(fmaxf(a[4], a[5]), fmaxf(a[6], a[7])));
+  return fmaxf(x, fmaxf(fmaxf(fmaxf(a[8], a[9]), fmaxf(a[10], a[11])),
+                        fmaxf(fmaxf(a[12], a[13]), fmaxf(a[14], a[15]))));
+}
+
+// Per-wave pipeline state of one 32-row slot.  It persists across blocks:
+// O^T += V^T P^T of a block's last chunk runs in the wave's next active
+// block (or after the last one).
+struct SlotPipe {
+  f32x16 s;        // S^T of the chunk whose softmax comes next
+  u32x4 kw[8];     // K fragments of the chunk after that
+  u32x2 vv[16];    // V^T fragments of the chunk awaiting O^T += V^T P^T
+  u32x4 p0, p1;    // P^T of that chunk
+};
+
+// One MFMA of O^T += V^T P^T: head-dim tile g / 2, k-step g % 2 (its V^T
+// fragments are vv[2 g] and vv[2 g + 1]).
+__device__ __forceinline__ void pv_step(f32x16 (&o)[4], const u32x2 (&vv)[16], u32x4 p0, u32x4 p1,
+                                        int g) {
+  const u32x4 w = {vv[2 * g][0], vv[2 * g][1], vv[2 * g + 1][0], vv[2 * g + 1][1]};
+  o[g >> 1] = mfma32(as_bf16x8(w), as_bf16x8((g & 1) ? p1 : p0), o[g >> 1]);
+}
+
+// The two V^T fragments vv[2 g], vv[2 g + 1] of chunk c.
+__device__ __forceinline__ void load_v2(u32x2 (&vv)[16], const ChunkAddr& a, int c, int g) {
+  const uint32_t base = a.v[g >> 1] + 8192 * c + 4096 * (g & 1);
+  vv[2 * g] = lds_tr16(base);
+  vv[2 * g + 1] = lds_tr16(base + 2048);
+}
+
+// MFMA k-step g of S^T (keys x query rows over head dims 16 g .. 16 g + 15).
+__device__ __forceinline__ f32x16 score_step(f32x16 s, const u32x4 (&kw)[8], const bf16x8 (&qf)[8],
+                                             int g) {
+  if (g == 0) {
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    return mfma32(as_bf16x8(kw[0]), qf[0], z);
+  }
+  return mfma32(as_bf16x8(kw[g]), qf[g], s);
+}
+
+// p = 2^(s c - mu) of scores r and r + 1, packed to one bf16 pair of P^T;
+// returns their sum.
+__device__ __forceinline__ float exp_pair(const f32x16& acc, int r, float cs, float mu, uint32_t& pw) {
+  const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], cs, -mu));
+  const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r + 1], cs, -mu));
+  pw = cvt_pk_bf16(e0, e1);
+  return e0 + e1;
+}
+
+// The chunk's 16 exponentials, their row sum and P^T, without scheduling
+// constraints (rare path).
+__device__ __forceinline__ float exp_all(const f32x16& acc, float cs, float mu, u32x4& q0, u32x4& q1) {
+  float ps[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t w;
+    ps[i] = exp_pair(acc, 2 * i, cs, mu, w);
+    if (i < 4) q0[i] = w;
+    else q1[i - 4] = w;
+  }
+  return ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+}
+
+// One 32-key chunk C of a block, software pipelined as groups of one MFMA,
+// its share of the LDS reads and a few vector-ALU instructions, each group
+// closed by a scheduling barrier so that a single wave keeps the matrix core
+// busy while it computes the softmax.  The softmax of chunk C reads S^T(C),
+// finished half a chunk earlier, and is spread over both halves:
+//  * first half: S^T of chunk C + 1 (K(C + 1) was read one chunk earlier)
+//    and the reads of V^T(C - 1);
+//  * second half: O^T += V^T P^T of chunk C - 1 (for chunk 0: the previous
+//    active block's last chunk, or zero), then the reads of K(C + 2) into the
+//    registers S^T(C + 1) released, or for chunk 3 the reads of V^T(3) into
+//    the registers each MFMA releases.
+//
+// The exponentials take the row's current reference max m as it stands, with
+// no max of the chunk in the common path: a score more than the slack above
+// m makes some p exceed 2^64 and the lane's 16-term sum exceed 2^68, which
+// sends the row (with rows that have no reference yet) down the rare path.
+// There the chunk's row max moves m, O^T (holding chunk C - 1 by then) and l
+// are rescaled, and the exponentials are redone.  Without the rare path every
+// p stays at most 2^68: exact in bf16 and fp32 range, like the sums.
+template <int C>
+__device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], float& m, float& l,
+                                              const bf16x8 (&qf)[8], const ChunkAddr& ad,
+                                              bool rowsel, int lim, int hf, float cs) {
+  f32x16 acc = sp.s;
+  // mask (diagonal / partial block only)
+  if (__ballot(rowsel && lim < 32 * C + 31) != 0ull) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 32 * C + 8 * (r >> 2) + 4 * hf + (r & 3);
+      acc[r] = key <= lim ? acc[r] : -INFINITY;
+    }
+  }
+  // +inf for rows that take no keys here (p = 0) or have no reference yet
+  const float mu = (rowsel && m > -INFINITY) ? m : INFINITY;
+  u32x4 q0, q1;
+  float ps[8], e[8];
+  f32x16 sn = sp.s;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    if constexpr (C < 3) sn = score_step(sn, sp.kw, qf, g);
+    if constexpr (C > 0) load_v2(sp.vv, ad, C - 1, g);
+    e[g] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g], cs, -mu));
+    if (g & 1) {
+      q0[g >> 1] = cvt_pk_bf16(e[g - 1], e[g]);
+      ps[g >> 1] = e[g - 1] + e[g];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    pv_step(o, sp.vv, sp.p0, sp.p1, g);
+    if constexpr (C < 2) sp.kw[g] = lds_b128(ad.k[g] + 8192 * (C + 2));
+    if constexpr (C == 3) load_v2(sp.vv, ad, 3, g);
+    e[g] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[8 + g], cs, -mu));
+    if (g & 1) {
+      q1[g >> 1] = cvt_pk_bf16(e[g - 1], e[g]);
+      ps[4 + (g >> 1)] = e[g - 1] + e[g];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (C < 3) sp.s = sn;
+  float lp = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+  if (__ballot(rowsel && (m == -INFINITY || !(lp <= kSumLimit))) != 0ull) {
+    float mx = max16(acc);
+    mx = rowsel ? mx * cs : -INFINITY;
+    const float mr = swap32_max(mx);   // the row's other 16 keys sit in lane l ^ 32
+    // first scores of a row: the max becomes the reference (O and l are
+    // still zero); afterwards m moves only when the max passed the slack
+    const bool up = mr > m + kRescaleSlack;
+    if (__ballot(up && m > -INFINITY) != 0ull) {
+      const float alpha = up ? __builtin_amdgcn_exp2f(m - mr) : 1.0f;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+    }
+    m = up ? mr : m;
+    const float mu2 = (rowsel && m > -INFINITY) ? m : INFINITY;
+    lp = exp_all(acc, cs, mu2, q0, q1);
+  }
+  l += lp;
+  sp.p0 = q0;
+  sp.p1 = q1;
 }
 
 }  // namespace
@@ -253,38 +391,45 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
 
   // Staging: lane l of wave w loads the 16-byte chunk (row r_i, logical
   // chunk c) for physical position (r_i, l % 16), r_i = 4 w + l / 16 + 16 i.
+  // Addresses are a scalar base (block start + 16 i rows) plus the lane's
+  // 32-bit offset within the row group (token strides are at most 16 MiB).
   const int lr0 = 4 * wave + (lane >> 4);
-  const int64_t koff0 = lr0 * kst + 16 * swz_k(lr0, lane & 15);
-  const int64_t voff0 = lr0 * vst + 16 * swz_v(lr0, lane & 15);
+  const uint32_t koff0 = (uint32_t)(lr0 * kst) + 16 * swz_k(lr0, lane & 15);
+  const uint32_t voff0 = (uint32_t)(lr0 * vst) + 16 * swz_v(lr0, lane & 15);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds.kv[0])) + wave * 1024;
 
   auto issue = [&](int u, int buf) {
     const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
     const int nvalid = min(kBlock, lk - kBlock * t);
-    const uint8_t* kb = p.k + lds.kbase[u];
-    const uint8_t* vb = p.v + lds.vbase[u];
+    const uint8_t* kb = p.k + (int64_t)uniform64((unsigned long long)lds.kbase[u]);
+    const uint8_t* vb = p.v + (int64_t)uniform64((unsigned long long)lds.vbase[u]);
     const uint32_t dst = lds0 + buf * (2 * kTileBytes);
+    // recomputed per block from an opaque copy of the lane's row: hoisted out
+    // of the loop, the per-row offsets would hold registers through the
+    // attention math
+    int lr = lr0;
+    asm volatile("" : "+v"(lr));
     if (nvalid == kBlock) {
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i)
-        g2lds16(kb + koff0 + (int64_t)(4 * NW * i) * kst, dst + i * NW * 1024);
+        g2lds16_sv(kb + (int64_t)(4 * NW * i) * kst, koff0, dst + i * NW * 1024);
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i)
-        g2lds16(vb + voff0 + (int64_t)(4 * NW * i) * vst, dst + kTileBytes + i * NW * 1024);
+        g2lds16_sv(vb + (int64_t)(4 * NW * i) * vst, voff0, dst + kTileBytes + i * NW * 1024);
     } else {
       // partial last block: rows past Lk read the block's row 0 instead
       // (finite values; those keys are masked and their P is 0)
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i) {
-        const bool in = lr0 + 4 * NW * i < nvalid;
-        g2lds16(kb + (in ? koff0 + (int64_t)(4 * NW * i) * kst : koff0 - lr0 * kst),
-                dst + i * NW * 1024);
+        const int row = lr + 4 * NW * i;
+        g2lds16_sv(kb, (uint32_t)((row < nvalid ? row : 0) * kst) + 16 * swz_k(lr, lane & 15),
+                   dst + i * NW * 1024);
       }
 #pragma unroll
       for (int i = 0; i < KLOADS; ++i) {
-        const bool in = lr0 + 4 * NW * i < nvalid;
-        g2lds16(vb + (in ? voff0 + (int64_t)(4 * NW * i) * vst : voff0 - lr0 * vst),
-                dst + kTileBytes + i * NW * 1024);
+        const int row = lr + 4 * NW * i;
+        g2lds16_sv(vb, (uint32_t)((row < nvalid ? row : 0) * vst) + 16 * swz_v(lr, lane & 15),
+                   dst + kTileBytes + i * NW * 1024);
       }
     }
   };
@@ -292,22 +437,37 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
   const float C = p.scale_log2;
   if (ucount > 0) issue(0, 0);
 
-  // per-lane constant parts of the transposed V reads: 16-lane group q16
-  // covers key half q16 / 2 and head-dim columns 16 * (q16 % 2) + 0..15 of a
-  // 32-column tile; its lane 4e + q reads row 4 * half + e, columns 4q..4q+3
-  uint32_t koffs[8];
+  // per-lane constant parts of the operand reads.  K: lane l reads row
+  // l % 32, logical chunk 2 ks + l / 32.  V^T: 16-lane group q16 covers key
+  // half q16 / 2 and head-dim columns 16 * (q16 % 2) + 0..15 of a 32-column
+  // tile; its lane 4e + q reads row 4 * half + e, columns 4q..4q+3.
+  ChunkAddr ad;
+  const uint32_t kv0 = lds_addr(lds.kv[0]);
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) koffs[ks] = l32 * 256 + 16 * swz_k(l32, 2 * ks + hf);
-  const int q16 = lane >> 4;
-  const int vrow = 4 * (q16 >> 1) + ((lane & 15) >> 2);
-  const int vchunk = 2 * (q16 & 1) + ((lane & 3) >> 1);
-  const int vbyte = 8 * (lane & 1);
+  for (int ks = 0; ks < 8; ++ks) ad.k[ks] = kv0 + l32 * 256 + 16 * swz_k(l32, 2 * ks + hf);
+  {
+    const int q16 = lane >> 4;
+    const int vrow = 4 * (q16 >> 1) + ((lane & 15) >> 2);
+    const int vchunk = 2 * (q16 & 1) + ((lane & 3) >> 1);
+    // the V swizzle depends on the row only through row % 4, the same for
+    // rows vrow + 8 i
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      ad.v[dt] = kv0 + kTileBytes + vrow * 256 + 16 * swz_v(vrow, 4 * dt + vchunk) + 8 * (lane & 1);
+  }
 
   static_assert(SPW == 1, "the software-pipelined loop runs one slot per wave");
   const unsigned long long tokmask0 = tokmask[0];
   const int tk0 = tk_[0];
   const int pos0 = pos_[0];
 
+  // the first active block's O^T += V^T P^T of "the previous block" adds
+  // zero
+  SlotPipe sp;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sp.vv[i] = u32x2{0, 0};
+  sp.p0 = u32x4{0, 0, 0, 0};
+  sp.p1 = u32x4{0, 0, 0, 0};
   for (int u = 0; u < ucount; ++u) {
     const int buf = u & 1;
     const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
@@ -323,128 +483,57 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
     }
     block_barrier();
 
-    const uint32_t kt_lds = lds_addr(lds.kv[buf]);
-    const uint32_t vt_lds = kt_lds + kTileBytes;
     const bool rowsel = (tk0 < ntok) && ((umask >> tk0) & 1ull);
     int lim = nvalid - 1;
     if (p.causal) lim = min(lim, pos0 - kBlock * t);
 
     if ((umask & tokmask0) != 0ull) {
-      // Software pipeline over the block's four 32-key chunks: S^T of chunk
-      // c + 1 and O^T += V^T P^T of chunk c are issued back to back, so the
-      // matrix core works through them while the softmax of chunk c + 1 runs
-      // on the vector ALU.
-      u32x4 kw[8];
-      {
-        uint32_t a[8];
+      // prologue: S^T of chunk 0; K(1) reads refill K(0)'s registers as the
+      // MFMAs release them
+      load_k(sp.kw, ad, 0);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) a[ks] = kt_lds + koffs[ks];
-        kfrag_issue(kw, a);
-        kfrag_wait(kw);
+      for (int g = 0; g < 8; ++g) {
+        sp.s = score_step(sp.s, sp.kw, qf[0], g);
+        sp.kw[g] = lds_b128(ad.k[g] + 8192);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      f32x16 s_next;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s_next = mfma32(as_bf16x8(kw[ks]), qf[0][ks], s_next);
-
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        f32x16 acc = s_next;
-        // V^T fragments of chunk c and K fragments of chunk c + 1, in flight
-        // during the softmax
-        u32x2 vv[16];
-        {
-          const int r = 32 * c + vrow;
-          uint32_t a[4];
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
-            a[dt] = vt_lds + r * 256 + 16 * swz_v(r, 4 * dt + vchunk) + vbyte;
-          vtr_issue(vv, a);
-        }
-        if (c < 3) {
-          uint32_t a[8];
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) a[ks] = kt_lds + 32 * (c + 1) * 256 + koffs[ks];
-          kfrag_issue(kw, a);
-        }
-        // ---- mask (diagonal / partial block only)
-        if (__ballot(rowsel && lim < 32 * c + 31) != 0ull) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * c + 8 * (r >> 2) + 4 * hf + (r & 3);
-            acc[r] = key <= lim ? acc[r] : -INFINITY;
-          }
-        }
-        float mx = fmaxf(fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])),
-                         fmaxf(fmaxf(acc[4], acc[5]), fmaxf(acc[6], acc[7])));
-        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(acc[8], acc[9]), fmaxf(acc[10], acc[11])),
-                             fmaxf(fmaxf(acc[12], acc[13]), fmaxf(acc[14], acc[15]))));
-        mx = rowsel ? mx * C : -INFINITY;
-        // first scores of a row: take the max as the reference (O and l are
-        // still zero); afterwards move it only when it grows past the slack
-        if (__ballot(mx > m_[0] + kRescaleSlack) != 0ull) {
-          const float mr = swap32_max(mx);
-          if (__ballot(mr > m_[0] + kRescaleSlack && m_[0] > -INFINITY) != 0ull) {
-            const float alpha =
-                mr > m_[0] + kRescaleSlack ? __builtin_amdgcn_exp2f(m_[0] - mr) : 1.0f;
-            l_[0] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o_[0][dt] *= alpha;
-          }
-          m_[0] = mr > m_[0] + kRescaleSlack ? mr : m_[0];
-        }
-        const float mu = (rowsel && m_[0] > -INFINITY) ? m_[0] : INFINITY;
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], C, -mu));
-        l_[0] += (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]))) +
-                 (((e[8] + e[9]) + (e[10] + e[11])) + ((e[12] + e[13]) + (e[14] + e[15])));
-        u32x4 pw0, pw1;  // P^T for the two 16-key k-steps
-        pw0[0] = cvt_pk_bf16(e[0], e[1]);
-        pw0[1] = cvt_pk_bf16(e[2], e[3]);
-        pw0[2] = cvt_pk_bf16(e[4], e[5]);
-        pw0[3] = cvt_pk_bf16(e[6], e[7]);
-        pw1[0] = cvt_pk_bf16(e[8], e[9]);
-        pw1[1] = cvt_pk_bf16(e[10], e[11]);
-        pw1[2] = cvt_pk_bf16(e[12], e[13]);
-        pw1[3] = cvt_pk_bf16(e[14], e[15]);
-        vtr_wait(vv);
-        if (c < 3) {
-          kfrag_wait(kw);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s_next[r] = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < 8; ++ks) s_next = mfma32(as_bf16x8(kw[ks]), qf[0][ks], s_next);
-        }
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const u32x4 w0 = {vv[4 * dt][0], vv[4 * dt][1], vv[4 * dt + 1][0], vv[4 * dt + 1][1]};
-          const u32x4 w1 = {vv[4 * dt + 2][0], vv[4 * dt + 2][1], vv[4 * dt + 3][0],
-                            vv[4 * dt + 3][1]};
-          o_[0][dt] = mfma32(as_bf16x8(w0), as_bf16x8(pw0), o_[0][dt]);
-          o_[0][dt] = mfma32(as_bf16x8(w1), as_bf16x8(pw1), o_[0][dt]);
-        }
-      }
+      prefill_chunk<0>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<1>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<2>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<3>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
     }
+    // the operand addresses move to the other buffer
+    const uint32_t step = buf ? (uint32_t)(-2 * kTileBytes) : (uint32_t)(2 * kTileBytes);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ad.k[ks] += step;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) ad.v[dt] += step;
     // every wave's LDS reads of buffer `buf` are done before it is refilled
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     block_barrier();
   }
+  // O^T += V^T P^T of the last active block's last chunk
+  pv(o_[0], sp.vv, sp.p0, sp.p1);
 
-  // ---- epilogue: out = O / l * v_gs (bf16), lse = (m + log2 l) * ln 2
+  // ---- epilogue: out = O / l * v_gs (bf16), lse = (m + log2 l) * ln 2.
+  // Lane quantities are recomputed from an opaque copy of the thread id:
+  // carried over from the prologue they would hold registers through the
+  // loop.
+  int etid = threadIdx.x;
+  asm volatile("" : "+v"(etid));
+  const int el32 = etid & 31, ehf = (etid >> 5) & 1;
   const int out_row0 = q0 + i0;
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     const float lsum = swap32_sum(l_[s]);
     const int slot = wave * SPW + s;
-    const int tk = tk_[s];
+    const int r = 32 * slot + el32;
+    const int tk = r / G;
     if (tk >= ntok) continue;
-    const int hh = (32 * slot + l32) % G;
+    const int hh = r % G;
     const int64_t row = (int64_t)(out_row0 + tk) * p.hq + g * G + hh;
     const float inv = lsum > 0.f ? p.v_gs / lsum : 0.f;
-    uint16_t* op = p.out + row * kHeadDim + 4 * hf;
+    uint16_t* op = p.out + row * kHeadDim + 4 * ehf;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -452,7 +541,7 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
         *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q) =
             u32x2{pack_bf16x2(o_[s][dt][4 * q] * inv, o_[s][dt][4 * q + 1] * inv),
                   pack_bf16x2(o_[s][dt][4 * q + 2] * inv, o_[s][dt][4 * q + 3] * inv)};
-    if (p.lse && hf == 0)
+    if (p.lse && ehf == 0)
       p.lse[row] = lsum > 0.f ? (m_[s] + __log2f(lsum)) * kLn2f : -INFINITY;
   }
 }

@@ -11,6 +11,7 @@
 // step.  With reduce_heads the max over query heads happens in-kernel: within
 // a wave across the G heads of a token, then across KV heads with an exact
 // order-independent atomic max into an output pre-filled with -inf.
+#include "async_lds.hpp"
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -111,17 +112,6 @@ __device__ __forceinline__ void g2lds16_px(const void* gaddr, uint32_t lds_base)
                "global_load_lds_dwordx4 %0, off"
                :
                : "v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// Same, addressed as scalar base + per-lane 32-bit byte offset (no 64-bit
-// address arithmetic per lane).
-__device__ __forceinline__ void g2lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\t"
-               "s_nop 0\n\t"
-               "global_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds_base)
                : "memory", "m0");
 }
 

@@ -28,8 +28,8 @@
  *   - head_dim is 128 and the KV block / page size is 128 tokens.
  *   - Strides are in BYTES; a stride of 0 selects the dense layout.  The last
  *     (head_dim) dimension must be contiguous and every row 16-byte aligned
- *     (8-byte for E4M3 block-scale rows); other views are rejected with
- *     MSA_ERR_UNSUPPORTED, never copied.
+ *     (8-byte for E4M3 block-scale rows), and the token stride at most
+ *     16 MiB; other views are rejected with MSA_ERR_UNSUPPORTED, never copied.
  */
 #ifndef MSA_H_
 #define MSA_H_

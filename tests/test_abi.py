@@ -92,6 +92,12 @@ def test_attention_rejects_unreadable_views():
     b = _attn(q=FAKE + 8)
     st, _ = _call(b)
     assert st == 5
+    # a 128-token block is addressed as base + 32-bit lane offset: token
+    # strides past 16 MiB are refused
+    c = _attn()
+    c.v_strides = msa.Strides(0, 256, (1 << 24) + 16)
+    st, msg = _call(c)
+    assert st == 5 and "token stride" in msg
 
 
 def test_attention_e2m1_needs_scales_and_paging():
