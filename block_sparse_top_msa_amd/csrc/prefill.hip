@@ -216,35 +216,42 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
   }
   // +inf for rows that take no keys here (p = 0) or have no reference yet
   const float mu = (rowsel && m > -INFINITY) ? m : INFINITY;
-  u32x4 q0, q1;
-  float ps[8], e[8];
+  // The softmax work of score r (fma, exp, then pack and sum with r - 1) is
+  // skewed over three groups, so that no instruction waits on a result of
+  // its own group: group G computes the fma of score G + 2, the exp of
+  // score G + 1 and packs the pair ending at G.
+  float x[16], e[16], ps[8];
+  uint32_t pw[8];
+  float lp = 0.f;
   f32x16 sn = sp.s;
+  x[0] = __builtin_fmaf(acc[0], cs, -mu);
+  x[1] = __builtin_fmaf(acc[1], cs, -mu);
+  e[0] = __builtin_amdgcn_exp2f(x[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    if constexpr (C < 3) sn = score_step(sn, sp.kw, qf, g);
-    if constexpr (C > 0) load_v2(sp.vv, ad, C - 1, g);
-    e[g] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[g], cs, -mu));
-    if (g & 1) {
-      q0[g >> 1] = cvt_pk_bf16(e[g - 1], e[g]);
-      ps[g >> 1] = e[g - 1] + e[g];
+  for (int G = 0; G < 16; ++G) {
+    const int g = G & 7;
+    if (G < 8) {
+      if constexpr (C < 3) sn = score_step(sn, sp.kw, qf, g);
+      if constexpr (C > 0) load_v2(sp.vv, ad, C - 1, g);
+    } else {
+      pv_step(o, sp.vv, sp.p0, sp.p1, g);
+      if constexpr (C < 2) sp.kw[g] = lds_b128(ad.k[g] + 8192 * (C + 2));
+      if constexpr (C == 3) load_v2(sp.vv, ad, 3, g);
     }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    pv_step(o, sp.vv, sp.p0, sp.p1, g);
-    if constexpr (C < 2) sp.kw[g] = lds_b128(ad.k[g] + 8192 * (C + 2));
-    if constexpr (C == 3) load_v2(sp.vv, ad, 3, g);
-    e[g] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[8 + g], cs, -mu));
-    if (g & 1) {
-      q1[g >> 1] = cvt_pk_bf16(e[g - 1], e[g]);
-      ps[4 + (g >> 1)] = e[g - 1] + e[g];
+    if (G + 2 < 16) x[G + 2] = __builtin_fmaf(acc[G + 2], cs, -mu);
+    if (G + 1 < 16) e[G + 1] = __builtin_amdgcn_exp2f(x[G + 1]);
+    if (G & 1) {
+      pw[G >> 1] = cvt_pk_bf16(e[G - 1], e[G]);
+      ps[G >> 1] = e[G - 1] + e[G];
+    } else if (G >= 2) {
+      lp += ps[(G >> 1) - 1];
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (C < 3) sp.s = sn;
-  float lp = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+  lp += ps[7];
+  u32x4 q0 = {pw[0], pw[1], pw[2], pw[3]}, q1 = {pw[4], pw[5], pw[6], pw[7]};
   if (__ballot(rowsel && (m == -INFINITY || !(lp <= kSumLimit))) != 0ull) {
     float mx = max16(acc);
     mx = rowsel ? mx * cs : -INFINITY;
@@ -473,15 +480,12 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
     const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u]);
     const unsigned long long umask = uniform64(lds.un.mask[u]);
     const int nvalid = min(kBlock, lk - kBlock * t);
-    // this wave's loads of block u done (block u+1's stay in flight), then
-    // every wave's
-    if (u + 1 < ucount) {
-      issue(u + 1, buf ^ 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+    // One barrier per block: past it, every wave's loads of block u have
+    // landed and every wave has finished reading block u - 1, whose buffer
+    // the prefetch of block u + 1 then refills.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     block_barrier();
+    if (u + 1 < ucount) issue(u + 1, buf ^ 1);
 
     const bool rowsel = (tk0 < ntok) && ((umask >> tk0) & 1ull);
     int lim = nvalid - 1;
@@ -508,9 +512,6 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
     for (int ks = 0; ks < 8; ++ks) ad.k[ks] += step;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) ad.v[dt] += step;
-    // every wave's LDS reads of buffer `buf` are done before it is refilled
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    block_barrier();
   }
   // O^T += V^T P^T of the last active block's last chunk
   pv(o_[0], sp.vv, sp.p0, sp.p1);
