@@ -385,7 +385,7 @@ __global__ __launch_bounds__(256) void msa_proxy_rows_kernel(ProxyParams p) {
 // interleaved; block maxima go out as coalesced rows.
 // ---------------------------------------------------------------------------
 template <int FMT, bool REDUCE>
-__global__ __launch_bounds__(256) void msa_proxy_wide_kernel(ProxyParams p) {
+__global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   using Geo = RowsGeom<FMT>;
   constexpr int LB = Geo::kLaneBytes / 16;   // 16-byte pieces per lane and key subtile
   constexpr int LOADS = Geo::kStage / 4096;  // 1 KiB loads per wave per block
@@ -484,17 +484,24 @@ __global__ __launch_bounds__(256) void msa_proxy_wide_kernel(ProxyParams p) {
   constexpr int LPR = Geo::kRow / 16;   // lanes per row
   constexpr int RPL = 64 / LPR;         // rows per load
   const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr32(&ring[0][0]));
+  // (scalar block base + 32-bit lane offsets; token strides are at most
+  // 16 MiB)
   auto issue = [&](int t, int buf) {
     const int i = t - t_beg;
     const int nvalid = min(kBlock, lk - kBlock * t);
-    const uint8_t* base = p.k + kbase[i];
+    const uint8_t* base = p.k + (int64_t)uniform64((unsigned long long)kbase[i]);
+    // lane offsets recomputed per block from the lane id, read again here
+    // (volatile, so not hoisted): kept from the prologue, it and the offsets
+    // would hold registers through the MFMAs
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
     for (int nn = 0; nn < LOADS; ++nn) {
       const int ld = 4 * nn + wave;
-      const int row = RPL * ld + lane / LPR;
-      const int c = (lane % LPR) ^ (row % SW);
+      const int row = RPL * ld + ln / LPR;
+      const int c = (ln % LPR) ^ (row % SW);
       const int rr = row < nvalid ? row : 0;   // past the end: row 0 (masked)
-      g2lds16_px(base + rr * kst + 16 * c, ring0 + buf * Geo::kStage + 1024 * ld);
+      g2lds16_sv(base, (uint32_t)(rr * kst) + 16 * c, ring0 + buf * Geo::kStage + 1024 * ld);
     }
   };
 
