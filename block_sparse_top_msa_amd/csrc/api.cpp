@@ -186,9 +186,10 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
       splits = a->splits;
     } else {
       // fill every CU (256) with as many workgroups as its LDS holds, with at
-      // least 4 pages per split
+      // least 8 pages per split (fewer leave a wave's page ring too short to
+      // hide its own latencies: 4 splits of 4 pages ran slower than 2 of 8)
       const int target = 256 * msa::decode_workgroups_per_cu(a->kv_dtype, rows_req);
-      splits = std::max(1, std::min((target + units - 1) / units, union_max / 4));
+      splits = std::max(1, std::min((target + units - 1) / units, union_max / 8));
       splits = std::min(splits, 16);
     }
     plan.splits = std::max(1, std::min(splits, 64));
