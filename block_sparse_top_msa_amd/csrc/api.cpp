@@ -347,7 +347,7 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   const int base = std::max(1, a->batch * a->num_kv_heads * p.row_tiles);
   int chunks = std::max(1, (2048 + base - 1) / base);
   int bpw = std::max(4, (a->max_k_tiles + chunks - 1) / chunks);
-  if (!wide) bpw = std::min(64, (bpw + 3) / 4 * 4);
+  if (!wide) bpw = std::min(32, (bpw + 3) / 4 * 4);
   else bpw = std::min(64, std::max(bpw, 16));   // amortise the Q tile over >= 16 blocks
   p.blocks_per_wg = bpw;
   p.block_chunks = (a->max_k_tiles + bpw - 1) / bpw;

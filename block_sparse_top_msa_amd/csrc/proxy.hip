@@ -35,7 +35,7 @@ template <>
 struct RowsGeom<kFmtFp8> {
   static constexpr int kRow = 128;
   static constexpr int kStage = kBlock * kRow;   // 16 KiB
-  static constexpr int kStages = 2;
+  static constexpr int kStages = 1;
   static constexpr int kLoads = kStage / 1024;
   static constexpr int kLaneBytes = 64;          // per lane and 32-key chunk
 };
@@ -48,7 +48,8 @@ struct RowsGeom<kFmtBf16> {
   static constexpr int kLaneBytes = 128;
 };
 
-constexpr int kRowsMaxBpw = 64;   // blocks per workgroup on this path
+constexpr int kRowsMaxBpw = 32;   // blocks per workgroup on this path
+constexpr int kWideMaxBpw = 64;   // ... and on the prefill-shaped path
 
 template <int FMT>
 struct RowsLds {
@@ -116,7 +117,7 @@ __device__ __forceinline__ void g2lds16_px(const void* gaddr, uint32_t lds_base)
 }
 
 template <int NT, int FMT, bool REDUCE>
-__global__ __launch_bounds__(256) void msa_proxy_rows_kernel(ProxyParams p) {
+__global__ __launch_bounds__(256, 2) void msa_proxy_rows_kernel(ProxyParams p) {
   using Geo = RowsGeom<FMT>;
   constexpr int NST = Geo::kStages;
   constexpr int LOADS = Geo::kLoads;
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   constexpr int LOADS = Geo::kStage / 4096;  // 1 KiB loads per wave per block
   constexpr int SW = FMT == kFmtFp8 ? 8 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t ring[2][Geo::kStage];
-  __shared__ int64_t kbase[kRowsMaxBpw];
+  __shared__ int64_t kbase[kWideMaxBpw];
 
   const int n = p.batch * p.hkv * p.row_tiles * p.block_chunks;
   const int lid = xcd_remap(blockIdx.x, n);
