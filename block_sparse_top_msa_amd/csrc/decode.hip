@@ -34,6 +34,12 @@
 
 namespace msa {
 
+// Lazy softmax rescale (log2 units): the reference max of a row moves only
+// when a score passes it by more than 64; a lane's 8 exponentials of a page
+// then stay below 8 * 2^64.
+constexpr float kDecRescaleSlack = 64.0f;
+constexpr float kDecSumLimit = 0x1p67f;
+
 namespace {
 
 constexpr float kLn2d = 0.69314718055994530942f;
@@ -630,31 +636,49 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       int lim = nvalid - 1;
       if (p.causal) lim = min(lim, pos_[rt] - kBlock * t);
       lim = sel ? lim : -1;
-      float mx = -INFINITY;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int key = kw0 + 16 * kt + 4 * q + r;
-          const float x = key <= lim ? acc[kt][r] * C : -INFINITY;
-          acc[kt][r] = x;
-          mx = fmaxf(mx, x);
+          acc[kt][r] = key <= lim ? acc[kt][r] * C : -INFINITY;
         }
-      mx = xmax16_32(mx);
-      const float m_new = fmaxf(m_[rt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_[rt] - m_use);
+      // Exponentials against the row's reference max m as it stands (no
+      // per-page max): a score more than the slack above m makes some p pass
+      // 2^64 and the lane's 8-term sum pass 2^67, which sends the rows (with
+      // rows that have no reference yet) down the rare path, where the page's
+      // row max moves m and O and l are rescaled.  Otherwise p <= 2^67.
+      const float mu = m_[rt] > -INFINITY ? m_[rt] : INFINITY;
       float e[8];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) e[4 * kt + r] = __builtin_amdgcn_exp2f(acc[kt][r] - m_use);
-      l_[rt] = l_[rt] * alpha + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
-      m_[rt] = m_new;
+        for (int r = 0; r < 4; ++r) e[4 * kt + r] = __builtin_amdgcn_exp2f(acc[kt][r] - mu);
+      float lp = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      if (__ballot(sel && (m_[rt] == -INFINITY || !(lp <= kDecSumLimit))) != 0ull) {
+        float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                         fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+        mx = xmax16_32(mx);   // the row's keys are spread over four lanes
+        const bool up = mx > m_[rt] + kDecRescaleSlack;
+        if (__ballot(up && m_[rt] > -INFINITY) != 0ull) {
+          const float alpha = up ? __builtin_amdgcn_exp2f(m_[rt] - mx) : 1.0f;
+          l_[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o_[rt][dt] *= alpha;
+        }
+        m_[rt] = up ? mx : m_[rt];
+        const float mu2 = m_[rt] > -INFINITY ? m_[rt] : INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) e[4 * kt + r] = __builtin_amdgcn_exp2f(acc[kt][r] - mu2);
+        lp = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+      }
+      l_[rt] += lp;
       const bf16x8 pf = as_bf16x8(u32x4{cvt_pk_bf16(e[0], e[1]), cvt_pk_bf16(e[2], e[3]),
                                         cvt_pk_bf16(e[4], e[5]), cvt_pk_bf16(e[6], e[7])});
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = mfma16(vf[dt], pf, o_[rt][dt] * alpha);
+      for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = mfma16(vf[dt], pf, o_[rt][dt]);
     }
     }  // any
     // the stage's reads completed (every fragment read above waited for
