@@ -79,19 +79,20 @@ struct DecGeom<kFmtE2m1> {
   static constexpr int kLoads = kStage / 1024;     // 5
 };
 
-template <int FMT>
+template <int FMT, int NWV>
 struct DecodeLds {
-  static constexpr int kRing = 4 * DecGeom<FMT>::kStages * DecGeom<FMT>::kStage;
+  static constexpr int kRing = NWV * DecGeom<FMT>::kStages * DecGeom<FMT>::kStage;
   uint8_t ring[kRing];       // [wave][stage][K | V | (scales)]
   UnionLds un;
   int32_t page[kMaxUnion];   // page id (paged) or first row (flat) of each entry of the share
   int32_t ptrow[kPtCache];   // the request's page-table row, when it is this short
 };
 
+template <int NWV>
 struct MergeLds {
-  float o[4][16][kHeadDim];
-  float m[4][16];
-  float l[4][16];
+  float o[NWV][16][kHeadDim];
+  float m[NWV][16];
+  float l[NWV][16];
 };
 
 __device__ __forceinline__ float xsum16_32(float x) {
@@ -271,12 +272,15 @@ __device__ __forceinline__ uint32_t gather_byte(uint32_t a, uint32_t b, uint32_t
 
 }  // namespace
 
-template <int FMT, int RT>
-__global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
+template <int FMT, int RT, int NWV>
+__global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
   using Geo = DecGeom<FMT>;
   constexpr int NST = Geo::kStages;
   constexpr int LOADS = Geo::kLoads;
-  __shared__ __attribute__((aligned(16))) DecodeLds<FMT> lds;
+  constexpr int NT = NWV * 64;
+  static_assert(NWV == 4 || NWV == 8, "4 waves, or 8 taking alternate pages");
+  static_assert(sizeof(MergeLds<NWV>) <= DecodeLds<FMT, NWV>::kRing, "merge buffer inside the ring");
+  __shared__ __attribute__((aligned(16))) DecodeLds<FMT, NWV> lds;
 
   const int lid = blockIdx.x;
   const int split = lid % p.splits;
@@ -329,12 +333,12 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
     }
   }
   const bool ptc = p.paged && nblk <= kPtCache;
-  int32_t ptr_[kPtCache / 256];
+  int32_t ptr_[kPtCache / NT];
   if (ptc) {
     const int32_t* prow = p.page_table + (int64_t)b * p.pt_width;
 #pragma unroll
-    for (int k = 0; k < kPtCache / 256; ++k) {
-      const int t = tid + 256 * k;
+    for (int k = 0; k < kPtCache / NT; ++k) {
+      const int t = tid + NT * k;
       ptr_[k] = t < nblk ? prow[t] : 0;
     }
   }
@@ -364,9 +368,9 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
     }
     __syncthreads();
     ucount = lds.un.count;
-    if (ucount < 0) ucount = build_tile_union<256>(lds.un, rows, ntok, p.topk, nblk);
+    if (ucount < 0) ucount = build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk);
   } else {
-    ucount = build_tile_union<256>(lds.un, rows, ntok, p.topk, nblk);
+    ucount = build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk);
   }
   ucount = __builtin_amdgcn_readfirstlane(ucount);
   const int u0 = (int)(((int64_t)ucount * split) / p.splits);
@@ -374,13 +378,13 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
   const int n = u1 - u0;
   if (ptc) {
 #pragma unroll
-    for (int k = 0; k < kPtCache / 256; ++k) {
-      const int t = tid + 256 * k;
+    for (int k = 0; k < kPtCache / NT; ++k) {
+      const int t = tid + NT * k;
       if (t < nblk) lds.ptrow[t] = ptr_[k];
     }
     __syncthreads();
   }
-  for (int i = tid; i < n; i += 256) {
+  for (int i = tid; i < n; i += NT) {
     const int t = lds.un.list[u0 + i];
     lds.page[i] = ptc ? lds.ptrow[t]
                       : (p.paged ? p.page_table[(int64_t)b * p.pt_width + t] : p.cu_k[b] + kBlock * t);
@@ -410,11 +414,17 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
   // ---- staging: wave w's load nn (< LOADS) of a page fills bytes
   // [1024 nn, 1024 nn + 1024) of its stage; lane l writes 16 bytes at 16 l.
   // Rows are the wave's local key rows 0..31 (key 32 w + row).
+  // With 8 waves, waves 4..7 take the odd entries of the share and 0..3
+  // the even ones: two independent page streams per SIMD.
   const uint32_t wring = __builtin_amdgcn_readfirstlane(lds_addr(lds.ring)) +
                          wave * NST * Geo::kStage;
   const int64_t kst = p.k_st.token, vst = p.v_st.token;
-  const int kw0 = 32 * wave;  // this wave's first key of every page
-  auto issue = [&](int i, int stage) {
+  const int kw0 = 32 * (wave & 3);  // this wave's first key of every page
+  constexpr int PSTRIDE = NWV / 4;
+  const int par = wave >> 2;        // page parity (8 waves)
+  const int nj = n > par ? (n - par + PSTRIDE - 1) / PSTRIDE : 0;   // this wave's pages
+  auto issue = [&](int j, int stage) {
+    const int i = par + PSTRIDE * j;
     const int t = __builtin_amdgcn_readfirstlane(lds.un.list[u0 + i]);
     const int pg = __builtin_amdgcn_readfirstlane(lds.page[i]);
     const int nvalid = min(kBlock, lk - kBlock * t) - kw0;  // valid local rows
@@ -476,15 +486,16 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
 
 #pragma unroll
   for (int s = 0; s < NST; ++s)
-    if (s < n) issue(s, s);
+    if (s < nj) issue(s, s);
 
   const float C = p.scale_log2;
 
-  for (int i = 0; i < n; ++i) {
-    const int stage = i % NST;
+  for (int j = 0; j < nj; ++j) {
+    const int i = par + PSTRIDE * j;
+    const int stage = j % NST;
     // wait for this page's loads; the wave's later pages (up to NST - 1)
     // stay in flight
-    const int later = min(NST - 1, n - 1 - i);
+    const int later = min(NST - 1, nj - 1 - j);
     if (later >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LOADS) : "memory");
     else if (later == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LOADS) : "memory");
     else if (later == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
@@ -683,13 +694,13 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
     }  // any
     // the stage's reads completed (every fragment read above waited for
     // its data), so it takes the page NST ahead
-    if (i + NST < n) issue(i + NST, stage);
+    if (j + NST < nj) issue(j + NST, stage);
   }
 
-  // ---- merge the four waves' states row tile by row tile through LDS
+  // ---- merge the waves' states row tile by row tile through LDS
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __syncthreads();
-  MergeLds& mg = *reinterpret_cast<MergeLds*>(lds.ring);
+  MergeLds<NWV>& mg = *reinterpret_cast<MergeLds<NWV>*>(lds.ring);
   const int unit_split = unit * p.splits + split;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
@@ -703,17 +714,17 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       mg.l[wave][l16] = lsum;
     }
     __syncthreads();
-    const int rr = tid >> 4;          // row within the tile
+    const int rr = (tid >> 4) & 15;   // row within the tile (threads 0..255)
     const int d0 = 8 * (tid & 15);
     const int row = 16 * rt + rr;
-    if (row < R) {
+    if (tid < 256 && row < R) {
       float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) M = fmaxf(M, mg.m[w][rr]);
+      for (int w = 0; w < NWV; ++w) M = fmaxf(M, mg.m[w][rr]);
       const float Mu = M == -INFINITY ? 0.f : M;
-      float wk[4], L = 0.f;
+      float wk[NWV], L = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NWV; ++w) {
         wk[w] = __builtin_amdgcn_exp2f(mg.m[w][rr] - Mu);
         L += mg.l[w][rr] * wk[w];
       }
@@ -723,7 +734,7 @@ __global__ __launch_bounds__(256) void msa_decode_kernel(AttnParams p) {
       for (int k = 0; k < 8; ++k) {
         float x = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) x += mg.o[w][rr][d0 + k] * wk[w];
+        for (int w = 0; w < NWV; ++w) x += mg.o[w][rr][d0 + k] * wk[w];
         acc8[k] = x * invL;
       }
       const float lse_nat = L > 0.f ? (M + __log2f(L)) * kLn2d : -INFINITY;
@@ -787,11 +798,11 @@ __global__ __launch_bounds__(256) void msa_decode_merge_kernel(AttnParams p) {
   if (p.lse && d0 == 0) p.lse[orow] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
-template <int FMT, int RT>
+template <int FMT, int RT, int NWV = 4>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
   const int n = p.batch * p.hkv * p.splits;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((msa_decode_kernel<FMT, RT>), dim3(n), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV>), dim3(n), dim3(NWV * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t tasks = (int64_t)p.batch * p.hkv * p.ws_rows * 16;
@@ -803,7 +814,8 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
 template <int FMT>
 static hipError_t launch_decode_fmt(const AttnParams& p, hipStream_t stream) {
   const int rows = p.tok_per_tile * p.group;
-  if (rows <= 16) return launch_decode_t<FMT, 1>(p, stream);
+  // E2M1 stages are small enough for 8 waves (two page streams per SIMD)
+  if (rows <= 16) return launch_decode_t<FMT, 1, FMT == kFmtE2m1 ? 8 : 4>(p, stream);
   if (rows <= 32) return launch_decode_t<FMT, 2>(p, stream);
   if (rows <= 48) return launch_decode_t<FMT, 3>(p, stream);
   return launch_decode_t<FMT, 4>(p, stream);
@@ -822,9 +834,9 @@ int decode_workgroups_per_cu(int fmt, int rows) {
   if (rows > 16) return 1;
   auto per = [](int bytes) { return (160 * 1024) / bytes; };
   switch (fmt) {
-    case kFmtBf16: return per(sizeof(DecodeLds<kFmtBf16>));
-    case kFmtFp8: return per(sizeof(DecodeLds<kFmtFp8>));
-    default: return per(sizeof(DecodeLds<kFmtE2m1>));
+    case kFmtBf16: return per(sizeof(DecodeLds<kFmtBf16, 4>));
+    case kFmtFp8: return per(sizeof(DecodeLds<kFmtFp8, 4>));
+    default: return per(sizeof(DecodeLds<kFmtE2m1, 8>));
   }
 }
 
