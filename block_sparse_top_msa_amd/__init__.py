@@ -92,7 +92,7 @@ class ProxyArgs(ctypes.Structure):
 def _load():
     if not os.path.exists(library_path):
         raise ImportError(
-            f"{library_path} is missing: build it with `python -m block_sparse_top_msa_amd.build` "
+            f"{library_path} is missing: build it with `python block_sparse_top_msa_amd/build.py` "
             "(the MSA path runs only in its HIP kernels; there is no fallback)")
     L = ctypes.CDLL(library_path)
     L.msa_sparse_attention_workspace_size.argtypes = [ctypes.POINTER(AttnArgs),

@@ -1,6 +1,8 @@
 """Build libmsa.so (HIP, gfx950 only) in-tree with hipcc.
 
-    python -m block_sparse_top_msa_amd.build [--verbose]
+    python block_sparse_top_msa_amd/build.py [--verbose]
+
+(run as a script: importing the package needs the library this builds)
 
 Every call recompiles all sources (one hipcc process per translation unit,
 in parallel) and links block_sparse_top_msa_amd/libmsa.so.
