@@ -175,12 +175,16 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows_req = lqmax * G;
   if (rows_req <= 64) {
-    // decode shape: one workgroup per (request, KV head, split); its 4 waves
-    // split every page's keys
+    // decode shape: one workgroup per (request, KV head, token tile, split);
+    // its waves split every page's keys.  When one token's G heads fill a
+    // 16-row MFMA tile, every token is a tile of its own: it streams just the
+    // pages it selected (a union over the request's tokens would make each
+    // page cost all of their row tiles), with less state per workgroup.
     plan.decode = 1;
-    plan.tok_per_tile = lqmax;
-    const int units = std::max(1, a->batch * a->num_kv_heads);
-    const int union_max = std::min(lqmax * a->topk, std::max(1, a->max_k_tiles));
+    plan.tok_per_tile = (G >= 16 && lqmax > 1) ? 1 : lqmax;
+    const int tiles = (lqmax + plan.tok_per_tile - 1) / plan.tok_per_tile;
+    const int units = std::max(1, a->batch * a->num_kv_heads * tiles);
+    const int union_max = std::min(plan.tok_per_tile * a->topk, std::max(1, a->max_k_tiles));
     int splits;
     if (a->splits > 0) {
       splits = a->splits;
@@ -188,7 +192,8 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
       // fill every CU (256) with as many workgroups as its LDS holds, with at
       // least 8 pages per split (fewer leave a wave's page ring too short to
       // hide its own latencies: 4 splits of 4 pages ran slower than 2 of 8)
-      const int target = 256 * msa::decode_workgroups_per_cu(a->kv_dtype, rows_req);
+      const int target =
+          256 * msa::decode_workgroups_per_cu(a->kv_dtype, plan.tok_per_tile * G);
       splits = std::max(1, std::min((target + units - 1) / units, union_max / 8));
       splits = std::min(splits, 16);
     }
@@ -224,7 +229,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   if (plan.splits > 1) {
     const int rows = plan.tok_per_tile * G;
     const int rows_pad = (rows + 31) / 32 * 32;
-    const size_t units = (size_t)a->batch * a->num_kv_heads;
+    const size_t units = (size_t)a->batch * a->num_kv_heads * p.tiles_per_req;
     p.ws_rows = rows;
     p.ws_lse_rows = rows_pad;
     r->ws_bytes = round_up(units * plan.splits * rows_pad * sizeof(float), 256) +
@@ -275,7 +280,7 @@ msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
                   workspace_bytes, workspace);
     if (!aligned(workspace, 256)) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
     // layout: [partial LSE][partial O]
-    const size_t units = (size_t)args->batch * args->num_kv_heads;
+    const size_t units = (size_t)args->batch * args->num_kv_heads * r.p.tiles_per_req;
     const size_t l_bytes = round_up(units * r.plan.splits * r.p.ws_lse_rows * sizeof(float), 256);
     char* base = static_cast<char*>(workspace);
     r.p.ws_lse = reinterpret_cast<float*>(base);

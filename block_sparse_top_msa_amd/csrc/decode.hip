@@ -284,18 +284,12 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
 
   const int lid = blockIdx.x;
   const int split = lid % p.splits;
-  const int unit = lid / p.splits;
-  const int g = unit % p.hkv;
-  const int b = unit / p.hkv;
+  const int unit = lid / p.splits;           // (request, KV head, token tile)
+  const int jt = unit % p.tiles_per_req;
+  const int g = (unit / p.tiles_per_req) % p.hkv;
+  const int b = unit / p.tiles_per_req / p.hkv;
   if (b >= p.batch) return;
-  const int q0 = p.cu_q[b];
-  const int lq = p.cu_q[b + 1] - q0;
-  if (lq <= 0) return;
-  const int ntok = min(lq, p.tok_per_tile);
   const int G = p.group;
-  const int R = ntok * G;
-  const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
-  const int nblk = max(0, min((lk + kBlock - 1) / kBlock, p.max_k_tiles));
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -303,11 +297,65 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
   const int l16 = lane & 15;
   const int q = lane >> 4;
 
-  // ---- prologue.  Three independent reads start together: the query rows,
-  // the request's q2k rows and (short enough) its page-table row; the page
-  // ids of the union then come from LDS instead of a dependent global read.
+  // ---- prologue.  Every global read it needs starts at once, so that the
+  // pages' loads wait on one memory round trip: the query rows and the q2k
+  // entries are read where request b starts if every request has the same
+  // length (b * tiles_per_req * tok_per_tile, the decode layout), the
+  // page-table row up to its width, and the lengths beside them.  A tile
+  // elsewhere or shorter reads its rows again once its start is known.
+  const int ntok_s = p.tok_per_tile;
+  const int q0s = (b * p.tiles_per_req + jt) * ntok_s;
   // Per row tile: lane l holds query row 16 rt + l % 16 (token r / G, head r % G).
   bf16x8 qf[RT][4];
+  auto load_q = [&](int qs, int rows_n) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int r = 16 * rt + l16;
+      const int tk = r / G;
+      if (r < rows_n && qs + tk < p.total_q) {
+        const uint8_t* qp = reinterpret_cast<const uint8_t*>(
+            p.q + ((int64_t)(qs + tk) * p.hq + g * G + r % G) * kHeadDim) + 64 * q;
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+          qf[rt][ds] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ds));
+      } else {
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) qf[rt][ds] = as_bf16x8(u32x4{0, 0, 0, 0});
+      }
+    }
+  };
+  load_q(q0s, ntok_s * G);
+  // q2k entry `tid` of the speculated rows
+  const int nsel_s = ntok_s * p.topk;
+  const bool pre_fits = nsel_s <= NT;
+  int pre_id = -1;
+  if (pre_fits && tid < nsel_s && q0s + tid / p.topk < p.total_q)
+    pre_id = p.q2k[((int64_t)g * p.total_q + q0s) * p.topk + tid];
+  const int ptw = p.paged ? min(p.pt_width, kPtCache) : 0;
+  int32_t ptr_[kPtCache / NT];
+  {
+    const int32_t* prow = p.page_table + (int64_t)b * p.pt_width;
+#pragma unroll
+    for (int k = 0; k < kPtCache / NT; ++k) {
+      const int t = tid + NT * k;
+      ptr_[k] = t < ptw ? prow[t] : 0;
+    }
+  }
+
+  // the lengths are read after the rows above (scalar reads return out of
+  // order: waiting for one waits for all, so they go last)
+  const int qb = p.cu_q[b];
+  const int lq = p.cu_q[b + 1] - qb;          // the request's query tokens
+  const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
+  const int j0 = jt * p.tok_per_tile;         // the tile's first token in the request
+  if (lq - j0 <= 0) return;
+  const int q0 = qb + j0;
+  const int ntok = min(lq - j0, p.tok_per_tile);
+  const int R = ntok * G;
+  const int nblk = max(0, min((lk + kBlock - 1) / kBlock, p.max_k_tiles));
+  const bool spec = q0 == q0s && ntok == ntok_s;   // workgroup-uniform
+  if (!spec) load_q(q0, R);
+
   int tk_[RT], pos_[RT];
   unsigned long long tokmask[RT];
 #pragma unroll
@@ -315,41 +363,23 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
     const int r = 16 * rt + l16;
     const int tk = r < R ? r / G : 64;
     tk_[rt] = tk;
-    pos_[rt] = lk - lq + tk;
+    pos_[rt] = lk - lq + j0 + tk;
     const int tfirst = (16 * rt) / G;
     const int tlast = min((16 * rt + 15) / G, ntok - 1);
     unsigned long long m = 0;
     for (int t = tfirst; t <= tlast && t < 64; ++t) m |= 1ull << t;
     tokmask[rt] = uniform64((16 * rt < R) ? m : 0ull);
-    if (r < R) {
-      const uint8_t* qp = reinterpret_cast<const uint8_t*>(
-          p.q + ((int64_t)(q0 + tk) * p.hq + g * G + r % G) * kHeadDim) + 64 * q;
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds)
-        qf[rt][ds] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ds));
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) qf[rt][ds] = as_bf16x8(u32x4{0, 0, 0, 0});
-    }
   }
-  const bool ptc = p.paged && nblk <= kPtCache;
-  int32_t ptr_[kPtCache / NT];
-  if (ptc) {
-    const int32_t* prow = p.page_table + (int64_t)b * p.pt_width;
-#pragma unroll
-    for (int k = 0; k < kPtCache / NT; ++k) {
-      const int t = tid + NT * k;
-      ptr_[k] = t < nblk ? prow[t] : 0;
-    }
-  }
+  const bool ptc = p.paged && nblk <= ptw;
 
   const int32_t* rows = p.q2k + ((int64_t)g * p.total_q + q0) * p.topk;
+  const bool use_pre = spec && pre_fits;
   int ucount;
   if (ntok == 1) {
     // one token: its row is the union when ascending without repeats (the
     // q2k contract); checked, with the general builder as the fallback
-    int id = -1;
-    if (tid < p.topk) id = rows[tid];
+    int id = use_pre ? pre_id : -1;
+    if (!use_pre && tid < p.topk) id = rows[tid];
     const bool in = tid < p.topk && id >= 0 && id < nblk;
     int bad = 0;
     if (wave == 0) {
@@ -368,9 +398,9 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
     }
     __syncthreads();
     ucount = lds.un.count;
-    if (ucount < 0) ucount = build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk);
+    if (ucount < 0) ucount = build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk, pre_id, use_pre);
   } else {
-    ucount = build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk);
+    ucount = build_tile_union<NT>(lds.un, rows, ntok, p.topk, nblk, pre_id, use_pre);
   }
   ucount = __builtin_amdgcn_readfirstlane(ucount);
   const int u0 = (int)(((int64_t)ucount * split) / p.splits);
@@ -697,9 +727,11 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
     if (j + NST < nj) issue(j + NST, stage);
   }
 
-  // ---- merge the waves' states row tile by row tile through LDS
+  // ---- merge the waves' states row tile by row tile through LDS.  The
+  // barriers only order LDS accesses (the ring is reused), so they wait on
+  // LDS counters alone and leave the output stores in flight.
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __syncthreads();
+  block_barrier();
   MergeLds<NWV>& mg = *reinterpret_cast<MergeLds<NWV>*>(lds.ring);
   const int unit_split = unit * p.splits + split;
 #pragma unroll
@@ -713,7 +745,8 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
       mg.m[wave][l16] = m_[rt];
       mg.l[wave][l16] = lsum;
     }
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
     const int rr = (tid >> 4) & 15;   // row within the tile (threads 0..255)
     const int d0 = 8 * (tid & 15);
     const int row = 16 * rt + rr;
@@ -752,7 +785,10 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
         if (d0 == 0) p.ws_lse[(int64_t)unit_split * p.ws_lse_rows + row] = lse_nat;
       }
     }
-    __syncthreads();
+    if (rt + 1 < RT && 16 * (rt + 1) < R) {   // the next tile rewrites the merge buffer
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      block_barrier();
+    }
   }
 }
 
@@ -762,11 +798,13 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
 __global__ __launch_bounds__(256) void msa_decode_merge_kernel(AttnParams p) {
   const int per_unit = p.ws_rows * 16;
   const int64_t task = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int unit = (int)(task / per_unit);
+  const int unit = (int)(task / per_unit);    // (request, KV head, token tile)
   const int rem = (int)(task % per_unit);
-  if (unit >= p.batch * p.hkv) return;
-  const int g = unit % p.hkv, b = unit / p.hkv;
-  const int q0 = p.cu_q[b];
+  if (unit >= p.batch * p.hkv * p.tiles_per_req) return;
+  const int jt = unit % p.tiles_per_req;
+  const int g = (unit / p.tiles_per_req) % p.hkv, b = unit / p.tiles_per_req / p.hkv;
+  const int j0 = jt * p.tok_per_tile;
+  const int q0 = p.cu_q[b] + j0;
   const int lq = min(p.cu_q[b + 1] - q0, p.tok_per_tile);
   const int row = rem >> 4, d0 = 8 * (rem & 15);
   if (row >= lq * p.group) return;
@@ -800,12 +838,12 @@ __global__ __launch_bounds__(256) void msa_decode_merge_kernel(AttnParams p) {
 
 template <int FMT, int RT, int NWV = 4>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
-  const int n = p.batch * p.hkv * p.splits;
+  const int n = p.batch * p.hkv * p.tiles_per_req * p.splits;
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV>), dim3(n), dim3(NWV * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t tasks = (int64_t)p.batch * p.hkv * p.ws_rows * 16;
+  const int64_t tasks = (int64_t)p.batch * p.hkv * p.tiles_per_req * p.ws_rows * 16;
   hipLaunchKernelGGL(msa_decode_merge_kernel, dim3((unsigned)((tasks + 255) / 256)), dim3(256), 0,
                      stream, p);
   return hipGetLastError();

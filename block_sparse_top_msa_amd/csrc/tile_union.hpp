@@ -23,10 +23,12 @@ struct UnionLds {
 
 // All threads of the workgroup must call this.  `rows` points at the
 // q2k row of the tile's first token for this KV head; rows are `topk` apart.
-// Returns the union size (also in u.count).  Ends with a barrier.
+// With `use_pre` (ntok * topk <= NT), thread e already holds entry e in
+// `pre` and the entries are not read again.  Returns the union size (also
+// in u.count).  Ends with a barrier.
 template <int NT>
 __device__ int build_tile_union(UnionLds& u, const int32_t* __restrict__ rows, int ntok,
-                                int topk, int n_blocks) {
+                                int topk, int n_blocks, int pre = -1, bool use_pre = false) {
   const int tid = threadIdx.x;
   const int words = (n_blocks + 31) >> 5;
   for (int w = tid; w < words; w += NT) u.bitmap[w] = 0u;
@@ -34,7 +36,7 @@ __device__ int build_tile_union(UnionLds& u, const int32_t* __restrict__ rows, i
 
   const int n = ntok * topk;
   for (int e = tid; e < n; e += NT) {
-    int id = rows[e];
+    int id = use_pre ? pre : rows[e];
     if (id >= 0 && id < n_blocks) atomicOr(&u.bitmap[id >> 5], 1u << (id & 31));
   }
   __syncthreads();
@@ -80,7 +82,7 @@ __device__ int build_tile_union(UnionLds& u, const int32_t* __restrict__ rows, i
   __syncthreads();
 
   for (int e = tid; e < n; e += NT) {
-    int id = rows[e];
+    int id = use_pre ? pre : rows[e];
     if (id >= 0 && id < n_blocks) {
       int w = id >> 5;
       int pos = u.prefix[w] + __popc(u.bitmap[w] & ((1u << (id & 31)) - 1u));
