@@ -264,7 +264,8 @@ def bench_decode(args, msa, synth, torch):
         step(evs[k])
     torch.cuda.synchronize()
     st = [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i in range(3)]
-    ms_step = sum(st)
+    # without the proxy and top-K stages a step is the attention call alone
+    ms_step = sum(st) if pipeline else st[2]
     gbs = nbytes / (st[2] * 1e-3) / 1e9
     res = {
         "metric": "KV GB/s",
@@ -276,8 +277,9 @@ def bench_decode(args, msa, synth, torch):
         "config": {"workload": p.name, "batch": B, "seqlen_q": mq, "num_qo_heads": p.num_qo_heads,
                    "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "topk": p.topk,
                    "kv_format": fmt, "cold_cache": True},
-        "stages_ms": {"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
-                      "sparse_attention": round(st[2], 4)},
+        "stages_ms": ({"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
+                       "sparse_attention": round(st[2], 4)} if pipeline
+                      else {"sparse_attention": round(st[2], 4)}),
         "work": {"kv_bytes": nbytes},
         "roofline": {"kernel": "msa_decode_kernel", "bound": "hbm",
                      "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",

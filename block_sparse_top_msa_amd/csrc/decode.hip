@@ -88,9 +88,13 @@ struct DecodeLds {
   int32_t ptrow[kPtCache];   // the request's page-table row, when it is this short
 };
 
+// Rows padded by 16 bytes: the 16 rows one wave writes at the same column
+// then fall on distinct banks.
+constexpr int kMergePitch = kHeadDim + 4;
+
 template <int NWV>
 struct MergeLds {
-  float o[NWV][16][kHeadDim];
+  float o[NWV][16][kMergePitch];
   float m[NWV][16];
   float l[NWV][16];
 };
