@@ -369,8 +369,8 @@ msa_status_t msa_topk_select(const float* scores, int32_t score_heads, int32_t m
   if (score_heads <= 0 || num_kv_heads <= 0 || total_q < 0 || max_k_tiles < 0)
     return fail(MSA_ERR_SHAPE, "bad sizes (score_heads %d, num_kv_heads %d, total_q %d, T %d)",
                 score_heads, num_kv_heads, total_q, max_k_tiles);
-  if (max_k_tiles > 4096)
-    return fail(MSA_ERR_UNSUPPORTED, "top-K select reads at most 4096 blocks per row (got %d)",
+  if (max_k_tiles > 16384)
+    return fail(MSA_ERR_UNSUPPORTED, "top-K select reads at most 16384 blocks per row (got %d)",
                 max_k_tiles);
   if (mode == MSA_REDUCE_NONE && score_heads != num_kv_heads)
     return fail(MSA_ERR_SHAPE, "mode NONE needs score_heads == num_kv_heads (%d vs %d)",

@@ -15,12 +15,56 @@ namespace msa {
 
 __device__ __forceinline__ int popc64(unsigned long long x) { return __popcll(x); }
 
+// The `topk` largest of a wave's candidates (key[c] of lane l is candidate
+// l + 64 c, valid[c] false for padding), equal keys going to the lower
+// candidate number: chosen[c] marks them.
+template <int C>
+__device__ __forceinline__ void select_topk(const uint32_t (&key)[C], const bool (&valid)[C],
+                                            int topk, int lane, bool (&chosen)[C]) {
+  int nvalid = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) nvalid += popc64(__ballot(valid[c]));
+
+  if (nvalid <= topk) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) chosen[c] = valid[c];
+  } else {
+    // largest x with #{key >= x} >= topk: the topk-th largest key
+    uint32_t x = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = x | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int c = 0; c < C; ++c) cnt += popc64(__ballot(valid[c] && key[c] >= cand));
+      if (cnt >= topk) x = cand;
+    }
+    int ngt = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) ngt += popc64(__ballot(valid[c] && key[c] > x));
+    const int need = topk - ngt;  // ties at x to take, lowest block ids first
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    int run = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const bool eq = valid[c] && key[c] == x;
+      const unsigned long long m = __ballot(eq);
+      const int rank = run + popc64(m & below);
+      chosen[c] = (valid[c] && key[c] > x) || (eq && rank < need);
+      run += popc64(m);
+    }
+  }
+}
+
+// Workgroups reach the XCDs round-robin: the remap gives each XCD a run of
+// consecutive rows, whose scores share cache lines (query index fastest).
 template <int C>
 __global__ __launch_bounds__(256) void msa_topk_kernel(const float* __restrict__ scores,
                                                       int hs, int T, int total_q, int topk,
                                                       int hkv, int mode, int sel_rows,
-                                                      int32_t* __restrict__ q2k) {
-  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+                                                      int n_wg, int32_t* __restrict__ q2k) {
+  const int wg = xcd_remap(blockIdx.x, n_wg);
+  if (wg < 0) return;
+  const int wave = wg * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (wave >= sel_rows * total_q) return;
   const int i = wave % total_q;
@@ -53,39 +97,8 @@ __global__ __launch_bounds__(256) void msa_topk_kernel(const float* __restrict__
     key[c] = valid[c] ? ordered_f32(s) : 0u;
   }
 
-  int nvalid = 0;
-#pragma unroll
-  for (int c = 0; c < C; ++c) nvalid += popc64(__ballot(valid[c]));
-
   bool chosen[C];
-  if (nvalid <= topk) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) chosen[c] = valid[c];
-  } else {
-    // largest x with #{key >= x} >= topk: the topk-th largest key
-    uint32_t x = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = x | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int c = 0; c < C; ++c) cnt += popc64(__ballot(valid[c] && key[c] >= cand));
-      if (cnt >= topk) x = cand;
-    }
-    int ngt = 0;
-#pragma unroll
-    for (int c = 0; c < C; ++c) ngt += popc64(__ballot(valid[c] && key[c] > x));
-    const int need = topk - ngt;  // ties at x to take, lowest block ids first
-    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    int run = 0;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const bool eq = valid[c] && key[c] == x;
-      const unsigned long long m = __ballot(eq);
-      const int rank = run + popc64(m & below);
-      chosen[c] = (valid[c] && key[c] > x) || (eq && rank < need);
-      run += popc64(m);
-    }
-  }
+  select_topk<C>(key, valid, topk, lane, chosen);
 
   // write ascending (t = lane + 64 c is ascending in (c, lane) order)
   const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
@@ -106,21 +119,146 @@ __global__ __launch_bounds__(256) void msa_topk_kernel(const float* __restrict__
     for (int g = g_lo; g < g_hi; ++g) q2k[((int64_t)g * total_q + i) * topk + pos] = -1;
 }
 
+// Long rows (more than 256 candidates): one workgroup of 16 waves per row.
+// Wave w takes candidates [64 C1 w, 64 C1 (w + 1)) and keeps its own top-K
+// (same order: larger score, then lower block id); the row's top-K lies in
+// the union of those, which one wave then selects from.  The survivors are
+// laid out by wave and then ascending id, so candidate order is block order
+// and the second selection breaks ties by block id too.
+constexpr int kWideWaves = 16;
+
+template <int C1, int C2>
+__global__ __launch_bounds__(kWideWaves * 64) void msa_topk_wide_kernel(
+    const float* __restrict__ scores, int hs, int T, int total_q, int topk, int hkv, int mode,
+    int sel_rows, int n_wg, int32_t* __restrict__ q2k) {
+  __shared__ uint32_t ckey[kWideWaves * kMaxTopk];
+  __shared__ int32_t cblk[kWideWaves * kMaxTopk];
+  __shared__ int32_t ccount[kWideWaves];
+  const int row = xcd_remap(blockIdx.x, n_wg);
+  if (row < 0 || row >= sel_rows * total_q) return;
+  const int i = row % total_q;
+  const int gs = row / total_q;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  int h_lo, h_hi;
+  if (mode == 1) {
+    h_lo = 0; h_hi = hs;
+  } else if (mode == 2) {
+    const int gsz = hs / hkv;
+    h_lo = gs * gsz; h_hi = h_lo + gsz;
+  } else {
+    h_lo = gs; h_hi = gs + 1;
+  }
+
+  // stage 1: this wave's candidates
+  const int t0 = 64 * C1 * wave;
+  uint32_t key[C1];
+  bool valid[C1];
+#pragma unroll
+  for (int c = 0; c < C1; ++c) {
+    const int t = t0 + lane + kWave * c;
+    float s = -INFINITY;
+    if (t < T) {
+      s = scores[((int64_t)h_lo * T + t) * total_q + i];
+      for (int h = h_lo + 1; h < h_hi; ++h)
+        s = fmaxf(s, scores[((int64_t)h * T + t) * total_q + i]);
+    }
+    valid[c] = (t < T) && (__float_as_uint(s) & 0x7F800000u) != 0x7F800000u;
+    key[c] = valid[c] ? ordered_f32(s) : 0u;
+  }
+  bool chosen[C1];
+  select_topk<C1>(key, valid, topk, lane, chosen);
+  const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  int base = 0;
+#pragma unroll
+  for (int c = 0; c < C1; ++c) {
+    const unsigned long long m = __ballot(chosen[c]);
+    if (chosen[c]) {
+      const int pos = wave * topk + base + popc64(m & below);
+      ckey[pos] = key[c];
+      cblk[pos] = t0 + lane + kWave * c;
+    }
+    base += popc64(m);
+  }
+  if (lane == 0) ccount[wave] = base;
+  __syncthreads();
+  if (wave != 0) return;
+
+  // stage 2: the survivors, candidate e = lane + 64 c (wave e / topk, rank e % topk)
+  uint32_t key2[C2];
+  bool valid2[C2];
+  int blk2[C2];
+#pragma unroll
+  for (int c = 0; c < C2; ++c) {
+    const int e = lane + kWave * c;
+    const int w = e / topk, r = e % topk;
+    valid2[c] = w < kWideWaves && r < ccount[w];
+    key2[c] = valid2[c] ? ckey[e] : 0u;
+    blk2[c] = valid2[c] ? cblk[e] : -1;
+  }
+  bool chosen2[C2];
+  select_topk<C2>(key2, valid2, topk, lane, chosen2);
+  const int g_lo = (mode == 1) ? 0 : gs;
+  const int g_hi = (mode == 1) ? hkv : gs + 1;
+  base = 0;
+#pragma unroll
+  for (int c = 0; c < C2; ++c) {
+    const unsigned long long m = __ballot(chosen2[c]);
+    if (chosen2[c]) {
+      const int pos = base + popc64(m & below);
+      for (int g = g_lo; g < g_hi; ++g) q2k[((int64_t)g * total_q + i) * topk + pos] = blk2[c];
+    }
+    base += popc64(m);
+  }
+  for (int pos = base + lane; pos < topk; pos += kWave)
+    for (int g = g_lo; g < g_hi; ++g) q2k[((int64_t)g * total_q + i) * topk + pos] = -1;
+}
+
 template <int C>
 static hipError_t launch_topk_c(const float* scores, int hs, int T, int total_q, int topk,
                                 int hkv, int mode, int32_t* q2k, hipStream_t stream) {
   const int sel_rows = (mode == 1) ? 1 : hkv;
   const int64_t waves = (int64_t)sel_rows * total_q;
   if (waves <= 0) return hipSuccess;
-  const int grid = (int)((waves + 3) / 4);
-  hipLaunchKernelGGL((msa_topk_kernel<C>), dim3(grid), dim3(256), 0, stream, scores, hs, T,
-                     total_q, topk, hkv, mode, sel_rows, q2k);
+  const int n_wg = (int)((waves + 3) / 4);
+  hipLaunchKernelGGL((msa_topk_kernel<C>), dim3(8 * ((n_wg + 7) / 8)), dim3(256), 0, stream,
+                     scores, hs, T, total_q, topk, hkv, mode, sel_rows, n_wg, q2k);
   return hipGetLastError();
+}
+
+template <int C1, int C2>
+static hipError_t launch_topk_wide(const float* scores, int hs, int T, int total_q, int topk,
+                                   int hkv, int mode, int32_t* q2k, hipStream_t stream) {
+  const int sel_rows = (mode == 1) ? 1 : hkv;
+  const int n = sel_rows * total_q;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((msa_topk_wide_kernel<C1, C2>), dim3(8 * ((n + 7) / 8)),
+                     dim3(kWideWaves * 64), 0, stream, scores, hs, T, total_q, topk, hkv, mode,
+                     sel_rows, n, q2k);
+  return hipGetLastError();
+}
+
+template <int C1>
+static hipError_t launch_topk_wide_c2(const float* scores, int hs, int T, int total_q, int topk,
+                                      int hkv, int mode, int32_t* q2k, hipStream_t stream) {
+  // survivors: kWideWaves * topk candidates, 64 per lane column
+  if (topk <= 16) return launch_topk_wide<C1, 4>(scores, hs, T, total_q, topk, hkv, mode, q2k, stream);
+  if (topk <= 32) return launch_topk_wide<C1, 8>(scores, hs, T, total_q, topk, hkv, mode, q2k, stream);
+  return launch_topk_wide<C1, 16>(scores, hs, T, total_q, topk, hkv, mode, q2k, stream);
 }
 
 hipError_t launch_topk(const float* scores, int score_heads, int T, int total_q, int topk,
                        int hkv, int mode, int32_t* q2k, hipStream_t stream) {
   const int c = (T + kWave - 1) / kWave;
+  if (c > 4) {
+    // per wave: ceil(T / 1024) candidates per lane
+    const int c1 = (T + 64 * kWideWaves - 1) / (64 * kWideWaves);
+    if (c1 <= 1) return launch_topk_wide_c2<1>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);
+    if (c1 <= 2) return launch_topk_wide_c2<2>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);
+    if (c1 <= 4) return launch_topk_wide_c2<4>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);
+    if (c1 <= 8) return launch_topk_wide_c2<8>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);
+    if (c1 <= 16) return launch_topk_wide_c2<16>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);
+  }
   if (c <= 1) return launch_topk_c<1>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);
   if (c <= 2) return launch_topk_c<2>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);
   if (c <= 4) return launch_topk_c<4>(scores, score_heads, T, total_q, topk, hkv, mode, q2k, stream);

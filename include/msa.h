@@ -184,7 +184,9 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* args, void* stream);
  * id), ascending, -1 padded.  -inf and NaN scores are never selected.
  * mode: MSA_REDUCE_NONE needs score_heads == num_kv_heads; MSA_REDUCE_ALL
  * takes the max over all score heads and writes the shared selection to every
- * KV head; MSA_REDUCE_GROUP needs score_heads % num_kv_heads == 0. */
+ * KV head; MSA_REDUCE_GROUP needs score_heads % num_kv_heads == 0.
+ * 1 <= topk <= 64 and max_k_tiles <= 16384, else MSA_ERR_SHAPE /
+ * MSA_ERR_UNSUPPORTED with nothing launched. */
 msa_status_t msa_topk_select(const float* scores, int32_t score_heads,
                              int32_t max_k_tiles, int32_t total_q, int32_t topk,
                              int32_t num_kv_heads, int32_t mode, int32_t* q2k,

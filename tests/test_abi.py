@@ -149,7 +149,7 @@ def test_proxy_and_topk_validation():
     assert f(FAKE, 2, 64, 8, 0, 2, 0, FAKE, None) == 2          # topk 0
     assert f(FAKE, 3, 64, 8, 4, 2, 0, FAKE, None) == 2          # NONE with 3 != 2 heads
     assert f(FAKE, 3, 64, 8, 4, 2, 2, FAKE, None) == 2          # GROUP 3 % 2
-    assert f(FAKE, 2, 5000, 8, 4, 2, 0, FAKE, None) == 5        # too many blocks
+    assert f(FAKE, 2, 20000, 8, 4, 2, 0, FAKE, None) == 5       # too many blocks
     assert f(FAKE, 2, 64, 8, 4, 2, 9, FAKE, None) == 5          # unknown mode
     assert f(FAKE, 2, 64, 0, 4, 2, 0, FAKE, None) == 0          # empty: no launch
     u = msa.lib.msa_tile_union

@@ -260,7 +260,8 @@ def _adversarial_scores(hs, T, n, seed):
 
 @pytest.mark.parametrize("T,topk,hs,hkv,mode", [
     (64, 16, 2, 2, 0), (7, 16, 2, 2, 0), (1024, 16, 1, 2, 1), (130, 4, 8, 2, 2),
-    (300, 33, 3, 1, 1), (64, 64, 1, 1, 0), (4096, 16, 1, 1, 0),
+    (300, 33, 3, 1, 1), (64, 64, 1, 1, 0), (4096, 16, 1, 1, 0), (16384, 64, 1, 1, 0),
+    (2000, 40, 2, 2, 0), (257, 16, 4, 2, 2),
 ])
 def test_topk_bit_exact(msa, T, topk, hs, hkv, mode):
     s = _adversarial_scores(hs, T, 257, seed=T + topk)
