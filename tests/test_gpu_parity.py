@@ -300,3 +300,23 @@ def test_tile_union_bit_exact(msa, tile_tokens):
                 assert blocks[g, b, j, :n].tolist() == ref_b
                 assert [m % (1 << 64) for m in masks[g, b, j, :n].tolist()] == ref_m
                 assert (blocks[g, b, j, n:] == -1).all()
+
+
+@pytest.mark.parametrize("fmt,hq,hkv,splits", [
+    (synth.KV_FP8, 32, 2, 0), (synth.KV_BF16, 32, 1, 2), (synth.KV_E2M1, 16, 1, 0),
+    (synth.KV_FP8, 16, 1, 3),
+])
+def test_decode_per_token_tiles_with_uneven_query_lengths(msa, fmt, hq, hkv, splits):
+    # G >= 16 puts every query token in a workgroup of its own; requests of
+    # different lengths (one empty) start away from b * max_seqlen_q, so the
+    # kernel re-reads their rows after the speculative first read
+    q_lens = [4, 1, 0, 3, 4, 2]
+    p = synth.make_problem("dec_uneven", q_lens=q_lens, k_lens=[2000, 129, 700, 5000, 300, 1500],
+                           num_qo_heads=hq, num_kv_heads=hkv, topk=8, paged=True, kv_dtype=fmt,
+                           seed=41 + hq + splits, selection="general",
+                           k_global_scale=0.5 if fmt == synth.KV_E2M1 else None,
+                           v_global_scale=2.0 if fmt == synth.KV_E2M1 else None)
+    print(f"uneven decode fmt {fmt} Hq {hq} Hkv {hkv} splits {splits}", flush=True)
+    out, lse = gpu_attention(msa, _dev(p), splits=splits)
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "uneven decode")
