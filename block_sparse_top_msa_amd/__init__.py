@@ -282,7 +282,9 @@ def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, sequs
                 causal=True, max_seqlen_q=None, max_k_tiles=None, output=None,
                 reduce_heads=False):
     """Stage-1 block max of unscaled masked QK^T (msa_proxy_score page).
-    Returns fp32 (num_qo_heads or 1, max_k_tiles, total_q)."""
+    reduce_heads: False (per query head), True (max over all heads) or
+    "group" (max over each KV head's query heads).  Returns fp32
+    (num_qo_heads | 1 | num_kv_heads, max_k_tiles, total_q)."""
     if q.dtype != torch.bfloat16 or not q.is_contiguous():
         raise ValueError("q must be a contiguous bf16 tensor (total_q, num_qo_heads, 128)")
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
@@ -296,7 +298,13 @@ def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, sequs
     else:
         raise ValueError(f"proxy K must be bf16 or float8_e4m3fn, got {k.dtype}")
     T = _host_max_tiles(cu_seqlens_k, seqused_k) if max_k_tiles is None else int(max_k_tiles)
-    H = 1 if reduce_heads else q.shape[1]
+    if reduce_heads == "group":
+        rmode, H = REDUCE_GROUP, k.shape[1]
+    elif reduce_heads in (False, True, 0, 1):
+        rmode = REDUCE_ALL if reduce_heads else REDUCE_NONE
+        H = 1 if reduce_heads else q.shape[1]
+    else:
+        raise ValueError(f"reduce_heads must be False, True or 'group', got {reduce_heads!r}")
     if output is None:
         output = torch.empty(H, T, q.shape[0], dtype=torch.float32, device=q.device)
     elif (output.shape != (H, T, q.shape[0]) or output.dtype != torch.float32
@@ -313,7 +321,7 @@ def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, sequs
     a.page_table_width = page_table.shape[1] if paged else 0
     a.causal = 1 if causal else 0
     a.kv_dtype = fmt
-    a.reduce_heads = 1 if reduce_heads else 0
+    a.reduce_heads = rmode
     a.q, a.k = _ptr(q), _ptr(k)
     a.k_strides = _strides(k, paged)
     a.cu_seqlens_q = _ptr(cu_seqlens_q)

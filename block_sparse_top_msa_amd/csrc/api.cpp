@@ -340,7 +340,10 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   p.hkv = a->num_kv_heads;
   p.group = G;
   p.causal = a->causal ? 1 : 0;
-  p.reduce = a->reduce_heads ? 1 : 0;
+  if (a->reduce_heads < 0 || a->reduce_heads > 2)
+    return fail(MSA_ERR_UNSUPPORTED, "reduce_heads must be 0, 1 (all heads) or 2 (per KV head group), got %d",
+                a->reduce_heads);
+  p.reduce = a->reduce_heads;
   p.max_k_tiles = a->max_k_tiles;
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows = lqmax * G;

@@ -8,7 +8,8 @@
 // (fp8 K upconverted in-kernel, msa_proxy_score page, Parameters: k) and read
 // by every wave.  S^T = K Q^T on 32x32x16 bf16 MFMA puts keys on the M axis,
 // so a query's block max is a max over its own registers plus one cross-half
-// step.  With reduce_heads the max over query heads happens in-kernel: within
+// step.  With reduce_heads (all heads, or the G heads of each KV head) the
+// max over query heads happens in-kernel: within
 // a wave across the G heads of a token, then across KV heads with an exact
 // order-independent atomic max into an output pre-filled with -inf.
 #include "async_lds.hpp"
@@ -130,6 +131,8 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_rows_kernel(ProxyParams p) {
   if (b >= p.batch) return;
 
   const int G = p.group;
+  // reduced output row block: all heads -> row 0, group of KV head g -> row g
+  const int64_t rbase = p.reduce == 2 ? (int64_t)g * p.max_k_tiles : 0;
   const int q0 = p.cu_q[b];
   const int lq = p.cu_q[b + 1] - q0;
   const int nrows = lq * G;
@@ -365,9 +368,9 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_rows_kernel(ProxyParams p) {
         if ((G & (G - 1)) == 0 && G <= 32) {
           for (int off = 1; off < G; off <<= 1) v = xor_max(v, off);
           if (half == 0 && r < nrows && hh == 0)
-            atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+            atomic_max_f32(&p.out[(rbase + t) * p.total_q + q0 + tk], v);
         } else if (half == 0 && r < nrows) {
-          atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+          atomic_max_f32(&p.out[(rbase + t) * p.total_q + q0 + tk], v);
         }
       }
     }
@@ -405,6 +408,8 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   const int b = rest / p.hkv;
 
   const int G = p.group;
+  // reduced output row block: all heads -> row 0, group of KV head g -> row g
+  const int64_t rbase = p.reduce == 2 ? (int64_t)g * p.max_k_tiles : 0;
   const int q0 = p.cu_q[b];
   const int lq = p.cu_q[b + 1] - q0;
   const int nrows = lq * G;
@@ -606,9 +611,9 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
         if ((G & (G - 1)) == 0 && G <= 32) {
           for (int off = 1; off < G; off <<= 1) v = xor_max(v, off);
           if (half == 0 && r < nrows && hh == 0)
-            atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+            atomic_max_f32(&p.out[(rbase + t) * p.total_q + q0 + tk], v);
         } else if (half == 0 && r < nrows) {
-          atomic_max_f32(&p.out[(int64_t)t * p.total_q + q0 + tk], v);
+          atomic_max_f32(&p.out[(rbase + t) * p.total_q + q0 + tk], v);
         }
       }
     }
@@ -630,7 +635,7 @@ static hipError_t launch_proxy_wide_t(const ProxyParams& p, hipStream_t stream) 
   if (n <= 0) return hipSuccess;
   const int grid = 8 * ((n + 7) / 8);
   if (p.reduce) {
-    const int64_t total = (int64_t)p.max_k_tiles * p.total_q;
+    const int64_t total = (int64_t)(p.reduce == 2 ? p.hkv : 1) * p.max_k_tiles * p.total_q;
     if (total > 0) {
       int fb = (int)std::min<int64_t>((total + 255) / 256, 4096);
       hipLaunchKernelGGL(msa_fill_kernel, dim3(fb), dim3(256), 0, stream, p.out, total, -INFINITY);
@@ -647,7 +652,7 @@ static hipError_t launch_proxy_rows_t(const ProxyParams& p, hipStream_t stream) 
   const int n = p.batch * p.hkv * p.block_chunks;
   if (n <= 0) return hipSuccess;
   if (p.reduce) {
-    const int64_t total = (int64_t)p.max_k_tiles * p.total_q;
+    const int64_t total = (int64_t)(p.reduce == 2 ? p.hkv : 1) * p.max_k_tiles * p.total_q;
     if (total > 0) {
       int fb = (int)std::min<int64_t>((total + 255) / 256, 4096);
       hipLaunchKernelGGL(msa_fill_kernel, dim3(fb), dim3(256), 0, stream, p.out, total, -INFINITY);

@@ -157,7 +157,10 @@ typedef struct {
   int32_t page_table_width;
   int32_t causal;         /* right-aligned, applied before the block max      */
   int32_t kv_dtype;       /* MSA_KV_BF16 or MSA_KV_FP8_E4M3                   */
-  int32_t reduce_heads;   /* 1: max over query heads, output (1, T, total_q)  */
+  int32_t reduce_heads;   /* 0: per query head, output (Hq, T, total_q);
+                             1: max over all query heads, output (1, T, total_q);
+                             2: max over the G query heads of each KV head,
+                                output (Hkv, T, total_q); else MSA_ERR_UNSUPPORTED */
   const void* q;          /* bf16 [total_q, Hq, 128] (the proxy Q)            */
   const void* k;          /* flat [total_k, Hkv, 128] or paged [pages, Hkv, 128, 128] */
   msa_strides_t k_strides;
@@ -165,13 +168,15 @@ typedef struct {
   const int32_t* cu_seqlens_k;   /* flat route                               */
   const int32_t* page_table;     /* paged route, with seqused_k              */
   const int32_t* seqused_k;
-  float* out;             /* fp32 [Hq or 1, max_k_tiles, total_q], written in full */
+  float* out;             /* fp32 [Hq | 1 | Hkv, max_k_tiles, total_q], written in full */
 } msa_proxy_args_t;
 
 /* max_score[h, t, i]: the max over the keys of block t of the UNSCALED dot
  * products q[i, h] . k[j, h / G], after the causal mask; -inf where no key of
  * the block is visible or the block is past the sequence (msa_proxy_score
- * page, summary).  With reduce_heads the max over h is taken in-kernel. */
+ * page, summary).  With reduce_heads the max over h (all heads, or the heads
+ * of each KV head's group) is taken in-kernel, so the per-head scores are
+ * never written (msa_proxy_score page, Parameters: reduce_heads). */
 msa_status_t msa_proxy_score(const msa_proxy_args_t* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

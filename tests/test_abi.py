@@ -145,6 +145,10 @@ def test_proxy_and_topk_validation():
     assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 4  # both lengths
     p.head_dim = 64
     assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 2
+    p.head_dim, p.page_table, p.seqused_k, p.page_table_width = 128, None, None, 0
+    p.reduce_heads = 3
+    assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 5  # unknown head reduction
+    p.reduce_heads = 0
     f = msa.lib.msa_topk_select
     assert f(FAKE, 2, 64, 8, 0, 2, 0, FAKE, None) == 2          # topk 0
     assert f(FAKE, 3, 64, 8, 4, 2, 0, FAKE, None) == 2          # NONE with 3 != 2 heads

@@ -320,3 +320,34 @@ def test_decode_per_token_tiles_with_uneven_query_lengths(msa, fmt, hq, hkv, spl
     out, lse = gpu_attention(msa, _dev(p), splits=splits)
     ref_out, ref_lse = oracle_attention(p)
     assert_attention_close(out, lse, ref_out, ref_lse, "uneven decode")
+
+
+@pytest.mark.parametrize("ql,kl,hq,hkv,paged,fmt", [
+    ([300, 200], [300, 456], 16, 2, False, synth.KV_BF16),     # > 64 rows: wide kernel
+    ([4, 4, 4], [3000, 700, 129], 32, 2, True, synth.KV_FP8),   # <= 64 rows: rows kernel
+    ([2, 1], [1000, 2000], 8, 1, True, synth.KV_BF16),
+])
+def test_proxy_group_reduction_in_kernel(msa, ql, kl, hq, hkv, paged, fmt):
+    # reduce_heads="group": the max over each KV head's G query heads is taken
+    # inside the proxy kernel; it must equal the per-head oracle maxed over
+    # the group, and select exactly what the top-K's own group mode selects
+    p = synth.make_problem("proxy_group", q_lens=ql, k_lens=kl, num_qo_heads=hq,
+                           num_kv_heads=hkv, paged=paged, kv_dtype=fmt, causal=True, seed=77,
+                           selection="proxy")
+    print(f"proxy group ql {ql} Hq {hq} Hkv {hkv} paged {paged} fmt {fmt}", flush=True)
+    d = _dev(p)
+    T = p.max_k_tiles + 1
+    kw = dict(page_table=d.page_table, seqused_k=d.seqused_k, causal=True,
+              max_seqlen_q=max(ql), max_k_tiles=T)
+    got = msa.proxy_score(d.q, d.k, d.cu_seqlens_q, d.cu_seqlens_k, reduce_heads="group", **kw)
+    assert got.shape == (hkv, T, sum(ql))
+    ref = oracle.proxy_score(p.q, p.k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k,
+                             page_table=p.page_table, seqused_k=p.seqused_k, causal=True,
+                             max_k_tiles=T, kv_format=fmt)
+    G = hq // hkv
+    ref_group = ref.view(hkv, G, T, -1).amax(dim=1)
+    assert_proxy_close(got, ref_group, "group-reduced proxy")
+    per_head = msa.proxy_score(d.q, d.k, d.cu_seqlens_q, d.cu_seqlens_k, **kw)
+    a = msa.topk_select(got, 4, hkv, mode=0)
+    b = msa.topk_select(per_head, 4, hkv, mode=2)
+    assert torch.equal(a.cpu(), b.cpu())
