@@ -26,6 +26,9 @@ as library steps:
   lse_merge         combining split partials by their LSE
                     (prepare_msa_nvfp4_sparse_decode page, Parameters:
                      workspace_buffer)
+  qsa_indexed_attention
+                    packed query sparse attention over caller-listed token
+                    indices (qsa page: indexed forward)
 
 Readings of points the pages leave open are stated where they are used.
 Every function is pinned by tests/test_oracle.py against something other than
@@ -468,3 +471,46 @@ def lse_merge(parts):
     wn = w / torch.where(tot > 0, tot, torch.ones_like(tot))
     o = (wn.unsqueeze(-1) * os_).sum(dim=0)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# QSA: packed query sparse attention from token indices (qsa page)
+# ---------------------------------------------------------------------------
+
+def qsa_indexed_attention(q, k, v, indices, softmax_scale=None):
+    """Packed query sparse attention over caller-selected tokens (qsa page:
+    the indexed API, its output and LSE description and its example).
+
+    q: bf16 [T, Hq, d]; k, v: bf16 [Tk, Hkv, d]; indices: int32 [T, W], the
+    absolute packed token ids (rows of k / v) query i attends, in groups of
+    four with -1 padding.  Query head h reads KV head h // (Hq / Hkv).
+    Readings: an index row is a set (negative entries are padding; entries
+    are distinct by the caller contract, so repeats are ignored); the
+    softmax scale defaults to d^-0.5 as on the MSA pages; causality is the
+    caller's, carried by the indices themselves.
+    Returns (out [T, Hq, d], lse [Hq, T]) in float64; a query with no index
+    gets out = 0 and lse = -inf.
+    """
+    qd = decode_bf16(q)
+    kd = decode_bf16(k)
+    vd = decode_bf16(v)
+    T, Hq, d = qd.shape
+    Hkv = kd.shape[1]
+    G = Hq // Hkv
+    scale = float(softmax_scale) if softmax_scale else d ** -0.5
+    out = torch.zeros(T, Hq, d, dtype=torch.float64)
+    lse = torch.full((Hq, T), -math.inf, dtype=torch.float64)
+    for i in range(T):
+        ids = sorted({int(x) for x in indices[i].tolist() if int(x) >= 0})
+        if not ids:
+            continue
+        sel = torch.tensor(ids, dtype=torch.long)
+        for h in range(Hq):
+            z = scale * (kd[sel, h // G] @ qd[i, h])          # [n]
+            m = z.max()
+            w = torch.exp(z - m)
+            s = w.sum()
+            lse[h, i] = m + torch.log(s)
+            out[i, h] = (w / s) @ vd[sel, h // G]
+    return out, lse
+

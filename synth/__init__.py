@@ -432,3 +432,76 @@ def workload(name: str, device="cpu", seed=None) -> Problem:
                             seed=seed, device=device, selection="decode",
                             k_global_scale=0.5, v_global_scale=2.0, g_cpu=g_len)
     raise ValueError(name)
+
+
+# --------------------------------------------------------------------------
+# QSA (packed query sparse attention over 4-token groups) inputs
+# --------------------------------------------------------------------------
+
+class QsaProblem:
+    """q [T, Hq, d], k / v [T, Hkv, d] bf16 (packed sequences), indices
+    [T, W] int32: per query, absolute token ids in groups of four, -1 padded."""
+
+    def __init__(self, name, q, k, v, indices, seq_lens):
+        self.name, self.q, self.k, self.v, self.indices = name, q, k, v, indices
+        self.seq_lens = list(seq_lens)
+
+    def to(self, device):
+        return QsaProblem(self.name, self.q.to(device), self.k.to(device), self.v.to(device),
+                          self.indices.to(device), self.seq_lens)
+
+
+def qsa_indices(seq_lens, width, g_cpu, mode="random"):
+    """Index rows of 4-token groups for packed causal sequences.
+
+    Query at position p of a sequence starting at row c sees groups
+    [4 j, 4 j + 3] of its sequence with 4 j <= p; its own group is the
+    partial causal tail (entries past p are -1).  mode "causal": every
+    visible group (the qsa page's example pattern, up to `width` entries:
+    the latest groups); "random": the tail group plus distinct uniformly
+    drawn earlier groups, ascending, up to width / 4 groups.
+    """
+    assert width % 4 == 0
+    ng_max = width // 4
+    T = sum(seq_lens)
+    out = torch.full((T, width), -1, dtype=torch.int32)
+    four = torch.arange(4)
+    c = 0
+    for L in seq_lens:
+        for p in range(L):
+            own = p // 4
+            if mode == "causal":
+                groups = torch.arange(max(0, own - ng_max + 1), own + 1)
+            else:
+                k = min(own, ng_max - 1)
+                earlier = torch.randperm(own, generator=g_cpu)[:k] if own else torch.zeros(0, dtype=torch.long)
+                groups = torch.cat([torch.sort(earlier).values, torch.tensor([own])])
+            tok = (4 * groups.view(-1, 1) + four.view(1, -1)).reshape(-1)
+            ids = torch.where(tok <= p, tok + c, torch.full_like(tok, -1))
+            out[c + p, :ids.numel()] = ids.to(torch.int32)
+        c += L
+    return out
+
+
+def make_qsa_problem(name, seq_lens, num_qo_heads, num_kv_heads, width, seed, head_dim=256,
+                     device="cpu", mode="random"):
+    """Seeded QSA inputs: lengths given; draws in the order indices (CPU
+    generator), then Q, K, V (generator on `device`), N(0,1) cast to bf16."""
+    g_cpu = _gen(seed, "cpu")
+    indices = qsa_indices(seq_lens, width, g_cpu, mode)
+    g = _gen(seed, device)
+    T = sum(seq_lens)
+    q = _randn_cast((T, num_qo_heads, head_dim), g, device, torch.bfloat16)
+    k = _randn_cast((T, num_kv_heads, head_dim), g, device, torch.bfloat16)
+    v = _randn_cast((T, num_kv_heads, head_dim), g, device, torch.bfloat16)
+    return QsaProblem(name, q, k, v, indices.to(device), seq_lens)
+
+
+QSA_WORKLOAD = "qsa_indexed_1x8192_h12kv1_d256_w2048"
+
+
+def qsa_workload(device="cpu", seed=6):
+    """One packed 8192-token sequence, 12 query heads / 1 KV head, head dim
+    256, 2048-wide index rows (the tail group plus up to 511 random earlier
+    groups per query)."""
+    return make_qsa_problem(QSA_WORKLOAD, [8192], 12, 1, 2048, seed, device=device)

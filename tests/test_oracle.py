@@ -551,3 +551,51 @@ def test_synthetic_selection_recipes():
         valid = [x for x in row if x >= 0]
         assert valid == sorted(set(valid)) and c in valid and max(valid) == c
         assert len(valid) == min(4, c + 1)
+
+
+# ---------------------------------------------------------------------------
+# QSA indexed attention (qsa page)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("hq,hkv", [(12, 1), (24, 2)])
+def test_qsa_causal_indices_equal_dense_causal_sdpa(hq, hkv):
+    # the qsa page's example pattern (every earlier token of the query's own
+    # packed sequence) must reproduce dense causal attention of each sequence
+    lens = [9, 14]
+    p = synth.make_qsa_problem("qsa", lens, hq, hkv, width=16, seed=3, mode="causal")
+    out, lse = oracle.qsa_indexed_attention(p.q, p.k, p.v, p.indices)
+    c = 0
+    for L in lens:
+        qq = p.q[c:c + L].to(torch.float64).transpose(0, 1)
+        kk = p.k[c:c + L].to(torch.float64).repeat_interleave(hq // hkv, 1).transpose(0, 1)
+        vv = p.v[c:c + L].to(torch.float64).repeat_interleave(hq // hkv, 1).transpose(0, 1)
+        mask = torch.ones(L, L, dtype=torch.bool).tril()
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask)
+        logits = (qq @ kk.transpose(1, 2)) * 256 ** -0.5
+        ref_lse = torch.logsumexp(logits.masked_fill(~mask, float("-inf")), dim=-1)
+        assert torch.allclose(out[c:c + L].transpose(0, 1), ref, atol=1e-12, rtol=1e-12)
+        assert torch.allclose(lse[:, c:c + L], ref_lse, atol=1e-12, rtol=1e-12)
+        c += L
+
+
+def test_qsa_empty_single_and_set_semantics():
+    p = synth.make_qsa_problem("qsa", [12], 12, 1, width=8, seed=4)
+    idx = p.indices.clone()
+    idx[0] = -1                                        # empty: 0 and -inf
+    idx[5] = torch.tensor([3, -1, -1, -1, -1, -1, -1, -1])   # one key: v_3, lse = z_3
+    out, lse = oracle.qsa_indexed_attention(p.q, p.k, p.v, idx)
+    assert (out[0] == 0).all() and torch.isneginf(lse[:, 0]).all()
+    v3 = p.v[3, 0].to(torch.float64)
+    for h in range(12):
+        assert torch.equal(out[5, h], v3)
+        z = (p.q[5, h].to(torch.float64) @ p.k[3, 0].to(torch.float64)) * 256 ** -0.5
+        assert abs(float(lse[h, 5] - z)) < 1e-12
+    # a row is a set: order and extra padding do not matter
+    g = torch.Generator().manual_seed(9)
+    perm = idx.clone()
+    for i in range(perm.shape[0]):
+        perm[i] = perm[i][torch.randperm(perm.shape[1], generator=g)]
+    wide = torch.cat([perm, torch.full((perm.shape[0], 4), -1, dtype=torch.int32)], dim=1)
+    out2, lse2 = oracle.qsa_indexed_attention(p.q, p.k, p.v, wide)
+    assert torch.equal(out, out2) or torch.allclose(out, out2, atol=1e-14, rtol=0)
+    assert torch.allclose(lse, lse2, atol=1e-14, rtol=0)
