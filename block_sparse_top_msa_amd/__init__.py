@@ -9,6 +9,7 @@ load, importing this package raises.
     topk_select(max_score, topk, num_kv_heads)    the top-K block select
     sparse_attention(q, k, v, q2k_indices, ...)   msa_sparse_attention page
     tile_union(q2k, cu_seqlens_q, lengths_k, ...) the per-tile union builder
+    qsa_indexed_forward(q, k, v, indices, ...)    qsa page, indexed API
 """
 from __future__ import annotations
 
@@ -20,7 +21,7 @@ import torch
 
 __all__ = [
     "MsaError", "lib", "library_path", "sparse_attention", "proxy_score", "topk_select",
-    "tile_union", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3", "KV_E2M1X2",
+    "tile_union", "qsa_indexed_forward", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3", "KV_E2M1X2",
     "REDUCE_NONE", "REDUCE_ALL", "REDUCE_GROUP", "EXPORTED_SYMBOLS",
 ]
 
@@ -33,7 +34,8 @@ BLOCK = 128
 
 EXPORTED_SYMBOLS = (
     "msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
-    "msa_topk_select", "msa_tile_union", "msa_status_string", "msa_last_error", "msa_version",
+    "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward", "msa_status_string",
+    "msa_last_error", "msa_version",
 )
 
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_DTYPE",
@@ -89,6 +91,16 @@ class ProxyArgs(ctypes.Structure):
     ]
 
 
+class QsaArgs(ctypes.Structure):
+    _fields_ = [
+        ("total_q", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("width", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("q", _P), ("k", _P), ("v", _P), ("k_strides", Strides), ("v_strides", Strides),
+        ("indices", _I32P), ("out", _P), ("out_f32", _P), ("lse", _P),
+    ]
+
+
 def _load():
     if not os.path.exists(library_path):
         raise ImportError(
@@ -102,8 +114,9 @@ def _load():
     L.msa_topk_select.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
     L.msa_tile_union.argtypes = [_P, _P, _P] + [ctypes.c_int32] * 8 + [_P, _P, _P, _P]
+    L.msa_qsa_indexed_forward.argtypes = [ctypes.POINTER(QsaArgs), _P]
     for fn in ("msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
-               "msa_topk_select", "msa_tile_union"):
+               "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward"):
         getattr(L, fn).restype = ctypes.c_int
     L.msa_status_string.argtypes = [ctypes.c_int]
     L.msa_status_string.restype = ctypes.c_char_p
@@ -369,3 +382,38 @@ def tile_union(q2k, cu_seqlens_q, lengths_k, tile_tokens, max_k_tiles, max_seqle
                               topk, mq, int(max_k_tiles), int(tile_tokens), mu, _ptr(blocks),
                               _ptr(masks), _ptr(counts), _stream()))
     return blocks, masks, counts
+
+
+def qsa_indexed_forward(q, k, v, indices, softmax_scale=None, out=None, out_f32=None, lse=None,
+                        return_f32=True, return_lse=True):
+    """Packed query sparse attention over caller-selected tokens (qsa page,
+    indexed API): q bf16 (T, Hq, 256); k, v bf16 (Tk, Hkv, 256), last dim
+    contiguous; indices int32 (T, W), absolute token ids in groups of four,
+    -1 padded.  Returns (out bf16, out_f32, lse (Hq, T)); out_f32 / lse are
+    None when not requested."""
+    if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 3:
+        raise ValueError("q must be a contiguous bf16 tensor (T, Hq, 256)")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
+            raise ValueError(f"{name} must be bf16 (Tk, Hkv, 256) with a contiguous last dim")
+    if indices.dtype != torch.int32 or not indices.is_contiguous() or indices.dim() != 2:
+        raise ValueError("indices must be a contiguous int32 (T, W) tensor")
+    T, hq, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if return_f32 and out_f32 is None:
+        out_f32 = torch.empty(T, hq, d, dtype=torch.float32, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
+    a = QsaArgs()
+    a.total_q, a.num_qo_heads, a.num_kv_heads, a.head_dim = T, hq, k.shape[1], d
+    a.width = indices.shape[1]
+    a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
+    a.k_strides = Strides(0, k.stride(1) * 2, k.stride(0) * 2)
+    a.v_strides = Strides(0, v.stride(1) * 2, v.stride(0) * 2)
+    a.indices = _ptr(indices)
+    a.out, a.out_f32, a.lse = _ptr(out), _ptr(out_f32), _ptr(lse)
+    _check(lib.msa_qsa_indexed_forward(ctypes.byref(a), _stream()))
+    return out, out_f32, lse
+

@@ -21,7 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 
-SOURCES = ["api.cpp", "attention.hip", "decode.hip", "prefill.hip", "proxy.hip", "topk.hip"]
+SOURCES = ["api.cpp", "attention.hip", "decode.hip", "prefill.hip", "proxy.hip", "qsa.hip",
+           "topk.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -43,6 +44,7 @@ FLAGS = [
 PER_FILE = {
     "prefill.hip": ["-fno-honor-nans"],
     "decode.hip": ["-fno-honor-nans"],
+    "qsa.hip": ["-fno-honor-nans"],
 }
 
 

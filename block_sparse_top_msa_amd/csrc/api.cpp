@@ -417,4 +417,50 @@ msa_status_t msa_tile_union(const int32_t* q2k, const int32_t* cu_seqlens_q,
                     "msa_tile_union launch");
 }
 
+msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* a, void* stream) {
+  if (!a) return fail(MSA_ERR_NULL, "args is NULL");
+  if (a->head_dim != 256) return fail(MSA_ERR_UNSUPPORTED, "QSA needs head_dim 256 (got %d)", a->head_dim);
+  if (a->total_q < 0 || a->num_kv_heads <= 0 || a->num_qo_heads <= 0 ||
+      a->num_qo_heads % a->num_kv_heads)
+    return fail(MSA_ERR_SHAPE, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_qo_heads, a->num_kv_heads);
+  if (a->num_qo_heads / a->num_kv_heads > 16)
+    return fail(MSA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)",
+                a->num_qo_heads / a->num_kv_heads);
+  if (a->width < 4 || a->width % 4 || a->width > 2052)
+    return fail(MSA_ERR_SHAPE, "width must be a multiple of 4 in [4, 2052] (got %d)", a->width);
+  if (a->total_q == 0) return ok();
+  if (!a->q || !a->k || !a->v || !a->indices || !a->out)
+    return fail(MSA_ERR_NULL, "q, k, v, indices and out must be non-NULL");
+  const int64_t row = 256 * 2;
+  const int64_t kt = a->k_strides.token ? a->k_strides.token : row * a->num_kv_heads;
+  const int64_t kh = a->k_strides.head ? a->k_strides.head : row;
+  const int64_t vt = a->v_strides.token ? a->v_strides.token : row * a->num_kv_heads;
+  const int64_t vh = a->v_strides.head ? a->v_strides.head : row;
+  if (!aligned(a->q, 16) || !aligned(a->k, 16) || !aligned(a->v, 16) || !aligned(a->out, 16) ||
+      !aligned(a->out_f32, 16) || kt % 16 || kh % 16 || vt % 16 || vh % 16)
+    return fail(MSA_ERR_UNSUPPORTED, "q, k, v, out, out_f32 and the k/v strides must be 16-byte aligned");
+  msa::QsaParams p;
+  p.q = static_cast<const uint16_t*>(a->q);
+  p.k = static_cast<const uint16_t*>(a->k);
+  p.v = static_cast<const uint16_t*>(a->v);
+  p.k_row_stride = kt;
+  p.k_head_stride = kh;
+  p.v_row_stride = vt;
+  p.v_head_stride = vh;
+  p.indices = a->indices;
+  p.out = static_cast<uint16_t*>(a->out);
+  p.out_f32 = a->out_f32;
+  p.lse = a->lse;
+  p.total_q = a->total_q;
+  p.hq = a->num_qo_heads;
+  p.hkv = a->num_kv_heads;
+  p.group = a->num_qo_heads / a->num_kv_heads;
+  p.width = a->width;
+  const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / 16.0f;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return hip_status(msa::launch_qsa_indexed(p, static_cast<hipStream_t>(stream)),
+                    "msa_qsa_indexed_forward launch");
+}
+
 }  // extern "C"

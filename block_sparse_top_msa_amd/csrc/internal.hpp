@@ -89,6 +89,21 @@ hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_
 hipError_t launch_topk(const float* scores, int score_heads, int T, int total_q, int topk,
                        int hkv, int mode, int32_t* q2k, hipStream_t stream);
 
+struct QsaParams {
+  const uint16_t* q;          // bf16 [total_q, hq, 256]
+  const uint16_t* k;          // bf16 rows of 256, addressed by token and head strides
+  const uint16_t* v;
+  int64_t k_row_stride, k_head_stride, v_row_stride, v_head_stride;   // bytes
+  const int32_t* indices;     // [total_q, width]
+  uint16_t* out;              // bf16 [total_q, hq, 256]
+  float* out_f32;             // fp32 [total_q, hq, 256] or null
+  float* lse;                 // fp32 [hq, total_q] or null
+  int total_q, hq, hkv, group, width;
+  float scale_log2;           // softmax_scale * log2(e)
+};
+
+hipError_t launch_qsa_indexed(const QsaParams& p, hipStream_t stream);
+
 hipError_t launch_tile_union(const int32_t* q2k, const int32_t* cu_q, const int32_t* len_k,
                              int batch, int total_q, int hkv, int topk, int max_seqlen_q,
                              int max_k_tiles, int tile_tokens, int max_union,

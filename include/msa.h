@@ -222,6 +222,44 @@ msa_status_t msa_tile_union(const int32_t* q2k, const int32_t* cu_seqlens_q,
                             int32_t* union_count, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* QSA: packed query sparse attention over caller-selected tokens            */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t total_q;        /* T: packed query tokens                           */
+  int32_t num_qo_heads;   /* Hq; Hq % Hkv == 0 and Hq / Hkv <= 16 (12/1, 24/2) */
+  int32_t num_kv_heads;   /* Hkv                                               */
+  int32_t head_dim;       /* 256 (the only head dimension the qsa page names) */
+  int32_t width;          /* W: index entries per query, W % 4 == 0, W <= 2052 */
+  float softmax_scale;    /* <= 0: head_dim^-0.5                               */
+  const void* q;          /* bf16 [T, Hq, 256], contiguous                     */
+  const void* k;          /* bf16 rows of 256 values: row t of head g at
+                             k + t * k_strides.token + g * k_strides.head      */
+  const void* v;          /* same layout as k (its own strides)                */
+  msa_strides_t k_strides, v_strides;   /* bytes; token and head used; 0 =
+                             dense [Tk, Hkv, 256]                              */
+  const int32_t* indices; /* [T, W]: absolute packed token ids (rows of k/v) in
+                             groups of four, -1 padding; query i attends the
+                             set of its non-negative entries                   */
+  void* out;              /* bf16 [T, Hq, 256]                                 */
+  float* out_f32;         /* nullable: fp32 [T, Hq, 256], the output before
+                             the bf16 cast                                     */
+  float* lse;             /* nullable: fp32 [Hq, T], natural log               */
+} msa_qsa_args_t;
+
+/* out[i, h] = softmax over the keys j listed in indices[i] of
+ * (softmax_scale * q[i, h] . k[j, h / G]) applied to v[j, h / G]; lse the
+ * natural-log normaliser; a query with no listed key gets zero output and
+ * -inf LSE (qsa page: the indexed API, outputs and LSE, empty selections).
+ * Causality is the caller's, carried by the indices.  Index values are a
+ * caller contract (distinct, < Tk), not validated on the device.  Host-side
+ * checks return MSA_ERR_SHAPE / MSA_ERR_NULL / MSA_ERR_UNSUPPORTED (head_dim
+ * != 256, Hq / Hkv > 16, misaligned pointers) before any launch.  Every
+ * (query, head) is computed in index order by one wave: results are bitwise
+ * repeatable. */
+msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */
 /* ------------------------------------------------------------------------ */
 

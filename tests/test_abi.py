@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declarations_are_exported():
     names = _declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     assert set(names) == set(msa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(msa.lib, n), n
@@ -159,3 +159,27 @@ def test_proxy_and_topk_validation():
     u = msa.lib.msa_tile_union
     assert u(FAKE, FAKE, FAKE, 1, 8, 1, 4, 8, 8, 65, 8, FAKE, FAKE, FAKE, None) == 2
     assert u(FAKE, FAKE, FAKE, 1, 8, 1, 4, 8, 8, 4, 3, FAKE, FAKE, FAKE, None) == 2
+
+
+def test_qsa_validation():
+    a = msa.QsaArgs()
+    a.total_q, a.num_qo_heads, a.num_kv_heads, a.head_dim, a.width = 8, 12, 1, 256, 8
+    a.q = a.k = a.v = a.out = a.indices = FAKE
+    f = lambda: msa.lib.msa_qsa_indexed_forward(ctypes.byref(a), None)
+    a.head_dim = 128
+    assert f() == 5                       # head_dim other than 256
+    a.head_dim = 256
+    a.width = 6
+    assert f() == 2                       # width not a multiple of 4
+    a.width = 2056
+    assert f() == 2                       # wider than 2052
+    a.width = 8
+    a.num_qo_heads = 24
+    assert f() == 5                       # 24 query heads on one KV head
+    a.num_qo_heads, a.num_kv_heads = 13, 2
+    assert f() == 2                       # Hq not a multiple of Hkv
+    a.num_qo_heads, a.num_kv_heads = 12, 1
+    a.out = None
+    assert f() == 1                       # missing output
+    a.total_q = 0
+    assert f() == 0                       # nothing to do, nothing launched

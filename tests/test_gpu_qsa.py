@@ -1,0 +1,79 @@
+"""QSA indexed forward (qsa page) through the C ABI against the fp64 oracle."""
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_sparse_top_msa_amd as m
+    return m
+
+
+def _check(p, out, out_f32, lse, what, rows=None):
+    ref_out, ref_lse = oracle.qsa_indexed_attention(p.q.cpu(), p.k.cpu(), p.v.cpu(),
+                                                    p.indices.cpu()) if rows is None else rows
+    o = out.float().cpu().double()
+    f = out_f32.cpu().double()
+    l = lse.cpu().double()
+    assert float((o - ref_out).abs().max()) <= 2e-2, what
+    assert float((f - ref_out).abs().max()) <= 2e-2, what
+    fin = torch.isfinite(ref_lse)
+    assert torch.equal(torch.isfinite(l), fin), what
+    assert float((l[fin] - ref_lse[fin]).abs().max()) <= 1e-3, what
+    empty = torch.isneginf(ref_lse).T      # [T, Hq]
+    assert (o[empty] == 0).all() and (f[empty] == 0).all(), what
+
+
+@pytest.mark.parametrize("lens,hq,hkv,width,mode", [
+    ([37, 50], 12, 1, 32, "random"),      # several chunks, ragged rows, packed ids
+    ([70], 24, 2, 64, "causal"),          # 24/2: two KV heads, the page's pattern
+    ([9, 3, 20], 12, 1, 2052, "random"),  # the widest rows, mostly padding
+    ([33], 16, 2, 36, "random"),          # G = 8, width not a multiple of 32
+])
+def test_qsa_indexed_matches_oracle(msa, lens, hq, hkv, width, mode):
+    print(f"qsa {lens} Hq {hq} Hkv {hkv} W {width} {mode}", flush=True)
+    p = synth.make_qsa_problem("qsa", lens, hq, hkv, width, seed=len(lens) + width, mode=mode)
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_indexed_forward(d.q, d.k, d.v, d.indices)
+    torch.cuda.synchronize()
+    _check(p, out, out_f32, lse, f"qsa {lens} {hq}/{hkv} W {width}")
+
+
+def test_qsa_empty_rows_strided_kv_and_repeatability(msa):
+    p = synth.make_qsa_problem("qsa_edge", [40], 12, 1, 16, seed=5)
+    idx = p.indices.clone()
+    idx[3] = -1            # no key at all
+    idx[7, 4:] = -1        # one group only
+    p.indices = idx
+    # K and V as views of one [Tk, 2, Hkv, 256] buffer (token stride 1 KiB)
+    kv = torch.stack([p.k, p.v], dim=1).cuda()
+    k, v = kv[:, 0], kv[:, 1]
+    q, ind = p.q.cuda(), idx.cuda()
+    a = msa.qsa_indexed_forward(q, k, v, ind)
+    b = msa.qsa_indexed_forward(q, k, v, ind)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    _check(p, *a, "qsa edges")
+    assert (a[0][3].float() == 0).all() and torch.isneginf(a[2][:, 3]).all()
+
+
+def test_qsa_workload_sampled_rows(msa):
+    # the benchmark workload at full size, checked on sampled query rows
+    p = synth.qsa_workload(device="cpu")
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_indexed_forward(d.q, d.k, d.v, d.indices)
+    torch.cuda.synchronize()
+    rows = [0, 1, 5, 1000, 2047, 2048, 4095, 6000, 8191]
+    sub = synth.QsaProblem("qsa_rows", p.q[rows], p.k, p.v, p.indices[rows], [len(rows)])
+    ref_out, ref_lse = oracle.qsa_indexed_attention(sub.q, sub.k, sub.v, sub.indices)
+    o = out.float().cpu().double()[rows]
+    l = lse.cpu().double()[:, rows]
+    assert float((o - ref_out).abs().max()) <= 2e-2
+    assert float((l - ref_lse).abs().max()) <= 1e-3
