@@ -11,7 +11,8 @@ step time.  Inputs are seeded synthetic tensors resident in HBM before timing.
 
 The decode workloads (--workload paged_decode_...) report KV GB/s over the
 K/V blocks actually gathered, timed cold: a 1 GiB read evicts L2 and MALL
-before every step, outside the timed events.
+before every step, outside the timed events.  --workload
+qsa_indexed_1x8192_h12kv1_d256_w2048 times the QSA indexed forward.
 
 Per-stage times come from HIP events recorded on the stream the kernels run
 on.  One JSON line is printed.
@@ -289,6 +290,72 @@ def bench_decode(args, msa, synth, torch):
     return res, p
 
 
+def bench_qsa(args, msa, synth, torch):
+    """QSA indexed forward (qsa page): selected-token attention TFLOP/s, FLOPs
+    counted as 4 * head_dim per (query head, listed key)."""
+    p = synth.qsa_workload(device="cuda")
+    T, hq, d = p.q.shape
+    out = torch.empty_like(p.q)
+    out_f32 = torch.empty(T, hq, d, dtype=torch.float32, device="cuda")
+    lse = torch.empty(hq, T, dtype=torch.float32, device="cuda")
+    keys = int((p.indices >= 0).sum())
+    flops = 4 * d * hq * keys
+
+    def step():
+        msa.qsa_indexed_forward(p.q, p.k, p.v, p.indices, out=out, out_f32=out_f32, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [_events(2) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        evs[k][0].record()
+        step()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    res = {
+        "metric": "selected-token attention TFLOP/s",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "ms_per_step": round(ms_step, 4),
+        "dtype": "bf16",
+        "config": {"workload": p.name, "total_q": T, "num_qo_heads": hq,
+                   "num_kv_heads": p.k.shape[1], "head_dim": d, "width": p.indices.shape[1]},
+        "stages_ms": {"qsa_indexed_forward": round(kern_ms, 4)},
+        "work": {"attention_flops": flops, "listed_keys": keys},
+        "roofline": {"kernel": "msa_qsa_indexed_kernel", "bound": "mfma",
+                     "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": _traffic_for("msa_qsa_indexed_kernel:" + p.name)},
+    }
+    return res, p
+
+
+def cpu_baseline_qsa(p, rows_n):
+    import torch
+    import oracle
+    import synth
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    pc = p.to("cpu")
+    T, hq, d = pc.q.shape
+    step = max(1, T // rows_n)
+    rows = list(range(step - 1, T, step))[:rows_n]
+    t0 = time.perf_counter()
+    oracle.qsa_indexed_attention(pc.q[rows], pc.k, pc.v, pc.indices[rows])
+    dt = time.perf_counter() - t0
+    keys = int((pc.indices[rows] >= 0).sum())
+    return {"value": round(4 * d * hq * keys / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {T} query rows (every {step}th), all {hq} heads: "
+                      f"fp64 indexed attention, {dt:.1f} s"}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -304,7 +371,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, args.steps)
         return
-    if args.workload == DEFAULT_WORKLOAD or args.workload.startswith("flat_prefill"):
+    if args.workload == synth.QSA_WORKLOAD:
+        res, p = bench_qsa(args, msa, synth, torch)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_qsa(p, 512)
+    elif args.workload == DEFAULT_WORKLOAD or args.workload.startswith("flat_prefill"):
         res, p = bench_prefill_pipeline(args, msa, synth, torch)
         cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(p, args.cpu_sample_rows)
     else:
