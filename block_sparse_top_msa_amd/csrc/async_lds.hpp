@@ -13,25 +13,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // global -> LDS, 16 bytes per lane, lane l writing at lds_base + 16 l.
 // Issued from inline asm so that the compiler does not treat the in-flight
 // LDS writes as pending on every later LDS read (it would wait for the whole
-// prefetch); completion is awaited explicitly with vmcnt.
+// prefetch); completion is awaited explicitly with vmcnt.  The LDS base goes
+// through M0, which the compiler does not expect an asm statement to change:
+// its previous value is kept in a scalar register and put back.
 __device__ __forceinline__ void g2lds16(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\t"
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\t"
+               "s_mov_b32 m0, %2\n\t"
                "s_nop 0\n\t"
-               "global_load_lds_dwordx4 %0, off"
-               :
+               "global_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Same, addressed as scalar base + per-lane 32-bit byte offset (the saddr
 // form: no 64-bit address arithmetic or registers per lane).
 __device__ __forceinline__ void g2lds16_sv(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\t"
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\t"
+               "s_mov_b32 m0, %3\n\t"
                "s_nop 0\n\t"
-               "global_load_lds_dwordx4 %0, %1"
-               :
+               "global_load_lds_dwordx4 %1, %2\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(voff), "s"(sbase), "s"(lds_base)
-               : "memory", "m0");
+               : "memory");
 }
 
 // Workgroup barrier that does not drain outstanding global loads (unlike

@@ -108,17 +108,23 @@ __device__ __forceinline__ uint32_t lds_addr32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// (M0 restored afterwards, as in g2lds16)
 __device__ __forceinline__ void g2lds16_px(const void* gaddr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\t"
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\t"
+               "s_mov_b32 m0, %2\n\t"
                "s_nop 0\n\t"
-               "global_load_lds_dwordx4 %0, off"
-               :
+               "global_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved)
                : "v"(gaddr), "s"(lds_base)
-               : "memory", "m0");
+               : "memory");
 }
 
+// fp8 stages fit two workgroups per CU (256 VGPRs per wave); bf16 stages
+// take the LDS of one, whose waves may then use the whole register file.
 template <int NT, int FMT, bool REDUCE>
-__global__ __launch_bounds__(256, 2) void msa_proxy_rows_kernel(ProxyParams p) {
+__global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_kernel(ProxyParams p) {
   using Geo = RowsGeom<FMT>;
   constexpr int NST = Geo::kStages;
   constexpr int LOADS = Geo::kLoads;

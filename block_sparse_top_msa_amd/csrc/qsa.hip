@@ -82,7 +82,6 @@ __global__ __launch_bounds__(64, 2) void msa_qsa_indexed_kernel(QsaParams p) {
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + (int64_t)g * p.k_head_stride;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + (int64_t)g * p.v_head_stride;
   const uint32_t vlds = __builtin_amdgcn_readfirstlane(lds_addr(lds.v));
-  const uint32_t ilds = lds_addr(lds.ids);
   const float C = p.scale_log2;
 
   float m = -INFINITY, l = 0.f;
