@@ -183,3 +183,17 @@ def test_qsa_validation():
     assert f() == 1                       # missing output
     a.total_q = 0
     assert f() == 0                       # nothing to do, nothing launched
+
+
+def test_package_refuses_to_import_without_the_library(tmp_path):
+    # no fallback: a copy of the package without libmsa.so fails at import
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "block_sparse_top_msa_amd")
+    dst = tmp_path / "block_sparse_top_msa_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    r = subprocess.run([sys.executable, "-c", "import block_sparse_top_msa_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libmsa.so" in r.stderr
