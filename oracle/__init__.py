@@ -45,7 +45,8 @@ import torch
 BLOCK = 128  # tokens per KV block / page
 
 __all__ = [
-    "BLOCK", "decode_bf16", "decode_e4m3fn", "decode_e2m1", "unpack_e2m1x2",
+    "BLOCK", "decode_bf16", "decode_f16", "decode_q", "decode_e4m3fn", "decode_e2m1",
+    "unpack_e2m1x2", "qsa_indexed_attention",
     "dequant_e2m1", "decode_kv", "request_lengths", "logical_kv", "proxy_score",
     "reduce_heads", "selection_scores", "topk_select", "tile_union",
     "allowed_keys", "sparse_attention", "lse_merge",
@@ -127,11 +128,35 @@ def dequant_e2m1(packed: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
     return vals * torch.repeat_interleave(sc, 16, dim=-1)
 
 
+def decode_f16(t: torch.Tensor) -> torch.Tensor:
+    """IEEE binary16 -> float64 from its fields: sign, 5-bit exponent (bias
+    15), 10-bit fraction; exponent 0 is subnormal (2^-14 * f / 1024), 31 is
+    inf / NaN (the msa_sparse_attention page, Parameters: q and k accept
+    fp16)."""
+    bits = t.contiguous().view(torch.int16).to(torch.int64) & 0xFFFF
+    sign = torch.where((bits >> 15) == 1, -1.0, 1.0).to(torch.float64)
+    e = (bits >> 10) & 0x1F
+    f = (bits & 0x3FF).to(torch.float64)
+    normal = torch.ldexp(1.0 + f / 1024.0, (e - 15).to(torch.float64).to(torch.int32))
+    sub = torch.ldexp(f / 1024.0, torch.full_like(e, -14, dtype=torch.int32))
+    val = torch.where(e == 0, sub, normal)
+    val = torch.where(e == 31, torch.where(f == 0, torch.tensor(math.inf, dtype=torch.float64),
+                                           torch.tensor(math.nan, dtype=torch.float64)), val)
+    return sign * val
+
+
+def decode_q(t: torch.Tensor) -> torch.Tensor:
+    """Query storage (bf16 or fp16) -> float64."""
+    return decode_f16(t) if t.dtype == torch.float16 else decode_bf16(t)
+
+
 def decode_kv(data: torch.Tensor, kv_format: str, scale: Optional[torch.Tensor] = None):
     """K or V storage -> float64 values of the same logical shape (..., d)."""
     data = data.cpu()
     if kv_format == "bf16":
         return decode_bf16(data)
+    if kv_format == "f16":
+        return decode_f16(data)
     if kv_format == "fp8_e4m3":
         return decode_e4m3fn(data.view(torch.uint8))
     if kv_format == "e2m1x2":
@@ -258,7 +283,7 @@ def proxy_score(q, k, cu_seqlens_q, *, cu_seqlens_k=None, page_table=None,
         for c0 in range(0, len(local), chunk):
             li = torch.tensor(local[c0:c0 + chunk], dtype=torch.int64)
             ok = allowed_keys(pos, lq, lk, causal)[li]            # (n, Lk)
-            qb = decode_bf16(q[q0 + li])                           # (n, hq, d)
+            qb = decode_q(q[q0 + li])                           # (n, hq, d)
             for h in range(hq):
                 z = qb[:, h, :] @ kv[:, h // G, :].T               # (n, Lk)
                 z = torch.where(ok, z, torch.full_like(z, float("-inf")))
@@ -415,7 +440,7 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
         nblk = (lk + BLOCK - 1) // BLOCK
         for c0 in range(0, len(local), chunk):
             li = torch.tensor(local[c0:c0 + chunk], dtype=torch.int64)
-            qi = decode_bf16(q[q0 + li])                             # (n, hq, d)
+            qi = decode_q(q[q0 + li])                             # (n, hq, d)
             dst = torch.tensor([where[q0 + int(x)] for x in li])
             for g in range(hkv):
                 sel = q2k[g, q0 + li]                                # (n, topk)

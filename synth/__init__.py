@@ -26,6 +26,7 @@ BLOCK = 128  # KV block / page size in tokens (msa_sparse_attention page, Parame
 KV_BF16 = "bf16"
 KV_FP8 = "fp8_e4m3"
 KV_E2M1 = "e2m1x2"
+KV_F16 = "f16"      # fp16 Q, K and V
 
 
 @dataclasses.dataclass
@@ -211,6 +212,8 @@ def _kv_pool(shape, dtype_name, g, device, global_scale=1.0):
     """K or V storage: bf16 / fp8 e4m3fn (unit scale) / packed E2M1 + scales."""
     if dtype_name == KV_BF16:
         return _randn_cast(shape, g, device, torch.bfloat16), None
+    if dtype_name == KV_F16:
+        return _randn_cast(shape, g, device, torch.float16), None
     if dtype_name == KV_FP8:
         return _randn_cast(shape, g, device, torch.float8_e4m3fn), None
     if dtype_name == KV_E2M1:
@@ -349,7 +352,8 @@ def make_problem(name, *, q_lens, k_lens, num_qo_heads, num_kv_heads, head_dim=1
         if kv_dtype == KV_E2M1:
             raise ValueError("packed E2M1 K/V is built for the paged layout only")
 
-    q = _randn_cast((total_q, num_qo_heads, d), g_dev, device, torch.bfloat16)
+    qdt = torch.float16 if kv_dtype == KV_F16 else torch.bfloat16
+    q = _randn_cast((total_q, num_qo_heads, d), g_dev, device, qdt)
     kgs = 1.0 if k_global_scale is None else k_global_scale
     vgs = 1.0 if v_global_scale is None else v_global_scale
     k, k_scale = _kv_pool(kv_shape, kv_dtype, g_dev, device, kgs)

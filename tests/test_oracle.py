@@ -599,3 +599,38 @@ def test_qsa_empty_single_and_set_semantics():
     out2, lse2 = oracle.qsa_indexed_attention(p.q, p.k, p.v, wide)
     assert torch.equal(out, out2) or torch.allclose(out, out2, atol=1e-14, rtol=0)
     assert torch.allclose(lse, lse2, atol=1e-14, rtol=0)
+
+
+def test_f16_decode_all_bit_patterns_match_torch_cast():
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    x = bits.view(torch.float16)
+    got = oracle.decode_f16(x)
+    ref = x.to(torch.float64)
+    nan = torch.isnan(ref)
+    assert torch.equal(torch.isnan(got), nan)
+    assert torch.equal(got[~nan], ref[~nan])
+    assert torch.equal(torch.signbit(got[~nan]), torch.signbit(ref[~nan]))   # -0 stays -0
+
+
+def test_fp16_full_selection_equals_dense_sdpa():
+    q_lens, k_lens = [70, 33], [200, 33]
+    hq, hkv, d = 4, 2, 32
+    p = synth.make_problem("t16", q_lens=q_lens, k_lens=k_lens, num_qo_heads=hq,
+                           num_kv_heads=hkv, head_dim=d, seed=8, selection="proxy",
+                           kv_dtype=synth.KV_F16)
+    assert p.q.dtype == torch.float16 and p.k.dtype == torch.float16
+    q2k = _all_blocks_q2k(q_lens, k_lens, hkv, True)
+    out, lse = oracle.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q,
+                                       cu_seqlens_k=p.cu_seqlens_k, causal=True,
+                                       kv_format=synth.KV_F16)
+    q0 = k0 = 0
+    for Lq, Lk in zip(q_lens, k_lens):
+        qq = p.q[q0:q0 + Lq].to(torch.float64).transpose(0, 1)
+        kk = p.k[k0:k0 + Lk].to(torch.float64).repeat_interleave(hq // hkv, 1).transpose(0, 1)
+        vv = p.v[k0:k0 + Lk].to(torch.float64).repeat_interleave(hq // hkv, 1).transpose(0, 1)
+        iq = torch.arange(Lq).view(-1, 1)
+        mask = torch.arange(Lk).view(1, -1) <= Lk - Lq + iq
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask)
+        assert torch.allclose(out[q0:q0 + Lq].transpose(0, 1), ref, atol=1e-12, rtol=1e-12)
+        q0 += Lq
+        k0 += Lk
