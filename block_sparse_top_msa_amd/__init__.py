@@ -21,14 +21,15 @@ import torch
 
 __all__ = [
     "MsaError", "lib", "library_path", "sparse_attention", "proxy_score", "topk_select",
-    "tile_union", "qsa_indexed_forward", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3", "KV_E2M1X2",
+    "tile_union", "qsa_indexed_forward", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3",
+    "KV_E2M1X2", "KV_F16",
     "REDUCE_NONE", "REDUCE_ALL", "REDUCE_GROUP", "EXPORTED_SYMBOLS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libmsa.so")
 
-KV_BF16, KV_FP8_E4M3, KV_E2M1X2 = 0, 1, 2
+KV_BF16, KV_FP8_E4M3, KV_E2M1X2, KV_F16 = 0, 1, 2, 3
 REDUCE_NONE, REDUCE_ALL, REDUCE_GROUP = 0, 1, 2
 BLOCK = 128
 
@@ -146,6 +147,8 @@ def _stream():
 def _kv_format(k: torch.Tensor, k_scale) -> int:
     if k.dtype == torch.bfloat16:
         return KV_BF16
+    if k.dtype == torch.float16:
+        return KV_F16
     if k.dtype == torch.float8_e4m3fn:
         return KV_FP8_E4M3
     if k.dtype == torch.uint8:
@@ -261,8 +264,10 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
                      max_k_tiles=None, workspace: Optional[Workspace] = None, out=None,
                      lse=None, splits=0):
     """MSA forward (msa_sparse_attention page).  Returns out, or (out, lse)."""
-    if q.dtype != torch.bfloat16 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 tensor (total_q, num_qo_heads, 128)")
+    want = torch.float16 if k.dtype == torch.float16 else torch.bfloat16
+    if q.dtype != want or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous {want} tensor (total_q, num_qo_heads, 128) "
+                         "(fp16 q goes with fp16 k / v, bf16 q with every other K/V format)")
     for name, t in (("q2k_indices", q2k_indices), ("cu_seqlens_q", cu_seqlens_q),
                     ("cu_seqlens_k", cu_seqlens_k), ("page_table", page_table),
                     ("seqused_k", seqused_k)):

@@ -66,7 +66,9 @@ msa_status_t resolve_strides(const char* name, const msa_strides_t& in, bool pag
   return MSA_OK;
 }
 
-int kv_row_bytes(int fmt) { return fmt == MSA_KV_BF16 ? 256 : (fmt == MSA_KV_FP8_E4M3 ? 128 : 64); }
+int kv_row_bytes(int fmt) {
+  return (fmt == MSA_KV_BF16 || fmt == MSA_KV_F16) ? 256 : (fmt == MSA_KV_FP8_E4M3 ? 128 : 64);
+}
 
 struct Resolved {
   msa::AttnParams p;
@@ -91,7 +93,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   if (a->max_k_tiles > msa::kMaxBitmapWords * 32)
     return fail(MSA_ERR_SHAPE, "max_k_tiles %d exceeds %d blocks", a->max_k_tiles,
                 msa::kMaxBitmapWords * 32);
-  if (a->kv_dtype < MSA_KV_BF16 || a->kv_dtype > MSA_KV_E2M1X2)
+  if (a->kv_dtype < MSA_KV_BF16 || a->kv_dtype > MSA_KV_F16)
     return fail(MSA_ERR_DTYPE, "unknown kv_dtype %d", a->kv_dtype);
   const bool paged = a->page_table != nullptr;
   if (paged) {
@@ -121,7 +123,8 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
 
   msa::AttnParams& p = r->p;
   std::memset(&p, 0, sizeof(p));
-  const int fmt = a->kv_dtype;
+  const int fmt = a->kv_dtype;   // msa_kv_dtype_t values are the kernels' formats
+  p.out_f16 = a->kv_dtype == MSA_KV_F16 ? 1 : 0;
   const int rb = kv_row_bytes(fmt);
   msa_status_t st;
   if ((st = resolve_strides("k", a->k_strides, paged, a->num_kv_heads, rb, 16, &p.k_st))) return st;
@@ -200,6 +203,8 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     plan.splits = std::max(1, std::min(splits, 64));
   } else {
     plan.decode = 0;
+    if (a->kv_dtype == MSA_KV_F16)
+      return fail(MSA_ERR_UNSUPPORTED, "fp16 Q/K/V runs on decode shapes (seqlen_q x G <= 64) only");
     plan.async_bf16 = (a->kv_dtype == MSA_KV_BF16);
     // bf16: 4 waves x spw slots x 32 rows per tile; other formats: 4 x 2 x 16
     int rows;

@@ -40,6 +40,31 @@ namespace msa {
 constexpr float kDecRescaleSlack = 64.0f;
 constexpr float kDecSumLimit = 0x1p67f;
 
+// fp16 P holds at most 65504: the slack drops to 15, and a lane's eight
+// exponentials must sum to at most 2^15, so that no single p can pass 2^15
+// unnoticed (for bf16 any p below the 2^67 sum limit is representable).
+template <int FMT>
+struct DecSoft {
+  static constexpr float kSlack = FMT == kFmtF16 ? 15.0f : kDecRescaleSlack;
+  static constexpr float kLimit = FMT == kFmtF16 ? 0x1p15f : kDecSumLimit;
+};
+
+template <int FMT>
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  if constexpr (FMT == kFmtF16) return mfma16_f16(a, b, c);
+  else return mfma16(a, b, c);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t pk_p(float lo, float hi) {
+  if constexpr (FMT == kFmtF16) return pack_f16x2(lo, hi);
+  else return cvt_pk_bf16(lo, hi);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t pk_out(float lo, float hi) {
+  if constexpr (FMT == kFmtF16) return pack_f16x2(lo, hi);
+  else return pack_bf16x2(lo, hi);
+}
+
 namespace {
 
 constexpr float kLn2d = 0.69314718055994530942f;
@@ -58,6 +83,9 @@ struct DecGeom<kFmtBf16> {
   static constexpr int kStages = 2;                // pages in flight per wave
   static constexpr int kLoads = kStage / 1024;     // 1 KiB loads per wave per page
 };
+
+template <>
+struct DecGeom<kFmtF16> : DecGeom<kFmtBf16> {};   // 16-bit rows, same staging
 
 template <>
 struct DecGeom<kFmtFp8> {
@@ -477,7 +505,7 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
 #pragma unroll
     for (int nn = 0; nn < LOADS; ++nn) {
       const uint8_t* src;
-      if constexpr (FMT == kFmtBf16) {
+      if constexpr (FMT == kFmtBf16 || FMT == kFmtF16) {
         // rows of 256 B: 4 rows per load
         constexpr int kHalf = LOADS / 2;
         const bool isv = nn >= kHalf;
@@ -547,7 +575,7 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
     // ---- K fragments (A operand of S^T): key kw0 + 16 kt + l % 16,
     // head dims 32 q + 8 ds .. + 7 for k-step ds
     bf16x8 kf[2][4];
-    if constexpr (FMT == kFmtBf16) {
+    if constexpr (FMT == kFmtBf16 || FMT == kFmtF16) {
       u32x4 kw[8];
       uint32_t a[8];
 #pragma unroll
@@ -601,7 +629,7 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
     // ---- V^T fragments (A operand of O^T): head dim 16 dt + l % 16, keys
     // kw0 + {4q..4q+3, 16+4q..16+4q+3} (the order of P in the S^T registers)
     bf16x8 vf[8];
-    if constexpr (FMT == kFmtBf16) {
+    if constexpr (FMT == kFmtBf16 || FMT == kFmtF16) {
       u32x2 vv[16];
       uint32_t a[8];
       const int e = l16 >> 2, aa = lane & 3;
@@ -675,7 +703,7 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
       for (int kt = 0; kt < 2; ++kt) {
         acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) acc[kt] = mfma16(kf[kt][ds], qf[rt][ds], acc[kt]);
+        for (int ds = 0; ds < 4; ++ds) acc[kt] = mma16<FMT>(kf[kt][ds], qf[rt][ds], acc[kt]);
       }
       const bool sel = (tk_[rt] < ntok) && ((umask >> tk_[rt]) & 1ull);
       int lim = nvalid - 1;
@@ -700,11 +728,11 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) e[4 * kt + r] = __builtin_amdgcn_exp2f(acc[kt][r] - mu);
       float lp = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-      if (__ballot(sel && (m_[rt] == -INFINITY || !(lp <= kDecSumLimit))) != 0ull) {
+      if (__ballot(sel && (m_[rt] == -INFINITY || !(lp <= DecSoft<FMT>::kLimit))) != 0ull) {
         float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
                          fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
         mx = xmax16_32(mx);   // the row's keys are spread over four lanes
-        const bool up = mx > m_[rt] + kDecRescaleSlack;
+        const bool up = mx > m_[rt] + DecSoft<FMT>::kSlack;
         if (__ballot(up && m_[rt] > -INFINITY) != 0ull) {
           const float alpha = up ? __builtin_amdgcn_exp2f(m_[rt] - mx) : 1.0f;
           l_[rt] *= alpha;
@@ -720,10 +748,10 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
         lp = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
       }
       l_[rt] += lp;
-      const bf16x8 pf = as_bf16x8(u32x4{cvt_pk_bf16(e[0], e[1]), cvt_pk_bf16(e[2], e[3]),
-                                        cvt_pk_bf16(e[4], e[5]), cvt_pk_bf16(e[6], e[7])});
+      const bf16x8 pf = as_bf16x8(u32x4{pk_p<FMT>(e[0], e[1]), pk_p<FMT>(e[2], e[3]),
+                                        pk_p<FMT>(e[4], e[5]), pk_p<FMT>(e[6], e[7])});
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = mfma16(vf[dt], pf, o_[rt][dt]);
+      for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = mma16<FMT>(vf[dt], pf, o_[rt][dt]);
     }
     }  // any
     // the stage's reads completed (every fragment read above waited for
@@ -779,7 +807,7 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
         const int64_t orow = (int64_t)(q0 + row / G) * p.hq + g * G + row % G;
         u32x4 w4;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) w4[k] = pack_bf16x2(acc8[2 * k] * p.v_gs, acc8[2 * k + 1] * p.v_gs);
+        for (int k = 0; k < 4; ++k) w4[k] = pk_out<FMT>(acc8[2 * k] * p.v_gs, acc8[2 * k + 1] * p.v_gs);
         *reinterpret_cast<u32x4*>(p.out + orow * kHeadDim + d0) = w4;
         if (p.lse && d0 == 0) p.lse[orow] = lse_nat;
       } else {
@@ -835,7 +863,9 @@ __global__ __launch_bounds__(256) void msa_decode_merge_kernel(AttnParams p) {
   const int64_t orow = (int64_t)(q0 + row / p.group) * p.hq + g * p.group + row % p.group;
   u32x4 w4;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) w4[k] = pack_bf16x2(acc[2 * k] * sc, acc[2 * k + 1] * sc);
+  for (int k = 0; k < 4; ++k)
+    w4[k] = p.out_f16 ? pack_f16x2(acc[2 * k] * sc, acc[2 * k + 1] * sc)
+                      : pack_bf16x2(acc[2 * k] * sc, acc[2 * k + 1] * sc);
   *reinterpret_cast<u32x4*>(p.out + orow * kHeadDim + d0) = w4;
   if (p.lse && d0 == 0) p.lse[orow] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
@@ -867,6 +897,7 @@ hipError_t launch_decode(const AttnParams& p, int fmt, hipStream_t stream) {
   switch (fmt) {
     case kFmtBf16: return launch_decode_fmt<kFmtBf16>(p, stream);
     case kFmtFp8: return launch_decode_fmt<kFmtFp8>(p, stream);
+    case kFmtF16: return launch_decode_fmt<kFmtF16>(p, stream);
     default: return launch_decode_fmt<kFmtE2m1>(p, stream);
   }
 }
@@ -876,7 +907,8 @@ int decode_workgroups_per_cu(int fmt, int rows) {
   if (rows > 16) return 1;
   auto per = [](int bytes) { return (160 * 1024) / bytes; };
   switch (fmt) {
-    case kFmtBf16: return per(sizeof(DecodeLds<kFmtBf16, 4>));
+    case kFmtBf16:
+    case kFmtF16: return per(sizeof(DecodeLds<kFmtBf16, 4>));
     case kFmtFp8: return per(sizeof(DecodeLds<kFmtFp8, 4>));
     default: return per(sizeof(DecodeLds<kFmtE2m1, 8>));
   }

@@ -7,7 +7,7 @@
 
 namespace msa {
 
-enum KvFmt : int { kFmtBf16 = 0, kFmtFp8 = 1, kFmtE2m1 = 2 };
+enum KvFmt : int { kFmtBf16 = 0, kFmtFp8 = 1, kFmtE2m1 = 2, kFmtF16 = 3 };  // kFmtF16: fp16 Q, K, V, out
 
 // Largest union a tile may hold (entries), and largest block-id bitmap.
 constexpr int kMaxUnion = 512;
@@ -33,6 +33,7 @@ struct AttnParams {
   int pt_width;
   int paged;
   uint16_t* out;
+  int out_f16;                // out (and Q) are fp16 rather than bf16
   float* lse;                 // may be null
   int batch, total_q, hq, hkv, group, topk, causal;
   int max_k_tiles;            // bound on ceil(Lk / 128)

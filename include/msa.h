@@ -56,8 +56,10 @@ typedef enum {
 typedef enum {
   MSA_KV_BF16 = 0,      /* bf16 values                                        */
   MSA_KV_FP8_E4M3 = 1,  /* OCP float8 E4M3FN bytes, upconverted in-kernel     */
-  MSA_KV_E2M1X2 = 2     /* packed E2M1, two per byte (element 2i = low nibble),
+  MSA_KV_E2M1X2 = 2,    /* packed E2M1, two per byte (element 2i = low nibble),
                            with E4M3 block scales, one per 16 values          */
+  MSA_KV_F16 = 3        /* fp16 values; q and out are fp16 too (the page's
+                           "bf16/fp16" q, k and v)                            */
 } msa_kv_dtype_t;
 
 /* How score heads map to the per-KV-head selections of q2k_indices. */

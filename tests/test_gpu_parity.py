@@ -351,3 +351,34 @@ def test_proxy_group_reduction_in_kernel(msa, ql, kl, hq, hkv, paged, fmt):
     a = msa.topk_select(got, 4, hkv, mode=0)
     b = msa.topk_select(per_head, 4, hkv, mode=2)
     assert torch.equal(a.cpu(), b.cpu())
+
+
+@pytest.mark.parametrize("B,sq,hq,hkv,paged,splits", [
+    (5, 1, 64, 4, True, 0), (5, 1, 64, 4, True, 3), (3, 4, 32, 2, True, 0),
+    (4, 2, 8, 1, False, 2),
+])
+def test_decode_fp16_matches_oracle(msa, B, sq, hq, hkv, paged, splits):
+    # fp16 q, k, v and out (the page's "bf16/fp16"); P is fp16 too, so its
+    # reference max moves once a score passes it by 15 (log2 units)
+    g = torch.Generator().manual_seed(900 + B * sq)
+    lens = [int(x) for x in torch.randint(200, 3000, (B,), generator=g)]
+    lens[0] = 129
+    p = synth.make_problem("dec16", q_lens=[sq] * B, k_lens=lens, num_qo_heads=hq,
+                           num_kv_heads=hkv, topk=8, paged=paged, kv_dtype=synth.KV_F16,
+                           seed=901 + B, selection="general")
+    print(f"fp16 decode B {B} sq {sq} Hq {hq} Hkv {hkv} paged {paged} splits {splits}", flush=True)
+    out, lse = gpu_attention(msa, _dev(p), splits=splits)
+    assert out.dtype == torch.float16
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "fp16 decode")
+
+
+def test_decode_fp16_large_score_spread(msa):
+    # scores spread far beyond the fp16 slack: the rare rescale path runs
+    p = synth.make_problem("dec16s", q_lens=[1] * 3, k_lens=[2000, 900, 3000], num_qo_heads=16,
+                           num_kv_heads=1, topk=8, paged=True, kv_dtype=synth.KV_F16, seed=5,
+                           selection="decode", softmax_scale=0.8)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert torch.isfinite(out.float()).all()
+    assert_attention_close(out, lse, ref_out, ref_lse, "fp16 decode, wide scores")
