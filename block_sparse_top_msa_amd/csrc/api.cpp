@@ -203,9 +203,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     plan.splits = std::max(1, std::min(splits, 64));
   } else {
     plan.decode = 0;
-    if (a->kv_dtype == MSA_KV_F16)
-      return fail(MSA_ERR_UNSUPPORTED, "fp16 Q/K/V runs on decode shapes (seqlen_q x G <= 64) only");
-    plan.async_bf16 = (a->kv_dtype == MSA_KV_BF16);
+    plan.async_bf16 = (a->kv_dtype == MSA_KV_BF16 || a->kv_dtype == MSA_KV_F16);
     // bf16: 4 waves x spw slots x 32 rows per tile; other formats: 4 x 2 x 16
     int rows;
     if (plan.async_bf16) {

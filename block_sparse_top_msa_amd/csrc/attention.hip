@@ -458,6 +458,8 @@ hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
     case kFmtBf16:
       if (plan.async_bf16) return launch_prefill_bf16(p, plan.spw, stream);
       return launch_one<4, 2, kFmtBf16>(p, stream);
+    case kFmtF16:   // the 16-bit prefill kernel, fp16 instantiation (p.out_f16)
+      return launch_prefill_bf16(p, plan.spw, stream);
     case kFmtFp8: return launch_one<4, 2, kFmtFp8>(p, stream);
     default: return launch_one<4, 2, kFmtE2m1>(p, stream);
   }

@@ -60,7 +60,7 @@ struct AttnPlan {
 hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
                             hipStream_t stream);
 
-// bf16 prefill tiles of 256 rows: 8 waves x 1 slot (spw 1) or 4 x 2 (spw 2)
+// 16-bit (bf16, or fp16 with p.out_f16) prefill tiles of 256 rows: 8 waves x 1 slot
 hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream);
 
 // decode kernel (+ split merge when p.splits > 1); workgroups one CU holds

@@ -50,6 +50,26 @@ constexpr float kRescaleSlack = 64.0f;
 // score is within the slack of the reference max.
 constexpr float kSumLimit = 0x1p68f;
 
+// fp16 Q/K/V (and P): P holds at most 65504, so the slack drops to 15 and a
+// lane's 16 exponentials must sum to at most 2^15 (no single p can pass
+// 2^15 unnoticed); bf16 P represents anything below the 2^68 sum limit.
+template <bool F16>
+struct Soft {
+  static constexpr float kSlack = F16 ? 15.0f : kRescaleSlack;
+  static constexpr float kLimit = F16 ? 0x1p15f : kSumLimit;
+};
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mm32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16) return mfma32_f16(a, b, c);
+  else return mfma32(a, b, c);
+}
+template <bool F16>
+__device__ __forceinline__ uint32_t pk_p(float lo, float hi) {
+  if constexpr (F16) return pack_f16x2(lo, hi);
+  else return cvt_pk_bf16(lo, hi);
+}
+
 struct PrefillLds {
   uint8_t kv[2][2 * kTileBytes];   // [buffer][K | V]
   UnionLds un;
@@ -105,13 +125,14 @@ __device__ __forceinline__ void load_k(u32x4 (&kw)[8], const ChunkAddr& a, int c
 }
 
 // O^T += V^T P^T for one chunk (two 16-key k-steps per head-dim tile).
+template <bool F16>
 __device__ __forceinline__ void pv(f32x16 (&o)[4], const u32x2 (&vv)[16], u32x4 p0, u32x4 p1) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
     const u32x4 w0 = {vv[4 * dt][0], vv[4 * dt][1], vv[4 * dt + 1][0], vv[4 * dt + 1][1]};
     const u32x4 w1 = {vv[4 * dt + 2][0], vv[4 * dt + 2][1], vv[4 * dt + 3][0], vv[4 * dt + 3][1]};
-    o[dt] = mfma32(as_bf16x8(w0), as_bf16x8(p0), o[dt]);
-    o[dt] = mfma32(as_bf16x8(w1), as_bf16x8(p1), o[dt]);
+    o[dt] = mm32<F16>(as_bf16x8(w0), as_bf16x8(p0), o[dt]);
+    o[dt] = mm32<F16>(as_bf16x8(w1), as_bf16x8(p1), o[dt]);
   }
 }
 
@@ -134,10 +155,11 @@ struct SlotPipe {
 
 // One MFMA of O^T += V^T P^T: head-dim tile g / 2, k-step g % 2 (its V^T
 // fragments are vv[2 g] and vv[2 g + 1]).
+template <bool F16>
 __device__ __forceinline__ void pv_step(f32x16 (&o)[4], const u32x2 (&vv)[16], u32x4 p0, u32x4 p1,
                                         int g) {
   const u32x4 w = {vv[2 * g][0], vv[2 * g][1], vv[2 * g + 1][0], vv[2 * g + 1][1]};
-  o[g >> 1] = mfma32(as_bf16x8(w), as_bf16x8((g & 1) ? p1 : p0), o[g >> 1]);
+  o[g >> 1] = mm32<F16>(as_bf16x8(w), as_bf16x8((g & 1) ? p1 : p0), o[g >> 1]);
 }
 
 // The two V^T fragments vv[2 g], vv[2 g + 1] of chunk c.
@@ -148,34 +170,37 @@ __device__ __forceinline__ void load_v2(u32x2 (&vv)[16], const ChunkAddr& a, int
 }
 
 // MFMA k-step g of S^T (keys x query rows over head dims 16 g .. 16 g + 15).
+template <bool F16>
 __device__ __forceinline__ f32x16 score_step(f32x16 s, const u32x4 (&kw)[8], const bf16x8 (&qf)[8],
                                              int g) {
   if (g == 0) {
     f32x16 z;
 #pragma unroll
     for (int r = 0; r < 16; ++r) z[r] = 0.f;
-    return mfma32(as_bf16x8(kw[0]), qf[0], z);
+    return mm32<F16>(as_bf16x8(kw[0]), qf[0], z);
   }
-  return mfma32(as_bf16x8(kw[g]), qf[g], s);
+  return mm32<F16>(as_bf16x8(kw[g]), qf[g], s);
 }
 
 // p = 2^(s c - mu) of scores r and r + 1, packed to one bf16 pair of P^T;
 // returns their sum.
+template <bool F16>
 __device__ __forceinline__ float exp_pair(const f32x16& acc, int r, float cs, float mu, uint32_t& pw) {
   const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r], cs, -mu));
   const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[r + 1], cs, -mu));
-  pw = cvt_pk_bf16(e0, e1);
+  pw = pk_p<F16>(e0, e1);
   return e0 + e1;
 }
 
 // The chunk's 16 exponentials, their row sum and P^T, without scheduling
 // constraints (rare path).
+template <bool F16>
 __device__ __forceinline__ float exp_all(const f32x16& acc, float cs, float mu, u32x4& q0, u32x4& q1) {
   float ps[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t w;
-    ps[i] = exp_pair(acc, 2 * i, cs, mu, w);
+    ps[i] = exp_pair<F16>(acc, 2 * i, cs, mu, w);
     if (i < 4) q0[i] = w;
     else q1[i - 4] = w;
   }
@@ -201,7 +226,7 @@ __device__ __forceinline__ float exp_all(const f32x16& acc, float cs, float mu, 
 // There the chunk's row max moves m, O^T (holding chunk C - 1 by then) and l
 // are rescaled, and the exponentials are redone.  Without the rare path every
 // p stays at most 2^68: exact in bf16 and fp32 range, like the sums.
-template <int C>
+template <int C, bool F16>
 __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], float& m, float& l,
                                               const bf16x8 (&qf)[8], const ChunkAddr& ad,
                                               bool rowsel, int lim, int hf, float cs) {
@@ -232,17 +257,17 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
   for (int G = 0; G < 16; ++G) {
     const int g = G & 7;
     if (G < 8) {
-      if constexpr (C < 3) sn = score_step(sn, sp.kw, qf, g);
+      if constexpr (C < 3) sn = score_step<F16>(sn, sp.kw, qf, g);
       if constexpr (C > 0) load_v2(sp.vv, ad, C - 1, g);
     } else {
-      pv_step(o, sp.vv, sp.p0, sp.p1, g);
+      pv_step<F16>(o, sp.vv, sp.p0, sp.p1, g);
       if constexpr (C < 2) sp.kw[g] = lds_b128(ad.k[g] + 8192 * (C + 2));
       if constexpr (C == 3) load_v2(sp.vv, ad, 3, g);
     }
     if (G + 2 < 16) x[G + 2] = __builtin_fmaf(acc[G + 2], cs, -mu);
     if (G + 1 < 16) e[G + 1] = __builtin_amdgcn_exp2f(x[G + 1]);
     if (G & 1) {
-      pw[G >> 1] = cvt_pk_bf16(e[G - 1], e[G]);
+      pw[G >> 1] = pk_p<F16>(e[G - 1], e[G]);
       ps[G >> 1] = e[G - 1] + e[G];
     } else if (G >= 2) {
       lp += ps[(G >> 1) - 1];
@@ -252,13 +277,13 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
   if constexpr (C < 3) sp.s = sn;
   lp += ps[7];
   u32x4 q0 = {pw[0], pw[1], pw[2], pw[3]}, q1 = {pw[4], pw[5], pw[6], pw[7]};
-  if (__ballot(rowsel && (m == -INFINITY || !(lp <= kSumLimit))) != 0ull) {
+  if (__ballot(rowsel && (m == -INFINITY || !(lp <= Soft<F16>::kLimit))) != 0ull) {
     float mx = max16(acc);
     mx = rowsel ? mx * cs : -INFINITY;
     const float mr = swap32_max(mx);   // the row's other 16 keys sit in lane l ^ 32
     // first scores of a row: the max becomes the reference (O and l are
     // still zero); afterwards m moves only when the max passed the slack
-    const bool up = mr > m + kRescaleSlack;
+    const bool up = mr > m + Soft<F16>::kSlack;
     if (__ballot(up && m > -INFINITY) != 0ull) {
       const float alpha = up ? __builtin_amdgcn_exp2f(m - mr) : 1.0f;
       l *= alpha;
@@ -267,7 +292,7 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
     }
     m = up ? mr : m;
     const float mu2 = (rowsel && m > -INFINITY) ? m : INFINITY;
-    lp = exp_all(acc, cs, mu2, q0, q1);
+    lp = exp_all<F16>(acc, cs, mu2, q0, q1);
   }
   l += lp;
   sp.p0 = q0;
@@ -276,7 +301,7 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
 
 }  // namespace
 
-template <int NW, int SPW>
+template <int NW, int SPW, bool F16>
 __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
   constexpr int NT = NW * kWave;
   constexpr int LOADS = 64 / NW;   // 1 KiB load instructions per wave per block
@@ -497,14 +522,14 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
       load_k(sp.kw, ad, 0);
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
-        sp.s = score_step(sp.s, sp.kw, qf[0], g);
+        sp.s = score_step<F16>(sp.s, sp.kw, qf[0], g);
         sp.kw[g] = lds_b128(ad.k[g] + 8192);
         __builtin_amdgcn_sched_barrier(0);
       }
-      prefill_chunk<0>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
-      prefill_chunk<1>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
-      prefill_chunk<2>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
-      prefill_chunk<3>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<0, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<1, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<2, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<3, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
     }
     // the operand addresses move to the other buffer
     const uint32_t step = buf ? (uint32_t)(-2 * kTileBytes) : (uint32_t)(2 * kTileBytes);
@@ -514,7 +539,7 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
     for (int dt = 0; dt < 4; ++dt) ad.v[dt] += step;
   }
   // O^T += V^T P^T of the last active block's last chunk
-  pv(o_[0], sp.vv, sp.p0, sp.p1);
+  pv<F16>(o_[0], sp.vv, sp.p0, sp.p1);
 
   // ---- epilogue: out = O / l * v_gs (bf16), lse = (m + log2 l) * ln 2.
   // Lane quantities are recomputed from an opaque copy of the thread id:
@@ -540,14 +565,16 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * q) =
-            u32x2{pack_bf16x2(o_[s][dt][4 * q] * inv, o_[s][dt][4 * q + 1] * inv),
-                  pack_bf16x2(o_[s][dt][4 * q + 2] * inv, o_[s][dt][4 * q + 3] * inv)};
+            F16 ? u32x2{pack_f16x2(o_[s][dt][4 * q] * inv, o_[s][dt][4 * q + 1] * inv),
+                        pack_f16x2(o_[s][dt][4 * q + 2] * inv, o_[s][dt][4 * q + 3] * inv)}
+                : u32x2{pack_bf16x2(o_[s][dt][4 * q] * inv, o_[s][dt][4 * q + 1] * inv),
+                        pack_bf16x2(o_[s][dt][4 * q + 2] * inv, o_[s][dt][4 * q + 3] * inv)};
     if (p.lse && ehf == 0)
       p.lse[row] = lsum > 0.f ? (m_[s] + __log2f(lsum)) * kLn2f : -INFINITY;
   }
 }
 
-template <int NW, int SPW>
+template <int NW, int SPW, bool F16>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
   const int units = p.batch * p.hkv;
   if (units <= 0 || p.tiles_per_req <= 0) return hipSuccess;
@@ -559,14 +586,14 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
     const int n = units * p.tiles_per_req;
     grid = 8 * ((n + 7) / 8);
   }
-  hipLaunchKernelGGL((msa_prefill_kernel<NW, SPW>), dim3(grid), dim3(NW * kWave), 0, stream, p);
+  hipLaunchKernelGGL((msa_prefill_kernel<NW, SPW, F16>), dim3(grid), dim3(NW * kWave), 0, stream, p);
   return hipGetLastError();
 }
 
 // Tiles of 256 rows: 8 waves x one 32-row slot.
 hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream) {
   (void)spw;
-  return launch_prefill_t<8, 1>(p, stream);
+  return p.out_f16 ? launch_prefill_t<8, 1, true>(p, stream) : launch_prefill_t<8, 1, false>(p, stream);
 }
 
 }  // namespace msa

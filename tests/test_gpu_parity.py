@@ -382,3 +382,29 @@ def test_decode_fp16_large_score_spread(msa):
     ref_out, ref_lse = oracle_attention(p)
     assert torch.isfinite(out.float()).all()
     assert_attention_close(out, lse, ref_out, ref_lse, "fp16 decode, wide scores")
+
+
+@pytest.mark.parametrize("hq,hkv,causal", [(16, 2, True), (4, 1, True), (8, 8, False)])
+def test_prefill_fp16_matches_oracle(msa, hq, hkv, causal):
+    # fp16 q, k, v and out through the prefill kernel: several tiles, a
+    # ragged tail, irregular selections
+    p = synth.make_problem("pf16", q_lens=[300, 77], k_lens=[300, 900], num_qo_heads=hq,
+                           num_kv_heads=hkv, topk=4, causal=causal, kv_dtype=synth.KV_F16,
+                           seed=31 + hq, selection="general")
+    print(f"fp16 prefill Hq {hq} Hkv {hkv} causal {causal}", flush=True)
+    out, lse = gpu_attention(msa, _dev(p))
+    assert out.dtype == torch.float16
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "fp16 prefill")
+
+
+def test_prefill_fp16_large_score_spread(msa):
+    # a large softmax scale spreads scores far past the fp16 slack of 15
+    # (log2 units): the reference max moves and O is rescaled, P stays finite
+    p = synth.make_problem("pf16s", q_lens=[260], k_lens=[700], num_qo_heads=8, num_kv_heads=1,
+                           topk=4, kv_dtype=synth.KV_F16, seed=77, selection="general",
+                           softmax_scale=0.7)
+    out, lse = gpu_attention(msa, _dev(p))
+    assert torch.isfinite(out.float()).all()
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "fp16 prefill, wide scores")
