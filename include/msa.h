@@ -107,9 +107,10 @@ typedef struct {
                              partials per (request, KV head) on the decode
                              route; ignored on the prefill route              */
   /* device tensors */
-  const void* q;          /* bf16 [total_q, Hq, 128], contiguous              */
+  const void* q;          /* bf16 [total_q, Hq, 128], contiguous (fp16 when
+                             kv_dtype is MSA_KV_F16)                          */
   const void* k;          /* flat [total_k, Hkv, d'] or paged [pages, Hkv, 128, d'];
-                             d' = 128 (bf16, fp8) or 64 bytes (E2M1)          */
+                             d' = 128 (bf16, fp16, fp8) or 64 bytes (E2M1)    */
   const void* v;          /* same layout rules as k                           */
   const void* k_scale;    /* E2M1 only: E4M3 bytes [pages, Hkv, 128, 8], one per
                              16 values of a row; rows contiguous (8 bytes),
@@ -121,7 +122,8 @@ typedef struct {
   const int32_t* cu_seqlens_k; /* flat route: [B + 1]; must be NULL when paged */
   const int32_t* page_table;   /* paged route: [B, page_table_width]          */
   const int32_t* seqused_k;    /* paged route: [B] valid KV tokens per request */
-  void* out;              /* bf16 [total_q, Hq, 128], written                 */
+  void* out;              /* bf16 [total_q, Hq, 128], written (fp16 with
+                             MSA_KV_F16)                                      */
   float* lse;             /* NULL or fp32 [total_q, Hq], natural log, written;
                              -inf for a row with no attended key (out = 0)    */
 } msa_attn_args_t;
