@@ -303,18 +303,22 @@ def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, sequs
     reduce_heads: False (per query head), True (max over all heads) or
     "group" (max over each KV head's query heads).  Returns fp32
     (num_qo_heads | 1 | num_kv_heads, max_k_tiles, total_q)."""
-    if q.dtype != torch.bfloat16 or not q.is_contiguous():
-        raise ValueError("q must be a contiguous bf16 tensor (total_q, num_qo_heads, 128)")
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
                     ("page_table", page_table), ("seqused_k", seqused_k)):
         _check_i32(name, t)
     paged = page_table is not None
     if k.dtype == torch.bfloat16:
         fmt = KV_BF16
+    elif k.dtype == torch.float16:
+        fmt = KV_F16
     elif k.dtype == torch.float8_e4m3fn:
         fmt = KV_FP8_E4M3
     else:
-        raise ValueError(f"proxy K must be bf16 or float8_e4m3fn, got {k.dtype}")
+        raise ValueError(f"proxy K must be bf16, float16 or float8_e4m3fn, got {k.dtype}")
+    want = torch.float16 if fmt == KV_F16 else torch.bfloat16
+    if q.dtype != want or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous {want} tensor (total_q, num_qo_heads, 128) "
+                         "(fp16 q goes with fp16 k, bf16 q with bf16 or fp8 k)")
     T = _host_max_tiles(cu_seqlens_k, seqused_k) if max_k_tiles is None else int(max_k_tiles)
     if reduce_heads == "group":
         rmode, H = REDUCE_GROUP, k.shape[1]

@@ -303,8 +303,9 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   if (a->num_qo_heads <= 0 || a->num_kv_heads <= 0 || a->num_qo_heads % a->num_kv_heads)
     return fail(MSA_ERR_SHAPE, "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 a->num_qo_heads, a->num_kv_heads);
-  if (a->kv_dtype != MSA_KV_BF16 && a->kv_dtype != MSA_KV_FP8_E4M3)
-    return fail(MSA_ERR_DTYPE, "proxy K must be bf16 or fp8 E4M3 (got kv_dtype %d)", a->kv_dtype);
+  if (a->kv_dtype != MSA_KV_BF16 && a->kv_dtype != MSA_KV_FP8_E4M3 && a->kv_dtype != MSA_KV_F16)
+    return fail(MSA_ERR_DTYPE, "proxy K must be bf16, fp16 or fp8 E4M3 (got kv_dtype %d)",
+                a->kv_dtype);
   const bool paged = a->page_table != nullptr;
   if (paged) {
     if (!a->seqused_k) return fail(MSA_ERR_NULL, "paged K needs page_table and seqused_k together");
@@ -362,7 +363,9 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   else bpw = std::min(64, std::max(bpw, 16));   // amortise the Q tile over >= 16 blocks
   p.blocks_per_wg = bpw;
   p.block_chunks = (a->max_k_tiles + bpw - 1) / bpw;
-  return hip_status(msa::launch_proxy(p, a->kv_dtype == MSA_KV_FP8_E4M3 ? msa::kFmtFp8 : msa::kFmtBf16,
+  return hip_status(msa::launch_proxy(p, a->kv_dtype == MSA_KV_FP8_E4M3 ? msa::kFmtFp8
+                                      : a->kv_dtype == MSA_KV_F16    ? msa::kFmtF16
+                                                                     : msa::kFmtBf16,
                                       wide, static_cast<hipStream_t>(stream)),
                     "msa_proxy_score launch");
 }

@@ -52,6 +52,9 @@ struct RowsGeom<kFmtBf16> {
 constexpr int kRowsMaxBpw = 32;   // blocks per workgroup on this path
 constexpr int kWideMaxBpw = 64;   // ... and on the prefill-shaped path
 
+template <>
+struct RowsGeom<kFmtF16> : RowsGeom<kFmtBf16> {};   // fp16 rows: same bytes as bf16
+
 template <int FMT>
 struct RowsLds {
   uint8_t ring[4 * RowsGeom<FMT>::kStages * RowsGeom<FMT>::kStage];   // [wave][stage]
@@ -68,6 +71,13 @@ __device__ __forceinline__ bf16x8 fp8x8_bf16(uint32_t w0, uint32_t w1) {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))});
+}
+
+// fp16 proxy Q and K run on the fp16 MFMA; bf16 and fp8 K on the bf16 one.
+template <int FMT>
+__device__ __forceinline__ f32x16 mm32(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (FMT == kFmtF16) return mfma32_f16(a, b, c);
+  else return mfma32(a, b, c);
 }
 
 __device__ __forceinline__ float max16(const f32x16& a) {
@@ -299,9 +309,9 @@ __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_ke
             f32x16 z;
 #pragma unroll
             for (int r = 0; r < 16; ++r) z[r] = 0.f;
-            acc[cc][nt] = mfma32(a, qf[nt][s], z);
+            acc[cc][nt] = mm32<FMT>(a, qf[nt][s], z);
           } else {
-            acc[cc][nt] = mfma32(a, qf[nt][s], acc[cc][nt]);
+            acc[cc][nt] = mm32<FMT>(a, qf[nt][s], acc[cc][nt]);
           }
         }
       }
@@ -595,9 +605,9 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
             f32x16 z;
 #pragma unroll
             for (int r = 0; r < 16; ++r) z[r] = 0.f;
-            acc[cur][nt] = mfma32(a, qf[nt][s], z);
+            acc[cur][nt] = mm32<FMT>(a, qf[nt][s], z);
           } else {
-            acc[cur][nt] = mfma32(a, qf[nt][s], acc[cur][nt]);
+            acc[cur][nt] = mm32<FMT>(a, qf[nt][s], acc[cur][nt]);
           }
         }
       }
@@ -676,12 +686,15 @@ static hipError_t launch_proxy_rows_t(const ProxyParams& p, hipStream_t stream) 
 hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream) {
   if (wide_rows) {
     return fmt == kFmtFp8 ? launch_proxy_wide_t<kFmtFp8>(p, stream)
+         : fmt == kFmtF16 ? launch_proxy_wide_t<kFmtF16>(p, stream)
                           : launch_proxy_wide_t<kFmtBf16>(p, stream);
   }
   if (p.rows_per_tile <= 32)
     return fmt == kFmtFp8 ? launch_proxy_rows_t<1, kFmtFp8>(p, stream)
+         : fmt == kFmtF16 ? launch_proxy_rows_t<1, kFmtF16>(p, stream)
                           : launch_proxy_rows_t<1, kFmtBf16>(p, stream);
   return fmt == kFmtFp8 ? launch_proxy_rows_t<2, kFmtFp8>(p, stream)
+       : fmt == kFmtF16 ? launch_proxy_rows_t<2, kFmtF16>(p, stream)
                         : launch_proxy_rows_t<2, kFmtBf16>(p, stream);
 }
 

@@ -160,12 +160,13 @@ typedef struct {
   int32_t max_k_tiles;    /* columns t of the output                          */
   int32_t page_table_width;
   int32_t causal;         /* right-aligned, applied before the block max      */
-  int32_t kv_dtype;       /* MSA_KV_BF16 or MSA_KV_FP8_E4M3                   */
+  int32_t kv_dtype;       /* K: MSA_KV_BF16 or MSA_KV_FP8_E4M3 (bf16 q), or
+                             MSA_KV_F16 (fp16 q and K)                        */
   int32_t reduce_heads;   /* 0: per query head, output (Hq, T, total_q);
                              1: max over all query heads, output (1, T, total_q);
                              2: max over the G query heads of each KV head,
                                 output (Hkv, T, total_q); else MSA_ERR_UNSUPPORTED */
-  const void* q;          /* bf16 [total_q, Hq, 128] (the proxy Q)            */
+  const void* q;          /* bf16 or fp16 [total_q, Hq, 128] (the proxy Q)    */
   const void* k;          /* flat [total_k, Hkv, 128] or paged [pages, Hkv, 128, 128] */
   msa_strides_t k_strides;
   const int32_t* cu_seqlens_q;

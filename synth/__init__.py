@@ -360,7 +360,7 @@ def make_problem(name, *, q_lens, k_lens, num_qo_heads, num_kv_heads, head_dim=1
     v, v_scale = _kv_pool(kv_shape, kv_dtype, g_dev, device, vgs)
     proxy_q = None
     if proxy_heads:
-        proxy_q = _randn_cast((total_q, proxy_heads, d), g_dev, device, torch.bfloat16)
+        proxy_q = _randn_cast((total_q, proxy_heads, d), g_dev, device, qdt)
 
     q2k = None
     if selection == "general":

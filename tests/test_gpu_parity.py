@@ -408,3 +408,25 @@ def test_prefill_fp16_large_score_spread(msa):
     assert torch.isfinite(out.float()).all()
     ref_out, ref_lse = oracle_attention(p)
     assert_attention_close(out, lse, ref_out, ref_lse, "fp16 prefill, wide scores")
+
+
+@pytest.mark.parametrize("ql,kl,hq,hkv,paged,reduce", [
+    ([300, 200], [300, 456], 8, 2, False, False),    # > 64 rows: wide kernel
+    ([4, 4], [2000, 700], 32, 2, True, True),        # <= 64 rows: rows kernel, reduce_heads
+    ([1, 1, 1], [900, 129, 3000], 16, 1, True, False),
+])
+def test_proxy_fp16_matches_oracle(msa, ql, kl, hq, hkv, paged, reduce):
+    # the msa_proxy_score page: "q ... bf16 or fp16"; fp16 q with fp16 K
+    p = synth.make_problem("proxy16", q_lens=ql, k_lens=kl, num_qo_heads=hq, num_kv_heads=hkv,
+                           paged=paged, kv_dtype=synth.KV_F16, causal=True, seed=55,
+                           selection="proxy", reduce_heads=reduce)
+    print(f"fp16 proxy ql {ql} Hq {hq} Hkv {hkv} paged {paged} reduce {reduce}", flush=True)
+    d = _dev(p)
+    T = p.max_k_tiles + 1
+    got = msa.proxy_score(d.q, d.k, d.cu_seqlens_q, d.cu_seqlens_k, page_table=d.page_table,
+                          seqused_k=d.seqused_k, causal=True, max_seqlen_q=max(ql),
+                          max_k_tiles=T, reduce_heads=reduce)
+    ref = oracle.proxy_score(p.q, p.k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k,
+                             page_table=p.page_table, seqused_k=p.seqused_k, causal=True,
+                             max_k_tiles=T, reduce_heads=reduce, kv_format=synth.KV_F16)
+    assert_proxy_close(got, ref, "fp16 proxy")
