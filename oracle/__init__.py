@@ -26,9 +26,9 @@ as library steps:
   lse_merge         combining split partials by their LSE
                     (prepare_msa_nvfp4_sparse_decode page, Parameters:
                      workspace_buffer)
-  qsa_indexed_attention
+  qsa_indexed_attention, qsa_bitmap_attention
                     packed query sparse attention over caller-listed token
-                    indices (qsa page: indexed forward)
+                    indices or a block bitmap (qsa page)
 
 Readings of points the pages leave open are stated where they are used.
 Every function is pinned by tests/test_oracle.py against something other than
@@ -46,7 +46,7 @@ BLOCK = 128  # tokens per KV block / page
 
 __all__ = [
     "BLOCK", "decode_bf16", "decode_f16", "decode_q", "decode_e4m3fn", "decode_e2m1",
-    "unpack_e2m1x2", "qsa_indexed_attention",
+    "unpack_e2m1x2", "qsa_indexed_attention", "qsa_bitmap_indices", "qsa_bitmap_attention",
     "dequant_e2m1", "decode_kv", "request_lengths", "logical_kv", "proxy_score",
     "reduce_heads", "selection_scores", "topk_select", "tile_union",
     "allowed_keys", "sparse_attention", "lse_merge",
@@ -539,3 +539,27 @@ def qsa_indexed_attention(q, k, v, indices, softmax_scale=None):
             out[i, h] = (w / s) @ vd[sel, h // G]
     return out, lse
 
+
+
+def qsa_bitmap_indices(bitmap, num_kv_tokens: int):
+    """Index rows equivalent to a QSA block bitmap (qsa page: the bitmap API).
+
+    Reading (the page names a uint8 block bitmap and its int32 [T, NB]
+    compact-index counterpart, nothing more): bitmap[i, b] != 0 selects the
+    four packed tokens 4 b .. 4 b + 3 (those below num_kv_tokens) for query
+    i.  Returns int32 [T, 4 * NB], ascending, -1 padded."""
+    T, NB = bitmap.shape
+    out = torch.full((T, 4 * NB), -1, dtype=torch.int32)
+    for i in range(T):
+        blocks = torch.nonzero(bitmap[i].cpu() != 0).flatten()
+        tok = (4 * blocks.view(-1, 1) + torch.arange(4).view(1, -1)).reshape(-1)
+        tok = tok[tok < num_kv_tokens]
+        out[i, :tok.numel()] = tok.to(torch.int32)
+    return out
+
+
+def qsa_bitmap_attention(q, k, v, bitmap, softmax_scale=None):
+    """QSA over a block bitmap: the indexed definition applied to the tokens
+    of every selected block (qsa page: the bitmap API and its outputs)."""
+    return qsa_indexed_attention(q, k, v, qsa_bitmap_indices(bitmap, k.shape[0]),
+                                 softmax_scale=softmax_scale)

@@ -634,3 +634,26 @@ def test_fp16_full_selection_equals_dense_sdpa():
         assert torch.allclose(out[q0:q0 + Lq].transpose(0, 1), ref, atol=1e-12, rtol=1e-12)
         q0 += Lq
         k0 += Lk
+
+
+def test_qsa_bitmap_full_map_equals_dense_sdpa():
+    # every block selected: plain (non-causal) attention over all packed
+    # tokens, including the partial last block
+    p = synth.make_qsa_problem("qsab", [14], 12, 1, width=8, seed=6)
+    bitmap = torch.ones(14, 4, dtype=torch.uint8)     # ceil(14 / 4) blocks
+    out, lse = oracle.qsa_bitmap_attention(p.q, p.k, p.v, bitmap)
+    qq = p.q.to(torch.float64).transpose(0, 1)
+    kk = p.k.to(torch.float64).repeat_interleave(12, 1).transpose(0, 1)
+    vv = p.v.to(torch.float64).repeat_interleave(12, 1).transpose(0, 1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)
+    ref_lse = torch.logsumexp((qq @ kk.transpose(1, 2)) * 256 ** -0.5, dim=-1)
+    assert torch.allclose(out.transpose(0, 1), ref, atol=1e-12, rtol=1e-12)
+    assert torch.allclose(lse, ref_lse, atol=1e-12, rtol=1e-12)
+
+
+def test_qsa_bitmap_indices_layout():
+    bm = torch.tensor([[0, 1, 0, 1], [0, 0, 0, 0], [1, 0, 0, 0]], dtype=torch.uint8)
+    idx = oracle.qsa_bitmap_indices(bm, num_kv_tokens=14)
+    assert idx[0].tolist()[:6] == [4, 5, 6, 7, 12, 13] and (idx[0, 6:] == -1).all()
+    assert (idx[1] == -1).all()
+    assert idx[2].tolist()[:4] == [0, 1, 2, 3]
