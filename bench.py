@@ -328,10 +328,10 @@ def bench_qsa(args, msa, synth, torch):
                    "num_kv_heads": p.k.shape[1], "head_dim": d, "width": p.indices.shape[1]},
         "stages_ms": {"qsa_indexed_forward": round(kern_ms, 4)},
         "work": {"attention_flops": flops, "listed_keys": keys},
-        "roofline": {"kernel": "msa_qsa_indexed_kernel", "bound": "mfma",
+        "roofline": {"kernel": "msa_qsa_kernel", "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": _traffic_for("msa_qsa_indexed_kernel:" + p.name)},
+                     "traffic": _traffic_for("msa_qsa_kernel:" + p.name)},
     }
     return res, p
 

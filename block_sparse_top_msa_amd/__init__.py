@@ -10,6 +10,7 @@ load, importing this package raises.
     sparse_attention(q, k, v, q2k_indices, ...)   msa_sparse_attention page
     tile_union(q2k, cu_seqlens_q, lengths_k, ...) the per-tile union builder
     qsa_indexed_forward(q, k, v, indices, ...)    qsa page, indexed API
+    qsa_bitmap_forward(q, k, v, bitmap, ...)      qsa page, bitmap API
 """
 from __future__ import annotations
 
@@ -21,7 +22,7 @@ import torch
 
 __all__ = [
     "MsaError", "lib", "library_path", "sparse_attention", "proxy_score", "topk_select",
-    "tile_union", "qsa_indexed_forward", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3",
+    "tile_union", "qsa_indexed_forward", "qsa_bitmap_forward", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3",
     "KV_E2M1X2", "KV_F16",
     "REDUCE_NONE", "REDUCE_ALL", "REDUCE_GROUP", "EXPORTED_SYMBOLS",
 ]
@@ -35,8 +36,8 @@ BLOCK = 128
 
 EXPORTED_SYMBOLS = (
     "msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
-    "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward", "msa_status_string",
-    "msa_last_error", "msa_version",
+    "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward", "msa_qsa_bitmap_forward",
+    "msa_status_string", "msa_last_error", "msa_version",
 )
 
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_DTYPE",
@@ -99,6 +100,7 @@ class QsaArgs(ctypes.Structure):
         ("width", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
         ("q", _P), ("k", _P), ("v", _P), ("k_strides", Strides), ("v_strides", Strides),
         ("indices", _I32P), ("out", _P), ("out_f32", _P), ("lse", _P),
+        ("bitmap", _P), ("num_kv_tokens", ctypes.c_int32),
     ]
 
 
@@ -116,8 +118,10 @@ def _load():
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
     L.msa_tile_union.argtypes = [_P, _P, _P] + [ctypes.c_int32] * 8 + [_P, _P, _P, _P]
     L.msa_qsa_indexed_forward.argtypes = [ctypes.POINTER(QsaArgs), _P]
+    L.msa_qsa_bitmap_forward.argtypes = [ctypes.POINTER(QsaArgs), _P]
     for fn in ("msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
-               "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward"):
+               "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward",
+               "msa_qsa_bitmap_forward"):
         getattr(L, fn).restype = ctypes.c_int
     L.msa_status_string.argtypes = [ctypes.c_int]
     L.msa_status_string.restype = ctypes.c_char_p
@@ -393,20 +397,12 @@ def tile_union(q2k, cu_seqlens_q, lengths_k, tile_tokens, max_k_tiles, max_seqle
     return blocks, masks, counts
 
 
-def qsa_indexed_forward(q, k, v, indices, softmax_scale=None, out=None, out_f32=None, lse=None,
-                        return_f32=True, return_lse=True):
-    """Packed query sparse attention over caller-selected tokens (qsa page,
-    indexed API): q bf16 (T, Hq, 256); k, v bf16 (Tk, Hkv, 256), last dim
-    contiguous; indices int32 (T, W), absolute token ids in groups of four,
-    -1 padded.  Returns (out bf16, out_f32, lse (Hq, T)); out_f32 / lse are
-    None when not requested."""
+def _qsa_args(q, k, v, softmax_scale, out, out_f32, lse, return_f32, return_lse):
     if q.dtype != torch.bfloat16 or not q.is_contiguous() or q.dim() != 3:
         raise ValueError("q must be a contiguous bf16 tensor (T, Hq, 256)")
     for name, t in (("k", k), ("v", v)):
         if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1:
             raise ValueError(f"{name} must be bf16 (Tk, Hkv, 256) with a contiguous last dim")
-    if indices.dtype != torch.int32 or not indices.is_contiguous() or indices.dim() != 2:
-        raise ValueError("indices must be a contiguous int32 (T, W) tensor")
     T, hq, d = q.shape
     if out is None:
         out = torch.empty_like(q)
@@ -416,13 +412,48 @@ def qsa_indexed_forward(q, k, v, indices, softmax_scale=None, out=None, out_f32=
         lse = torch.empty(hq, T, dtype=torch.float32, device=q.device)
     a = QsaArgs()
     a.total_q, a.num_qo_heads, a.num_kv_heads, a.head_dim = T, hq, k.shape[1], d
-    a.width = indices.shape[1]
     a.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
     a.q, a.k, a.v = _ptr(q), _ptr(k), _ptr(v)
     a.k_strides = Strides(0, k.stride(1) * 2, k.stride(0) * 2)
     a.v_strides = Strides(0, v.stride(1) * 2, v.stride(0) * 2)
-    a.indices = _ptr(indices)
     a.out, a.out_f32, a.lse = _ptr(out), _ptr(out_f32), _ptr(lse)
+    return a, out, out_f32, lse
+
+
+def qsa_indexed_forward(q, k, v, indices, softmax_scale=None, out=None, out_f32=None, lse=None,
+                        return_f32=True, return_lse=True):
+    """Packed query sparse attention over caller-selected tokens (qsa page,
+    indexed API): q bf16 (T, Hq, 256); k, v bf16 (Tk, Hkv, 256), last dim
+    contiguous; indices int32 (T, W), absolute token ids in groups of four,
+    -1 padded.  Returns (out bf16, out_f32, lse (Hq, T)); out_f32 / lse are
+    None when not requested."""
+    if indices.dtype != torch.int32 or not indices.is_contiguous() or indices.dim() != 2:
+        raise ValueError("indices must be a contiguous int32 (T, W) tensor")
+    a, out, out_f32, lse = _qsa_args(q, k, v, softmax_scale, out, out_f32, lse, return_f32,
+                                     return_lse)
+    a.width = indices.shape[1]
+    a.indices = _ptr(indices)
     _check(lib.msa_qsa_indexed_forward(ctypes.byref(a), _stream()))
+    return out, out_f32, lse
+
+
+def qsa_bitmap_forward(q, k, v, bitmap, softmax_scale=None, out=None, out_f32=None, lse=None,
+                       return_f32=True, return_lse=True):
+    """Packed query sparse attention with each query's keys given by a
+    4-token block bitmap (qsa page, bitmap API): bitmap uint8 or bool
+    (T, ceil(Tk / 4)), a non-zero entry selecting the block's tokens (< Tk);
+    q, k, v and the outputs as in qsa_indexed_forward."""
+    if bitmap.dtype == torch.bool:
+        bitmap = bitmap.view(torch.uint8)
+    if bitmap.dtype != torch.uint8 or not bitmap.is_contiguous() or bitmap.dim() != 2:
+        raise ValueError("bitmap must be a contiguous uint8 or bool (T, ceil(Tk / 4)) tensor")
+    tk = k.shape[0]
+    if bitmap.shape != (q.shape[0], (tk + 3) // 4):
+        raise ValueError(f"bitmap must be ({q.shape[0]}, {(tk + 3) // 4}), got {tuple(bitmap.shape)}")
+    a, out, out_f32, lse = _qsa_args(q, k, v, softmax_scale, out, out_f32, lse, return_f32,
+                                     return_lse)
+    a.bitmap = _ptr(bitmap)
+    a.num_kv_tokens = tk
+    _check(lib.msa_qsa_bitmap_forward(ctypes.byref(a), _stream()))
     return out, out_f32, lse
 

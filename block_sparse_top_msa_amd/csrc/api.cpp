@@ -423,8 +423,9 @@ msa_status_t msa_tile_union(const int32_t* q2k, const int32_t* cu_seqlens_q,
                     "msa_tile_union launch");
 }
 
-msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* a, void* stream) {
-  if (!a) return fail(MSA_ERR_NULL, "args is NULL");
+static msa_status_t qsa_forward(const msa_qsa_args_t* a, bool bitmap, void* stream) {
+  const char* name = bitmap ? "msa_qsa_bitmap_forward" : "msa_qsa_indexed_forward";
+  if (!a) return fail(MSA_ERR_NULL, "%s: args is NULL", name);
   if (a->head_dim != 256) return fail(MSA_ERR_UNSUPPORTED, "QSA needs head_dim 256 (got %d)", a->head_dim);
   if (a->total_q < 0 || a->num_kv_heads <= 0 || a->num_qo_heads <= 0 ||
       a->num_qo_heads % a->num_kv_heads)
@@ -433,11 +434,13 @@ msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* a, void* stream) {
   if (a->num_qo_heads / a->num_kv_heads > 16)
     return fail(MSA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)",
                 a->num_qo_heads / a->num_kv_heads);
-  if (a->width < 4 || a->width % 4 || a->width > 2052)
+  if (!bitmap && (a->width < 4 || a->width % 4 || a->width > 2052))
     return fail(MSA_ERR_SHAPE, "width must be a multiple of 4 in [4, 2052] (got %d)", a->width);
+  if (bitmap && (a->num_kv_tokens < 0 || a->num_kv_tokens > INT32_MAX - 4))
+    return fail(MSA_ERR_SHAPE, "num_kv_tokens out of range (got %d)", a->num_kv_tokens);
   if (a->total_q == 0) return ok();
-  if (!a->q || !a->k || !a->v || !a->indices || !a->out)
-    return fail(MSA_ERR_NULL, "q, k, v, indices and out must be non-NULL");
+  if (!a->q || !a->k || !a->v || !a->out || (bitmap ? !a->bitmap : !a->indices))
+    return fail(MSA_ERR_NULL, "q, k, v, %s and out must be non-NULL", bitmap ? "bitmap" : "indices");
   const int64_t row = 256 * 2;
   const int64_t kt = a->k_strides.token ? a->k_strides.token : row * a->num_kv_heads;
   const int64_t kh = a->k_strides.head ? a->k_strides.head : row;
@@ -454,7 +457,10 @@ msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* a, void* stream) {
   p.k_head_stride = kh;
   p.v_row_stride = vt;
   p.v_head_stride = vh;
-  p.indices = a->indices;
+  p.indices = bitmap ? nullptr : a->indices;
+  p.bitmap = bitmap ? a->bitmap : nullptr;
+  p.num_kv_tokens = bitmap ? a->num_kv_tokens : 0;
+  p.num_blocks = bitmap ? (a->num_kv_tokens + 3) / 4 : 0;
   p.out = static_cast<uint16_t*>(a->out);
   p.out_f32 = a->out_f32;
   p.lse = a->lse;
@@ -462,11 +468,20 @@ msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* a, void* stream) {
   p.hq = a->num_qo_heads;
   p.hkv = a->num_kv_heads;
   p.group = a->num_qo_heads / a->num_kv_heads;
-  p.width = a->width;
+  p.width = bitmap ? 0 : a->width;
   const float scale = a->softmax_scale > 0.f ? a->softmax_scale : 1.0f / 16.0f;
   p.scale_log2 = scale * 1.4426950408889634f;
-  return hip_status(msa::launch_qsa_indexed(p, static_cast<hipStream_t>(stream)),
-                    "msa_qsa_indexed_forward launch");
+  char what[64];
+  snprintf(what, sizeof what, "%s launch", name);
+  return hip_status(msa::launch_qsa(p, static_cast<hipStream_t>(stream)), what);
+}
+
+msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* a, void* stream) {
+  return qsa_forward(a, false, stream);
+}
+
+msa_status_t msa_qsa_bitmap_forward(const msa_qsa_args_t* a, void* stream) {
+  return qsa_forward(a, true, stream);
 }
 
 }  // extern "C"

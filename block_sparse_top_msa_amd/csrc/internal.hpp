@@ -95,7 +95,9 @@ struct QsaParams {
   const uint16_t* k;          // bf16 rows of 256, addressed by token and head strides
   const uint16_t* v;
   int64_t k_row_stride, k_head_stride, v_row_stride, v_head_stride;   // bytes
-  const int32_t* indices;     // [total_q, width]
+  const int32_t* indices;     // [total_q, width] (indexed source)
+  const uint8_t* bitmap;      // [total_q, num_blocks] (bitmap source) or null
+  int num_blocks, num_kv_tokens;
   uint16_t* out;              // bf16 [total_q, hq, 256]
   float* out_f32;             // fp32 [total_q, hq, 256] or null
   float* lse;                 // fp32 [hq, total_q] or null
@@ -103,7 +105,7 @@ struct QsaParams {
   float scale_log2;           // softmax_scale * log2(e)
 };
 
-hipError_t launch_qsa_indexed(const QsaParams& p, hipStream_t stream);
+hipError_t launch_qsa(const QsaParams& p, hipStream_t stream);   // bitmap source when p.bitmap
 
 hipError_t launch_tile_union(const int32_t* q2k, const int32_t* cu_q, const int32_t* len_k,
                              int batch, int total_q, int hkv, int topk, int max_seqlen_q,

@@ -1,15 +1,16 @@
 // Packed query sparse attention over caller-listed tokens (qsa page: the
-// indexed API; outputs BF16 and FP32 [T, Hq, 256] and the natural-log LSE
+// indexed and bitmap APIs; outputs BF16 and FP32 [T, Hq, 256] and the natural-log LSE
 // [Hq, T]; an empty selection gives zero output and -inf LSE).
 //
 // gfx950 design, one wave per (query token, KV head):
 //  * The token's G <= 16 query heads of the KV head fill one 16-row tile of
 //    v_mfma_f32_16x16x32_bf16.  Its index row is consumed 32 entries at a
 //    time (eight 4-token groups); entries < 0 are padding and are masked.
-//  * K is gathered straight into MFMA operand registers: lane (key l % 16,
-//    quarter l / 16) loads the 128 bytes of head dims 64 q .. 64 q + 63 of
-//    its key row, and k-step s of S^T = K Q^T takes dims 64 q + 8 s .. + 7
-//    from them; the query fragments use the same permutation of the head
+//  * K is gathered straight into MFMA operand registers: k-step s of
+//    S^T = K Q^T gives lane (key l % 16, quarter q = l / 16) head dims
+//    32 s + 8 q .. + 7 of its key row, so the four lanes of a key read 64
+//    contiguous bytes per load (16 cache-line segments per wave load, not
+//    64); the query fragments use the same permutation of the head
 //    dimension, so the dot products are unchanged.
 //  * V rows are gathered into LDS with global_load_lds (no register
 //    staging) and read back transposed with ds_read_b64_tr_b16, which hands
@@ -50,11 +51,18 @@ __device__ __forceinline__ float xsum_16_32(float x) {
 struct QsaLds {
   uint8_t v[32 * kQsaRowBytes];   // V rows of the chunk (16 KiB)
   int32_t ids[32];                // the chunk's index entries (-1: padding)
+  int32_t blk[8];                 // bitmap source: the chunk's selected blocks
 };
 
 }  // namespace
 
-__global__ __launch_bounds__(64, 2) void msa_qsa_indexed_kernel(QsaParams p) {
+// BITMAP: the keys come from a uint8 [T, num_blocks] block bitmap instead of
+// index rows; each chunk takes the next eight selected blocks (32 tokens),
+// found with a ballot over 64 bitmap bytes at a time, so no [T, NB] index
+// scratch is ever written (qsa page: the bitmap API and its compact-index
+// scratch).
+template <bool BITMAP>
+__global__ __launch_bounds__(64, 2) void msa_qsa_kernel(QsaParams p) {
   __shared__ __attribute__((aligned(16))) QsaLds lds;
   const int tok = blockIdx.x / p.hkv;
   const int g = blockIdx.x % p.hkv;
@@ -66,19 +74,19 @@ __global__ __launch_bounds__(64, 2) void msa_qsa_indexed_kernel(QsaParams p) {
   const int hrow = g * G + l16;              // this lane's query head (row l16)
   const bool live = l16 < G;
 
-  // query fragments: row l16, head dims 64 q + 8 s .. + 7 for k-step s
+  // query fragments: row l16, head dims 32 s + 8 q .. + 7 for k-step s
   bf16x8 qf[8];
   {
     const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) +
-                        ((int64_t)tok * p.hq + (live ? hrow : g * G)) * kQsaRowBytes + 128 * q;
+                        ((int64_t)tok * p.hq + (live ? hrow : g * G)) * kQsaRowBytes + 16 * q;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qp + 64 * s);
       qf[s] = as_bf16x8(live ? w : u32x4{0, 0, 0, 0});
     }
   }
 
-  const int32_t* irow = p.indices + (int64_t)tok * p.width;
+  const int32_t* irow = BITMAP ? nullptr : p.indices + (int64_t)tok * p.width;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(p.k) + (int64_t)g * p.k_head_stride;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(p.v) + (int64_t)g * p.v_head_stride;
   const uint32_t vlds = __builtin_amdgcn_readfirstlane(lds_addr(lds.v));
@@ -89,14 +97,48 @@ __global__ __launch_bounds__(64, 2) void msa_qsa_indexed_kernel(QsaParams p) {
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunks = (p.width + 31) / 32;
-  for (int c = 0; c < nchunks; ++c) {
+  const int nchunks = BITMAP ? 0 : (p.width + 31) / 32;
+  const uint8_t* brow = BITMAP ? p.bitmap + (int64_t)tok * p.num_blocks : nullptr;
+  int cursor = 0;   // bitmap: the next block to scan (wave-uniform)
+  for (int c = 0;; ++c) {
+    if (!BITMAP && c >= nchunks) break;
     // every LDS read of the previous chunk has completed before its
     // buffers are refilled
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    if (lane < 32) {
-      const int e = 32 * c + lane;
-      lds.ids[lane] = e < p.width ? irow[e] : -1;
+    if constexpr (BITMAP) {
+      int have = 0;
+      while (have < 8 && cursor < p.num_blocks) {
+        const int b = cursor + lane;
+        const bool sel = b < p.num_blocks && brow[b] != 0;
+        const unsigned long long sm = __ballot(sel);
+        const int cnt = __popcll(sm);
+        const int take = min(8 - have, cnt);
+        const int rank = __popcll(sm & ((1ull << lane) - 1ull));
+        if (sel && rank < take) lds.blk[have + rank] = b;
+        if (take < cnt) {
+          unsigned long long rest = sm;
+          for (int k = 0; k < take; ++k) rest &= rest - 1ull;
+          cursor += __builtin_ctzll(rest);   // the first selected block not taken
+        } else {
+          cursor += 64;
+        }
+        have += take;
+      }
+      if (have == 0) break;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (lane < 32) {
+        int id = -1;
+        if ((lane >> 2) < have) {
+          const int t = 4 * lds.blk[lane >> 2] + (lane & 3);
+          id = t < p.num_kv_tokens ? t : -1;
+        }
+        lds.ids[lane] = id;
+      }
+    } else {
+      if (lane < 32) {
+        const int e = 32 * c + lane;
+        lds.ids[lane] = e < p.width ? irow[e] : -1;
+      }
     }
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
 
@@ -114,9 +156,9 @@ __global__ __launch_bounds__(64, 2) void msa_qsa_indexed_kernel(QsaParams p) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int id = lds.ids[16 * kt + l16];
-      const uint8_t* kp = kbase + (int64_t)(id >= 0 ? id : 0) * p.k_row_stride + 128 * q;
+      const uint8_t* kp = kbase + (int64_t)(id >= 0 ? id : 0) * p.k_row_stride + 16 * q;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) kw[kt][s] = *reinterpret_cast<const u32x4*>(kp + 16 * s);
+      for (int s = 0; s < 8; ++s) kw[kt][s] = *reinterpret_cast<const u32x4*>(kp + 64 * s);
     }
     // validity of the eight keys whose scores this lane holds
     const int4 va = *reinterpret_cast<const int4*>(&lds.ids[4 * q]);
@@ -185,10 +227,13 @@ __global__ __launch_bounds__(64, 2) void msa_qsa_indexed_kernel(QsaParams p) {
     p.lse[(int64_t)hrow * p.total_q + tok] = lsum > 0.f ? (m + __log2f(lsum)) * kQsaLn2 : -INFINITY;
 }
 
-hipError_t launch_qsa_indexed(const QsaParams& p, hipStream_t stream) {
+hipError_t launch_qsa(const QsaParams& p, hipStream_t stream) {
   const int64_t n = (int64_t)p.total_q * p.hkv;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(msa_qsa_indexed_kernel, dim3((unsigned)n), dim3(64), 0, stream, p);
+  if (p.bitmap)
+    hipLaunchKernelGGL(msa_qsa_kernel<true>, dim3((unsigned)n), dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL(msa_qsa_kernel<false>, dim3((unsigned)n), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

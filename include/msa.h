@@ -250,6 +250,11 @@ typedef struct {
   float* out_f32;         /* nullable: fp32 [T, Hq, 256], the output before
                              the bf16 cast                                     */
   float* lse;             /* nullable: fp32 [Hq, T], natural log               */
+  /* bitmap entry point only (ignored by the indexed one):                    */
+  const uint8_t* bitmap;  /* [T, ceil(Tk / 4)]: a non-zero byte b of row i
+                             selects packed tokens 4 b .. 4 b + 3 (those < Tk)
+                             for query i                                       */
+  int32_t num_kv_tokens;  /* Tk: rows of k/v the bitmap covers                 */
 } msa_qsa_args_t;
 
 /* out[i, h] = softmax over the keys j listed in indices[i] of
@@ -263,6 +268,16 @@ typedef struct {
  * (query, head) is computed in index order by one wave: results are bitwise
  * repeatable. */
 msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* args, void* stream);
+
+/* The same attention with the key set of query i given by row i of a block
+ * bitmap over the packed K/V (qsa page: the bitmap API over 4-token blocks):
+ * keys are the tokens of the selected blocks, in ascending order, the last
+ * block cut at Tk.  The selected blocks are compacted on the device, 32
+ * tokens per step, so nothing is allocated and no index scratch is written;
+ * width and indices are ignored, any number of blocks may be selected.
+ * Host-side checks as for the indexed entry point, plus bitmap non-NULL
+ * (when T > 0) and 0 <= Tk < 2^31 - 4 (MSA_ERR_SHAPE). */
+msa_status_t msa_qsa_bitmap_forward(const msa_qsa_args_t* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */

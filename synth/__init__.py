@@ -16,6 +16,7 @@ the same tensors to both sides.
 from __future__ import annotations
 
 import dataclasses
+import itertools
 import math
 from typing import Optional
 
@@ -444,15 +445,18 @@ def workload(name: str, device="cpu", seed=None) -> Problem:
 
 class QsaProblem:
     """q [T, Hq, d], k / v [T, Hkv, d] bf16 (packed sequences), indices
-    [T, W] int32: per query, absolute token ids in groups of four, -1 padded."""
+    [T, W] int32: per query, absolute token ids in groups of four, -1 padded;
+    or (bitmap problems) bitmap uint8 [T, ceil(T / 4)] over 4-token blocks."""
 
-    def __init__(self, name, q, k, v, indices, seq_lens):
+    def __init__(self, name, q, k, v, indices, seq_lens, bitmap=None):
         self.name, self.q, self.k, self.v, self.indices = name, q, k, v, indices
         self.seq_lens = list(seq_lens)
+        self.bitmap = bitmap
 
     def to(self, device):
-        return QsaProblem(self.name, self.q.to(device), self.k.to(device), self.v.to(device),
-                          self.indices.to(device), self.seq_lens)
+        mv = lambda t: None if t is None else t.to(device)
+        return QsaProblem(self.name, mv(self.q), mv(self.k), mv(self.v), mv(self.indices),
+                          self.seq_lens, mv(self.bitmap))
 
 
 def qsa_indices(seq_lens, width, g_cpu, mode="random"):
@@ -509,3 +513,37 @@ def qsa_workload(device="cpu", seed=6):
     256, 2048-wide index rows (the tail group plus up to 511 random earlier
     groups per query)."""
     return make_qsa_problem(QSA_WORKLOAD, [8192], 12, 1, 2048, seed, device=device)
+
+
+def qsa_bitmap(seq_lens, g_cpu, density, mode="random"):
+    """uint8 [T, ceil(T / 4)] block maps over the packed tokens.
+
+    mode "random": every block selected with probability `density`;
+    "causal": blocks overlapping the query's own sequence up to its position,
+    each with probability `density`, its own block always."""
+    T = sum(seq_lens)
+    nb = (T + 3) // 4
+    draw = torch.rand(T, nb, generator=g_cpu) < density
+    if mode == "random":
+        return draw.to(torch.uint8)
+    start = torch.cat([torch.full((L,), c, dtype=torch.long)
+                       for L, c in zip(seq_lens, [0] + list(itertools.accumulate(seq_lens))[:-1])])
+    pos = torch.arange(T)
+    b = torch.arange(nb).view(1, -1)
+    inside = (b >= (start // 4).view(-1, 1)) & (b <= (pos // 4).view(-1, 1))
+    own = b == (pos // 4).view(-1, 1)
+    return ((draw & inside) | own).to(torch.uint8)
+
+
+def make_qsa_bitmap_problem(name, seq_lens, num_qo_heads, num_kv_heads, density, seed,
+                            head_dim=256, device="cpu", mode="random"):
+    """Seeded QSA bitmap inputs: the bitmap (CPU generator), then Q, K, V
+    (generator on `device`), N(0,1) cast to bf16."""
+    g_cpu = _gen(seed, "cpu")
+    bitmap = qsa_bitmap(seq_lens, g_cpu, density, mode)
+    g = _gen(seed, device)
+    T = sum(seq_lens)
+    q = _randn_cast((T, num_qo_heads, head_dim), g, device, torch.bfloat16)
+    k = _randn_cast((T, num_kv_heads, head_dim), g, device, torch.bfloat16)
+    v = _randn_cast((T, num_kv_heads, head_dim), g, device, torch.bfloat16)
+    return QsaProblem(name, q, k, v, None, seq_lens, bitmap.to(device))

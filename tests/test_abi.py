@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declarations_are_exported():
     names = _declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     assert set(names) == set(msa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(msa.lib, n), n
@@ -181,6 +181,31 @@ def test_qsa_validation():
     a.num_qo_heads, a.num_kv_heads = 12, 1
     a.out = None
     assert f() == 1                       # missing output
+    a.total_q = 0
+    assert f() == 0                       # nothing to do, nothing launched
+
+
+def test_qsa_bitmap_validation():
+    a = msa.QsaArgs()
+    a.total_q, a.num_qo_heads, a.num_kv_heads, a.head_dim = 8, 12, 1, 256
+    a.q = a.k = a.v = a.out = FAKE
+    a.num_kv_tokens = 100
+    f = lambda: msa.lib.msa_qsa_bitmap_forward(ctypes.byref(a), None)
+    assert f() == 1                       # no bitmap (width / indices are not needed)
+    a.bitmap = FAKE
+    a.num_kv_tokens = -1
+    assert f() == 2                       # negative Tk
+    a.num_kv_tokens = 100
+    a.head_dim = 64
+    assert f() == 5                       # head_dim other than 256
+    a.head_dim = 256
+    a.num_qo_heads = 17
+    a.num_kv_heads = 1
+    assert f() == 5                       # more than 16 query heads per KV head
+    a.num_qo_heads = 12
+    a.q = FAKE + 4
+    assert f() == 5                       # misaligned q
+    a.q = FAKE
     a.total_q = 0
     assert f() == 0                       # nothing to do, nothing launched
 

@@ -77,3 +77,69 @@ def test_qsa_workload_sampled_rows(msa):
     l = lse.cpu().double()[:, rows]
     assert float((o - ref_out).abs().max()) <= 2e-2
     assert float((l - ref_lse).abs().max()) <= 1e-3
+
+
+def _bitmap_rows(p):
+    return oracle.qsa_bitmap_attention(p.q, p.k, p.v, p.bitmap)
+
+
+@pytest.mark.parametrize("lens,hq,hkv,density,mode", [
+    ([37, 50], 12, 1, 0.5, "random"),     # Tk = 87: the last block is cut at 3 tokens
+    ([300], 24, 2, 0.4, "causal"),        # 75 blocks: two 64-block scan windows
+    ([1000], 12, 1, 0.02, "random"),      # few blocks spread over 250: long empty scans
+    ([9, 3, 20], 16, 2, 1.0, "random"),   # every block: the dense map
+])
+def test_qsa_bitmap_matches_oracle(msa, lens, hq, hkv, density, mode):
+    print(f"qsa bitmap {lens} Hq {hq} Hkv {hkv} density {density} {mode}", flush=True)
+    p = synth.make_qsa_bitmap_problem("qsa_bm", lens, hq, hkv, density, seed=len(lens) + 7,
+                                      mode=mode)
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_bitmap_forward(d.q, d.k, d.v, d.bitmap)
+    torch.cuda.synchronize()
+    _check(p, out, out_f32, lse, f"qsa bitmap {lens} {hq}/{hkv}", rows=_bitmap_rows(p))
+
+
+def test_qsa_bitmap_hand_rows_and_indexed_equivalence(msa):
+    # rows that exercise the device compaction: exactly 8 and 9 selected
+    # blocks, hits at window edges (63, 64, 127), an empty row, one block
+    T, tk = 12, 517                            # 130 blocks, the last one token long
+    p = synth.make_qsa_bitmap_problem("qsa_bm_hand", [T], 12, 1, 0.0, seed=3)
+    k = synth._randn_cast((tk, 1, 256), synth._gen(4, "cpu"), "cpu", torch.bfloat16)
+    v = synth._randn_cast((tk, 1, 256), synth._gen(5, "cpu"), "cpu", torch.bfloat16)
+    bm = torch.zeros(T, (tk + 3) // 4, dtype=torch.uint8)
+    bm[0, :8] = 1
+    bm[1, :9] = 1
+    bm[2, [63, 64, 127, 129]] = 1
+    bm[4, 129] = 1                               # only the one-token block
+    bm[5, ::2] = 7                               # any non-zero byte selects
+    bm[6, 56:72] = 1                             # a run across the window edge
+    bm[7] = 1
+    bm[8, [0, 1, 2, 3, 4, 5, 6, 62, 63]] = 1
+    bm[9, 120:] = 1
+    bm[10, 64] = 1
+    bm[11, [5, 70, 100]] = 1
+    p = synth.QsaProblem("qsa_bm_hand", p.q, k, v, None, [T], bm)
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_bitmap_forward(d.q, d.k, d.v, d.bitmap)
+    torch.cuda.synchronize()
+    _check(p, out, out_f32, lse, "qsa bitmap hand rows", rows=_bitmap_rows(p))
+    assert torch.isneginf(lse[:, 3]).all() and (out[3].float() == 0).all()
+    # the indexed entry point over the same key lists (ascending, -1 padded)
+    # consumes the same 32-token chunks: bitwise equal results
+    ind = oracle.qsa_bitmap_indices(bm, tk).cuda()
+    b = msa.qsa_indexed_forward(d.q, d.k, d.v, ind)
+    torch.cuda.synchronize()
+    assert torch.equal(out, b[0]) and torch.equal(out_f32, b[1]) and torch.equal(lse, b[2])
+
+
+def test_qsa_bitmap_full_size_sampled_rows(msa):
+    # one 8192-token sequence, 12/1 heads, causal maps with a quarter of the
+    # visible blocks: checked on sampled rows
+    p = synth.make_qsa_bitmap_problem("qsa_bm_8192", [8192], 12, 1, 0.25, seed=8, mode="causal")
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_bitmap_forward(d.q, d.k, d.v, d.bitmap)
+    torch.cuda.synchronize()
+    rows = [0, 3, 4, 777, 4096, 8191]
+    ref_out, ref_lse = oracle.qsa_bitmap_attention(p.q[rows], p.k, p.v, p.bitmap[rows])
+    assert float((out.float().cpu().double()[rows] - ref_out).abs().max()) <= 2e-2
+    assert float((lse.cpu().double()[:, rows] - ref_lse).abs().max()) <= 1e-3
