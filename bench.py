@@ -12,7 +12,8 @@ step time.  Inputs are seeded synthetic tensors resident in HBM before timing.
 The decode workloads (--workload paged_decode_...) report KV GB/s over the
 K/V blocks actually gathered, timed cold: a 1 GiB read evicts L2 and MALL
 before every step, outside the timed events.  --workload
-qsa_indexed_1x8192_h12kv1_d256_w2048 times the QSA indexed forward.
+qsa_indexed_1x8192_h12kv1_d256_w2048 times the QSA indexed forward,
+qsa_bitmap_1x8192_h12kv1_d256_causal_q25 the QSA bitmap forward.
 
 Per-stage times come from HIP events recorded on the stream the kernels run
 on.  One JSON line is printed.
@@ -290,19 +291,36 @@ def bench_decode(args, msa, synth, torch):
     return res, p
 
 
+def _qsa_keys(p):
+    """Attended (query, key) pairs of a QSA problem: listed entries >= 0, or
+    the tokens (< Tk) of every selected 4-token block."""
+    if p.bitmap is None:
+        return int((p.indices >= 0).sum())
+    tk = p.k.shape[0]
+    sel = p.bitmap != 0
+    keys = 4 * int(sel.sum())
+    if tk % 4:
+        keys -= (4 - tk % 4) * int(sel[:, -1].sum())
+    return keys
+
+
 def bench_qsa(args, msa, synth, torch):
-    """QSA indexed forward (qsa page): selected-token attention TFLOP/s, FLOPs
-    counted as 4 * head_dim per (query head, listed key)."""
-    p = synth.qsa_workload(device="cuda")
+    """QSA forward (qsa page, indexed or bitmap API): selected-token attention
+    TFLOP/s, FLOPs counted as 4 * head_dim per (query head, attended key)."""
+    bitmap = args.workload == synth.QSA_BITMAP_WORKLOAD
+    p = synth.qsa_bitmap_workload(device="cuda") if bitmap else synth.qsa_workload(device="cuda")
     T, hq, d = p.q.shape
     out = torch.empty_like(p.q)
     out_f32 = torch.empty(T, hq, d, dtype=torch.float32, device="cuda")
     lse = torch.empty(hq, T, dtype=torch.float32, device="cuda")
-    keys = int((p.indices >= 0).sum())
+    keys = _qsa_keys(p)
     flops = 4 * d * hq * keys
 
     def step():
-        msa.qsa_indexed_forward(p.q, p.k, p.v, p.indices, out=out, out_f32=out_f32, lse=lse)
+        if bitmap:
+            msa.qsa_bitmap_forward(p.q, p.k, p.v, p.bitmap, out=out, out_f32=out_f32, lse=lse)
+        else:
+            msa.qsa_indexed_forward(p.q, p.k, p.v, p.indices, out=out, out_f32=out_f32, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -325,9 +343,11 @@ def bench_qsa(args, msa, synth, torch):
         "ms_per_step": round(ms_step, 4),
         "dtype": "bf16",
         "config": {"workload": p.name, "total_q": T, "num_qo_heads": hq,
-                   "num_kv_heads": p.k.shape[1], "head_dim": d, "width": p.indices.shape[1]},
-        "stages_ms": {"qsa_indexed_forward": round(kern_ms, 4)},
-        "work": {"attention_flops": flops, "listed_keys": keys},
+                   "num_kv_heads": p.k.shape[1], "head_dim": d,
+                   **({"num_blocks": p.bitmap.shape[1]} if bitmap else
+                      {"width": p.indices.shape[1]})},
+        "stages_ms": {("qsa_bitmap_forward" if bitmap else "qsa_indexed_forward"): round(kern_ms, 4)},
+        "work": {"attention_flops": flops, "attended_keys": keys},
         "roofline": {"kernel": "msa_qsa_kernel", "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -347,13 +367,20 @@ def cpu_baseline_qsa(p, rows_n):
     step = max(1, T // rows_n)
     rows = list(range(step - 1, T, step))[:rows_n]
     t0 = time.perf_counter()
-    oracle.qsa_indexed_attention(pc.q[rows], pc.k, pc.v, pc.indices[rows])
+    if pc.bitmap is None:
+        oracle.qsa_indexed_attention(pc.q[rows], pc.k, pc.v, pc.indices[rows])
+    else:
+        oracle.qsa_bitmap_attention(pc.q[rows], pc.k, pc.v, pc.bitmap[rows])
     dt = time.perf_counter() - t0
-    keys = int((pc.indices[rows] >= 0).sum())
+    sub = synth.QsaProblem("rows", pc.q[rows], pc.k, pc.v,
+                           None if pc.indices is None else pc.indices[rows], [len(rows)],
+                           None if pc.bitmap is None else pc.bitmap[rows])
+    keys = _qsa_keys(sub)
     return {"value": round(4 * d * hq * keys / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{len(rows)} of {T} query rows (every {step}th), all {hq} heads: "
-                      f"fp64 indexed attention, {dt:.1f} s"}
+                      f"fp64 {'bitmap' if pc.bitmap is not None else 'indexed'} attention, "
+                      f"{dt:.1f} s"}
 
 
 def main():
@@ -371,7 +398,7 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, args.steps)
         return
-    if args.workload == synth.QSA_WORKLOAD:
+    if args.workload in (synth.QSA_WORKLOAD, synth.QSA_BITMAP_WORKLOAD):
         res, p = bench_qsa(args, msa, synth, torch)
         cpu = None if args.no_cpu_baseline else cpu_baseline_qsa(p, 512)
     elif args.workload == DEFAULT_WORKLOAD or args.workload.startswith("flat_prefill"):

@@ -64,9 +64,11 @@ struct QsaLds {
 template <bool BITMAP>
 __global__ __launch_bounds__(64, 2) void msa_qsa_kernel(QsaParams p) {
   __shared__ __attribute__((aligned(16))) QsaLds lds;
-  const int tok = blockIdx.x / p.hkv;
+  // last tokens first: causal selections grow with the position, so the
+  // longest waves start earliest and the short ones fill the tail
+  const int tok = p.total_q - 1 - (int)(blockIdx.x / p.hkv);
   const int g = blockIdx.x % p.hkv;
-  if (tok >= p.total_q) return;
+  if (tok < 0) return;
   const int lane = threadIdx.x;
   const int l16 = lane & 15;
   const int q = lane >> 4;

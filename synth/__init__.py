@@ -547,3 +547,14 @@ def make_qsa_bitmap_problem(name, seq_lens, num_qo_heads, num_kv_heads, density,
     k = _randn_cast((T, num_kv_heads, head_dim), g, device, torch.bfloat16)
     v = _randn_cast((T, num_kv_heads, head_dim), g, device, torch.bfloat16)
     return QsaProblem(name, q, k, v, None, seq_lens, bitmap.to(device))
+
+
+QSA_BITMAP_WORKLOAD = "qsa_bitmap_1x8192_h12kv1_d256_causal_q25"
+
+
+def qsa_bitmap_workload(device="cpu", seed=9):
+    """One packed 8192-token sequence, 12 query heads / 1 KV head, head dim
+    256; each query's block map holds its own 4-token block plus a random
+    quarter of its earlier blocks."""
+    return make_qsa_bitmap_problem(QSA_BITMAP_WORKLOAD, [8192], 12, 1, 0.25, seed, device=device,
+                                   mode="causal")
