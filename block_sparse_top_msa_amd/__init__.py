@@ -8,6 +8,7 @@ load, importing this package raises.
     proxy_score(q, k, cu_seqlens_q, ...)          msa_proxy_score page
     topk_select(max_score, topk, num_kv_heads)    the top-K block select
     sparse_attention(q, k, v, q2k_indices, ...)   msa_sparse_attention page
+    validate_attention(q, k, v, q2k_indices, ...) its device-side caller contracts
     tile_union(q2k, cu_seqlens_q, lengths_k, ...) the per-tile union builder
     qsa_indexed_forward(q, k, v, indices, ...)    qsa page, indexed API
     qsa_bitmap_forward(q, k, v, bitmap, ...)      qsa page, bitmap API
@@ -21,7 +22,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "MsaError", "lib", "library_path", "sparse_attention", "proxy_score", "topk_select",
+    "MsaError", "lib", "library_path", "sparse_attention", "validate_attention", "proxy_score",
+    "topk_select",
     "tile_union", "qsa_indexed_forward", "qsa_bitmap_forward", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3",
     "KV_E2M1X2", "KV_F16",
     "REDUCE_NONE", "REDUCE_ALL", "REDUCE_GROUP", "EXPORTED_SYMBOLS",
@@ -37,12 +39,12 @@ BLOCK = 128
 EXPORTED_SYMBOLS = (
     "msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
     "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward", "msa_qsa_bitmap_forward",
-    "msa_status_string", "msa_last_error", "msa_version",
+    "msa_validate_attention", "msa_status_string", "msa_last_error", "msa_version",
 )
 
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_DTYPE",
            4: "MSA_ERR_CONFLICT", 5: "MSA_ERR_UNSUPPORTED", 6: "MSA_ERR_WORKSPACE",
-           7: "MSA_ERR_HIP"}
+           7: "MSA_ERR_HIP", 8: "MSA_ERR_CONTRACT"}
 
 
 class MsaError(RuntimeError):
@@ -119,9 +121,10 @@ def _load():
     L.msa_tile_union.argtypes = [_P, _P, _P] + [ctypes.c_int32] * 8 + [_P, _P, _P, _P]
     L.msa_qsa_indexed_forward.argtypes = [ctypes.POINTER(QsaArgs), _P]
     L.msa_qsa_bitmap_forward.argtypes = [ctypes.POINTER(QsaArgs), _P]
+    L.msa_validate_attention.argtypes = [ctypes.POINTER(AttnArgs), _P]
     for fn in ("msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
                "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward",
-               "msa_qsa_bitmap_forward"):
+               "msa_qsa_bitmap_forward", "msa_validate_attention"):
         getattr(L, fn).restype = ctypes.c_int
     L.msa_status_string.argtypes = [ctypes.c_int]
     L.msa_status_string.restype = ctypes.c_char_p
@@ -259,6 +262,25 @@ def workspace_size(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, *, pag
     n = ctypes.c_size_t(0)
     _check(lib.msa_sparse_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)))
     return int(n.value)
+
+
+def validate_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, causal=False,
+                       page_table=None, seqused_k=None, k_scale=None, v_scale=None, *,
+                       max_seqlen_q=None, max_k_tiles=None, out=None):
+    """Debug check of the device-side caller contracts of sparse_attention
+    with these arguments (cu_seqlens, KV lengths, page ids, q2k row order and
+    padding).  Synchronises the stream; raises MsaError (MSA_ERR_CONTRACT)
+    naming the first violation.  Never runs the attention.  Setting
+    MSA_VALIDATE=1 in the environment makes every sparse_attention call run
+    this check first."""
+    for name, t in (("q2k_indices", q2k_indices), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k), ("page_table", page_table),
+                    ("seqused_k", seqused_k)):
+        _check_i32(name, t)
+    a = _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, causal, None, page_table,
+                   seqused_k, k_scale, v_scale, None, None, max_seqlen_q, max_k_tiles,
+                   torch.empty_like(q) if out is None else out, None, 0)
+    _check(lib.msa_validate_attention(ctypes.byref(a), _stream()))
 
 
 def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, causal=False,

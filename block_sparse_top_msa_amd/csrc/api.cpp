@@ -255,6 +255,7 @@ const char* msa_status_string(msa_status_t s) {
     case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
     case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
     case MSA_ERR_HIP: return "MSA_ERR_HIP";
+    case MSA_ERR_CONTRACT: return "MSA_ERR_CONTRACT";
   }
   return "MSA_ERR_UNKNOWN";
 }
@@ -272,11 +273,66 @@ msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args, si
   return ok();
 }
 
+msa_status_t msa_validate_attention(const msa_attn_args_t* a, void* stream) {
+  Resolved r;
+  msa_status_t st = resolve_attention(a, &r, true);
+  if (st) return st;
+  if (a->total_q == 0 || a->batch == 0) return ok();
+  msa::ValidateParams v;
+  v.batch = a->batch;
+  v.total_q = a->total_q;
+  v.hkv = a->num_kv_heads;
+  v.topk = a->topk;
+  v.max_seqlen_q = a->max_seqlen_q;
+  v.max_k_tiles = a->max_k_tiles;
+  v.paged = a->page_table != nullptr;
+  v.pt_width = v.paged ? a->page_table_width : 0;
+  v.q2k = a->q2k;
+  v.cu_q = a->cu_seqlens_q;
+  v.cu_k = a->cu_seqlens_k;
+  v.page_table = a->page_table;
+  v.seqused = a->seqused_k;
+  unsigned long long word = ~0ull;
+  if ((st = hip_status(msa::run_validate(v, static_cast<hipStream_t>(stream), &word),
+                       "msa_validate_attention")))
+    return st;
+  if (word == ~0ull) return ok();
+  const int kind = (int)(word >> 48);
+  const long long pos = (long long)(word & ((1ull << 48) - 1));
+  switch (kind) {
+    case msa::kValCuQ:
+      return fail(MSA_ERR_CONTRACT, "cu_seqlens_q at request %lld: must start at 0, end at "
+                  "total_q (%d) and give lengths in [0, max_seqlen_q = %d]", pos, a->total_q,
+                  a->max_seqlen_q);
+    case msa::kValCuK:
+      return fail(MSA_ERR_CONTRACT, "cu_seqlens_k decreases after request %lld", pos);
+    case msa::kValKvLen:
+      return fail(MSA_ERR_CONTRACT, "KV length of request %lld is outside [0, 128 * %d]", pos,
+                  v.paged ? std::min(a->max_k_tiles, a->page_table_width) : a->max_k_tiles);
+    case msa::kValPage:
+      return fail(MSA_ERR_CONTRACT, "page_table[%lld, %lld] is negative inside the request's "
+                  "pages", pos / v.pt_width, pos % v.pt_width);
+    case msa::kValQ2kPad:
+    case msa::kValQ2kOrder: {
+      const long long row = pos / a->topk, e = pos % a->topk;
+      return fail(MSA_ERR_CONTRACT, "q2k[g=%lld, i=%lld] entry %lld %s", row / a->total_q,
+                  row % a->total_q, e,
+                  kind == msa::kValQ2kPad ? "follows -1 padding (padding must be trailing)"
+                                          : "is not above the previous block id (rows ascend "
+                                            "without repeats)");
+    }
+  }
+  return fail(MSA_ERR_CONTRACT, "contract violation kind %d at %lld", kind, pos);
+}
+
 msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   Resolved r;
   msa_status_t st = resolve_attention(args, &r, true);
   if (st) return st;
+  // debug path: check the device-side contracts first (synchronises the stream)
+  const char* env = std::getenv("MSA_VALIDATE");
+  if (env && env[0] == '1' && (st = msa_validate_attention(args, stream))) return st;
   if (r.ws_bytes) {
     if (!workspace || workspace_bytes < r.ws_bytes)
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", r.ws_bytes,

@@ -24,7 +24,11 @@
  *     enqueues nothing; msa_last_error() then holds a message for the calling
  *     thread.  MSA_ERR_HIP means a launch was rejected by the runtime.
  *   - Device-side contents (sequence boundaries, indices, page ids) are
- *     caller contracts and are not copied to the host for checking.
+ *     caller contracts and are not copied to the host for checking on the
+ *     timed path.  msa_validate_attention checks them on the device; with
+ *     the environment variable MSA_VALIDATE=1, msa_sparse_attention runs that
+ *     check first (and then synchronises the stream: a debug mode, not for
+ *     graph capture).
  *   - head_dim is 128 and the KV block / page size is 128 tokens.
  *   - Strides are in BYTES; a stride of 0 selects the dense layout.  The last
  *     (head_dim) dimension must be contiguous and every row 16-byte aligned
@@ -49,7 +53,9 @@ typedef enum {
   MSA_ERR_CONFLICT = 4,    /* both cu_seqlens_k and seqused_k on the paged route */
   MSA_ERR_UNSUPPORTED = 5, /* a view or option this library does not read   */
   MSA_ERR_WORKSPACE = 6,   /* workspace missing or too small                 */
-  MSA_ERR_HIP = 7          /* the HIP runtime rejected a launch              */
+  MSA_ERR_HIP = 7,         /* the HIP runtime rejected a launch              */
+  MSA_ERR_CONTRACT = 8     /* a device-side caller contract is broken (found
+                              only by msa_validate_attention / MSA_VALIDATE=1) */
 } msa_status_t;
 
 /* K/V storage formats (msa_sparse_attention page, Parameters: k). */
@@ -149,6 +155,21 @@ msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args,
  * `workspace` may be NULL when the size query returned 0. */
 msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Debug check of the device-side caller contracts of msa_sparse_attention
+ * with these arguments (msa_sparse_attention page, Parameters: cu_seqlens_q,
+ * cu_seqlens_k, q2k_indices, page_table, seqused_k): cu_seqlens_q starts at
+ * 0, ends at total_q and gives lengths in [0, max_seqlen_q]; cu_seqlens_k
+ * does not decrease; every KV length is in [0, 128 * max_k_tiles] (paged:
+ * also <= 128 * page_table_width); page_table[b, t] >= 0 for
+ * t < ceil(seqused_k[b] / 128); in every q2k row the non-negative block ids
+ * ascend without repeats and -1 padding is trailing.  Page ids are not
+ * bounded above (the pool size is not an argument).  Runs the host checks of
+ * msa_sparse_attention, then one small kernel on `stream`, and waits for it
+ * (synchronises the stream).  Returns MSA_ERR_CONTRACT, with the first
+ * violation (kind, then position) in msa_last_error(), or MSA_OK; never
+ * launches the attention. */
+msa_status_t msa_validate_attention(const msa_attn_args_t* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Proxy score (stage 1)                                                     */

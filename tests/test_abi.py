@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declarations_are_exported():
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     assert set(names) == set(msa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(msa.lib, n), n
@@ -33,6 +33,7 @@ def test_header_declarations_are_exported():
 def test_status_strings_and_version():
     assert msa.lib.msa_status_string(0) == b"MSA_OK"
     assert msa.lib.msa_status_string(4) == b"MSA_ERR_CONFLICT"
+    assert msa.lib.msa_status_string(8) == b"MSA_ERR_CONTRACT"
     assert msa.lib.msa_version().decode().count(".") == 2
 
 
@@ -159,6 +160,23 @@ def test_proxy_and_topk_validation():
     u = msa.lib.msa_tile_union
     assert u(FAKE, FAKE, FAKE, 1, 8, 1, 4, 8, 8, 65, 8, FAKE, FAKE, FAKE, None) == 2
     assert u(FAKE, FAKE, FAKE, 1, 8, 1, 4, 8, 8, 4, 3, FAKE, FAKE, FAKE, None) == 2
+
+
+def test_validate_attention_host_checks_run_first():
+    # the device check is reached only after the host checks pass; these fail
+    # before any HIP call
+    f = msa.lib.msa_validate_attention
+    assert f(None, None) == 1
+    a = msa.AttnArgs()
+    a.batch, a.total_q, a.num_qo_heads, a.num_kv_heads, a.head_dim, a.topk = 1, 4, 8, 2, 128, 4
+    a.max_seqlen_q, a.max_k_tiles = 4, 8
+    a.cu_seqlens_k = FAKE
+    a.head_dim = 64
+    assert f(ctypes.byref(a), None) == 2                  # head_dim
+    a.head_dim = 128
+    assert f(ctypes.byref(a), None) == 1                  # q, k, v, q2k ... missing
+    a.total_q = 0
+    assert f(ctypes.byref(a), None) == 0                  # nothing to check
 
 
 def test_qsa_validation():
