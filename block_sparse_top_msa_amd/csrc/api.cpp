@@ -12,6 +12,7 @@
 
 #include "../../include/msa.h"
 #include "internal.hpp"
+#include "validate.hpp"
 
 namespace {
 

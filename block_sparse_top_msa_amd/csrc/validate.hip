@@ -6,7 +6,7 @@
 // kind and, within it, the first position, whatever the thread order.
 #include <algorithm>
 
-#include "internal.hpp"
+#include "validate.hpp"
 
 namespace msa {
 
