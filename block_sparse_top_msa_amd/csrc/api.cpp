@@ -108,8 +108,6 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
                   a->page_table_width, a->max_k_tiles);
   } else {
     if (!a->cu_seqlens_k) return fail(MSA_ERR_NULL, "flat route needs cu_seqlens_k");
-    if (a->kv_dtype == MSA_KV_E2M1X2)
-      return fail(MSA_ERR_UNSUPPORTED, "packed E2M1 K/V is read from the paged layout only");
   }
   if (need_ptrs && a->kv_dtype == MSA_KV_E2M1X2 && (!a->k_scale || !a->v_scale))
     return fail(MSA_ERR_NULL, "packed E2M1 K/V needs k_scale and v_scale");
@@ -135,12 +133,16 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
       return st;
     if ((st = resolve_strides("v_scale", a->v_scale_strides, paged, a->num_kv_heads, 8, 8, &p.vs_st)))
       return st;
-    // scale rows are staged two at a time (16 bytes)
-    if (p.ks_st.token != 8 || p.vs_st.token != 8 || p.ks_st.page % 16 || p.vs_st.page % 16 ||
-        p.ks_st.head % 16 || p.vs_st.head % 16)
+    // paged: the decode kernel stages a head's scale rows two at a time (16
+    // bytes), so they must be contiguous within the page; flat scales (any
+    // (token, head) strides of 8-byte rows) are read row by row by the
+    // general kernel
+    if (paged && (p.ks_st.token != 8 || p.vs_st.token != 8 || p.ks_st.page % 16 ||
+                  p.vs_st.page % 16 ||
+                  (a->num_kv_heads > 1 && (p.ks_st.head % 16 || p.vs_st.head % 16))))
       return fail(MSA_ERR_UNSUPPORTED,
-                  "k_scale/v_scale: token rows must be contiguous (8 bytes) and page/head "
-                  "strides multiples of 16 bytes");
+                  "paged k_scale/v_scale: a head's token rows must be contiguous (8 bytes) and "
+                  "page/head strides multiples of 16 bytes");
     if (need_ptrs && (!aligned(a->k_scale, 16) || !aligned(a->v_scale, 16)))
       return fail(MSA_ERR_UNSUPPORTED, "k_scale/v_scale must be 16-byte aligned");
   }
@@ -178,7 +180,12 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   plan = msa::AttnPlan{};
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows_req = lqmax * G;
-  if (rows_req <= 64) {
+  // packed E2M1 in the flat layout goes through the general kernel at every
+  // shape: the decode kernel stages block-scale rows two at a time, which
+  // needs a head's rows contiguous and stays inside a 128-row page, but could
+  // pass the end of a flat tensor
+  const bool flat_e2m1 = !paged && a->kv_dtype == MSA_KV_E2M1X2;
+  if (rows_req <= 64 && !flat_e2m1) {
     // decode shape: one workgroup per (request, KV head, token tile, split);
     // its waves split every page's keys.  When one token's G heads fill a
     // 16-row MFMA tile, every token is a tile of its own: it streams just the

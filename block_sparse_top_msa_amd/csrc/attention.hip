@@ -247,7 +247,8 @@ __device__ __forceinline__ BlockAddr block_addr(const AttnParams& p, int b, int 
     int64_t row0 = (int64_t)p.cu_k[b] + kBlock * t;
     a.k = p.k + row0 * p.k_st.token + g * p.k_st.head;
     a.v = p.v + row0 * p.v_st.token + g * p.v_st.head;
-    a.ks = a.vs = nullptr;
+    a.ks = p.ks ? p.ks + row0 * p.ks_st.token + g * p.ks_st.head : nullptr;
+    a.vs = p.vs ? p.vs + row0 * p.vs_st.token + g * p.vs_st.head : nullptr;
   }
   return a;
 }

@@ -118,9 +118,13 @@ typedef struct {
   const void* k;          /* flat [total_k, Hkv, d'] or paged [pages, Hkv, 128, d'];
                              d' = 128 (bf16, fp16, fp8) or 64 bytes (E2M1)    */
   const void* v;          /* same layout rules as k                           */
-  const void* k_scale;    /* E2M1 only: E4M3 bytes [pages, Hkv, 128, 8], one per
-                             16 values of a row; rows contiguous (8 bytes),
-                             16-byte aligned page/head strides and base       */
+  const void* k_scale;    /* E2M1 only: E4M3 bytes, one per 16 values of a row,
+                             16-byte aligned base.  Paged [pages, Hkv, 128, 8]:
+                             a head's rows contiguous (8 bytes), page/head
+                             strides multiples of 16.  Flat [total_k, Hkv, 8]
+                             in (token, head) order or any view of 8-byte rows
+                             (strides multiples of 8); flat E2M1 runs on the
+                             general (prefill) kernel at every shape          */
   const void* v_scale;    /* E2M1 only: same, stored linearly                 */
   msa_strides_t k_strides, v_strides, k_scale_strides, v_scale_strides;
   const int32_t* q2k;     /* [Hkv, total_q, topk] block ids, ascending, -1 padded */

@@ -37,7 +37,8 @@ class Problem:
     q            (total_q, Hq, d) bf16
     k, v         flat (total_k, Hkv, d') or paged (num_pages, Hkv, 128, d');
                  d' = d for bf16 / fp8, d // 2 bytes for packed E2M1
-    k_scale, v_scale  E2M1 only: (num_pages, Hkv, 128, d // 16) uint8 E4M3 bytes
+    k_scale, v_scale  E2M1 only: (num_pages, Hkv, 128, d // 16) uint8 E4M3 bytes,
+                 flat (total_k, Hkv, d // 16) in (token, head) order
     q2k          (Hkv, total_q, topk) int32, ascending, -1 padded, or None
                  when the selection is to come from the proxy pass
     proxy_q      (total_q, Hp, d) bf16 or None (the proxy reuses q then)
@@ -350,8 +351,6 @@ def make_problem(name, *, q_lens, k_lens, num_qo_heads, num_kv_heads, head_dim=1
     else:
         cu_k = _cu(k_lens, device)
         kv_shape = (sum(k_lens), num_kv_heads, d)
-        if kv_dtype == KV_E2M1:
-            raise ValueError("packed E2M1 K/V is built for the paged layout only")
 
     qdt = torch.float16 if kv_dtype == KV_F16 else torch.bfloat16
     q = _randn_cast((total_q, num_qo_heads, d), g_dev, device, qdt)

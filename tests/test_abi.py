@@ -101,9 +101,17 @@ def test_attention_rejects_unreadable_views():
     assert st == 5 and "token stride" in msg
 
 
-def test_attention_e2m1_needs_scales_and_paging():
-    st, _ = _call(_attn(kv_dtype=2))  # flat E2M1
-    assert st == 5
+def test_attention_e2m1_needs_scales_with_contiguous_rows():
+    st, _ = _call(_attn(kv_dtype=2))  # flat E2M1 without scales
+    assert st == 1
+    # paged scales whose rows are 16 bytes apart: the decode kernel's
+    # two-row staging cannot read them
+    a = _attn(kv_dtype=2, page_table=FAKE, seqused_k=FAKE, page_table_width=4, k_scale=FAKE,
+              v_scale=FAKE)
+    a.cu_seqlens_k = None
+    a.k_scale_strides = msa.Strides(0, 0, 16)
+    st, msg = _call(a)
+    assert st == 5 and "paged k_scale/v_scale" in msg
     a = _attn(kv_dtype=2, page_table=FAKE, seqused_k=FAKE, page_table_width=4)
     a.cu_seqlens_k = None
     st, _ = _call(a)

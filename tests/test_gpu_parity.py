@@ -63,6 +63,37 @@ def test_prefill_fp8_and_scales(msa):
     assert_attention_close(out, lse, ref_out, ref_lse, "prefill fp8")
 
 
+@pytest.mark.parametrize("hkv,q_lens,k_lens,head_major", [
+    (1, [200, 64], [300, 64], False),   # one KV head
+    (2, [260, 33], [400, 34], False),   # (token, head) scale rows, Lq != Lk
+    (2, [90, 40], [129, 300], True),    # a head-major view of the scales
+])
+def test_prefill_flat_e2m1(msa, hkv, q_lens, k_lens, head_major):
+    print(f"flat E2M1 prefill Hkv {hkv} {q_lens} {k_lens} head-major {head_major}", flush=True)
+    p = synth.make_problem("prefill_e2m1_flat", q_lens=q_lens, k_lens=k_lens, num_qo_heads=8,
+                           num_kv_heads=hkv, topk=3, kv_dtype=synth.KV_E2M1, seed=9 + hkv,
+                           selection="general", k_global_scale=0.5, v_global_scale=2.0)
+    if head_major:
+        hm = lambda t: t.permute(1, 0, 2).contiguous().permute(1, 0, 2)
+        p.k_scale, p.v_scale = hm(p.k_scale), hm(p.v_scale)
+        assert p.k_scale.stride() == (8, 8 * sum(k_lens), 1)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "prefill flat e2m1")
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+def test_decode_flat_e2m1(msa, splits):
+    print(f"flat E2M1 decode splits {splits}", flush=True)
+    p = synth.make_problem("decode_e2m1_flat", q_lens=[1, 1, 1, 1], k_lens=[2000, 129, 700, 3001],
+                           num_qo_heads=16, num_kv_heads=2, topk=6, kv_dtype=synth.KV_E2M1,
+                           seed=31 + splits, selection="decode", k_global_scale=0.5,
+                           v_global_scale=2.0)
+    out, lse = gpu_attention(msa, _dev(p), splits=splits)
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "decode flat e2m1")
+
+
 def test_prefill_without_lse_and_diagonal_selection(msa):
     p = synth.make_problem("prefill_diag", q_lens=[640], k_lens=[640], num_qo_heads=8,
                            num_kv_heads=1, topk=4, seed=8, selection="diagonal")
