@@ -13,7 +13,9 @@ The decode workloads (--workload paged_decode_...) report KV GB/s over the
 K/V blocks actually gathered, timed cold: a 1 GiB read evicts L2 and MALL
 before every step, outside the timed events.  --workload
 qsa_indexed_1x8192_h12kv1_d256_w2048 times the QSA indexed forward,
-qsa_bitmap_1x8192_h12kv1_d256_causal_q25 the QSA bitmap forward.
+qsa_bitmap_1x8192_h12kv1_d256_causal_q25 the QSA bitmap forward.  --graph
+(decode workloads) adds the same step replayed as one HIP graph
+(graph_ms_per_step).
 
 Per-stage times come from HIP events recorded on the stream the kernels run
 on.  One JSON line is printed.
@@ -42,6 +44,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: also time the whole step replayed as one HIP graph")
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run plain copies of BYTES bytes (profiler counter scaling)")
@@ -217,6 +221,25 @@ def bench_prefill_pipeline(args, msa, synth, torch):
     return res, p
 
 
+def _graph_decode_ms(args, p, scrub32, sink, torch):
+    """The same cold decode step (proxy and top-K included when the workload
+    has them) captured once and replayed as one HIP graph: ms per step."""
+    from block_sparse_top_msa_amd.graph import DecodeGraph
+    g = DecodeGraph(p.q, p.k, p.v, p.cu_seqlens_q, max_seqlen_q=max(p.q_lens),
+                    max_k_tiles=p.max_k_tiles, topk=p.topk, page_table=p.page_table,
+                    seqused_k=p.seqused_k, q2k=p.q2k, reduce_heads=p.reduce_heads,
+                    k_scale=p.k_scale, v_scale=p.v_scale, k_global_scale=p.k_global_scale,
+                    v_global_scale=p.v_global_scale, warmup=max(1, args.warmup))
+    evs = [_events(2) for _ in range(args.steps)]
+    for k in range(args.steps):
+        torch.sum(scrub32, dim=0, out=sink)
+        evs[k][0].record()
+        g.replay()
+        evs[k][1].record()
+    torch.cuda.synchronize()
+    return round(sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps, 4)
+
+
 def bench_decode(args, msa, synth, torch):
     from block_sparse_top_msa_amd import accounting
     p = synth.workload(args.workload, device="cuda")
@@ -283,6 +306,8 @@ def bench_decode(args, msa, synth, torch):
                        "sparse_attention": round(st[2], 4)} if pipeline
                       else {"sparse_attention": round(st[2], 4)}),
         "work": {"kv_bytes": nbytes},
+        **({"graph_ms_per_step": _graph_decode_ms(args, p, scrub32, sink, torch)}
+           if args.graph else {}),
         "roofline": {"kernel": "msa_decode_kernel", "bound": "hbm",
                      "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -414,7 +439,7 @@ def main():
         "dtype": res["dtype"], "data": "synthetic (seeded, generated on the GPU)",
         "config": res["config"],
     }
-    for k in ("tokens_per_s", "stages_ms", "work"):
+    for k in ("tokens_per_s", "stages_ms", "graph_ms_per_step", "work"):
         if k in res:
             line[k] = res[k]
     line["roofline"] = res["roofline"]

@@ -1,0 +1,70 @@
+"""Decode steps captured as one HIP graph (block_sparse_top_msa_amd.graph):
+every replay equals the eager step on the same inputs, bit for bit, with the
+program's own eager work and synchronisations between replays and new
+queries written into the bound tensors in place."""
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def msa():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import block_sparse_top_msa_amd as m
+    return m
+
+
+def _graph(msa, p, **kw):
+    from block_sparse_top_msa_amd.graph import DecodeGraph
+    return DecodeGraph(p.q, p.k, p.v, p.cu_seqlens_q, max_seqlen_q=max(p.q_lens),
+                       max_k_tiles=p.max_k_tiles, topk=p.topk, page_table=p.page_table,
+                       seqused_k=p.seqused_k, cu_seqlens_k=p.cu_seqlens_k, k_scale=p.k_scale,
+                       v_scale=p.v_scale, k_global_scale=p.k_global_scale,
+                       v_global_scale=p.v_global_scale, **kw)
+
+
+def _replays_match_eager(g, q_new, rounds=3):
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    for r in range(rounds):
+        # next step's queries, written in place; eager work and a sync between
+        g.q.copy_(torch.randn(g.q.shape, generator=gen, device="cuda").to(g.q.dtype)
+                  if q_new else g.q)
+        torch.cuda.synchronize()
+        out, lse = g.replay()
+        got_out, got_lse = out.clone(), lse.clone()
+        got_q2k = g.q2k.clone()
+        torch.cuda.synchronize()
+        ref_out, ref_lse = g.step()
+        torch.cuda.synchronize()
+        assert torch.equal(got_q2k, g.q2k), f"replay {r}: q2k"
+        assert torch.equal(got_out, ref_out), f"replay {r}: out"
+        assert torch.equal(got_lse, ref_lse), f"replay {r}: lse"
+
+
+def test_fp8_mtp_pipeline_graph(msa):
+    # proxy (fp8 K, reduce_heads) -> top-K -> attention, 4 tokens per request
+    print("graph: fp8 MTP pipeline", flush=True)
+    p = synth.make_problem("graph_mtp", q_lens=[4] * 5, k_lens=[9000, 130, 4000, 20000, 700],
+                           num_qo_heads=32, num_kv_heads=2, topk=16, paged=True,
+                           kv_dtype=synth.KV_FP8, seed=51, selection="proxy",
+                           reduce_heads=True).to("cuda")
+    g = _graph(msa, p, reduce_heads=True)
+    _replays_match_eager(g, q_new=True)
+
+
+@pytest.mark.parametrize("fmt,splits", [(synth.KV_BF16, 0), (synth.KV_E2M1, 3)])
+def test_decode_graph_with_given_selection(msa, fmt, splits):
+    print(f"graph: decode {fmt} splits {splits}", flush=True)
+    kw = dict(k_global_scale=0.5, v_global_scale=2.0) if fmt == synth.KV_E2M1 else {}
+    p = synth.make_problem("graph_dec", q_lens=[1] * 6, k_lens=[3000, 129, 7000, 900, 5000, 64],
+                           num_qo_heads=16, num_kv_heads=1 if fmt == synth.KV_E2M1 else 2,
+                           topk=8, paged=True, kv_dtype=fmt, seed=52, selection="decode",
+                           **kw).to("cuda")
+    g = _graph(msa, p, q2k=p.q2k, splits=splits)
+    if splits > 1:
+        assert g.workspace is not None          # split partials bound before capture
+    _replays_match_eager(g, q_new=True)
