@@ -503,7 +503,9 @@ static msa_status_t qsa_forward(const msa_qsa_args_t* a, bool bitmap, void* stre
   if (bitmap && (a->num_kv_tokens < 0 || a->num_kv_tokens > INT32_MAX - 4))
     return fail(MSA_ERR_SHAPE, "num_kv_tokens out of range (got %d)", a->num_kv_tokens);
   if (a->total_q == 0) return ok();
-  if (!a->q || !a->k || !a->v || !a->out || (bitmap ? !a->bitmap : !a->indices))
+  // a bitmap over no KV tokens selects nothing: k, v and bitmap are never read
+  const bool no_kv = bitmap && a->num_kv_tokens == 0;
+  if (!a->q || !a->out || (!no_kv && (!a->k || !a->v || (bitmap ? !a->bitmap : !a->indices))))
     return fail(MSA_ERR_NULL, "q, k, v, %s and out must be non-NULL", bitmap ? "bitmap" : "indices");
   const int64_t row = 256 * 2;
   const int64_t kt = a->k_strides.token ? a->k_strides.token : row * a->num_kv_heads;

@@ -287,7 +287,8 @@ typedef struct {
  * natural-log normaliser; a query with no listed key gets zero output and
  * -inf LSE (qsa page: the indexed API, outputs and LSE, empty selections).
  * Causality is the caller's, carried by the indices.  Index values are a
- * caller contract (distinct, < Tk), not validated on the device.  Host-side
+ * caller contract (distinct, < Tk), not validated on the device; k and v
+ * must hold at least one row (-1 padding entries read row 0, with weight 0).  Host-side
  * checks return MSA_ERR_SHAPE / MSA_ERR_NULL / MSA_ERR_UNSUPPORTED (head_dim
  * != 256, Hq / Hkv > 16, misaligned pointers) before any launch.  Every
  * (query, head) is computed in index order by one wave: results are bitwise
@@ -301,7 +302,8 @@ msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* args, void* stream);
  * tokens per step, so nothing is allocated and no index scratch is written;
  * width and indices are ignored, any number of blocks may be selected.
  * Host-side checks as for the indexed entry point, plus bitmap non-NULL
- * (when T > 0) and 0 <= Tk < 2^31 - 4 (MSA_ERR_SHAPE). */
+ * (when T > 0 and Tk > 0; with Tk == 0 nothing is selected and k, v and
+ * bitmap may be NULL) and 0 <= Tk < 2^31 - 4 (MSA_ERR_SHAPE). */
 msa_status_t msa_qsa_bitmap_forward(const msa_qsa_args_t* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

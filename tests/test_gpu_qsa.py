@@ -143,3 +143,14 @@ def test_qsa_bitmap_full_size_sampled_rows(msa):
     ref_out, ref_lse = oracle.qsa_bitmap_attention(p.q[rows], p.k, p.v, p.bitmap[rows])
     assert float((out.float().cpu().double()[rows] - ref_out).abs().max()) <= 2e-2
     assert float((lse.cpu().double()[:, rows] - ref_lse).abs().max()) <= 1e-3
+
+
+def test_qsa_bitmap_without_kv_tokens(msa):
+    # Tk = 0: every query is empty (0 output, -inf LSE); nothing is read
+    p = synth.make_qsa_problem("qsa_nokv", [5], 12, 1, 4, seed=2)
+    q = p.q.cuda()
+    k = torch.empty(0, 1, 256, dtype=torch.bfloat16, device="cuda")
+    bm = torch.empty(5, 0, dtype=torch.uint8, device="cuda")
+    out, out_f32, lse = msa.qsa_bitmap_forward(q, k, k, bm)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all() and (out_f32 == 0).all() and torch.isneginf(lse).all()
