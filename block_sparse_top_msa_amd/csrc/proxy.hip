@@ -414,8 +414,30 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   __shared__ int64_t kbase[kWideMaxBpw];
 
   const int n = p.batch * p.hkv * p.row_tiles * p.block_chunks;
-  const int lid = xcd_remap(blockIdx.x, n);
-  if (lid < 0) return;
+  int lid;
+  if (p.causal && (p.row_tiles & 1) == 0 && n % 512 == 0) {
+    // Passes of two workgroups per CU (256 CUs): within each run of 512,
+    // blockIdx b and b + 256 land on the same CU (XCD b % 8, CU (b / 8) %
+    // 32).  Under the causal mask row tile rt sees about 2 rt + 2 blocks, so
+    // (rt, chunk c) and its reflection (R - 1 - rt, C - 1 - c) together hold
+    // an almost constant amount of work: give them the same CU.
+    const int b2 = blockIdx.x;
+    if (b2 >= n) return;
+    const int half_rt = p.row_tiles / 2;
+    // representative (b, g, rt < R / 2, c)
+    const int k = (b2 / 512) * 256 + b2 % 256;
+    const int c = k % p.block_chunks;
+    int r2 = k / p.block_chunks;
+    const int rtr = r2 % half_rt;
+    const int bg = r2 / half_rt;
+    const bool mirror = b2 % 512 >= 256;
+    const int rt_sel = mirror ? p.row_tiles - 1 - rtr : rtr;
+    const int c_sel = mirror ? p.block_chunks - 1 - c : c;
+    lid = (bg * p.row_tiles + rt_sel) * p.block_chunks + c_sel;
+  } else {
+    lid = xcd_remap(blockIdx.x, n);
+    if (lid < 0) return;
+  }
   const int chunk = lid % p.block_chunks;
   int rest = lid / p.block_chunks;
   const int rt = rest % p.row_tiles;
