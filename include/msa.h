@@ -288,11 +288,11 @@ typedef struct {
  * -inf LSE (qsa page: the indexed API, outputs and LSE, empty selections).
  * Causality is the caller's, carried by the indices.  Index values are a
  * caller contract (distinct, < Tk), not validated on the device; k and v
- * must hold at least one row (-1 padding entries read row 0, with weight 0).  Host-side
- * checks return MSA_ERR_SHAPE / MSA_ERR_NULL / MSA_ERR_UNSUPPORTED (head_dim
- * != 256, Hq / Hkv > 16, misaligned pointers) before any launch.  Every
- * (query, head) is computed in index order by one wave: results are bitwise
- * repeatable. */
+ * must hold at least one row (-1 padding entries read row 0, with weight
+ * 0).  Host-side checks return MSA_ERR_SHAPE / MSA_ERR_NULL /
+ * MSA_ERR_UNSUPPORTED (head_dim != 256, Hq / Hkv > 16, misaligned pointers)
+ * before any launch.  Every (query, head) is computed in index order by one
+ * wave: results are bitwise repeatable. */
 msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* args, void* stream);
 
 /* The same attention with the key set of query i given by row i of a block
