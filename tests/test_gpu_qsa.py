@@ -36,6 +36,8 @@ def _check(p, out, out_f32, lse, what, rows=None):
     ([70], 24, 2, 64, "causal"),          # 24/2: two KV heads, the page's pattern
     ([9, 3, 20], 12, 1, 2052, "random"),  # the widest rows, mostly padding
     ([33], 16, 2, 36, "random"),          # G = 8, width not a multiple of 32
+    ([45, 20], 16, 1, 96, "random"),      # G = 16: every row of the MFMA tile live
+    ([50], 16, 4, 64, "causal"),          # G = 4, four KV heads
 ])
 def test_qsa_indexed_matches_oracle(msa, lens, hq, hkv, width, mode):
     print(f"qsa {lens} Hq {hq} Hkv {hkv} W {width} {mode}", flush=True)
@@ -88,6 +90,7 @@ def _bitmap_rows(p):
     ([300], 24, 2, 0.4, "causal"),        # 75 blocks: two 64-block scan windows
     ([1000], 12, 1, 0.02, "random"),      # few blocks spread over 250: long empty scans
     ([9, 3, 20], 16, 2, 1.0, "random"),   # every block: the dense map
+    ([130], 32, 2, 0.3, "causal"),        # G = 16
 ])
 def test_qsa_bitmap_matches_oracle(msa, lens, hq, hkv, density, mode):
     print(f"qsa bitmap {lens} Hq {hq} Hkv {hkv} density {density} {mode}", flush=True)
