@@ -400,7 +400,8 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
                      page_table=None, seqused_k=None, causal=False,
                      softmax_scale=None, kv_format="bf16", k_scale=None,
                      v_scale=None, k_global_scale=None, v_global_scale=None,
-                     rows: Optional[Sequence[int]] = None, chunk: int = 256):
+                     rows: Optional[Sequence[int]] = None, chunk: int = 256,
+                     lse_temperature_scale: Optional[float] = None):
     """Dense attention masked down to each query's selected blocks.
 
     For query i of request b, query head h and its KV head g = h // G
@@ -419,6 +420,13 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
 
     Returns float64 (out [n, Hq, d], lse [n, Hq]) for all rows, or for
     `rows` in the given order.
+
+    With `lse_temperature_scale` = tau also returns the temperature LSE
+    lse_t [n, Hq] = ln sum_j exp(tau * z_j) over the same keys (-inf when A
+    is empty).  Reading: the msa_sparse_attention page (Parameters:
+    return_temperature_lse, lse_temperature_scale) says only that the scale
+    multiplies the exponent; z_j are the logits whose LSE is lse, so tau = 1
+    gives lse_t = lse.
     """
     q = q.cpu()
     q2k = torch.as_tensor(q2k).cpu()
@@ -434,6 +442,8 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
     where = {r: n for n, r in enumerate(row_list)}
     out = torch.zeros((len(row_list), hq, d), dtype=torch.float64)
     lse = torch.full((len(row_list), hq), float("-inf"), dtype=torch.float64)
+    tau = None if lse_temperature_scale is None else float(lse_temperature_scale)
+    lse_t = torch.full((len(row_list), hq), float("-inf"), dtype=torch.float64)
 
     for b, (q0, lq, lk) in enumerate(reqs):
         local = [iq for iq in range(lq) if (q0 + iq) in where]
@@ -468,7 +478,13 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
                     o_h = torch.where(any_ok.unsqueeze(1), o_h, torch.zeros_like(o_h))
                     out[dst, h] = o_h
                     lse[dst, h] = l_h
-    return out, lse
+                    if tau is not None:
+                        zt = torch.where(ok, tau * z, torch.full_like(z, float("-inf")))
+                        mt = zt.max(dim=1, keepdim=True).values
+                        mt = torch.where(torch.isfinite(mt), mt, torch.zeros_like(mt))
+                        lt = (mt + torch.log(torch.exp(zt - mt).sum(dim=1, keepdim=True))).squeeze(1)
+                        lse_t[dst, h] = torch.where(any_ok, lt, torch.full_like(lt, float("-inf")))
+    return (out, lse) if tau is None else (out, lse, lse_t)
 
 
 # ---------------------------------------------------------------------------

@@ -311,6 +311,47 @@ def test_full_selection_equals_dense_sdpa(causal):
         k0 += Lk
 
 
+@pytest.mark.parametrize("tau", [0.5, 2.0])
+def test_temperature_lse_full_selection_equals_scaled_logsumexp(tau):
+    # every valid block selected: lse_t = logsumexp(tau * z) of the dense
+    # masked logits, computed here without the oracle
+    q_lens, k_lens = [70, 33], [300, 33]
+    hq, hkv, d = 4, 2, 32
+    p = synth.make_problem("t", q_lens=q_lens, k_lens=k_lens, num_qo_heads=hq,
+                           num_kv_heads=hkv, head_dim=d, seed=8, selection="proxy")
+    q2k = _all_blocks_q2k(q_lens, k_lens, hkv, True)
+    out, lse, lse_t = oracle.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q,
+                                              cu_seqlens_k=p.cu_seqlens_k, causal=True,
+                                              softmax_scale=0.3, k_global_scale=0.5,
+                                              lse_temperature_scale=tau)
+    q0 = k0 = 0
+    for Lq, Lk in zip(q_lens, k_lens):
+        qq = p.q[q0:q0 + Lq].to(torch.float64).transpose(0, 1)
+        kk = p.k[k0:k0 + Lk].to(torch.float64).repeat_interleave(hq // hkv, 1).transpose(0, 1)
+        mask = torch.arange(Lk).view(1, -1) <= Lk - Lq + torch.arange(Lq).view(-1, 1)
+        logits = (qq @ kk.transpose(1, 2)) * (0.3 * 0.5)
+        ref = torch.logsumexp((tau * logits).masked_fill(~mask, float("-inf")), dim=-1)
+        assert torch.allclose(lse_t[q0:q0 + Lq].T, ref, atol=1e-12, rtol=1e-12)
+        q0 += Lq
+        k0 += Lk
+    # tau = 1 is the plain LSE; a single key gives tau * z_j; no key gives -inf
+    _, lse1, lse_t1 = oracle.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q,
+                                              cu_seqlens_k=p.cu_seqlens_k, causal=True,
+                                              lse_temperature_scale=1.0)
+    assert torch.allclose(lse1, lse_t1, atol=1e-12, rtol=0)
+    one = synth.make_problem("t", q_lens=[1], k_lens=[1], num_qo_heads=2, num_kv_heads=1,
+                             head_dim=16, seed=3, selection="proxy")
+    q2k1 = torch.tensor([[[0]]], dtype=torch.int32)
+    _, l1, lt1 = oracle.sparse_attention(one.q, one.k, one.v, q2k1, one.cu_seqlens_q,
+                                         cu_seqlens_k=one.cu_seqlens_k, causal=True,
+                                         lse_temperature_scale=tau)
+    assert torch.allclose(lt1, tau * l1, atol=1e-12, rtol=0)
+    _, _, lt0 = oracle.sparse_attention(one.q, one.k, one.v, -torch.ones_like(q2k1),
+                                        one.cu_seqlens_q, cu_seqlens_k=one.cu_seqlens_k,
+                                        causal=True, lse_temperature_scale=tau)
+    assert torch.isneginf(lt0).all()
+
+
 def test_empty_selection_gives_zero_and_neg_inf():
     p = synth.make_problem("t", q_lens=[40], k_lens=[500], num_qo_heads=2,
                            num_kv_heads=1, head_dim=16, seed=1, selection="general")
