@@ -78,6 +78,7 @@ class AttnArgs(ctypes.Structure):
         ("q2k", _I32P), ("cu_seqlens_q", _I32P), ("cu_seqlens_k", _I32P),
         ("page_table", _I32P), ("seqused_k", _I32P),
         ("out", _P), ("lse", _P),
+        ("lse_t", _P), ("lse_temperature_scale", ctypes.c_float),
     ]
 
 
@@ -288,8 +289,11 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
                      return_softmax_lse=False, k_scale=None, v_scale=None,
                      k_global_scale=None, v_global_scale=None, *, max_seqlen_q=None,
                      max_k_tiles=None, workspace: Optional[Workspace] = None, out=None,
-                     lse=None, splits=0):
-    """MSA forward (msa_sparse_attention page).  Returns out, or (out, lse)."""
+                     lse=None, splits=0, return_temperature_lse=False,
+                     lse_temperature_scale=1.0, lse_t=None):
+    """MSA forward (msa_sparse_attention page).  Returns out, or (out, lse),
+    or with return_temperature_lse (out, lse, lse_t), lse_t = ln sum_j
+    exp(lse_temperature_scale * z_j) over the attended keys."""
     want = torch.float16 if k.dtype == torch.float16 else torch.bfloat16
     if q.dtype != want or not q.is_contiguous():
         raise ValueError(f"q must be a contiguous {want} tensor (total_q, num_qo_heads, 128) "
@@ -300,11 +304,16 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
         _check_i32(name, t)
     if out is None:
         out = torch.empty_like(q)
-    if lse is None and return_softmax_lse:
+    if lse is None and (return_softmax_lse or return_temperature_lse):
         lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    if return_temperature_lse and lse_t is None:
+        lse_t = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
     a = _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, causal, softmax_scale,
                    page_table, seqused_k, k_scale, v_scale, k_global_scale, v_global_scale,
                    max_seqlen_q, max_k_tiles, out, lse, splits)
+    if return_temperature_lse:
+        a.lse_t = _ptr(lse_t)
+        a.lse_temperature_scale = float(lse_temperature_scale)
     need = ctypes.c_size_t(0)
     _check(lib.msa_sparse_attention_workspace_size(ctypes.byref(a), ctypes.byref(need)))
     ws_ptr, ws_bytes = None, 0
@@ -319,6 +328,8 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
             raise MsaError(6, f"workspace of {need.value} bytes needed, got {workspace.nbytes}")
         ws_ptr, ws_bytes = _ptr(workspace.view), workspace.nbytes
     _check(lib.msa_sparse_attention(ctypes.byref(a), ws_ptr, ws_bytes, _stream()))
+    if return_temperature_lse:
+        return out, lse, lse_t
     return (out, lse) if return_softmax_lse else out
 
 

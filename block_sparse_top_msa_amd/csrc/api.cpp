@@ -12,6 +12,7 @@
 
 #include "../../include/msa.h"
 #include "internal.hpp"
+#include "temperature.hpp"
 #include "validate.hpp"
 
 namespace {
@@ -185,7 +186,14 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   // needs a head's rows contiguous and stays inside a 128-row page, but could
   // pass the end of a flat tensor
   const bool flat_e2m1 = !paged && a->kv_dtype == MSA_KV_E2M1X2;
-  if (rows_req <= 64 && !flat_e2m1) {
+  // the temperature LSE is accumulated by the general kernel only
+  const bool temp = a->lse_t != nullptr;
+  if (temp && !(a->lse_temperature_scale > 0.f))
+    return fail(MSA_ERR_UNSUPPORTED, "lse_temperature_scale must be > 0 (got %g)",
+                (double)a->lse_temperature_scale);
+  if (temp && a->kv_dtype == MSA_KV_F16)
+    return fail(MSA_ERR_UNSUPPORTED, "the temperature LSE is computed for bf16 / fp8 / E2M1 K/V");
+  if (rows_req <= 64 && !flat_e2m1 && !temp) {
     // decode shape: one workgroup per (request, KV head, token tile, split);
     // its waves split every page's keys.  When one token's G heads fill a
     // 16-row MFMA tile, every token is a tile of its own: it streams just the
@@ -211,7 +219,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     plan.splits = std::max(1, std::min(splits, 64));
   } else {
     plan.decode = 0;
-    plan.async_bf16 = (a->kv_dtype == MSA_KV_BF16 || a->kv_dtype == MSA_KV_F16);
+    plan.async_bf16 = (a->kv_dtype == MSA_KV_BF16 || a->kv_dtype == MSA_KV_F16) && !temp;
     // bf16: 4 waves x spw slots x 32 rows per tile; other formats: 4 x 2 x 16
     int rows;
     if (plan.async_bf16) {
@@ -354,6 +362,11 @@ msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
     r.p.ws_o = reinterpret_cast<float*>(base + l_bytes);
   }
   if (args->total_q == 0 || args->batch == 0) return ok();
+  if (args->lse_t)
+    return hip_status(msa::launch_attention_temperature(r.p, args->kv_dtype, args->lse_t,
+                                                        args->lse_temperature_scale,
+                                                        static_cast<hipStream_t>(stream)),
+                      "msa_sparse_attention launch (temperature LSE)");
   return hip_status(msa::launch_attention(r.p, args->kv_dtype, r.plan,
                                           static_cast<hipStream_t>(stream)),
                     "msa_sparse_attention launch");

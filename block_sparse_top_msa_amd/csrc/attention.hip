@@ -16,6 +16,7 @@
 // registers as the B operand.
 #include "common.hpp"
 #include "internal.hpp"
+#include "temperature.hpp"
 #include "tile_union.hpp"
 
 namespace msa {
@@ -256,8 +257,11 @@ __device__ __forceinline__ BlockAddr block_addr(const AttnParams& p, int b, int 
 // ---------------------------------------------------------------------------
 // The kernel.
 // ---------------------------------------------------------------------------
+// lse_t (nullable): also the temperature LSE, ln sum_j exp(tau * z_j) over
+// the same keys, accumulated against the row's running max (tau > 0).
 template <int NW, int SPW, int FMT>
-__global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p, float* lse_t,
+                                                                   float tau) {
   constexpr int NT = NW * kWave;
   constexpr int NKT = kBlock / 16;      // 16-key S^T subtiles
   constexpr int NKS = kBlock / 32;      // 32-key PV steps
@@ -322,12 +326,13 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
     }
   }
 
-  float m_[SPW], l_[SPW];
+  float m_[SPW], l_[SPW], lt_[SPW];
   f32x4 o_[SPW][8];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     m_[s] = -INFINITY;
     l_[s] = 0.f;
+    lt_[s] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o_[s][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -383,12 +388,14 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
       const float m_new = fmaxf(m_[s], mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_[s] - m_use);
-      float sum = 0.f;
+      float sum = 0.f, sum_t = 0.f;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float e = __builtin_amdgcn_exp2f(acc[kt][r] - m_use);
+          const float xv = acc[kt][r];
+          if (lse_t) sum_t += __builtin_amdgcn_exp2f(tau * (xv - m_use));
+          float e = __builtin_amdgcn_exp2f(xv - m_use);
           acc[kt][r] = e;
           sum += e;
         }
@@ -396,6 +403,11 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
       sum = xor_sum(sum, 16);
       sum = xor_sum(sum, 32);
       l_[s] = l_[s] * alpha + sum;
+      if (lse_t) {
+        sum_t = xor_sum(sum_t, 16);
+        sum_t = xor_sum(sum_t, 32);
+        lt_[s] = lt_[s] * __builtin_amdgcn_exp2f(tau * (m_[s] - m_use)) + sum_t;
+      }
       m_[s] = m_new;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) o_[s][dt] *= alpha;
@@ -439,16 +451,19 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p)
     }
     if (p.lse && lg == 0)
       p.lse[row] = l_[s] > 0.f ? (m_[s] + __log2f(l_[s])) * kLn2 : -INFINITY;
+    if (lse_t && lg == 0)
+      lse_t[row] = l_[s] > 0.f ? (tau * m_[s] + __log2f(lt_[s])) * kLn2 : -INFINITY;
   }
 }
 
 template <int NW, int SPW, int FMT>
-static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
+static hipError_t launch_one(const AttnParams& p, hipStream_t stream, float* lse_t = nullptr,
+                             float tau = 1.f) {
   const int n = p.batch * p.hkv * p.tiles_per_req;
   if (n <= 0) return hipSuccess;
   const int grid = 8 * ((n + 7) / 8);
   hipLaunchKernelGGL((msa_attention_kernel<NW, SPW, FMT>), dim3(grid), dim3(NW * kWave), 0, stream,
-                     p);
+                     p, lse_t, tau);
   return hipGetLastError();
 }
 
@@ -464,6 +479,16 @@ hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
     case kFmtFp8: return launch_one<4, 2, kFmtFp8>(p, stream);
     default: return launch_one<4, 2, kFmtE2m1>(p, stream);
   }
+}
+
+hipError_t launch_attention_temperature(const AttnParams& p, int fmt, float* lse_t, float tau,
+                                        hipStream_t stream) {
+  switch (fmt) {
+    case kFmtBf16: return launch_one<4, 2, kFmtBf16>(p, stream, lse_t, tau);
+    case kFmtFp8: return launch_one<4, 2, kFmtFp8>(p, stream, lse_t, tau);
+    case kFmtE2m1: return launch_one<4, 2, kFmtE2m1>(p, stream, lse_t, tau);
+  }
+  return hipErrorInvalidValue;
 }
 
 // ---------------------------------------------------------------------------

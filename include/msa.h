@@ -136,6 +136,14 @@ typedef struct {
                              MSA_KV_F16)                                      */
   float* lse;             /* NULL or fp32 [total_q, Hq], natural log, written;
                              -inf for a row with no attended key (out = 0)    */
+  float* lse_t;           /* NULL or fp32 [total_q, Hq]: the temperature LSE
+                             ln sum_j exp(lse_temperature_scale * z_j) over the
+                             attended keys (z_j the logits of lse), -inf for an
+                             empty row (msa_sparse_attention page, Parameters:
+                             return_temperature_lse, lse_temperature_scale).
+                             Computed by the general kernel at every shape;
+                             bf16 / fp8 / E2M1 K/V; else MSA_ERR_UNSUPPORTED  */
+  float lse_temperature_scale; /* > 0 when lse_t is set (1 gives lse)        */
 } msa_attn_args_t;
 
 /* Bytes of workspace msa_sparse_attention needs for these arguments: the

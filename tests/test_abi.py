@@ -120,6 +120,17 @@ def test_attention_e2m1_needs_scales_with_contiguous_rows():
     assert st == 5
 
 
+def test_temperature_lse_needs_positive_scale_and_a_supported_format():
+    st, msg = _call(_attn(lse_t=FAKE, lse_temperature_scale=0.0))
+    assert st == 5 and "lse_temperature_scale" in msg
+    st, msg = _call(_attn(lse_t=FAKE, lse_temperature_scale=1.0, kv_dtype=3))
+    assert st == 5 and "temperature" in msg
+    # the temperature route never splits: no workspace for a decode shape
+    a = _attn(lse_t=FAKE, lse_temperature_scale=2.0, total_q=2, max_seqlen_q=1,
+              max_k_tiles=512, splits=4)
+    assert _size(a) == (0, 0)
+
+
 def test_workspace_sizing_and_enforcement():
     # decode shape (1 query x 16 heads per KV head): splits > 1 need a workspace
     a = _attn(num_qo_heads=32, num_kv_heads=2, total_q=4, batch=4, max_seqlen_q=1,

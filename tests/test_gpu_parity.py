@@ -94,6 +94,44 @@ def test_decode_flat_e2m1(msa, splits):
     assert_attention_close(out, lse, ref_out, ref_lse, "decode flat e2m1")
 
 
+TEMPERATURE_CASES = [
+    # q_lens, k_lens, Hq, Hkv, paged, fmt, tau, selection
+    ([300, 77], [300, 500], 16, 2, False, synth.KV_BF16, 0.5, "general"),
+    ([260, 33], [400, 33], 8, 2, False, synth.KV_FP8, 2.0, "general"),
+    ([1, 1, 1], [2000, 129, 700], 16, 2, True, synth.KV_BF16, 1.5, "decode"),
+    ([1, 1], [3000, 900], 16, 1, True, synth.KV_E2M1, 0.7, "decode"),
+    ([4, 4], [2500, 600], 32, 2, True, synth.KV_FP8, 1.0, "decode"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TEMPERATURE_CASES)))
+def test_temperature_lse_matches_oracle(msa, case):
+    ql, kl, hq, hkv, paged, fmt, tau, selection = TEMPERATURE_CASES[case]
+    print(f"temperature LSE case {case}", flush=True)
+    kw = dict(k_global_scale=0.5, v_global_scale=2.0) if fmt == synth.KV_E2M1 else {}
+    p = synth.make_problem("temp", q_lens=ql, k_lens=kl, num_qo_heads=hq, num_kv_heads=hkv,
+                           topk=6, paged=paged, kv_dtype=fmt, seed=60 + case,
+                           selection=selection, **kw)
+    d = _dev(p)
+    out, lse, lse_t = msa.sparse_attention(
+        d.q, d.k, d.v, d.q2k, d.cu_seqlens_q, d.cu_seqlens_k, causal=p.causal,
+        page_table=d.page_table, seqused_k=d.seqused_k, k_scale=d.k_scale, v_scale=d.v_scale,
+        k_global_scale=p.k_global_scale, v_global_scale=p.v_global_scale,
+        max_seqlen_q=max(ql), max_k_tiles=p.max_k_tiles, return_temperature_lse=True,
+        lse_temperature_scale=tau)
+    torch.cuda.synchronize()
+    ref_out, ref_lse, ref_lt = oracle.sparse_attention(
+        p.q, p.k, p.v, p.q2k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k,
+        page_table=p.page_table, seqused_k=p.seqused_k, causal=p.causal, kv_format=fmt,
+        k_scale=p.k_scale, v_scale=p.v_scale, k_global_scale=p.k_global_scale,
+        v_global_scale=p.v_global_scale, lse_temperature_scale=tau)
+    assert_attention_close(out, lse, ref_out, ref_lse, f"temperature case {case}")
+    lt = lse_t.cpu().double()
+    fin = torch.isfinite(ref_lt)
+    assert torch.equal(torch.isfinite(lt), fin)
+    assert float((lt[fin] - ref_lt[fin]).abs().max()) <= 1e-3 * max(1.0, tau)
+
+
 def test_prefill_without_lse_and_diagonal_selection(msa):
     p = synth.make_problem("prefill_diag", q_lens=[640], k_lens=[640], num_qo_heads=8,
                            num_kv_heads=1, topk=4, seed=8, selection="diagonal")
