@@ -15,7 +15,8 @@ before every step, outside the timed events.  --workload
 qsa_indexed_1x8192_h12kv1_d256_w2048 times the QSA indexed forward,
 qsa_bitmap_1x8192_h12kv1_d256_causal_q25 the QSA bitmap forward.  --graph
 (decode workloads) adds the same step replayed as one HIP graph
-(graph_ms_per_step).
+(graph_ms_per_step); --temperature-lse TAU (prefill workloads) also returns
+the temperature LSE, which runs the attention on the general kernel.
 
 Per-stage times come from HIP events recorded on the stream the kernels run
 on.  One JSON line is printed.
@@ -44,6 +45,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--temperature-lse", type=float, default=None, metavar="TAU",
+                    help="prefill workloads: also return the temperature LSE with this scale "
+                         "(the attention then runs on the general kernel)")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also time the whole step replayed as one HIP graph")
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
@@ -169,6 +173,8 @@ def bench_prefill_pipeline(args, msa, synth, torch):
     q2k = torch.empty(p.num_kv_heads, p.total_q, p.topk, dtype=torch.int32, device="cuda")
     out = torch.empty_like(p.q)
     lse = torch.empty(p.total_q, p.num_qo_heads, dtype=torch.float32, device="cuda")
+    temp = args.temperature_lse is not None
+    lse_t = torch.empty_like(lse) if temp else None
 
     def step(ev=None):
         if ev: ev[0].record()
@@ -179,7 +185,8 @@ def bench_prefill_pipeline(args, msa, synth, torch):
         if ev: ev[2].record()
         msa.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q, p.cu_seqlens_k, causal=True,
                              return_softmax_lse=True, max_seqlen_q=mq, max_k_tiles=T,
-                             out=out, lse=lse)
+                             out=out, lse=lse, return_temperature_lse=temp,
+                             lse_temperature_scale=args.temperature_lse or 1.0, lse_t=lse_t)
         if ev: ev[3].record()
 
     for _ in range(args.warmup):
@@ -208,15 +215,17 @@ def bench_prefill_pipeline(args, msa, synth, torch):
         "dtype": "bf16",
         "config": {"workload": p.name, "batch": B, "seq_len": mq, "num_qo_heads": p.num_qo_heads,
                    "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "topk": p.topk,
-                   "proxy_heads": p.proxy_q.shape[1], "causal": True},
+                   "proxy_heads": p.proxy_q.shape[1], "causal": True,
+                   **({"temperature_lse": args.temperature_lse} if temp else {})},
         "stages_ms": {"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
                       "sparse_attention": round(st[2], 4)},
         "work": {"attention_flops": flops, "proxy_flops": pflops,
                  "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3)},
-        "roofline": {"kernel": "msa_prefill_kernel<8,1>", "bound": "mfma",
+        "roofline": {"kernel": "msa_attention_kernel<4,2,bf16>" if temp else "msa_prefill_kernel<8,1>",
+                     "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": _traffic_for("msa_prefill_kernel:" + p.name)},
+                     "traffic": None if temp else _traffic_for("msa_prefill_kernel:" + p.name)},
     }
     return res, p
 
