@@ -107,10 +107,14 @@ def cpu_baseline_prefill(p, rows_n):
     total = pc.total_q
     step = max(1, total // rows_n)
     rows = list(range(step - 1, total, step))[:rows_n]
+    pipeline = pc.proxy_q is not None
     t0 = time.perf_counter()
-    s = oracle.proxy_score(pc.proxy_q, pc.k, pc.cu_seqlens_q, cu_seqlens_k=pc.cu_seqlens_k,
-                           causal=True, max_k_tiles=pc.max_k_tiles, rows=rows)
-    q2k = oracle.topk_select(s.float(), pc.topk, pc.num_kv_heads, rows=rows)
+    if pipeline:
+        s = oracle.proxy_score(pc.proxy_q, pc.k, pc.cu_seqlens_q, cu_seqlens_k=pc.cu_seqlens_k,
+                               causal=True, max_k_tiles=pc.max_k_tiles, rows=rows)
+        q2k = oracle.topk_select(s.float(), pc.topk, pc.num_kv_heads, rows=rows)
+    else:
+        q2k = pc.q2k
     oracle.sparse_attention(pc.q, pc.k, pc.v, q2k, pc.cu_seqlens_q,
                             cu_seqlens_k=pc.cu_seqlens_k, causal=True, rows=rows)
     dt = time.perf_counter() - t0
@@ -119,8 +123,9 @@ def cpu_baseline_prefill(p, rows_n):
     flops = int(keys.sum()) * (pc.num_qo_heads // pc.num_kv_heads) * 4 * pc.head_dim
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"{len(rows)} of {total} query rows (every {step}th), all 16 heads: "
-                      f"fp64 proxy + top-K + attention, {dt:.1f} s"}
+            "sample": f"{len(rows)} of {total} query rows (every {step}th), all "
+                      f"{pc.num_qo_heads} heads: fp64 "
+                      f"{'proxy + top-K + attention' if pipeline else 'attention'}, {dt:.1f} s"}
 
 
 def cpu_baseline_decode(p, rows_n, fmt):
@@ -169,8 +174,15 @@ def bench_prefill_pipeline(args, msa, synth, torch):
     p = synth.workload(args.workload, device="cuda")
     T, B = p.max_k_tiles, p.batch
     mq = max(p.q_lens)
-    scores = torch.empty(p.proxy_q.shape[1], T, p.total_q, dtype=torch.float32, device="cuda")
-    q2k = torch.empty(p.num_kv_heads, p.total_q, p.topk, dtype=torch.int32, device="cuda")
+    # a workload without proxy heads comes with its q2k: the step is the
+    # attention alone
+    pipeline = p.proxy_q is not None
+    if pipeline:
+        scores = torch.empty(p.proxy_q.shape[1], T, p.total_q, dtype=torch.float32,
+                             device="cuda")
+        q2k = torch.empty(p.num_kv_heads, p.total_q, p.topk, dtype=torch.int32, device="cuda")
+    else:
+        q2k = p.q2k
     out = torch.empty_like(p.q)
     lse = torch.empty(p.total_q, p.num_qo_heads, dtype=torch.float32, device="cuda")
     temp = args.temperature_lse is not None
@@ -178,10 +190,12 @@ def bench_prefill_pipeline(args, msa, synth, torch):
 
     def step(ev=None):
         if ev: ev[0].record()
-        msa.proxy_score(p.proxy_q, p.k, p.cu_seqlens_q, p.cu_seqlens_k, causal=True,
-                        max_seqlen_q=mq, max_k_tiles=T, output=scores)
+        if pipeline:
+            msa.proxy_score(p.proxy_q, p.k, p.cu_seqlens_q, p.cu_seqlens_k, causal=True,
+                            max_seqlen_q=mq, max_k_tiles=T, output=scores)
         if ev: ev[1].record()
-        msa.topk_select(scores, p.topk, p.num_kv_heads, out=q2k)
+        if pipeline:
+            msa.topk_select(scores, p.topk, p.num_kv_heads, out=q2k)
         if ev: ev[2].record()
         msa.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q, p.cu_seqlens_k, causal=True,
                              return_softmax_lse=True, max_seqlen_q=mq, max_k_tiles=T,
@@ -194,7 +208,7 @@ def bench_prefill_pipeline(args, msa, synth, torch):
     torch.cuda.synchronize()
     lens = p.cu_seqlens_k[1:] - p.cu_seqlens_k[:-1]
     flops = accounting.attention_flops(q2k, p.cu_seqlens_q, lens, p.num_qo_heads)
-    pflops = accounting.proxy_flops(p.cu_seqlens_q, lens, p.proxy_q.shape[1])
+    pflops = accounting.proxy_flops(p.cu_seqlens_q, lens, p.proxy_q.shape[1]) if pipeline else 0
 
     evs = [_events(4) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -215,12 +229,13 @@ def bench_prefill_pipeline(args, msa, synth, torch):
         "dtype": "bf16",
         "config": {"workload": p.name, "batch": B, "seq_len": mq, "num_qo_heads": p.num_qo_heads,
                    "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "topk": p.topk,
-                   "proxy_heads": p.proxy_q.shape[1], "causal": True,
+                   "proxy_heads": p.proxy_q.shape[1] if pipeline else 0, "causal": True,
                    **({"temperature_lse": args.temperature_lse} if temp else {})},
-        "stages_ms": {"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
-                      "sparse_attention": round(st[2], 4)},
+        "stages_ms": ({"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
+                       "sparse_attention": round(st[2], 4)} if pipeline
+                      else {"sparse_attention": round(st[2], 4)}),
         "work": {"attention_flops": flops, "proxy_flops": pflops,
-                 "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3)},
+                 "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3) if pipeline else None},
         "roofline": {"kernel": "msa_attention_kernel<4,2,bf16>" if temp else "msa_prefill_kernel<8,1>",
                      "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
