@@ -9,6 +9,7 @@ load, importing this package raises.
     topk_select(max_score, topk, num_kv_heads)    the top-K block select
     sparse_attention(q, k, v, q2k_indices, ...)   msa_sparse_attention page
     validate_attention(q, k, v, q2k_indices, ...) its device-side caller contracts
+    prepare_msa_nvfp4_sparse_decode(q, k, v, ...) a bound E2M1 paged decode runner
     tile_union(q2k, cu_seqlens_q, lengths_k, ...) the per-tile union builder
     qsa_indexed_forward(q, k, v, indices, ...)    qsa page, indexed API
     qsa_bitmap_forward(q, k, v, bitmap, ...)      qsa page, bitmap API
@@ -22,7 +23,8 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "MsaError", "lib", "library_path", "sparse_attention", "validate_attention", "proxy_score",
+    "MsaError", "lib", "library_path", "sparse_attention", "validate_attention",
+    "prepare_msa_nvfp4_sparse_decode", "MSANvfp4DecodeRunner", "proxy_score",
     "topk_select",
     "tile_union", "qsa_indexed_forward", "qsa_bitmap_forward", "workspace_size", "Workspace", "KV_BF16", "KV_FP8_E4M3",
     "KV_E2M1X2", "KV_F16",
@@ -39,7 +41,8 @@ BLOCK = 128
 EXPORTED_SYMBOLS = (
     "msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
     "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward", "msa_qsa_bitmap_forward",
-    "msa_validate_attention", "msa_status_string", "msa_last_error", "msa_version",
+    "msa_validate_attention", "msa_sparse_attention_plan", "msa_status_string",
+    "msa_last_error", "msa_version",
 )
 
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_DTYPE",
@@ -123,9 +126,13 @@ def _load():
     L.msa_qsa_indexed_forward.argtypes = [ctypes.POINTER(QsaArgs), _P]
     L.msa_qsa_bitmap_forward.argtypes = [ctypes.POINTER(QsaArgs), _P]
     L.msa_validate_attention.argtypes = [ctypes.POINTER(AttnArgs), _P]
+    L.msa_sparse_attention_plan.argtypes = [ctypes.POINTER(AttnArgs),
+                                            ctypes.POINTER(ctypes.c_int32),
+                                            ctypes.POINTER(ctypes.c_int32)]
     for fn in ("msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
                "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward",
-               "msa_qsa_bitmap_forward", "msa_validate_attention"):
+               "msa_qsa_bitmap_forward", "msa_validate_attention",
+               "msa_sparse_attention_plan"):
         getattr(L, fn).restype = ctypes.c_int
     L.msa_status_string.argtypes = [ctypes.c_int]
     L.msa_status_string.restype = ctypes.c_char_p
@@ -331,6 +338,98 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
     if return_temperature_lse:
         return out, lse, lse_t
     return (out, lse) if return_softmax_lse else out
+
+
+class MSANvfp4DecodeRunner:
+    """Bound packed-E2M1 paged decode (prepare_msa_nvfp4_sparse_decode page):
+    every tensor, the output, the LSE and the split-KV workspace are fixed
+    at preparation; calling the runner launches the decode on the current
+    stream with no allocation and no host synchronisation (so it can be
+    captured in a HIP graph) and returns out.  `splits` is the split-KV
+    factor the launch uses."""
+
+    def __init__(self, args: "AttnArgs", keep: tuple, out, lse, workspace, splits: int):
+        self._args, self._keep = args, keep
+        self.out, self.lse, self.workspace, self.splits = out, lse, workspace, splits
+        self._ws = (None, 0) if workspace is None else (_ptr(workspace.view), workspace.nbytes)
+
+    def __call__(self):
+        _check(lib.msa_sparse_attention(ctypes.byref(self._args), self._ws[0], self._ws[1],
+                                        _stream()))
+        return self.out
+
+
+def prepare_msa_nvfp4_sparse_decode(q, k, v, q2k_indices, *, k_scale, v_scale, page_table,
+                                    seqused_k, k_global_scale, v_global_scale,
+                                    workspace_buffer=None, seqlen_q=1, softmax_scale=None,
+                                    out=None, lse=None, backend="hip"):
+    """Validate and bind a packed-E2M1 (NVFP4-layout) paged decode
+    (prepare_msa_nvfp4_sparse_decode page): q bf16 [batch * seqlen_q, Hq,
+    128], request b owning rows [b * seqlen_q, (b + 1) * seqlen_q); k, v
+    uint8 [num_pages, Hkv, 128, 64]; q2k [Hkv, batch * seqlen_q, 16];
+    k_scale, v_scale [num_pages, Hkv, 128, 8] E4M3 bytes (uint8 or
+    float8_e4m3fn views, both stored linearly); page_table [batch,
+    max_pages]; seqused_k [batch] including the new tokens; positive global
+    scales.  Causal, right-aligned: token i of request b sits at KV position
+    seqused_k[b] - seqlen_q + i.  workspace_buffer: optional caller-owned
+    uint8 bytes for the split-KV partials (otherwise allocated here, once).
+    Returns an MSANvfp4DecodeRunner."""
+    if backend not in ("hip", "cake"):
+        raise ValueError(f"unknown backend {backend!r}")
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.shape[2] != 128 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous bf16 [batch * seqlen_q, num_q_heads, 128] tensor")
+    if not 1 <= int(seqlen_q) <= 32:
+        raise ValueError(f"seqlen_q must be in [1, 32], got {seqlen_q}")
+    for name, t in (("k", k), ("v", v)):
+        if t.dtype != torch.uint8 or t.dim() != 4 or t.shape[2] != BLOCK or t.shape[3] != 64:
+            raise ValueError(f"{name} must be uint8 [num_pages, num_kv_heads, 128, 64]")
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or t.dim() != 4 or t.shape[3] != 8:
+            raise ValueError(f"{name} must be uint8 or float8_e4m3fn [num_pages, num_kv_heads, 128, 8]")
+    k_scale, v_scale = k_scale.view(torch.uint8), v_scale.view(torch.uint8)
+    hkv = k.shape[1]
+    if q2k_indices.dim() != 3 or q2k_indices.shape[0] != hkv or q2k_indices.shape[2] != 16 \
+            or q2k_indices.shape[1] != q.shape[0]:
+        raise ValueError("q2k_indices must be int32 [num_kv_heads, batch * seqlen_q, 16]")
+    if q.shape[1] % hkv or q.shape[1] // hkv > 16:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads, at most 16 per KV head")
+    if not (k_global_scale > 0 and v_global_scale > 0):
+        raise ValueError("k_global_scale and v_global_scale must be positive")
+    for name, t in (("q2k_indices", q2k_indices), ("page_table", page_table),
+                    ("seqused_k", seqused_k)):
+        _check_i32(name, t)
+    batch = seqused_k.numel()
+    if q.shape[0] != batch * int(seqlen_q):
+        raise ValueError(f"q has {q.shape[0]} rows, expected batch * seqlen_q = {batch * seqlen_q}")
+    cu_q = torch.arange(0, batch + 1, dtype=torch.int32, device=q.device) * int(seqlen_q)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device)
+    a = _attn_args(q, k, v, q2k_indices, cu_q, None, True, softmax_scale, page_table, seqused_k,
+                   k_scale, v_scale, k_global_scale, v_global_scale, int(seqlen_q),
+                   page_table.shape[1], out, lse, 0)
+    need = ctypes.c_size_t(0)
+    _check(lib.msa_sparse_attention_workspace_size(ctypes.byref(a), ctypes.byref(need)))
+    route, splits = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.msa_sparse_attention_plan(ctypes.byref(a), ctypes.byref(route), ctypes.byref(splits)))
+    ws = None
+    if need.value:
+        if workspace_buffer is None:
+            ws = Workspace(need.value, q.device)
+        else:
+            if workspace_buffer.dtype != torch.uint8 or not workspace_buffer.is_contiguous():
+                raise ValueError("workspace_buffer must be contiguous uint8 bytes")
+            off = (-workspace_buffer.data_ptr()) % 256
+            if workspace_buffer.numel() - off < need.value:
+                raise MsaError(6, f"workspace_buffer needs {need.value} bytes past 256-byte "
+                                  f"alignment, got {workspace_buffer.numel() - off}")
+            ws = Workspace.__new__(Workspace)
+            ws.nbytes = workspace_buffer.numel() - off
+            ws.buffer = workspace_buffer
+            ws.view = workspace_buffer[off:]
+    keep = (q, k, v, q2k_indices, k_scale, v_scale, page_table, seqused_k, cu_q)
+    return MSANvfp4DecodeRunner(a, keep, out, lse, ws, int(splits.value))
 
 
 def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, seqused_k=None,

@@ -289,6 +289,17 @@ msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args, si
   return ok();
 }
 
+msa_status_t msa_sparse_attention_plan(const msa_attn_args_t* args, int32_t* decode_route,
+                                       int32_t* splits) {
+  if (!decode_route || !splits) return fail(MSA_ERR_NULL, "decode_route and splits must be non-NULL");
+  Resolved r;
+  msa_status_t st = resolve_attention(args, &r, false);
+  if (st) return st;
+  *decode_route = r.plan.decode;
+  *splits = r.plan.splits;
+  return ok();
+}
+
 msa_status_t msa_validate_attention(const msa_attn_args_t* a, void* stream) {
   Resolved r;
   msa_status_t st = resolve_attention(a, &r, true);

@@ -158,6 +158,14 @@ typedef struct {
 msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args,
                                                  size_t* bytes);
 
+/* The launch plan msa_sparse_attention would use for these arguments: the
+ * route (1: the paged/flat decode kernel, 0: a prefill-tile kernel) and the
+ * split-KV factor (1 when not split; prepare_msa_nvfp4_sparse_decode page:
+ * the runner reports the chosen factor).  Host-side only; the same checks
+ * and statuses as msa_sparse_attention_workspace_size. */
+msa_status_t msa_sparse_attention_plan(const msa_attn_args_t* args, int32_t* decode_route,
+                                       int32_t* splits);
+
 /* Forward sparse attention (msa_sparse_attention page).  Each query token,
  * per KV head, attends only to the 128-token KV blocks listed in its q2k row;
  * query tiles run one online softmax over the union of their tokens' blocks

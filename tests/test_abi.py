@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declarations_are_exported():
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(msa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(msa.lib, n), n
@@ -259,3 +259,27 @@ def test_package_refuses_to_import_without_the_library(tmp_path):
                        capture_output=True, text=True)
     assert r.returncode != 0
     assert "ImportError" in r.stderr and "libmsa.so" in r.stderr
+
+
+def test_nvfp4_decode_preparation_checks_shapes():
+    import torch
+    q = torch.zeros(4, 16, 128, dtype=torch.bfloat16)
+    k = torch.zeros(8, 1, 128, 64, dtype=torch.uint8)
+    sc = torch.zeros(8, 1, 128, 8, dtype=torch.uint8)
+    q2k = torch.zeros(1, 4, 16, dtype=torch.int32)
+    pt = torch.zeros(2, 4, dtype=torch.int32)
+    su = torch.full((2,), 300, dtype=torch.int32)
+    prep = lambda **kw: msa.prepare_msa_nvfp4_sparse_decode(
+        kw.get("q", q), k, k, kw.get("q2k", q2k), k_scale=sc, v_scale=sc, page_table=pt,
+        seqused_k=su, k_global_scale=kw.get("kgs", 0.5), v_global_scale=2.0,
+        seqlen_q=kw.get("seqlen_q", 2))
+    with pytest.raises(ValueError):
+        prep(seqlen_q=33)                                   # seqlen_q past 32
+    with pytest.raises(ValueError):
+        prep(seqlen_q=1)                                    # 4 rows for 2 requests x 1 token
+    with pytest.raises(ValueError):
+        prep(q2k=torch.zeros(1, 4, 8, dtype=torch.int32))  # topk other than 16
+    with pytest.raises(ValueError):
+        prep(kgs=0.0)                                       # global scales must be positive
+    with pytest.raises(ValueError):
+        prep(q=torch.zeros(4, 32, 128, dtype=torch.bfloat16))   # 32 query heads on 1 KV head

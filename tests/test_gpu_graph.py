@@ -68,3 +68,46 @@ def test_decode_graph_with_given_selection(msa, fmt, splits):
     if splits > 1:
         assert g.workspace is not None          # split partials bound before capture
     _replays_match_eager(g, q_new=True)
+
+
+@pytest.mark.parametrize("seqlen_q,given_ws", [(1, False), (4, True)])
+def test_nvfp4_decode_runner(msa, seqlen_q, given_ws):
+    # prepare once, call: equals the plain call bitwise and the oracle within
+    # tolerance; a captured call replays the same result
+    import oracle
+    from gpu_helpers import assert_attention_close, gpu_attention
+    print(f"nvfp4 runner seqlen_q {seqlen_q} workspace given {given_ws}", flush=True)
+    p = synth.make_problem("nvfp4_runner", q_lens=[seqlen_q] * 3, k_lens=[5000, 700, 2600],
+                           num_qo_heads=16, num_kv_heads=1, topk=16, paged=True,
+                           kv_dtype=synth.KV_E2M1, seed=70 + seqlen_q, selection="decode",
+                           k_global_scale=0.5, v_global_scale=2.0).to("cuda")
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda") if given_ws else None
+    run = msa.prepare_msa_nvfp4_sparse_decode(
+        p.q, p.k, p.v, p.q2k, k_scale=p.k_scale, v_scale=p.v_scale, page_table=p.page_table,
+        seqused_k=p.seqused_k, k_global_scale=0.5, v_global_scale=2.0, workspace_buffer=ws,
+        seqlen_q=seqlen_q)
+    assert run.splits >= 1
+    out = run().clone()
+    lse = run.lse.clone()
+    ref = gpu_attention(msa, p)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+    ref_out, ref_lse = oracle.sparse_attention(
+        p.q, p.k, p.v, p.q2k.cpu(), p.cu_seqlens_q.cpu(), page_table=p.page_table.cpu(),
+        seqused_k=p.seqused_k.cpu(), causal=True, kv_format=p.kv_dtype, k_scale=p.k_scale,
+        v_scale=p.v_scale, k_global_scale=0.5, v_global_scale=2.0)
+    assert_attention_close(out, lse, ref_out, ref_lse, "nvfp4 runner")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for _ in range(3):
+        run.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(run.out, out) and torch.equal(run.lse, lse)
