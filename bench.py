@@ -16,7 +16,8 @@ qsa_indexed_1x8192_h12kv1_d256_w2048 times the QSA indexed forward,
 qsa_bitmap_1x8192_h12kv1_d256_causal_q25 the QSA bitmap forward.  --graph
 (decode workloads) adds the same step replayed as one HIP graph
 (graph_ms_per_step); --temperature-lse TAU (prefill workloads) also returns
-the temperature LSE, which runs the attention on the general kernel.
+the temperature LSE, which runs the attention on the general kernel;
+--kv-format fp8 (prefill workloads) stores K/V as fp8 E4M3.
 
 Per-stage times come from HIP events recorded on the stream the kernels run
 on.  One JSON line is printed.
@@ -45,6 +46,9 @@ def _args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kv-format", choices=("bf16", "fp8"), default="bf16",
+                    help="prefill workloads: K/V stored as bf16 (default) or fp8 E4M3 (the "
+                         "same values cast; proxy and attention read fp8)")
     ap.add_argument("--temperature-lse", type=float, default=None, metavar="TAU",
                     help="prefill workloads: also return the temperature LSE with this scale "
                          "(the attention then runs on the general kernel)")
@@ -111,12 +115,14 @@ def cpu_baseline_prefill(p, rows_n):
     t0 = time.perf_counter()
     if pipeline:
         s = oracle.proxy_score(pc.proxy_q, pc.k, pc.cu_seqlens_q, cu_seqlens_k=pc.cu_seqlens_k,
-                               causal=True, max_k_tiles=pc.max_k_tiles, rows=rows)
+                               causal=True, max_k_tiles=pc.max_k_tiles, rows=rows,
+                               kv_format=pc.kv_dtype)
         q2k = oracle.topk_select(s.float(), pc.topk, pc.num_kv_heads, rows=rows)
     else:
         q2k = pc.q2k
     oracle.sparse_attention(pc.q, pc.k, pc.v, q2k, pc.cu_seqlens_q,
-                            cu_seqlens_k=pc.cu_seqlens_k, causal=True, rows=rows)
+                            cu_seqlens_k=pc.cu_seqlens_k, causal=True, rows=rows,
+                            kv_format=pc.kv_dtype)
     dt = time.perf_counter() - t0
     lens = pc.cu_seqlens_k[1:] - pc.cu_seqlens_k[:-1]
     keys = accounting.attended_keys(q2k, pc.cu_seqlens_q, lens, causal=True)[:, rows]
@@ -172,6 +178,9 @@ def cpu_baseline_decode(p, rows_n, fmt):
 def bench_prefill_pipeline(args, msa, synth, torch):
     from block_sparse_top_msa_amd import accounting
     p = synth.workload(args.workload, device="cuda")
+    if args.kv_format == "fp8":
+        p.k, p.v = p.k.to(torch.float8_e4m3fn), p.v.to(torch.float8_e4m3fn)
+        p.kv_dtype = synth.KV_FP8
     T, B = p.max_k_tiles, p.batch
     mq = max(p.q_lens)
     # a workload without proxy heads comes with its q2k: the step is the
@@ -226,21 +235,25 @@ def bench_prefill_pipeline(args, msa, synth, torch):
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "ms_per_step": round(ms_step, 4),
-        "dtype": "bf16",
+        "dtype": "bf16" if args.kv_format == "bf16" else "fp8_e4m3->bf16",
         "config": {"workload": p.name, "batch": B, "seq_len": mq, "num_qo_heads": p.num_qo_heads,
                    "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "topk": p.topk,
                    "proxy_heads": p.proxy_q.shape[1] if pipeline else 0, "causal": True,
+                   **({"kv_format": "fp8_e4m3"} if args.kv_format == "fp8" else {}),
                    **({"temperature_lse": args.temperature_lse} if temp else {})},
         "stages_ms": ({"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
                        "sparse_attention": round(st[2], 4)} if pipeline
                       else {"sparse_attention": round(st[2], 4)}),
         "work": {"attention_flops": flops, "proxy_flops": pflops,
                  "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3) if pipeline else None},
-        "roofline": {"kernel": "msa_attention_kernel<4,2,bf16>" if temp else "msa_prefill_kernel<8,1>",
+        "roofline": {"kernel": ("msa_attention_kernel<4,2,fp8>" if args.kv_format == "fp8" else
+                                "msa_attention_kernel<4,2,bf16>" if temp else
+                                "msa_prefill_kernel<8,1>"),
                      "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None if temp else _traffic_for("msa_prefill_kernel:" + p.name)},
+                     "traffic": (None if temp or args.kv_format == "fp8"
+                                 else _traffic_for("msa_prefill_kernel:" + p.name))},
     }
     return res, p
 
