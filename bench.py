@@ -246,9 +246,9 @@ def bench_prefill_pipeline(args, msa, synth, torch):
                       else {"sparse_attention": round(st[2], 4)}),
         "work": {"attention_flops": flops, "proxy_flops": pflops,
                  "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3) if pipeline else None},
-        "roofline": {"kernel": ("msa_attention_kernel<4,2,fp8>" if args.kv_format == "fp8" else
-                                "msa_attention_kernel<4,2,bf16>" if temp else
-                                "msa_prefill_kernel<8,1>"),
+        "roofline": {"kernel": ("msa_attention_kernel<4,2,bf16>" if temp else
+                                "msa_stage16_kernel + msa_prefill_kernel<8,1>"
+                                if args.kv_format == "fp8" else "msa_prefill_kernel<8,1>"),
                      "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -22,7 +22,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 
 SOURCES = ["api.cpp", "attention.hip", "decode.hip", "prefill.hip", "proxy.hip", "qsa.hip",
-           "topk.hip", "validate.hip"]
+           "stage16.hip", "topk.hip", "validate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

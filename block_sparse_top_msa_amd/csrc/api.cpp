@@ -12,6 +12,7 @@
 
 #include "../../include/msa.h"
 #include "internal.hpp"
+#include "stage16.hpp"
 #include "temperature.hpp"
 #include "validate.hpp"
 
@@ -76,6 +77,7 @@ struct Resolved {
   msa::AttnParams p;
   msa::AttnPlan plan;
   size_t ws_bytes;
+  bool stage16;   // fp8 / E2M1 prefill: K/V staged to bf16 pages in the workspace
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -179,6 +181,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   // ---- plan ----
   msa::AttnPlan& plan = r->plan;
   plan = msa::AttnPlan{};
+  r->stage16 = false;
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows_req = lqmax * G;
   // packed E2M1 in the flat layout goes through the general kernel at every
@@ -219,7 +222,10 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     plan.splits = std::max(1, std::min(splits, 64));
   } else {
     plan.decode = 0;
-    plan.async_bf16 = (a->kv_dtype == MSA_KV_BF16 || a->kv_dtype == MSA_KV_F16) && !temp;
+    // fp8 / E2M1 K/V: converted to bf16 pages once, then the bf16 kernel
+    r->stage16 = !temp && (a->kv_dtype == MSA_KV_FP8_E4M3 || a->kv_dtype == MSA_KV_E2M1X2);
+    plan.async_bf16 =
+        (a->kv_dtype == MSA_KV_BF16 || a->kv_dtype == MSA_KV_F16 || r->stage16) && !temp;
     // bf16: 4 waves x spw slots x 32 rows per tile; other formats: 4 x 2 x 16
     int rows;
     if (plan.async_bf16) {
@@ -245,6 +251,7 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   p.splits = plan.splits;
 
   r->ws_bytes = 0;
+  if (r->stage16) r->ws_bytes = msa::stage16_bytes(a->batch, a->max_k_tiles, a->num_kv_heads);
   if (plan.splits > 1) {
     const int rows = plan.tok_per_tile * G;
     const int rows_pad = (rows + 31) / 32 * 32;
@@ -365,6 +372,8 @@ msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
       return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", r.ws_bytes,
                   workspace_bytes, workspace);
     if (!aligned(workspace, 256)) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  if (r.ws_bytes && !r.stage16) {
     // layout: [partial LSE][partial O]
     const size_t units = (size_t)args->batch * args->num_kv_heads * r.p.tiles_per_req;
     const size_t l_bytes = round_up(units * r.plan.splits * r.p.ws_lse_rows * sizeof(float), 256);
@@ -373,6 +382,15 @@ msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
     r.p.ws_o = reinterpret_cast<float*>(base + l_bytes);
   }
   if (args->total_q == 0 || args->batch == 0) return ok();
+  if (r.stage16) {
+    msa::AttnParams pq;
+    msa_status_t st2 = hip_status(msa::launch_stage16(r.p, args->kv_dtype, workspace, &pq,
+                                                      static_cast<hipStream_t>(stream)),
+                                  "msa_sparse_attention staging launch");
+    if (st2) return st2;
+    return hip_status(msa::launch_prefill_bf16(pq, r.plan.spw, static_cast<hipStream_t>(stream)),
+                      "msa_sparse_attention launch");
+  }
   if (args->lse_t)
     return hip_status(msa::launch_attention_temperature(r.p, args->kv_dtype, args->lse_t,
                                                         args->lse_temperature_scale,

@@ -123,8 +123,8 @@ typedef struct {
                              a head's rows contiguous (8 bytes), page/head
                              strides multiples of 16.  Flat [total_k, Hkv, 8]
                              in (token, head) order or any view of 8-byte rows
-                             (strides multiples of 8); flat E2M1 runs on the
-                             general (prefill) kernel at every shape          */
+                             (strides multiples of 8); flat E2M1 takes the
+                             prefill route at every shape                     */
   const void* v_scale;    /* E2M1 only: same, stored linearly                 */
   msa_strides_t k_strides, v_strides, k_scale_strides, v_scale_strides;
   const int32_t* q2k;     /* [Hkv, total_q, topk] block ids, ascending, -1 padded */
@@ -148,12 +148,14 @@ typedef struct {
 
 /* Bytes of workspace msa_sparse_attention needs for these arguments: the
  * fp32 split-KV partials (O / l per row) and their LSE
- * (prepare_msa_nvfp4_sparse_decode page, Parameters: workspace_buffer).  0
- * when the call runs without splitting (prefill shapes; decode shapes whose
- * plan uses one split).  The buffer is 256-byte aligned, owned by the
- * caller, needs no initialisation and carries no state between launches:
- * every launch writes the partials before a second kernel on the same
- * stream merges them.  Launches that may run concurrently need separate
+ * (prepare_msa_nvfp4_sparse_decode page, Parameters: workspace_buffer), or,
+ * for fp8 / E2M1 K/V on the prefill route, the bf16 pages their visible
+ * blocks are converted to (2 * batch * max_k_tiles * Hkv * 32 KiB plus the
+ * page table and lengths).  0 for bf16 / fp16 K/V on the prefill route and
+ * for decode shapes whose plan uses one split.  The buffer is 256-byte
+ * aligned, owned by the caller, needs no initialisation and carries no
+ * state between launches: every launch writes what it reads later on the
+ * same stream.  Launches that may run concurrently need separate
  * workspaces. */
 msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args,
                                                  size_t* bytes);

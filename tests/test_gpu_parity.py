@@ -82,6 +82,20 @@ def test_prefill_flat_e2m1(msa, hkv, q_lens, k_lens, head_major):
     assert_attention_close(out, lse, ref_out, ref_lse, "prefill flat e2m1")
 
 
+@pytest.mark.parametrize("fmt", [synth.KV_FP8, synth.KV_E2M1])
+def test_prefill_paged_quantised_kv(msa, fmt):
+    # prefill shapes over a paged fp8 / E2M1 cache: the blocks are staged to
+    # bf16 pages in the workspace and read by the bf16 prefill kernel
+    print(f"paged {fmt} prefill", flush=True)
+    kw = dict(k_global_scale=0.5, v_global_scale=2.0) if fmt == synth.KV_E2M1 else {}
+    p = synth.make_problem("prefill_paged_q", q_lens=[200, 70, 9], k_lens=[700, 300, 129],
+                           num_qo_heads=8, num_kv_heads=2, topk=4, paged=True, kv_dtype=fmt,
+                           seed=81, selection="general", extra_pages=5, **kw)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, f"paged {fmt} prefill")
+
+
 @pytest.mark.parametrize("splits", [0, 1, 3])
 def test_decode_flat_e2m1(msa, splits):
     print(f"flat E2M1 decode splits {splits}", flush=True)
