@@ -76,11 +76,21 @@ __global__ __launch_bounds__(256) void msa_stage16_kernel(Stage16Params s) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) x[e] = 0.f;
     } else if (s.fmt == kFmtFp8) {
+      // E4M3 -> bf16 with the hardware conversion (scale 1: exact)
       const uint8_t* src = (isv ? p.v + vo + g * p.v_st.head + r * p.v_st.token
                                 : p.k + ko + g * p.k_st.head + r * p.k_st.token) + 16 * j;
       const u32x4 q = *reinterpret_cast<const u32x4*>(src);
+      u32x4 a, c;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = e4m3_to_f32((q[e >> 2] >> (8 * (e & 3))) & 0xFFu);
+      for (int h = 0; h < 2; ++h) {
+        a[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[h], 1.0f, false));
+        a[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[h], 1.0f, true));
+        c[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[2 + h], 1.0f, false));
+        c[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q[2 + h], 1.0f, true));
+      }
+      *reinterpret_cast<u32x4*>(dst) = a;
+      *reinterpret_cast<u32x4*>(dst + 16) = c;
+      continue;
     } else {
       const uint8_t* src = (isv ? p.v + vo + g * p.v_st.head + r * p.v_st.token
                                 : p.k + ko + g * p.k_st.head + r * p.k_st.token) + 8 * j;
