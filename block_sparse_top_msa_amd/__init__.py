@@ -23,6 +23,7 @@ from typing import Optional
 import torch
 
 __all__ = [
+    "attention_plan",
     "MsaError", "lib", "library_path", "sparse_attention", "validate_attention",
     "prepare_msa_nvfp4_sparse_decode", "MSANvfp4DecodeRunner", "proxy_score",
     "topk_select",
@@ -272,6 +273,23 @@ def workspace_size(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, *, pag
     return int(n.value)
 
 
+def attention_plan(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None,
+                   seqused_k=None, k_scale=None, v_scale=None, max_seqlen_q=None,
+                   max_k_tiles=None, splits=0, return_temperature_lse=False):
+    """(decode_route, splits) that sparse_attention takes for these arguments:
+    decode_route 1 is the paged/flat decode kernel (split-KV partials merged
+    by LSE when splits > 1), 0 the prefill tiles."""
+    a = _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, False, None, page_table,
+                   seqused_k, k_scale, v_scale, None, None, max_seqlen_q, max_k_tiles, None,
+                   None, splits)
+    if return_temperature_lse:
+        a.lse_t, a.lse_temperature_scale = a.q, 1.0   # only tested for non-NULL
+    route, nsplit = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib.msa_sparse_attention_plan(ctypes.byref(a), ctypes.byref(route),
+                                         ctypes.byref(nsplit)))
+    return int(route.value), int(nsplit.value)
+
+
 def validate_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, causal=False,
                        page_table=None, seqused_k=None, k_scale=None, v_scale=None, *,
                        max_seqlen_q=None, max_k_tiles=None, out=None):
@@ -346,7 +364,10 @@ class MSANvfp4DecodeRunner:
     at preparation; calling the runner launches the decode on the current
     stream with no allocation and no host synchronisation (so it can be
     captured in a HIP graph) and returns out.  `splits` is the split-KV
-    factor the launch uses."""
+    factor the launch uses; `decode_route` is 1 when the call takes the
+    decode kernel (the E2M1 pages dequantised in registers)."""
+
+    decode_route = 1
 
     def __init__(self, args: "AttnArgs", keep: tuple, out, lse, workspace, splits: int):
         self._args, self._keep = args, keep
@@ -429,7 +450,9 @@ def prepare_msa_nvfp4_sparse_decode(q, k, v, q2k_indices, *, k_scale, v_scale, p
             ws.buffer = workspace_buffer
             ws.view = workspace_buffer[off:]
     keep = (q, k, v, q2k_indices, k_scale, v_scale, page_table, seqused_k, cu_q)
-    return MSANvfp4DecodeRunner(a, keep, out, lse, ws, int(splits.value))
+    run = MSANvfp4DecodeRunner(a, keep, out, lse, ws, int(splits.value))
+    run.decode_route = int(route.value)
+    return run
 
 
 def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, seqused_k=None,

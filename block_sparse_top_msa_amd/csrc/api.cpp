@@ -42,6 +42,10 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr int64_t kMaxTokenStride = (int64_t)1 << 24;
 
+// Longest query (tokens per request) that takes the decode kernel with one
+// token per tile (G >= 16); longer queries take the prefill tiles.
+constexpr int kDecodeMaxTokens = 64;
+
 // Resolve a stride triple for a tensor with `row_bytes` contiguous bytes per
 // token row.  Dense layout for zeros.  Rejects unaligned views.
 msa_status_t resolve_strides(const char* name, const msa_strides_t& in, bool paged, int hkv,
@@ -78,6 +82,7 @@ struct Resolved {
   msa::AttnPlan plan;
   size_t ws_bytes;
   bool stage16;   // fp8 / E2M1 prefill: K/V staged to bf16 pages in the workspace
+  int stage_slots; // staged pages per request when only selected blocks are staged, else 0
 };
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -196,14 +201,17 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
                 (double)a->lse_temperature_scale);
   if (temp && a->kv_dtype == MSA_KV_F16)
     return fail(MSA_ERR_UNSUPPORTED, "the temperature LSE is computed for bf16 / fp8 / E2M1 K/V");
-  if (rows_req <= 64 && !flat_e2m1 && !temp) {
+  // When one token's G heads fill a 16-row MFMA tile, every token of a short
+  // query is a decode tile of its own: it streams just the pages it selected
+  // (a union over the request's tokens would make each page cost all of
+  // their row tiles), with less state per workgroup.
+  const bool per_token = G >= 16 && G <= 64 && lqmax > 1 && lqmax <= kDecodeMaxTokens;
+  const int dec_rows = per_token ? G : rows_req;
+  if (dec_rows <= 64 && !flat_e2m1 && !temp) {
     // decode shape: one workgroup per (request, KV head, token tile, split);
-    // its waves split every page's keys.  When one token's G heads fill a
-    // 16-row MFMA tile, every token is a tile of its own: it streams just the
-    // pages it selected (a union over the request's tokens would make each
-    // page cost all of their row tiles), with less state per workgroup.
+    // its waves split every page's keys
     plan.decode = 1;
-    plan.tok_per_tile = (G >= 16 && lqmax > 1) ? 1 : lqmax;
+    plan.tok_per_tile = per_token ? 1 : lqmax;
     const int tiles = (lqmax + plan.tok_per_tile - 1) / plan.tok_per_tile;
     const int units = std::max(1, a->batch * a->num_kv_heads * tiles);
     const int union_max = std::min(plan.tok_per_tile * a->topk, std::max(1, a->max_k_tiles));
@@ -237,6 +245,10 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
       plan.spw = 2;
       rows = 128;
     }
+    if (G > rows)
+      return fail(MSA_ERR_SHAPE,
+                  "num_qo_heads / num_kv_heads = %d exceeds the %d query rows of a prefill tile",
+                  G, rows);
     plan.tok_per_tile = std::max(1, std::min(64, rows / G));
     plan.splits = 1;
   }
@@ -251,7 +263,11 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   p.splits = plan.splits;
 
   r->ws_bytes = 0;
-  if (r->stage16) r->ws_bytes = msa::stage16_bytes(a->batch, a->max_k_tiles, a->num_kv_heads);
+  r->stage_slots = 0;
+  if (r->stage16) {
+    r->stage_slots = msa::stage16_slots(a->max_seqlen_q, a->num_kv_heads, a->topk, a->max_k_tiles);
+    r->ws_bytes = msa::stage16_bytes(a->batch, a->max_k_tiles, a->num_kv_heads, r->stage_slots);
+  }
   if (plan.splits > 1) {
     const int rows = plan.tok_per_tile * G;
     const int rows_pad = (rows + 31) / 32 * 32;
@@ -384,7 +400,7 @@ msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
   if (args->total_q == 0 || args->batch == 0) return ok();
   if (r.stage16) {
     msa::AttnParams pq;
-    msa_status_t st2 = hip_status(msa::launch_stage16(r.p, args->kv_dtype, workspace, &pq,
+    msa_status_t st2 = hip_status(msa::launch_stage16(r.p, args->kv_dtype, r.stage_slots, workspace, &pq,
                                                       static_cast<hipStream_t>(stream)),
                                   "msa_sparse_attention staging launch");
     if (st2) return st2;

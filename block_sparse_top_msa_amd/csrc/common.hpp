@@ -85,12 +85,12 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
 // 2^-6 * 0.mmm (e = 0).  Placing the 7 magnitude bits at bits 26..20 of an
 // fp32 word gives 2^(e-127) * 1.mmm (or the fp32 subnormal 2^-126 * 0.mmm),
 // i.e. exactly the value times 2^-120, so one multiply by 2^120 restores it
-// with no rounding.  NaN codes (s.1111.111) are not produced by valid
-// producers and are not special-cased.
+// with no rounding.  The NaN codes s.1111.111 decode to NaN, as the
+// hardware conversion does.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   uint32_t bits = ((byte & 0x80u) << 24) | ((byte & 0x7Fu) << 20);
-  return __uint_as_float(bits) * 0x1p120f;
+  return (byte & 0x7Fu) == 0x7Fu ? __uint_as_float(0x7FC00000u) : __uint_as_float(bits) * 0x1p120f;
 }
 
 // E2M1 nibble s.ee.m -> value: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.

@@ -291,13 +291,16 @@ def proxy_score(q, k, cu_seqlens_q, *, cu_seqlens_k=None, page_table=None,
                 bm = z.view(len(li), nblk, BLOCK).max(dim=2).values  # (n, nblk)
                 out[h, :tiles, q0 + li] = bm[:, :tiles].T
     if reduce_heads:
-        out = out.max(dim=0, keepdim=True).values
+        out = _reduce_heads(out)   # the module-level reduce_heads below
     return out
 
 
 def reduce_heads(scores: torch.Tensor) -> torch.Tensor:
     """amax over the query-head axis: (H, T, total_q) -> (1, T, total_q)."""
     return torch.as_tensor(scores).max(dim=0, keepdim=True).values
+
+
+_reduce_heads = reduce_heads   # proxy_score's keyword argument shadows the name
 
 
 def selection_scores(scores: torch.Tensor, num_kv_heads: int, mode: str = "auto"):

@@ -283,3 +283,60 @@ def test_nvfp4_decode_preparation_checks_shapes():
         prep(kgs=0.0)                                       # global scales must be positive
     with pytest.raises(ValueError):
         prep(q=torch.zeros(4, 32, 128, dtype=torch.bfloat16))   # 32 query heads on 1 KV head
+
+
+def _plan(a):
+    route, splits = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = msa.lib.msa_sparse_attention_plan(ctypes.byref(a), ctypes.byref(route),
+                                           ctypes.byref(splits))
+    return st, route.value, splits.value
+
+
+@pytest.mark.parametrize("seqlen_q", [1, 4, 8, 32, 64])
+@pytest.mark.parametrize("kv_dtype", [0, 1, 2])
+def test_g16_short_queries_take_the_decode_route(seqlen_q, kv_dtype):
+    # one token's 16 heads fill a row tile: each token of a short query is a
+    # decode tile, whatever the format (no bf16 staging of the context)
+    a = _attn(batch=128, total_q=128 * seqlen_q, num_qo_heads=16, num_kv_heads=1, topk=16,
+              max_seqlen_q=seqlen_q, max_k_tiles=1024, page_table=FAKE, seqused_k=FAKE,
+              page_table_width=1024, kv_dtype=kv_dtype)
+    a.cu_seqlens_k = None
+    if kv_dtype == 2:
+        a.k_scale = a.v_scale = FAKE
+    st, route, splits = _plan(a)
+    assert st == 0 and route == 1 and splits >= 1
+    st, n = _size(a)
+    # split partials at most: far below the 8.6 GB a staged context would take
+    assert st == 0 and n < 64 << 20
+
+
+def test_long_queries_take_the_prefill_route():
+    a = _attn(batch=1, total_q=128, num_qo_heads=16, num_kv_heads=1, topk=16, max_seqlen_q=128,
+              max_k_tiles=64)
+    assert _plan(a)[:2] == (0, 0)
+
+
+@pytest.mark.parametrize("hq,hkv,temp", [(512, 1, False), (256, 1, True), (1024, 2, False)])
+def test_group_larger_than_a_tile_is_rejected(hq, hkv, temp):
+    kw = dict(num_qo_heads=hq, num_kv_heads=hkv, total_q=64, max_seqlen_q=32)
+    if temp:
+        kw.update(lse_t=FAKE, lse_temperature_scale=1.0)
+    st, msg = _call(_attn(**kw))
+    assert st == 2 and "prefill tile" in msg
+
+
+def test_flat_e2m1_decode_stages_only_selected_blocks():
+    # one token per request, flat E2M1: the workspace holds the selected
+    # blocks (at most topk per request and KV head), not every visible block
+    a = _attn(batch=64, total_q=64, num_qo_heads=16, num_kv_heads=1, topk=16, max_seqlen_q=1,
+              max_k_tiles=1024, kv_dtype=2, k_scale=FAKE, v_scale=FAKE)
+    st, route, splits = _plan(a)
+    assert (st, route, splits) == (0, 0, 1)
+    st, n = _size(a)
+    page = 2 * 128 * 256                  # K and V, 128 rows of 256 bytes
+    assert st == 0 and 64 * 16 * page <= n < 64 * 16 * page + (1 << 20)
+    # long queries stage every visible block
+    b = _attn(batch=2, total_q=4096, num_qo_heads=16, num_kv_heads=1, topk=16,
+              max_seqlen_q=2048, max_k_tiles=16, kv_dtype=2, k_scale=FAKE, v_scale=FAKE)
+    st, n = _size(b)
+    assert st == 0 and 2 * 16 * page <= n < 2 * 16 * page + (1 << 20)

@@ -70,7 +70,7 @@ def test_decode_graph_with_given_selection(msa, fmt, splits):
     _replays_match_eager(g, q_new=True)
 
 
-@pytest.mark.parametrize("seqlen_q,given_ws", [(1, False), (4, True)])
+@pytest.mark.parametrize("seqlen_q,given_ws", [(1, False), (4, True), (8, False), (32, True)])
 def test_nvfp4_decode_runner(msa, seqlen_q, given_ws):
     # prepare once, call: equals the plain call bitwise and the oracle within
     # tolerance; a captured call replays the same result
@@ -81,12 +81,15 @@ def test_nvfp4_decode_runner(msa, seqlen_q, given_ws):
                            num_qo_heads=16, num_kv_heads=1, topk=16, paged=True,
                            kv_dtype=synth.KV_E2M1, seed=70 + seqlen_q, selection="decode",
                            k_global_scale=0.5, v_global_scale=2.0).to("cuda")
-    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda") if given_ws else None
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda") if given_ws else None
     run = msa.prepare_msa_nvfp4_sparse_decode(
         p.q, p.k, p.v, p.q2k, k_scale=p.k_scale, v_scale=p.v_scale, page_table=p.page_table,
         seqused_k=p.seqused_k, k_global_scale=0.5, v_global_scale=2.0, workspace_buffer=ws,
         seqlen_q=seqlen_q)
     assert run.splits >= 1
+    # one token's 16 heads fill a row tile: every seqlen_q in the runner's
+    # envelope takes the decode kernel (in-register E2M1, no staged context)
+    assert run.decode_route == 1
     out = run().clone()
     lse = run.lse.clone()
     ref = gpu_attention(msa, p)

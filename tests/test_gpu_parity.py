@@ -103,7 +103,14 @@ def test_decode_flat_e2m1(msa, splits):
                            num_qo_heads=16, num_kv_heads=2, topk=6, kv_dtype=synth.KV_E2M1,
                            seed=31 + splits, selection="decode", k_global_scale=0.5,
                            v_global_scale=2.0)
-    out, lse = gpu_attention(msa, _dev(p), splits=splits)
+    d = _dev(p)
+    # flat E2M1 takes the prefill tiles over staged bf16 pages of only the
+    # selected blocks; a requested split factor is not used there
+    route = msa.attention_plan(d.q, d.k, d.v, d.q2k, d.cu_seqlens_q, d.cu_seqlens_k,
+                               k_scale=d.k_scale, v_scale=d.v_scale, max_seqlen_q=1,
+                               max_k_tiles=p.max_k_tiles, splits=splits)
+    assert route == (0, 1)
+    out, lse = gpu_attention(msa, d, splits=splits)
     ref_out, ref_lse = oracle_attention(p)
     assert_attention_close(out, lse, ref_out, ref_lse, "decode flat e2m1")
 
@@ -513,3 +520,51 @@ def test_proxy_fp16_matches_oracle(msa, ql, kl, hq, hkv, paged, reduce):
                              page_table=p.page_table, seqused_k=p.seqused_k, causal=True,
                              max_k_tiles=T, reduce_heads=reduce, kv_format=synth.KV_F16)
     assert_proxy_close(got, ref, "fp16 proxy")
+
+
+@pytest.mark.parametrize("route", ["flat_selected", "flat_whole", "paged_decode"])
+def test_e2m1_every_scale_byte(msa, route):
+    # 256 one-key requests; request b's K and V block scales are the E4M3 byte
+    # b and every E2M1 code is 1.0, so out = v_gs * decode(b) and lse = z of
+    # that one key, NaN for the NaN bytes 0x7F / 0xFF.  Covers the staged
+    # flat route (selected blocks, and every visible block) and the paged
+    # decode kernel.
+    print(f"E2M1 scale bytes, {route}", flush=True)
+    dev = torch.device("cuda", 0)
+    n, hq = 256, 16
+    byte = torch.arange(n, dtype=torch.int32).to(torch.uint8)
+    q = torch.full((n, hq, 128), 0.01, dtype=torch.bfloat16)
+    cu = torch.arange(n + 1, dtype=torch.int32)
+    q2k = torch.zeros(1, n, 1, dtype=torch.int32)
+    paged = route == "paged_decode"
+    if paged:
+        k = torch.full((n, 1, 128, 64), 0x22, dtype=torch.uint8)
+        sc = byte.view(n, 1, 1, 1).expand(n, 1, 128, 8).contiguous()
+        pt = torch.arange(n, dtype=torch.int32).view(n, 1)
+        used = torch.ones(n, dtype=torch.int32)
+        kw = dict(page_table=pt, seqused_k=used)
+    else:
+        k = torch.full((n, 1, 64), 0x22, dtype=torch.uint8)
+        sc = byte.view(n, 1, 1).expand(n, 1, 8).contiguous()
+        kw = dict(cu_seqlens_k=cu)
+    v = k.clone()
+    ref_out, ref_lse = oracle.sparse_attention(
+        q, k, v, q2k, cu, causal=True, kv_format=synth.KV_E2M1, k_scale=sc, v_scale=sc.clone(),
+        k_global_scale=0.5, v_global_scale=2.0, **kw)
+    d = {key: val.to(dev) for key, val in kw.items()}
+    out, lse = msa.sparse_attention(
+        q.to(dev), k.to(dev), v.to(dev), q2k.to(dev), cu.to(dev), d.get("cu_seqlens_k"),
+        causal=True, page_table=d.get("page_table"), seqused_k=d.get("seqused_k"),
+        return_softmax_lse=True, k_scale=sc.to(dev), v_scale=sc.to(dev), k_global_scale=0.5,
+        v_global_scale=2.0, max_seqlen_q=4096 if route == "flat_whole" else 1, max_k_tiles=1)
+    torch.cuda.synchronize()
+    out, lse = out.cpu().double(), lse.cpu().double()
+    nan = torch.isnan(ref_out)
+    assert torch.equal(torch.isnan(out), nan) and torch.equal(torch.isnan(lse), torch.isnan(ref_lse))
+    assert bool(nan[0x7F].all() and nan[0xFF].all()) and int(nan.any(-1).any(-1).sum()) == 2
+    fin = ~nan
+    # every E4M3 value is a bf16 value: the output is that value to within
+    # the bf16 rounding of a softmax weight of one
+    assert bool(((out[fin] - ref_out[fin]).abs() <= ref_out[fin].abs() * 2.0 ** -8).all())
+    f = ~torch.isnan(ref_lse)
+    assert float((lse[f] - ref_lse[f]).abs().max()) <= 1e-3

@@ -698,3 +698,75 @@ def test_qsa_bitmap_indices_layout():
     assert idx[0].tolist()[:6] == [4, 5, 6, 7, 12, 13] and (idx[0, 6:] == -1).all()
     assert (idx[1] == -1).all()
     assert idx[2].tolist()[:4] == [0, 1, 2, 3]
+
+
+# ---------------------------------------------------------------------------
+# head reduction and the score -> KV-head mapping (msa_proxy_score page,
+# Parameters: reduce_heads; msa_sparse_attention page, Parameters: q2k_indices)
+# ---------------------------------------------------------------------------
+
+def test_reduce_heads_hand_built():
+    # 3 heads, 2 blocks, 2 queries; the maximum sits in a different head for
+    # every (block, query), so taking any single head, a mean, or the wrong
+    # axis gives a different tensor
+    s = torch.tensor([[[1.0, -5.0], [0.0, 2.0]],
+                      [[3.0, -6.0], [float("-inf"), 1.0]],
+                      [[2.0, -4.0], [-1.0, 7.0]]], dtype=torch.float64)
+    want = torch.tensor([[[3.0, -4.0], [0.0, 7.0]]], dtype=torch.float64)
+    assert torch.equal(oracle.reduce_heads(s), want)
+    # all -inf across heads stays -inf
+    z = torch.full((2, 1, 1), float("-inf"))
+    assert oracle.reduce_heads(z).item() == float("-inf")
+
+
+def _brute_group_topk(s, hkv, topk, heads_of):
+    """Per KV head g: max over the score heads heads_of(g), then rank counting."""
+    hs, T, n = len(s), len(s[0]), len(s[0][0])
+    out = []
+    for g in range(hkv):
+        rows = []
+        for i in range(n):
+            row = []
+            for t in range(T):
+                m = float("-inf")
+                for h in heads_of(g):
+                    if s[h][t][i] > m:
+                        m = s[h][t][i]
+                row.append(m)
+            rows.append(_brute_topk(row, topk))
+        out.append(rows)
+    return out
+
+
+@pytest.mark.parametrize("G,hkv", [(4, 3), (2, 2), (3, 1)])
+def test_group_and_all_modes_match_brute_force(G, hkv):
+    rng = random.Random(G * 10 + hkv)
+    hs, T, n, topk = G * hkv, 9, 6, 3
+    s = [[[float(np.float32(rng.gauss(0, 1))) for _ in range(n)] for _ in range(T)]
+         for _ in range(hs)]
+    for h in range(hs):                           # some -inf blocks
+        s[h][T - 1][0] = float("-inf")
+    st = torch.tensor(s, dtype=torch.float32)
+    got = oracle.topk_select(st, topk, hkv, mode="group").tolist()
+    assert got == _brute_group_topk(s, hkv, topk, lambda g: range(g * G, g * G + G))
+    got_all = oracle.topk_select(st, topk, hkv, mode="all").tolist()
+    assert got_all == _brute_group_topk(s, hkv, topk, lambda g: range(hs))
+    # auto picks "group" for H_s = G * Hkv > Hkv
+    if G > 1:
+        assert oracle.topk_select(st, topk, hkv).tolist() == got
+
+
+def test_group_mode_uses_contiguous_heads():
+    # Hq = 4, Hkv = 2: query heads 0, 1 belong to KV head 0 (h // G), not
+    # heads 0, 2 (h % Hkv).  Head 1 alone scores block 2 highest, so KV head 0
+    # must select block 2 and KV head 1 must not; taking one head per group
+    # (the first) would not select it either.
+    s = torch.full((4, 4, 1), 0.0)
+    s[:, 0, 0] = 1.0                     # every head likes block 0
+    s[1, 2, 0] = 9.0                     # only head 1 likes block 2
+    s[3, 3, 0] = 5.0                     # only head 3 likes block 3
+    got = oracle.topk_select(s, 2, 2, mode="group")[:, 0].tolist()
+    assert got == [[0, 2], [0, 3]]
+    # "all": the max over the four heads, shared by both KV heads
+    got = oracle.topk_select(s, 2, 2, mode="all")[:, 0].tolist()
+    assert got == [[2, 3], [2, 3]]
