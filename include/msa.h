@@ -124,7 +124,9 @@ typedef struct {
                              strides multiples of 16.  Flat [total_k, Hkv, 8]
                              in (token, head) order or any view of 8-byte rows
                              (strides multiples of 8); flat E2M1 takes the
-                             prefill route at every shape                     */
+                             prefill route at every shape.  The E4M3 NaN
+                             bytes (0x7F, 0xFF) are outside the caller
+                             contract: outputs are NaN, the LSE unspecified   */
   const void* v_scale;    /* E2M1 only: same, stored linearly                 */
   msa_strides_t k_strides, v_strides, k_scale_strides, v_scale_strides;
   const int32_t* q2k;     /* [Hkv, total_q, topk] block ids, ascending, -1 padded */
@@ -149,9 +151,11 @@ typedef struct {
 /* Bytes of workspace msa_sparse_attention needs for these arguments: the
  * fp32 split-KV partials (O / l per row) and their LSE
  * (prepare_msa_nvfp4_sparse_decode page, Parameters: workspace_buffer), or,
- * for fp8 / E2M1 K/V on the prefill route, the bf16 pages their visible
- * blocks are converted to (2 * batch * max_k_tiles * Hkv * 32 KiB plus the
- * page table and lengths).  0 for bf16 / fp16 K/V on the prefill route and
+ * for fp8 / E2M1 K/V on the prefill route, the bf16 pages their blocks are
+ * converted to: 2 * batch * S * Hkv * 32 KiB plus the page table and
+ * lengths, with S = max_k_tiles (every visible block), or, when
+ * max_seqlen_q * Hkv * topk <= 2048, S = min(that product, max_k_tiles)
+ * (only the blocks some query of the request selected).  0 for bf16 / fp16 K/V on the prefill route and
  * for decode shapes whose plan uses one split.  The buffer is 256-byte
  * aligned, owned by the caller, needs no initialisation and carries no
  * state between launches: every launch writes what it reads later on the
@@ -174,7 +178,11 @@ msa_status_t msa_sparse_attention_plan(const msa_attn_args_t* args, int32_t* dec
  * and write out (and lse) directly, or through split-KV partials merged by
  * LSE on the decode route.  q2k entries outside [0, ceil(Lk/128)) and -1 are
  * ignored; rows must be ascending without duplicates (caller contract).
- * `workspace` may be NULL when the size query returned 0. */
+ * Route: the decode kernel when max_seqlen_q * G <= 64, or, with
+ * G = Hq / Hkv in [16, 64], when max_seqlen_q <= 64 (one token per tile);
+ * flat E2M1 and the temperature LSE always take prefill tiles.  A prefill
+ * tile holds 256 query rows (128 with the temperature LSE): a larger G is
+ * MSA_ERR_SHAPE.  `workspace` may be NULL when the size query returned 0. */
 msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
