@@ -2,12 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Default workload: flat causal prefill, 2 x 8192 tokens, 16 q heads / 2 KV
+Headline workload: flat causal prefill, 2 x 8192 tokens, 16 q heads / 2 KV
 heads, head_dim 128, topk 16, with the full pipeline per step: proxy score
 (2 indexer heads) -> top-K block select -> sparse attention with LSE.  The
 metric is selected-block attention TFLOP/s: FLOPs counted over the keys each
 query actually attends (4 * head_dim per key and query head), divided by the
 step time.  Inputs are seeded synthetic tensors resident in HBM before timing.
+Without --workload the line also carries, under "configs", the other four
+MSA workloads (the 1 x 1024 prefill and the three paged decodes), each with
+its time, throughput, roofline fraction and oracle baseline.
 
 The decode workloads (--workload paged_decode_...) report KV GB/s over the
 K/V blocks actually gathered, timed cold: a 1 GiB read evicts L2 and MALL
@@ -44,7 +47,9 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help="time this workload alone (default: the 2 x 8192 prefill pipeline as "
+                         "the headline line, with every other MSA workload under 'configs')")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kv-format", choices=("bf16", "fp8"), default="bf16",
                     help="prefill workloads: K/V stored as bf16 (default) or fp8 E4M3 (the "
@@ -63,6 +68,11 @@ def _args():
 def _events(n):
     import torch
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+TRAFFIC_SOURCE = ("stored: profiles/traffic.json, rocprofv3 FETCH_SIZE + WRITE_SIZE per launch "
+                  "(copy-calibrated), used only while the kernel sources hash as when taken; "
+                  "not measured in this run")
 
 
 def _traffic_for(kernel: str):
@@ -460,15 +470,10 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy, args.steps)
         return
-    if args.workload in (synth.QSA_WORKLOAD, synth.QSA_BITMAP_WORKLOAD):
-        res, p = bench_qsa(args, msa, synth, torch)
-        cpu = None if args.no_cpu_baseline else cpu_baseline_qsa(p, 512)
-    elif args.workload == DEFAULT_WORKLOAD or args.workload.startswith("flat_prefill"):
-        res, p = bench_prefill_pipeline(args, msa, synth, torch)
-        cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(p, args.cpu_sample_rows)
-    else:
-        res, p = bench_decode(args, msa, synth, torch)
-        cpu = None if args.no_cpu_baseline else cpu_baseline_decode(p, p.total_q, p.kv_dtype)
+    single = args.workload is not None
+    if not single:
+        args.workload = DEFAULT_WORKLOAD
+    res, cpu = run_workload(args, msa, synth, torch)
     line = {
         "metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
@@ -481,7 +486,42 @@ def main():
             line[k] = res[k]
     line["roofline"] = res["roofline"]
     line["cpu_baseline"] = cpu
+    if not single:
+        # the other MSA workloads, each timed as in its own --workload run
+        # (decode cold), with its roofline fraction and oracle baseline
+        line["configs"] = {}
+        for name in synth.WORKLOADS:
+            if name == DEFAULT_WORKLOAD:
+                continue
+            args.workload = name
+            r, c = run_workload(args, msa, synth, torch)
+            ent = {"metric": r["metric"], "value": r["value"], "unit": r["unit"],
+                   "ms_per_step": r["ms_per_step"], "dtype": r["dtype"]}
+            for k in ("tokens_per_s", "stages_ms", "work"):
+                if k in r:
+                    ent[k] = r[k]
+            ent["roofline"] = r["roofline"]
+            ent["cpu_baseline"] = c
+            line["configs"][name] = ent
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
+
+
+def run_workload(args, msa, synth, torch):
+    """(result, cpu baseline) of args.workload."""
+    if args.workload in (synth.QSA_WORKLOAD, synth.QSA_BITMAP_WORKLOAD):
+        res, p = bench_qsa(args, msa, synth, torch)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_qsa(p, 512)
+    elif args.workload.startswith("flat_prefill"):
+        res, p = bench_prefill_pipeline(args, msa, synth, torch)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_prefill(p, args.cpu_sample_rows)
+    else:
+        res, p = bench_decode(args, msa, synth, torch)
+        cpu = None if args.no_cpu_baseline else cpu_baseline_decode(p, p.total_q, p.kv_dtype)
+    rf = res["roofline"]
+    rf["traffic_source"] = TRAFFIC_SOURCE if rf.get("traffic") is not None else None
+    del p
+    return res, cpu
 
 
 if __name__ == "__main__":
