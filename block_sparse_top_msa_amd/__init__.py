@@ -23,7 +23,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "attention_plan",
+    "attention_plan", "sparse_attention_noalloc",
     "MsaError", "lib", "library_path", "sparse_attention", "validate_attention",
     "prepare_msa_nvfp4_sparse_decode", "MSANvfp4DecodeRunner", "proxy_score",
     "topk_select",
@@ -42,8 +42,8 @@ BLOCK = 128
 EXPORTED_SYMBOLS = (
     "msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
     "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward", "msa_qsa_bitmap_forward",
-    "msa_validate_attention", "msa_sparse_attention_plan", "msa_status_string",
-    "msa_last_error", "msa_version",
+    "msa_validate_attention", "msa_sparse_attention_plan", "msa_sparse_attention_noalloc",
+    "msa_status_string", "msa_last_error", "msa_version",
 )
 
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_DTYPE",
@@ -120,6 +120,7 @@ def _load():
     L.msa_sparse_attention_workspace_size.argtypes = [ctypes.POINTER(AttnArgs),
                                                       ctypes.POINTER(ctypes.c_size_t)]
     L.msa_sparse_attention.argtypes = [ctypes.POINTER(AttnArgs), _P, ctypes.c_size_t, _P]
+    L.msa_sparse_attention_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _P]
     L.msa_proxy_score.argtypes = [ctypes.POINTER(ProxyArgs), _P]
     L.msa_topk_select.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
@@ -133,7 +134,7 @@ def _load():
     for fn in ("msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
                "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward",
                "msa_qsa_bitmap_forward", "msa_validate_attention",
-               "msa_sparse_attention_plan"):
+               "msa_sparse_attention_plan", "msa_sparse_attention_noalloc"):
         getattr(L, fn).restype = ctypes.c_int
     L.msa_status_string.argtypes = [ctypes.c_int]
     L.msa_status_string.restype = ctypes.c_char_p
@@ -356,6 +357,27 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
     if return_temperature_lse:
         return out, lse, lse_t
     return (out, lse) if return_softmax_lse else out
+
+
+def sparse_attention_noalloc(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None,
+                             causal=False, softmax_scale=None, page_table=None, seqused_k=None,
+                             k_scale=None, v_scale=None, k_global_scale=None,
+                             v_global_scale=None, *, max_seqlen_q, max_k_tiles, out, lse=None,
+                             splits=0):
+    """sparse_attention through msa_sparse_attention_noalloc: the library's
+    own per-GPU scratch serves as the workspace, and the caller passes every
+    output, so nothing is allocated (on the host side nothing is read from
+    the device either).  Calls that may overlap on one GPU race on the
+    scratch.  Returns out (and lse when given)."""
+    for name, t in (("q2k_indices", q2k_indices), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k), ("page_table", page_table),
+                    ("seqused_k", seqused_k)):
+        _check_i32(name, t)
+    a = _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, causal, softmax_scale,
+                   page_table, seqused_k, k_scale, v_scale, k_global_scale, v_global_scale,
+                   max_seqlen_q, max_k_tiles, out, lse, splits)
+    _check(lib.msa_sparse_attention_noalloc(ctypes.byref(a), _stream()))
+    return out if lse is None else (out, lse)
 
 
 class MSANvfp4DecodeRunner:

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/msa.h"
 #include "internal.hpp"
@@ -375,11 +376,15 @@ msa_status_t msa_validate_attention(const msa_attn_args_t* a, void* stream) {
   return fail(MSA_ERR_CONTRACT, "contract violation kind %d at %lld", kind, pos);
 }
 
-msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  Resolved r;
-  msa_status_t st = resolve_attention(args, &r, true);
-  if (st) return st;
+}  // extern "C"
+
+namespace {
+
+// Launches a resolved attention call with `workspace` (already checked for
+// size when r.ws_bytes > 0).
+msa_status_t run_attention(const msa_attn_args_t* args, Resolved& r, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  msa_status_t st;
   // debug path: check the device-side contracts first (synchronises the stream)
   const char* env = std::getenv("MSA_VALIDATE");
   if (env && env[0] == '1' && (st = msa_validate_attention(args, stream))) return st;
@@ -415,6 +420,62 @@ msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
   return hip_status(msa::launch_attention(r.p, args->kv_dtype, r.plan,
                                           static_cast<hipStream_t>(stream)),
                     "msa_sparse_attention launch");
+}
+
+// Scratch of the allocation-free entry point: one array per GPU the library
+// runs on, held until the process ends.  Host code never passes `scratch`
+// itself (in host code the name is not a device address): it looks up each
+// device's address once with hipGetSymbolAddress and passes that.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on its first use.
+msa_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MSA_ERR_UNSUPPORTED, "device %d is past the %d devices the scratch table holds",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  Resolved r;
+  msa_status_t st = resolve_attention(args, &r, true);
+  if (st) return st;
+  return run_attention(args, r, workspace, workspace_bytes, stream);
+}
+
+msa_status_t msa_sparse_attention_noalloc(const msa_attn_args_t* args, void* stream) {
+  Resolved r;
+  msa_status_t st = resolve_attention(args, &r, true);
+  if (st) return st;
+  if (r.ws_bytes > kScratchBytes)
+    return fail(MSA_ERR_WORKSPACE,
+                "these arguments need %zu bytes of workspace; the allocation-free entry point "
+                "holds %zu (use msa_sparse_attention with a caller workspace)",
+                r.ws_bytes, kScratchBytes);
+  void* ws = nullptr;
+  if (r.ws_bytes && (st = scratch_address(&ws))) return st;
+  return run_attention(args, r, ws, r.ws_bytes ? kScratchBytes : 0, stream);
 }
 
 msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {

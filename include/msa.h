@@ -186,6 +186,19 @@ msa_status_t msa_sparse_attention_plan(const msa_attn_args_t* args, int32_t* dec
 msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* msa_sparse_attention for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the workspace is the library's own scratch array of 32 MiB per
+ * GPU (a file-scope device array, held until the process ends), so the
+ * caller passes only inputs and outputs.  Nothing is allocated or freed.
+ * Arguments whose workspace size query exceeds 32 MiB return
+ * MSA_ERR_WORKSPACE before any launch (msa_sparse_attention with a caller
+ * workspace takes them).  Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (different streams or threads) race and
+ * must be serialised by the caller.  The scratch needs no clearing: every
+ * launch writes what it later reads.  Same statuses otherwise. */
+msa_status_t msa_sparse_attention_noalloc(const msa_attn_args_t* args, void* stream);
+
 /* Debug check of the device-side caller contracts of msa_sparse_attention
  * with these arguments (msa_sparse_attention page, Parameters: cu_seqlens_q,
  * cu_seqlens_k, q2k_indices, page_table, seqused_k): cu_seqlens_q starts at

@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declarations_are_exported():
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(msa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(msa.lib, n), n
@@ -340,3 +340,13 @@ def test_flat_e2m1_decode_stages_only_selected_blocks():
               max_seqlen_q=2048, max_k_tiles=16, kv_dtype=2, k_scale=FAKE, v_scale=FAKE)
     st, n = _size(b)
     assert st == 0 and 2 * 16 * page <= n < 2 * 16 * page + (1 << 20)
+
+
+def test_noalloc_rejects_workspace_beyond_its_scratch():
+    # fp8 prefill over 64 requests x 1024 blocks stages GBs: declined before
+    # any device call, naming the limit
+    a = _attn(batch=64, total_q=64 * 1024, num_qo_heads=16, num_kv_heads=2, topk=16,
+              max_seqlen_q=1024, max_k_tiles=1024, kv_dtype=1)
+    st = msa.lib.msa_sparse_attention_noalloc(ctypes.byref(a), None)
+    msg = msa.lib.msa_last_error().decode()
+    assert st == 6 and "33554432" in msg
