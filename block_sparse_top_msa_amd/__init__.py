@@ -83,6 +83,8 @@ class AttnArgs(ctypes.Structure):
         ("page_table", _I32P), ("seqused_k", _I32P),
         ("out", _P), ("lse", _P),
         ("lse_t", _P), ("lse_temperature_scale", ctypes.c_float),
+        ("q_offset_mode", ctypes.c_int32), ("q_offset_value", ctypes.c_int32),
+        ("q_offset", _I32P),
     ]
 
 
@@ -97,6 +99,8 @@ class ProxyArgs(ctypes.Structure):
         ("q", _P), ("k", _P), ("k_strides", Strides),
         ("cu_seqlens_q", _I32P), ("cu_seqlens_k", _I32P), ("page_table", _I32P),
         ("seqused_k", _I32P), ("out", _P),
+        ("q_offset_mode", ctypes.c_int32), ("q_offset_value", ctypes.c_int32),
+        ("q_offset", _I32P),
     ]
 
 
@@ -258,6 +262,22 @@ def _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, causal, softmax
     return a
 
 
+def _set_q_offset(a, q_offset, total_q):
+    """q_offset: None (right-aligned causal positions), an int o (query iq of
+    every request at KV position o + iq) or a device int32 tensor [total_q]
+    (each query row's own position)."""
+    if q_offset is None:
+        a.q_offset_mode = 0
+    elif isinstance(q_offset, int):
+        a.q_offset_mode, a.q_offset_value = 1, int(q_offset)
+    else:
+        if (q_offset.dtype != torch.int32 or not q_offset.is_contiguous()
+                or q_offset.numel() != total_q):
+            raise ValueError(f"q_offset must be an int or a contiguous int32 tensor of "
+                             f"{total_q} query positions")
+        a.q_offset_mode, a.q_offset = 2, _ptr(q_offset)
+
+
 def _check_i32(name, t):
     if t is not None and (t.dtype != torch.int32 or not t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous int32 tensor")
@@ -316,10 +336,13 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
                      k_global_scale=None, v_global_scale=None, *, max_seqlen_q=None,
                      max_k_tiles=None, workspace: Optional[Workspace] = None, out=None,
                      lse=None, splits=0, return_temperature_lse=False,
-                     lse_temperature_scale=1.0, lse_t=None):
+                     lse_temperature_scale=1.0, lse_t=None, q_offset=None):
     """MSA forward (msa_sparse_attention page).  Returns out, or (out, lse),
     or with return_temperature_lse (out, lse, lse_t), lse_t = ln sum_j
-    exp(lse_temperature_scale * z_j) over the attended keys."""
+    exp(lse_temperature_scale * z_j) over the attended keys.  q_offset: the
+    queries' causal positions, None (right-aligned), an int o (query iq of
+    every request at o + iq) or an int32 tensor [total_q] of per-row
+    positions."""
     want = torch.float16 if k.dtype == torch.float16 else torch.bfloat16
     if q.dtype != want or not q.is_contiguous():
         raise ValueError(f"q must be a contiguous {want} tensor (total_q, num_qo_heads, 128) "
@@ -340,6 +363,7 @@ def sparse_attention(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=None, caus
     if return_temperature_lse:
         a.lse_t = _ptr(lse_t)
         a.lse_temperature_scale = float(lse_temperature_scale)
+    _set_q_offset(a, q_offset, q.shape[0])
     need = ctypes.c_size_t(0)
     _check(lib.msa_sparse_attention_workspace_size(ctypes.byref(a), ctypes.byref(need)))
     ws_ptr, ws_bytes = None, 0
@@ -363,7 +387,7 @@ def sparse_attention_noalloc(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=No
                              causal=False, softmax_scale=None, page_table=None, seqused_k=None,
                              k_scale=None, v_scale=None, k_global_scale=None,
                              v_global_scale=None, *, max_seqlen_q, max_k_tiles, out, lse=None,
-                             splits=0):
+                             splits=0, q_offset=None):
     """sparse_attention through msa_sparse_attention_noalloc: the library's
     own per-GPU scratch serves as the workspace, and the caller passes every
     output, so nothing is allocated (on the host side nothing is read from
@@ -376,6 +400,7 @@ def sparse_attention_noalloc(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k=No
     a = _attn_args(q, k, v, q2k_indices, cu_seqlens_q, cu_seqlens_k, causal, softmax_scale,
                    page_table, seqused_k, k_scale, v_scale, k_global_scale, v_global_scale,
                    max_seqlen_q, max_k_tiles, out, lse, splits)
+    _set_q_offset(a, q_offset, q.shape[0])
     _check(lib.msa_sparse_attention_noalloc(ctypes.byref(a), _stream()))
     return out if lse is None else (out, lse)
 
@@ -479,11 +504,13 @@ def prepare_msa_nvfp4_sparse_decode(q, k, v, q2k_indices, *, k_scale, v_scale, p
 
 def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, seqused_k=None,
                 causal=True, max_seqlen_q=None, max_k_tiles=None, output=None,
-                reduce_heads=False):
+                reduce_heads=False, q_offset=None):
     """Stage-1 block max of unscaled masked QK^T (msa_proxy_score page).
     reduce_heads: False (per query head), True (max over all heads) or
-    "group" (max over each KV head's query heads).  Returns fp32
-    (num_qo_heads | 1 | num_kv_heads, max_k_tiles, total_q)."""
+    "group" (max over each KV head's query heads).  q_offset: None
+    (right-aligned), an int o (query iq at o + iq) or an int32 tensor of
+    per-row positions.  Returns fp32 (num_qo_heads | 1 | num_kv_heads,
+    max_k_tiles, total_q)."""
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
                     ("page_table", page_table), ("seqused_k", seqused_k)):
         _check_i32(name, t)
@@ -532,6 +559,7 @@ def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, sequs
     a.page_table = _ptr(page_table)
     a.seqused_k = _ptr(seqused_k)
     a.out = _ptr(output)
+    _set_q_offset(a, q_offset, q.shape[0])
     _check(lib.msa_proxy_score(ctypes.byref(a), _stream()))
     return output
 

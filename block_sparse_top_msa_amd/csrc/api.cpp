@@ -41,6 +41,23 @@ msa_status_t hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// q_offset_mode / q_offset_value / q_offset of the attention and proxy
+// arguments -> the kernels' query positions.
+msa_status_t resolve_qpos(int32_t mode, int32_t value, const int32_t* rows, bool need_ptrs,
+                          msa::QueryPos* out) {
+  if (mode < 0 || mode > 2)
+    return fail(MSA_ERR_UNSUPPORTED, "q_offset_mode must be 0 (right-aligned), 1 (q_offset_value "
+                "+ iq) or 2 (per-row q_offset), got %d", mode);
+  if (mode == 1 && (value < -(1 << 30) || value > (1 << 30)))
+    return fail(MSA_ERR_SHAPE, "q_offset_value %d is outside [-2^30, 2^30]", value);
+  if (mode == 2 && need_ptrs && !rows)
+    return fail(MSA_ERR_NULL, "q_offset_mode 2 needs the q_offset tensor");
+  out->mode = mode;
+  out->base = mode == 1 ? value : 0;
+  out->rows = mode == 2 ? rows : nullptr;
+  return MSA_OK;
+}
+
 constexpr int64_t kMaxTokenStride = (int64_t)1 << 24;
 
 // Longest query (tokens per request) that takes the decode kernel with one
@@ -183,6 +200,9 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   const float kgs = a->k_global_scale > 0.f ? a->k_global_scale : 1.0f;
   p.scale_log2 = scale * kgs * 1.4426950408889634f;
   p.v_gs = a->v_global_scale > 0.f ? a->v_global_scale : 1.0f;
+  if ((st = resolve_qpos(a->q_offset_mode, a->q_offset_value, a->q_offset,
+                         need_ptrs && a->total_q > 0 && a->batch > 0, &p.qpos)))
+    return st;
 
   // ---- plan ----
   msa::AttnPlan& plan = r->plan;
@@ -532,6 +552,8 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
                 a->reduce_heads);
   p.reduce = a->reduce_heads;
   p.max_k_tiles = a->max_k_tiles;
+  if ((st = resolve_qpos(a->q_offset_mode, a->q_offset_value, a->q_offset, true, &p.qpos)))
+    return st;
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows = lqmax * G;
   const int wide = rows > 64;

@@ -309,7 +309,9 @@ __global__ __launch_bounds__(NW * kWave) void msa_attention_kernel(AttnParams p,
     const int tk = r / G;
     const int hh = r % G;
     tk_[s] = tk;
-    pos_[s] = lk - lq + i0 + tk;
+    pos_[s] = tk < ntok ? query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0 + i0 + tk, i0 + tk,
+                                    lq, lk)
+                        : 0;
     const int tfirst = (16 * slot) / G;
     const int tlast = min((16 * slot + 15) / G, ntok - 1);
     unsigned long long m = 0;

@@ -132,6 +132,14 @@ __device__ __forceinline__ void atomic_max_f32(float* addr, float v) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// KV position of local query iq (query row i) of a request with lq queries
+// and lk keys, for the causal mask: right-aligned (mode 0), base + iq (1),
+// or the caller's per-row position (2).
+__device__ __forceinline__ int query_pos(const int32_t* rows, int mode, int base, int i, int iq,
+                                         int lq, int lk) {
+  return mode == 2 ? rows[i] : (mode == 1 ? base + iq : lk - lq + iq);
+}
+
 // Workgroups are handed to the 8 XCDs round-robin by id.  Remapping so that
 // consecutive logical ids share an XCD keeps a (request, KV head)'s K/V in
 // one L2.  `n` logical ids; returns -1 for the padding ids of the last round.

@@ -395,7 +395,9 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
     const int r = 16 * rt + l16;
     const int tk = r < R ? r / G : 64;
     tk_[rt] = tk;
-    pos_[rt] = lk - lq + j0 + tk;
+    pos_[rt] = tk < ntok ? query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0 + tk, j0 + tk,
+                                     lq, lk)
+                         : 0;
     const int tfirst = (16 * rt) / G;
     const int tlast = min((16 * rt + 15) / G, ntok - 1);
     unsigned long long m = 0;

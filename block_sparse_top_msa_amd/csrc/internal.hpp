@@ -18,6 +18,14 @@ struct Strides {
   int64_t page, head, token;  // bytes
 };
 
+// Causal position of the queries: mode 0 right-aligned (Lk - Lq + iq),
+// 1 base + iq, 2 rows[i] for query row i.
+struct QueryPos {
+  const int32_t* rows;
+  int mode;
+  int base;
+};
+
 struct AttnParams {
   const uint16_t* q;          // bf16 [total_q, Hq, 128]
   const uint8_t* k;
@@ -46,6 +54,7 @@ struct AttnParams {
   float* ws_lse;              // [units, splits, rows_pad] their natural-log LSE
   int ws_rows;                // rows per unit (tok_per_tile * group)
   int ws_lse_rows;            // rows_pad: rows rounded up to 32
+  QueryPos qpos;              // causal positions of the queries
 };
 
 // Kernel family selection for one attention call.
@@ -83,6 +92,7 @@ struct ProxyParams {
   int row_tiles;              // ceil(max_seqlen_q * group / rows_per_tile)
   int blocks_per_wg;          // KV blocks per workgroup
   int block_chunks;           // ceil(max_k_tiles / blocks_per_wg)
+  QueryPos qpos;              // causal positions of the queries
 };
 
 hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream);

@@ -12,6 +12,8 @@
 // max over query heads happens in-kernel: within
 // a wave across the G heads of a token, then across KV heads with an exact
 // order-independent atomic max into an output pre-filled with -inf.
+#include <climits>
+
 #include "async_lds.hpp"
 #include "common.hpp"
 #include "internal.hpp"
@@ -158,8 +160,13 @@ __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_ke
   const int t_beg = chunk * p.blocks_per_wg;
   const int t_end = min(t_beg + p.blocks_per_wg, p.max_k_tiles);
   if (t_beg >= t_end) return;
-  const int pos_min = lk - lq;                    // causal position of the first token
-  const int pos_max = lk - lq + (nrows - 1) / G;  // ... and of the last
+  // causal positions of the first and last token (bounds of the block
+  // range and of fully visible blocks); per-row positions have no order,
+  // so they bound nothing
+  const bool rowpos = p.qpos.mode == 2;
+  const int pos0 = query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0, 0, lq, lk);
+  const int pos_min = rowpos ? INT_MIN : pos0;
+  const int pos_max = rowpos ? INT_MAX : pos0 + (nrows - 1) / G;
   int t_act = min(t_end, nblk);
   if (p.paged) t_act = min(t_act, p.pt_width);
   if (p.causal) t_act = min(t_act, pos_max < 0 ? 0 : pos_max / kBlock + 1);
@@ -184,7 +191,7 @@ __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_ke
     const int r = 32 * nt + col;
     row_[nt] = r;
     const int tk = r / G, hh = r % G;
-    pos_[nt] = lk - lq + tk;
+    pos_[nt] = r < nrows ? query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0 + tk, tk, lq, lk) : 0;
     if (r < nrows) {
       const uint8_t* qp = reinterpret_cast<const uint8_t*>(
           p.q + ((int64_t)(q0 + tk) * p.hq + g * G + hh) * kHeadDim) + 128 * half;
@@ -459,8 +466,10 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   const int t_end = min(t_beg + p.blocks_per_wg, p.max_k_tiles);
   if (t_beg >= t_end) return;
   const int r_last = min(r0 + 256, nrows) - 1;
-  const int pos_min = lk - lq + r0 / G;
-  const int pos_max = lk - lq + r_last / G;
+  const bool rowpos = p.qpos.mode == 2;
+  const int pos0 = query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0, 0, lq, lk);
+  const int pos_min = rowpos ? INT_MIN : pos0 + r0 / G;
+  const int pos_max = rowpos ? INT_MAX : pos0 + r_last / G;
   int t_act = min(t_end, nblk);
   if (p.paged) t_act = min(t_act, p.pt_width);
   if (p.causal) t_act = min(t_act, pos_max < 0 ? 0 : pos_max / kBlock + 1);
@@ -491,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
     const int r = r0 + 64 * wave + 32 * nt + col;
     row_[nt] = r;
     const int tk = r / G, hh = r % G;
-    pos_[nt] = lk - lq + tk;
+    pos_[nt] = r < nrows ? query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0 + tk, tk, lq, lk) : 0;
     if (r < nrows) {
       const uint8_t* qp = reinterpret_cast<const uint8_t*>(
           p.q + ((int64_t)(q0 + tk) * p.hq + g * G + hh) * kHeadDim) + 128 * half;

@@ -146,6 +146,17 @@ typedef struct {
                              Computed by the general kernel at every shape;
                              bf16 / fp8 / E2M1 K/V; else MSA_ERR_UNSUPPORTED  */
   float lse_temperature_scale; /* > 0 when lse_t is set (1 gives lse)        */
+  /* Causal positions of the queries (msa_sparse_attention page, Parameters:
+     q_offset; the page calls it a per-query offset tensor and defines it no
+     further).  Reading: q_offset_mode 0 (default): right-aligned, query iq
+     of a request at KV position Lk - Lq + iq; 1: query iq of every request
+     at q_offset_value + iq; 2: query row i at q_offset[i] (device int32
+     [total_q]).  Key j is visible iff j <= that position (and j < Lk); a
+     position below 0 leaves the row empty (out 0, lse -inf).  Read only
+     with causal; other modes are MSA_ERR_UNSUPPORTED. */
+  int32_t q_offset_mode;
+  int32_t q_offset_value;
+  const int32_t* q_offset;
 } msa_attn_args_t;
 
 /* Bytes of workspace msa_sparse_attention needs for these arguments: the
@@ -238,6 +249,13 @@ typedef struct {
   const int32_t* page_table;     /* paged route, with seqused_k              */
   const int32_t* seqused_k;
   float* out;             /* fp32 [Hq | 1 | Hkv, max_k_tiles, total_q], written in full */
+  /* Causal positions of the queries (msa_proxy_score page, Parameters:
+     q_offset, an int or a tensor used by the causal alignment), as in
+     msa_attn_args_t: mode 0 right-aligned, 1 q_offset_value + iq, 2
+     q_offset[i] per query row. */
+  int32_t q_offset_mode;
+  int32_t q_offset_value;
+  const int32_t* q_offset;
 } msa_proxy_args_t;
 
 /* max_score[h, t, i]: the max over the keys of block t of the UNSCALED dot

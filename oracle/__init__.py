@@ -47,7 +47,8 @@ BLOCK = 128  # tokens per KV block / page
 __all__ = [
     "BLOCK", "decode_bf16", "decode_f16", "decode_q", "decode_e4m3fn", "decode_e2m1",
     "unpack_e2m1x2", "qsa_indexed_attention", "qsa_bitmap_indices", "qsa_bitmap_attention",
-    "dequant_e2m1", "decode_kv", "request_lengths", "logical_kv", "proxy_score",
+    "dequant_e2m1", "decode_kv", "request_lengths", "logical_kv", "query_positions",
+    "proxy_score",
     "reduce_heads", "selection_scores", "topk_select", "tile_union",
     "allowed_keys", "sparse_attention", "lse_merge",
 ]
@@ -227,20 +228,42 @@ def logical_kv(side, kv_format, scale, b, blocks, lk, cu_seqlens_k=None, page_ta
     return torch.cat(pos), torch.cat(vals, dim=0)
 
 
-def allowed_keys(pos_keys: torch.Tensor, lq: int, lk: int, causal: bool) -> torch.Tensor:
+def query_positions(q0: int, lq: int, lk: int, q_offset=None) -> torch.Tensor:
+    """KV position of each local query iq of a request (int64 [Lq]).
+
+    Default: right-aligned, Lk - Lq + iq (msa_proxy_score page, Parameters:
+    causal; prepare_msa_nvfp4_sparse_decode page, Parameters: seqlen_q).
+    With q_offset (msa_proxy_score page, Parameters: q_offset, a query
+    position offset used by the causal alignment; msa_sparse_attention page,
+    Parameters: q_offset, a per-query offset tensor).  Reading, since the
+    pages define neither form further: an int o places query iq of every
+    request at o + iq (o replaces the right alignment's Lk - Lq); a tensor
+    holds each query row's own position, q_offset[q0 + iq].  Parity of this
+    reading against the pages' kernels is unpinned.
+    """
+    iq = torch.arange(lq, dtype=torch.int64)
+    if q_offset is None:
+        return (lk - lq) + iq
+    if isinstance(q_offset, int):
+        return int(q_offset) + iq
+    return torch.as_tensor(q_offset).cpu().to(torch.int64)[q0:q0 + lq].clone()
+
+
+def allowed_keys(pos_keys: torch.Tensor, lq: int, lk: int, causal: bool,
+                 qpos: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Bool [Lq, n]: key j may be seen by local query iq.
 
-    Causal masking is right-aligned: query iq sits at KV position
-    Lk - Lq + iq and sees keys j <= that position (msa_proxy_score page,
-    Parameters: causal; prepare_msa_nvfp4_sparse_decode page, Parameters:
-    seqlen_q).  Reading for flat prefill with Lq != Lk: the same right
-    alignment.  Keys j >= Lk never exist.
+    Causal: query iq sees keys j <= its KV position, qpos[iq] (default the
+    right alignment Lk - Lq + iq, see query_positions).  Reading for flat
+    prefill with Lq != Lk: the same right alignment.  Keys j >= Lk never
+    exist.
     """
-    iq = torch.arange(lq, dtype=torch.int64).unsqueeze(1)
+    if qpos is None:
+        qpos = (lk - lq) + torch.arange(lq, dtype=torch.int64)
     j = pos_keys.unsqueeze(0)
     ok = (j < lk).expand(lq, -1)
     if causal:
-        ok = ok & (j <= (lk - lq) + iq)
+        ok = ok & (j <= qpos.unsqueeze(1))
     return ok
 
 
@@ -251,7 +274,7 @@ def allowed_keys(pos_keys: torch.Tensor, lq: int, lk: int, causal: bool) -> torc
 def proxy_score(q, k, cu_seqlens_q, *, cu_seqlens_k=None, page_table=None,
                 seqused_k=None, causal=True, max_k_tiles=None, reduce_heads=False,
                 kv_format="bf16", rows: Optional[Sequence[int]] = None,
-                chunk: int = 512):
+                chunk: int = 512, q_offset=None):
     """max_score[h, t, i]: max over keys j of block t (128 t <= j < 128 t + 128,
     j < Lk, j allowed by the causal rule) of the unscaled dot product
     q[i, h] . k[j, h // G]; -inf where no key qualifies or t is past the
@@ -282,7 +305,8 @@ def proxy_score(q, k, cu_seqlens_q, *, cu_seqlens_k=None, page_table=None,
         pad = nblk * BLOCK - lk
         for c0 in range(0, len(local), chunk):
             li = torch.tensor(local[c0:c0 + chunk], dtype=torch.int64)
-            ok = allowed_keys(pos, lq, lk, causal)[li]            # (n, Lk)
+            qpos = query_positions(q0, lq, lk, q_offset)
+            ok = allowed_keys(pos, lq, lk, causal, qpos)[li]      # (n, Lk)
             qb = decode_q(q[q0 + li])                           # (n, hq, d)
             for h in range(hq):
                 z = qb[:, h, :] @ kv[:, h // G, :].T               # (n, Lk)
@@ -404,7 +428,7 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
                      softmax_scale=None, kv_format="bf16", k_scale=None,
                      v_scale=None, k_global_scale=None, v_global_scale=None,
                      rows: Optional[Sequence[int]] = None, chunk: int = 256,
-                     lse_temperature_scale: Optional[float] = None):
+                     lse_temperature_scale: Optional[float] = None, q_offset=None):
     """Dense attention masked down to each query's selected blocks.
 
     For query i of request b, query head h and its KV head g = h // G
@@ -430,6 +454,8 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
     return_temperature_lse, lse_temperature_scale) says only that the scale
     multiplies the exponent; z_j are the logits whose LSE is lse, so tau = 1
     gives lse_t = lse.
+
+    q_offset: the queries' causal positions (see query_positions).
     """
     q = q.cpu()
     q2k = torch.as_tensor(q2k).cpu()
@@ -464,7 +490,8 @@ def sparse_attention(q, k, v, q2k, cu_seqlens_q, *, cu_seqlens_k=None,
                 _, vv = logical_kv(v, kv_format, v_scale, b, blocks, lk, cu_seqlens_k, page_table)
                 kblk = pos // BLOCK
                 chosen = (sel.unsqueeze(2) == kblk.view(1, 1, -1)).any(dim=1)  # (n, nkeys)
-                ok = chosen & allowed_keys(pos, lq, lk, causal)[li]
+                qpos = query_positions(q0, lq, lk, q_offset)
+                ok = chosen & allowed_keys(pos, lq, lk, causal, qpos)[li]
                 any_ok = ok.any(dim=1)
                 for hh in range(G):
                     h = g * G + hh

@@ -350,3 +350,18 @@ def test_noalloc_rejects_workspace_beyond_its_scratch():
     st = msa.lib.msa_sparse_attention_noalloc(ctypes.byref(a), None)
     msg = msa.lib.msa_last_error().decode()
     assert st == 6 and "33554432" in msg
+
+
+def test_q_offset_modes_are_checked_on_the_host():
+    st, msg = _call(_attn(q_offset_mode=3, causal=1))
+    assert st == 5 and "q_offset_mode" in msg
+    st, msg = _call(_attn(q_offset_mode=1, q_offset_value=(1 << 30) + 1, causal=1))
+    assert st == 2 and "q_offset_value" in msg
+    st, msg = _call(_attn(q_offset_mode=2, causal=1))          # no tensor
+    assert st == 1 and "q_offset" in msg
+    p = msa.ProxyArgs()
+    p.batch, p.total_q, p.num_qo_heads, p.num_kv_heads = 1, 4, 4, 2
+    p.head_dim, p.max_seqlen_q, p.max_k_tiles, p.kv_dtype = 128, 4, 2, 0
+    p.q = p.k = p.out = p.cu_seqlens_q = p.cu_seqlens_k = FAKE
+    p.q_offset_mode = 2
+    assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 1

@@ -770,3 +770,114 @@ def test_group_mode_uses_contiguous_heads():
     # "all": the max over the four heads, shared by both KV heads
     got = oracle.topk_select(s, 2, 2, mode="all")[:, 0].tolist()
     assert got == [[2, 3], [2, 3]]
+
+
+# ---------------------------------------------------------------------------
+# q_offset (msa_proxy_score page, Parameters: q_offset; msa_sparse_attention
+# page, Parameters: q_offset).  Reading: the queries' causal positions (an
+# int o: o + iq; a tensor: each row's own position).  The reading itself is
+# unpinned; these pin that the oracle applies it as stated.
+# ---------------------------------------------------------------------------
+
+def _positions(q_lens, k_lens, q_offset):
+    pos = []
+    for b, (Lq, Lk) in enumerate(zip(q_lens, k_lens)):
+        q0 = sum(q_lens[:b])
+        for iq in range(Lq):
+            if q_offset is None:
+                pos.append(Lk - Lq + iq)
+            elif isinstance(q_offset, int):
+                pos.append(q_offset + iq)
+            else:
+                pos.append(int(q_offset[q0 + iq]))
+    return pos
+
+
+def test_q_offset_right_alignment_tensor_is_the_default():
+    q_lens, k_lens = [70, 5], [300, 260]
+    p = synth.make_problem("t", q_lens=q_lens, k_lens=k_lens, num_qo_heads=4, num_kv_heads=2,
+                           head_dim=16, seed=12, selection="general", topk=3)
+    qo = torch.tensor(_positions(q_lens, k_lens, None), dtype=torch.int32)
+    a = oracle.sparse_attention(p.q, p.k, p.v, p.q2k, p.cu_seqlens_q,
+                                cu_seqlens_k=p.cu_seqlens_k, causal=True)
+    b = oracle.sparse_attention(p.q, p.k, p.v, p.q2k, p.cu_seqlens_q,
+                                cu_seqlens_k=p.cu_seqlens_k, causal=True, q_offset=qo)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+    s0 = oracle.proxy_score(p.q, p.k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k, causal=True)
+    s1 = oracle.proxy_score(p.q, p.k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k, causal=True,
+                            q_offset=qo)
+    assert torch.equal(s0, s1)
+
+
+@pytest.mark.parametrize("form", ["int", "tensor"])
+def test_q_offset_proxy_matches_brute_force(form):
+    # queries at the given positions, including ones before every key (all
+    # -inf) and past the sequence end (every key visible)
+    q_lens, k_lens = [6, 9], [300, 150]
+    g = torch.Generator().manual_seed(21)
+    d, hq, hkv = 8, 4, 2
+    q = torch.randn(sum(q_lens), hq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(sum(k_lens), hkv, d, generator=g).to(torch.bfloat16)
+    cu_q = torch.tensor([0, 6, 15], dtype=torch.int32)
+    cu_k = torch.tensor([0, 300, 450], dtype=torch.int32)
+    qo = 129 if form == "int" else torch.tensor([-1, 0, 127, 128, 290, 1000,
+                                                  -5, 3, 40, 127, 128, 129, 140, 149, 700],
+                                                 dtype=torch.int32)
+    pos = _positions(q_lens, k_lens, qo)
+    got = oracle.proxy_score(q, k, cu_q, cu_seqlens_k=cu_k, causal=True, q_offset=qo)
+    G, T = hq // hkv, 3
+    qf, kf = q.to(torch.float64).tolist(), k.to(torch.float64).tolist()
+    q0 = k0 = 0
+    for Lq, Lk in zip(q_lens, k_lens):
+        for iq in range(Lq):
+            i = q0 + iq
+            for h in range(hq):
+                for t in range(T):
+                    best = float("-inf")
+                    for j in range(BLOCK * t, min(BLOCK * t + BLOCK, Lk)):
+                        if j <= pos[i]:
+                            best = max(best, math.fsum(qf[i][h][e] * kf[k0 + j][h // G][e]
+                                                       for e in range(d)))
+                    ref = best
+                    assert (got[h, t, i] == ref) if ref == float("-inf") else \
+                        abs(float(got[h, t, i]) - ref) <= 1e-12, (h, t, i)
+        q0 += Lq
+        k0 += Lk
+    if form == "tensor":
+        assert torch.isinf(got[:, :, 0]).all() and torch.isinf(got[:, :, 6]).all()
+
+
+def test_q_offset_full_selection_equals_dense_sdpa():
+    # every block selected: attention equals SDPA with the mask j <= pos(i),
+    # j < Lk built here; a row positioned before every key is empty (0, -inf)
+    q_lens, k_lens = [40, 20], [300, 140]
+    hq, hkv, d = 4, 2, 32
+    p = synth.make_problem("t", q_lens=q_lens, k_lens=k_lens, num_qo_heads=hq,
+                           num_kv_heads=hkv, head_dim=d, seed=23, selection="proxy")
+    g = torch.Generator().manual_seed(5)
+    qo = torch.randint(-3, 320, (sum(q_lens),), generator=g, dtype=torch.int32)
+    qo[0] = -1
+    q2k = _all_blocks_q2k(q_lens, k_lens, hkv, False)
+    out, lse = oracle.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q,
+                                       cu_seqlens_k=p.cu_seqlens_k, causal=True, q_offset=qo)
+    q0 = k0 = 0
+    for Lq, Lk in zip(q_lens, k_lens):
+        qq = p.q[q0:q0 + Lq].to(torch.float64).transpose(0, 1)
+        kk = p.k[k0:k0 + Lk].to(torch.float64).repeat_interleave(hq // hkv, 1).transpose(0, 1)
+        vv = p.v[k0:k0 + Lk].to(torch.float64).repeat_interleave(hq // hkv, 1).transpose(0, 1)
+        pos = qo[q0:q0 + Lq].to(torch.int64).view(-1, 1)
+        mask = torch.arange(Lk).view(1, -1) <= pos
+        nonempty = mask.any(dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq[:, nonempty], kk, vv, attn_mask=mask[nonempty])
+        logits = (qq @ kk.transpose(1, 2)) * d ** -0.5
+        ref_lse = torch.logsumexp(logits.masked_fill(~mask, float("-inf")), dim=-1)
+        o = out[q0:q0 + Lq].transpose(0, 1)
+        assert torch.allclose(o[:, nonempty], ref, atol=1e-12, rtol=1e-12)
+        assert (o[:, ~nonempty] == 0).all()
+        assert torch.allclose(lse[q0:q0 + Lq].T[:, nonempty], ref_lse[:, nonempty],
+                              atol=1e-12, rtol=1e-12)
+        assert torch.isneginf(lse[q0:q0 + Lq].T[:, ~nonempty]).all()
+        q0 += Lq
+        k0 += Lk
+    assert torch.isneginf(lse[0]).all()
