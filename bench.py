@@ -19,7 +19,7 @@ qsa_indexed_1x8192_h12kv1_d256_w2048 times the QSA indexed forward,
 qsa_bitmap_1x8192_h12kv1_d256_causal_q25 the QSA bitmap forward.  --graph
 (decode workloads) adds the same step replayed as one HIP graph
 (graph_ms_per_step); --temperature-lse TAU (prefill workloads) also returns
-the temperature LSE, which runs the attention on the general kernel;
+the temperature LSE (accumulated by the same prefill kernel);
 --kv-format fp8 (prefill workloads) stores K/V as fp8 E4M3.
 
 Per-stage times come from HIP events recorded on the stream the kernels run
@@ -55,8 +55,7 @@ def _args():
                     help="prefill workloads: K/V stored as bf16 (default) or fp8 E4M3 (the "
                          "same values cast; proxy and attention read fp8)")
     ap.add_argument("--temperature-lse", type=float, default=None, metavar="TAU",
-                    help="prefill workloads: also return the temperature LSE with this scale "
-                         "(the attention then runs on the general kernel)")
+                    help="prefill workloads: also return the temperature LSE with this scale")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: also time the whole step replayed as one HIP graph")
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
@@ -256,8 +255,7 @@ def bench_prefill_pipeline(args, msa, synth, torch):
                       else {"sparse_attention": round(st[2], 4)}),
         "work": {"attention_flops": flops, "proxy_flops": pflops,
                  "proxy_tflops": round(pflops / (st[0] * 1e-3) / 1e12, 3) if pipeline else None},
-        "roofline": {"kernel": ("msa_attention_kernel<4,2,bf16>" if temp else
-                                "msa_stage16_kernel + msa_prefill_kernel<8,1>"
+        "roofline": {"kernel": ("msa_stage16_kernel + msa_prefill_kernel<8,1>"
                                 if args.kv_format == "fp8" else "msa_prefill_kernel<8,1>"),
                      "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -194,6 +194,9 @@ def _strides(t: Optional[torch.Tensor], paged: bool) -> Strides:
     return Strides(0, t.stride(1) * es, t.stride(0) * es)
 
 
+# Convenience bounds for calls that omit max_seqlen_q / max_k_tiles: these read
+# device lengths on the host, which synchronises the stream.  Callers on the
+# launch path (graphs, serving loops) pass both bounds instead.
 def _host_max_seqlen(cu: torch.Tensor) -> int:
     c = cu.to("cpu", torch.int64)
     return int((c[1:] - c[:-1]).max()) if c.numel() > 1 else 0

@@ -21,8 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmsa.so")
 
-SOURCES = ["api.cpp", "attention.hip", "decode.hip", "prefill.hip", "proxy.hip", "qsa.hip",
-           "stage16.hip", "topk.hip", "validate.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "proxy.hip", "qsa.hip", "stage16.hip",
+           "tile_union.hip", "topk.hip", "validate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -14,7 +14,6 @@
 #include "../../include/msa.h"
 #include "internal.hpp"
 #include "stage16.hpp"
-#include "temperature.hpp"
 #include "validate.hpp"
 
 namespace {
@@ -210,25 +209,33 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   r->stage16 = false;
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows_req = lqmax * G;
-  // packed E2M1 in the flat layout goes through the general kernel at every
-  // shape: the decode kernel stages block-scale rows two at a time, which
-  // needs a head's rows contiguous and stays inside a 128-row page, but could
-  // pass the end of a flat tensor
+  // packed E2M1 in the flat layout takes the prefill tiles at every shape:
+  // the decode kernel stages block-scale rows two at a time, which needs a
+  // head's rows contiguous and stays inside a 128-row page, but could pass
+  // the end of a flat tensor
   const bool flat_e2m1 = !paged && a->kv_dtype == MSA_KV_E2M1X2;
-  // the temperature LSE is accumulated by the general kernel only
+  // the temperature LSE is accumulated by the decode and prefill kernels
+  // beside the row sum
   const bool temp = a->lse_t != nullptr;
-  if (temp && !(a->lse_temperature_scale > 0.f))
-    return fail(MSA_ERR_UNSUPPORTED, "lse_temperature_scale must be > 0 (got %g)",
+  if (temp && !(a->lse_temperature_scale > 0.f && std::isfinite(a->lse_temperature_scale)))
+    return fail(MSA_ERR_UNSUPPORTED, "lse_temperature_scale must be finite and > 0 (got %g)",
                 (double)a->lse_temperature_scale);
-  if (temp && a->kv_dtype == MSA_KV_F16)
-    return fail(MSA_ERR_UNSUPPORTED, "the temperature LSE is computed for bf16 / fp8 / E2M1 K/V");
+  p.lse_t = a->lse_t;
+  p.tau = temp ? a->lse_temperature_scale : 1.0f;
+  {
+    // 2^(tau (x - m)) <= 2^64 for every accepted score: the reference max
+    // moves once a score passes it by 64 / tau (and at most by the format's
+    // own slack)
+    const float base = a->kv_dtype == MSA_KV_F16 ? 15.0f : 64.0f;
+    p.tslack = std::min(base, 64.0f / p.tau);
+  }
   // When one token's G heads fill a 16-row MFMA tile, every token of a short
   // query is a decode tile of its own: it streams just the pages it selected
   // (a union over the request's tokens would make each page cost all of
   // their row tiles), with less state per workgroup.
   const bool per_token = G >= 16 && G <= 64 && lqmax > 1 && lqmax <= kDecodeMaxTokens;
   const int dec_rows = per_token ? G : rows_req;
-  if (dec_rows <= 64 && !flat_e2m1 && !temp) {
+  if (dec_rows <= 64 && !flat_e2m1) {
     // decode shape: one workgroup per (request, KV head, token tile, split);
     // its waves split every page's keys
     plan.decode = 1;
@@ -252,20 +259,10 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   } else {
     plan.decode = 0;
     // fp8 / E2M1 K/V: converted to bf16 pages once, then the bf16 kernel
-    r->stage16 = !temp && (a->kv_dtype == MSA_KV_FP8_E4M3 || a->kv_dtype == MSA_KV_E2M1X2);
-    plan.async_bf16 =
-        (a->kv_dtype == MSA_KV_BF16 || a->kv_dtype == MSA_KV_F16 || r->stage16) && !temp;
-    // bf16: 4 waves x spw slots x 32 rows per tile; other formats: 4 x 2 x 16
-    int rows;
-    if (plan.async_bf16) {
-      // 8 waves x one 32-row slot (two waves per SIMD overlap MFMA and
-      // softmax work)
-      plan.spw = 1;
-      rows = 256;
-    } else {
-      plan.spw = 2;
-      rows = 128;
-    }
+    r->stage16 = a->kv_dtype == MSA_KV_FP8_E4M3 || a->kv_dtype == MSA_KV_E2M1X2;
+    // 8 waves x one 32-row slot (two waves per SIMD overlap MFMA and
+    // softmax work)
+    const int rows = 256;
     if (G > rows)
       return fail(MSA_ERR_SHAPE,
                   "num_qo_heads / num_kv_heads = %d exceeds the %d query rows of a prefill tile",
@@ -290,13 +287,15 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     r->ws_bytes = msa::stage16_bytes(a->batch, a->max_k_tiles, a->num_kv_heads, r->stage_slots);
   }
   if (plan.splits > 1) {
+    // [partial LSE][partial O][partial temperature LSE (with lse_t)]
     const int rows = plan.tok_per_tile * G;
     const int rows_pad = (rows + 31) / 32 * 32;
     const size_t units = (size_t)a->batch * a->num_kv_heads * p.tiles_per_req;
     p.ws_rows = rows;
     p.ws_lse_rows = rows_pad;
-    r->ws_bytes = round_up(units * plan.splits * rows_pad * sizeof(float), 256) +
-                  round_up(units * plan.splits * rows * 128 * sizeof(float), 256);
+    const size_t l_bytes = round_up(units * plan.splits * rows_pad * sizeof(float), 256);
+    r->ws_bytes = l_bytes + round_up(units * plan.splits * rows * 128 * sizeof(float), 256) +
+                  (temp ? l_bytes : 0);
   }
   return MSA_OK;
 }
@@ -415,12 +414,15 @@ msa_status_t run_attention(const msa_attn_args_t* args, Resolved& r, void* works
     if (!aligned(workspace, 256)) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
   if (r.ws_bytes && !r.stage16) {
-    // layout: [partial LSE][partial O]
+    // layout: [partial LSE][partial O][partial temperature LSE]
     const size_t units = (size_t)args->batch * args->num_kv_heads * r.p.tiles_per_req;
     const size_t l_bytes = round_up(units * r.plan.splits * r.p.ws_lse_rows * sizeof(float), 256);
+    const size_t o_bytes =
+        round_up(units * r.plan.splits * r.p.ws_rows * 128 * sizeof(float), 256);
     char* base = static_cast<char*>(workspace);
     r.p.ws_lse = reinterpret_cast<float*>(base);
     r.p.ws_o = reinterpret_cast<float*>(base + l_bytes);
+    r.p.ws_lse_t = args->lse_t ? reinterpret_cast<float*>(base + l_bytes + o_bytes) : nullptr;
   }
   if (args->total_q == 0 || args->batch == 0) return ok();
   if (r.stage16) {
@@ -429,16 +431,12 @@ msa_status_t run_attention(const msa_attn_args_t* args, Resolved& r, void* works
                                                       static_cast<hipStream_t>(stream)),
                                   "msa_sparse_attention staging launch");
     if (st2) return st2;
-    return hip_status(msa::launch_prefill_bf16(pq, r.plan.spw, static_cast<hipStream_t>(stream)),
+    return hip_status(msa::launch_prefill_bf16(pq, static_cast<hipStream_t>(stream)),
                       "msa_sparse_attention launch");
   }
-  if (args->lse_t)
-    return hip_status(msa::launch_attention_temperature(r.p, args->kv_dtype, args->lse_t,
-                                                        args->lse_temperature_scale,
-                                                        static_cast<hipStream_t>(stream)),
-                      "msa_sparse_attention launch (temperature LSE)");
-  return hip_status(msa::launch_attention(r.p, args->kv_dtype, r.plan,
-                                          static_cast<hipStream_t>(stream)),
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  return hip_status(r.plan.decode ? msa::launch_decode(r.p, args->kv_dtype, hs)
+                                  : msa::launch_prefill_bf16(r.p, hs),
                     "msa_sparse_attention launch");
 }
 

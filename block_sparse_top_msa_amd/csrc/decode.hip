@@ -125,6 +125,7 @@ struct MergeLds {
   float o[NWV][16][kMergePitch];
   float m[NWV][16];
   float l[NWV][16];
+  float lt[NWV][16];   // temperature sums
 };
 
 __device__ __forceinline__ float xsum16_32(float x) {
@@ -304,7 +305,10 @@ __device__ __forceinline__ uint32_t gather_byte(uint32_t a, uint32_t b, uint32_t
 
 }  // namespace
 
-template <int FMT, int RT, int NWV>
+// TEMP: also accumulate the temperature LSE, sum 2^(tau (x - m)) beside the
+// row sum against the same reference max, whose slack shrinks to 64 / tau
+// for tau > 1 so that no term passes 2^64.
+template <int FMT, int RT, int NWV, bool TEMP>
 __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
   using Geo = DecGeom<FMT>;
   constexpr int NST = Geo::kStages;
@@ -464,12 +468,14 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
       qf[rt][ds] = as_bf16x8(w);
     }
 
-  float m_[RT], l_[RT];
+  float m_[RT], l_[RT], lt_[RT];
   f32x4 o_[RT][8];
+  const float slack = TEMP ? p.tslack : DecSoft<FMT>::kSlack;
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m_[rt] = -INFINITY;
     l_[rt] = 0.f;
+    lt_[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o_[rt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -730,14 +736,23 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) e[4 * kt + r] = __builtin_amdgcn_exp2f(acc[kt][r] - mu);
       float lp = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-      if (__ballot(sel && (m_[rt] == -INFINITY || !(lp <= DecSoft<FMT>::kLimit))) != 0ull) {
+      float ltp = 0.f;
+      if constexpr (TEMP) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ltp += __builtin_amdgcn_exp2f(p.tau * (acc[kt][r] - mu));
+      }
+      if (__ballot(sel && (m_[rt] == -INFINITY || !(lp <= DecSoft<FMT>::kLimit) ||
+                           (TEMP && !(ltp <= DecSoft<FMT>::kLimit)))) != 0ull) {
         float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
                          fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
         mx = xmax16_32(mx);   // the row's keys are spread over four lanes
-        const bool up = mx > m_[rt] + DecSoft<FMT>::kSlack;
+        const bool up = mx > m_[rt] + slack;
         if (__ballot(up && m_[rt] > -INFINITY) != 0ull) {
           const float alpha = up ? __builtin_amdgcn_exp2f(m_[rt] - mx) : 1.0f;
           l_[rt] *= alpha;
+          if constexpr (TEMP) lt_[rt] *= up ? __builtin_amdgcn_exp2f(p.tau * (m_[rt] - mx)) : 1.0f;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) o_[rt][dt] *= alpha;
         }
@@ -748,8 +763,16 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) e[4 * kt + r] = __builtin_amdgcn_exp2f(acc[kt][r] - mu2);
         lp = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        if constexpr (TEMP) {
+          ltp = 0.f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ltp += __builtin_amdgcn_exp2f(p.tau * (acc[kt][r] - mu2));
+        }
       }
       l_[rt] += lp;
+      if constexpr (TEMP) lt_[rt] += ltp;
       const bf16x8 pf = as_bf16x8(u32x4{pk_p<FMT>(e[0], e[1]), pk_p<FMT>(e[2], e[3]),
                                         pk_p<FMT>(e[4], e[5]), pk_p<FMT>(e[6], e[7])});
 #pragma unroll
@@ -772,12 +795,14 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
   for (int rt = 0; rt < RT; ++rt) {
     if (16 * rt >= R) break;
     const float lsum = xsum16_32(l_[rt]);
+    const float ltsum = TEMP ? xsum16_32(lt_[rt]) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
       *reinterpret_cast<f32x4*>(&mg.o[wave][l16][16 * dt + 4 * q]) = o_[rt][dt];
     if (q == 0) {
       mg.m[wave][l16] = m_[rt];
       mg.l[wave][l16] = lsum;
+      if constexpr (TEMP) mg.lt[wave][l16] = ltsum;
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     block_barrier();
@@ -805,6 +830,14 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
         acc8[k] = x * invL;
       }
       const float lse_nat = L > 0.f ? (M + __log2f(L)) * kLn2d : -INFINITY;
+      float lset_nat = -INFINITY;
+      if constexpr (TEMP) {
+        float Lt = 0.f;
+#pragma unroll
+        for (int w = 0; w < NWV; ++w)
+          Lt += mg.lt[w][rr] * __builtin_amdgcn_exp2f(p.tau * (mg.m[w][rr] - Mu));
+        lset_nat = (L > 0.f && Lt > 0.f) ? (p.tau * M + __log2f(Lt)) * kLn2d : -INFINITY;
+      }
       if (p.splits == 1) {
         const int64_t orow = (int64_t)(q0 + row / G) * p.hq + g * G + row % G;
         u32x4 w4;
@@ -812,11 +845,13 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
         for (int k = 0; k < 4; ++k) w4[k] = pk_out<FMT>(acc8[2 * k] * p.v_gs, acc8[2 * k + 1] * p.v_gs);
         *reinterpret_cast<u32x4*>(p.out + orow * kHeadDim + d0) = w4;
         if (p.lse && d0 == 0) p.lse[orow] = lse_nat;
+        if (TEMP && d0 == 0) p.lse_t[orow] = lset_nat;
       } else {
         float* po = p.ws_o + ((int64_t)unit_split * p.ws_rows + row) * kHeadDim + d0;
         *reinterpret_cast<f32x4*>(po) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
         *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
         if (d0 == 0) p.ws_lse[(int64_t)unit_split * p.ws_lse_rows + row] = lse_nat;
+        if (TEMP && d0 == 0) p.ws_lse_t[(int64_t)unit_split * p.ws_lse_rows + row] = lset_nat;
       }
     }
     if (rt + 1 < RT && 16 * (rt + 1) < R) {   // the next tile rewrites the merge buffer
@@ -863,6 +898,16 @@ __global__ __launch_bounds__(256) void msa_decode_merge_kernel(AttnParams p) {
   }
   const float sc = W > 0.f ? p.v_gs / W : 0.f;
   const int64_t orow = (int64_t)(q0 + row / p.group) * p.hq + g * p.group + row % p.group;
+  if (p.lse_t && d0 == 0) {
+    // lse_t = ln sum_s exp(lse_t_s)
+    const float* ltp = p.ws_lse_t + (int64_t)unit * nsp * p.ws_lse_rows + row;
+    float Mt = -INFINITY;
+    for (int s = 0; s < nsp; ++s) Mt = fmaxf(Mt, ltp[(int64_t)s * p.ws_lse_rows]);
+    float St = 0.f;
+    if (Mt > -INFINITY)
+      for (int s = 0; s < nsp; ++s) St += __expf(ltp[(int64_t)s * p.ws_lse_rows] - Mt);
+    p.lse_t[orow] = St > 0.f ? Mt + __logf(St) : -INFINITY;
+  }
   u32x4 w4;
 #pragma unroll
   for (int k = 0; k < 4; ++k)
@@ -876,7 +921,10 @@ template <int FMT, int RT, int NWV = 4>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
   const int n = p.batch * p.hkv * p.tiles_per_req * p.splits;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV>), dim3(n), dim3(NWV * 64), 0, stream, p);
+  if (p.lse_t)
+    hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, true>), dim3(n), dim3(NWV * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, false>), dim3(n), dim3(NWV * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t tasks = (int64_t)p.batch * p.hkv * p.tiles_per_req * p.ws_rows * 16;

@@ -55,22 +55,22 @@ struct AttnParams {
   int ws_rows;                // rows per unit (tok_per_tile * group)
   int ws_lse_rows;            // rows_pad: rows rounded up to 32
   QueryPos qpos;              // causal positions of the queries
+  // temperature LSE (ln sum_j exp(tau z_j)), written when lse_t is set
+  float* lse_t;
+  float tau;                  // lse_temperature_scale
+  float tslack;               // rescale slack (log2 units) keeping 2^(tau (x - m)) <= 2^64
+  float* ws_lse_t;            // [units, splits, rows_pad] split partials of lse_t
 };
 
 // Kernel family selection for one attention call.
 struct AttnPlan {
-  int decode;       // 1: decode kernel (<= 64 rows per request and KV head)
-  int async_bf16;   // prefill with bf16 K/V: asynchronous LDS staging kernel
-  int spw;          // prefill slots per wave
+  int decode;       // 1: decode kernel (<= 64 rows per token tile), 0: prefill tiles
   int tok_per_tile;
   int splits;
 };
 
-hipError_t launch_attention(const AttnParams& p, int fmt, const AttnPlan& plan,
-                            hipStream_t stream);
-
 // 16-bit (bf16, or fp16 with p.out_f16) prefill tiles of 256 rows: 8 waves x 1 slot
-hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream);
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream);
 
 // decode kernel (+ split merge when p.splits > 1); workgroups one CU holds
 hipError_t launch_decode(const AttnParams& p, int fmt, hipStream_t stream);

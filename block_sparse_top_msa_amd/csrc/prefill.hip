@@ -226,10 +226,16 @@ __device__ __forceinline__ float exp_all(const f32x16& acc, float cs, float mu, 
 // There the chunk's row max moves m, O^T (holding chunk C - 1 by then) and l
 // are rescaled, and the exponentials are redone.  Without the rare path every
 // p stays at most 2^68: exact in bf16 and fp32 range, like the sums.
-template <int C, bool F16>
+//
+// TEMP: the temperature sum lt += 2^(tau (x - m)) of the same exponents x
+// (one multiply, exp and add per score beside e), whose own overflow check
+// joins the rare path's; there the reference max moves past `slack`
+// (64 / tau for tau > 1), so no temperature term passes 2^64.
+template <int C, bool F16, bool TEMP>
 __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], float& m, float& l,
-                                              const bf16x8 (&qf)[8], const ChunkAddr& ad,
-                                              bool rowsel, int lim, int hf, float cs) {
+                                              float& lt, const bf16x8 (&qf)[8],
+                                              const ChunkAddr& ad, bool rowsel, int lim, int hf,
+                                              float cs, float tau, float slack) {
   f32x16 acc = sp.s;
   // mask (diagonal / partial block only)
   if (__ballot(rowsel && lim < 32 * C + 31) != 0ull) {
@@ -247,7 +253,7 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
   // score G + 1 and packs the pair ending at G.
   float x[16], e[16], ps[8];
   uint32_t pw[8];
-  float lp = 0.f;
+  float lp = 0.f, ltp = 0.f;
   f32x16 sn = sp.s;
   x[0] = __builtin_fmaf(acc[0], cs, -mu);
   x[1] = __builtin_fmaf(acc[1], cs, -mu);
@@ -266,6 +272,7 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
     }
     if (G + 2 < 16) x[G + 2] = __builtin_fmaf(acc[G + 2], cs, -mu);
     if (G + 1 < 16) e[G + 1] = __builtin_amdgcn_exp2f(x[G + 1]);
+    if constexpr (TEMP) ltp += __builtin_amdgcn_exp2f(tau * x[G]);
     if (G & 1) {
       pw[G >> 1] = pk_p<F16>(e[G - 1], e[G]);
       ps[G >> 1] = e[G - 1] + e[G];
@@ -277,31 +284,39 @@ __device__ __forceinline__ void prefill_chunk(SlotPipe& sp, f32x16 (&o)[4], floa
   if constexpr (C < 3) sp.s = sn;
   lp += ps[7];
   u32x4 q0 = {pw[0], pw[1], pw[2], pw[3]}, q1 = {pw[4], pw[5], pw[6], pw[7]};
-  if (__ballot(rowsel && (m == -INFINITY || !(lp <= Soft<F16>::kLimit))) != 0ull) {
+  if (__ballot(rowsel && (m == -INFINITY || !(lp <= Soft<F16>::kLimit) ||
+                          (TEMP && !(ltp <= Soft<F16>::kLimit)))) != 0ull) {
     float mx = max16(acc);
     mx = rowsel ? mx * cs : -INFINITY;
     const float mr = swap32_max(mx);   // the row's other 16 keys sit in lane l ^ 32
     // first scores of a row: the max becomes the reference (O and l are
     // still zero); afterwards m moves only when the max passed the slack
-    const bool up = mr > m + Soft<F16>::kSlack;
+    const bool up = mr > m + (TEMP ? slack : Soft<F16>::kSlack);
     if (__ballot(up && m > -INFINITY) != 0ull) {
       const float alpha = up ? __builtin_amdgcn_exp2f(m - mr) : 1.0f;
       l *= alpha;
+      if constexpr (TEMP) lt *= up ? __builtin_amdgcn_exp2f(tau * (m - mr)) : 1.0f;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
     }
     m = up ? mr : m;
     const float mu2 = (rowsel && m > -INFINITY) ? m : INFINITY;
     lp = exp_all<F16>(acc, cs, mu2, q0, q1);
+    if constexpr (TEMP) {
+      ltp = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ltp += __builtin_amdgcn_exp2f(tau * __builtin_fmaf(acc[r], cs, -mu2));
+    }
   }
   l += lp;
+  if constexpr (TEMP) lt += ltp;
   sp.p0 = q0;
   sp.p1 = q1;
 }
 
 }  // namespace
 
-template <int NW, int SPW, bool F16>
+template <int NW, int SPW, bool F16, bool TEMP>
 __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
   constexpr int NT = NW * kWave;
   constexpr int LOADS = 64 / NW;   // 1 KiB load instructions per wave per block
@@ -410,12 +425,13 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
       qf[s][ks] = as_bf16x8(w);
     }
 
-  float m_[SPW], l_[SPW];
+  float m_[SPW], l_[SPW], lt_[SPW];
   f32x16 o_[SPW][4];
 #pragma unroll
   for (int s = 0; s < SPW; ++s) {
     m_[s] = -INFINITY;
     l_[s] = 0.f;
+    lt_[s] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -528,10 +544,14 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
         sp.kw[g] = lds_b128(ad.k[g] + 8192);
         __builtin_amdgcn_sched_barrier(0);
       }
-      prefill_chunk<0, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
-      prefill_chunk<1, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
-      prefill_chunk<2, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
-      prefill_chunk<3, F16>(sp, o_[0], m_[0], l_[0], qf[0], ad, rowsel, lim, hf, C);
+      prefill_chunk<0, F16, TEMP>(sp, o_[0], m_[0], l_[0], lt_[0], qf[0], ad, rowsel, lim, hf, C,
+                                  p.tau, p.tslack);
+      prefill_chunk<1, F16, TEMP>(sp, o_[0], m_[0], l_[0], lt_[0], qf[0], ad, rowsel, lim, hf, C,
+                                  p.tau, p.tslack);
+      prefill_chunk<2, F16, TEMP>(sp, o_[0], m_[0], l_[0], lt_[0], qf[0], ad, rowsel, lim, hf, C,
+                                  p.tau, p.tslack);
+      prefill_chunk<3, F16, TEMP>(sp, o_[0], m_[0], l_[0], lt_[0], qf[0], ad, rowsel, lim, hf, C,
+                                  p.tau, p.tslack);
     }
     // the operand addresses move to the other buffer
     const uint32_t step = buf ? (uint32_t)(-2 * kTileBytes) : (uint32_t)(2 * kTileBytes);
@@ -573,10 +593,16 @@ __global__ __launch_bounds__(NW * kWave) void msa_prefill_kernel(AttnParams p) {
                         pack_bf16x2(o_[s][dt][4 * q + 2] * inv, o_[s][dt][4 * q + 3] * inv)};
     if (p.lse && ehf == 0)
       p.lse[row] = lsum > 0.f ? (m_[s] + __log2f(lsum)) * kLn2f : -INFINITY;
+    if constexpr (TEMP) {
+      const float ltsum = swap32_sum(lt_[s]);
+      if (ehf == 0)
+        p.lse_t[row] = (lsum > 0.f && ltsum > 0.f) ? (p.tau * m_[s] + __log2f(ltsum)) * kLn2f
+                                                   : -INFINITY;
+    }
   }
 }
 
-template <int NW, int SPW, bool F16>
+template <int NW, int SPW, bool F16, bool TEMP>
 static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
   const int units = p.batch * p.hkv;
   if (units <= 0 || p.tiles_per_req <= 0) return hipSuccess;
@@ -588,14 +614,18 @@ static hipError_t launch_prefill_t(const AttnParams& p, hipStream_t stream) {
     const int n = units * p.tiles_per_req;
     grid = 8 * ((n + 7) / 8);
   }
-  hipLaunchKernelGGL((msa_prefill_kernel<NW, SPW, F16>), dim3(grid), dim3(NW * kWave), 0, stream, p);
+  hipLaunchKernelGGL((msa_prefill_kernel<NW, SPW, F16, TEMP>), dim3(grid), dim3(NW * kWave), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 // Tiles of 256 rows: 8 waves x one 32-row slot.
-hipError_t launch_prefill_bf16(const AttnParams& p, int spw, hipStream_t stream) {
-  (void)spw;
-  return p.out_f16 ? launch_prefill_t<8, 1, true>(p, stream) : launch_prefill_t<8, 1, false>(p, stream);
+hipError_t launch_prefill_bf16(const AttnParams& p, hipStream_t stream) {
+  if (p.lse_t)
+    return p.out_f16 ? launch_prefill_t<8, 1, true, true>(p, stream)
+                     : launch_prefill_t<8, 1, false, true>(p, stream);
+  return p.out_f16 ? launch_prefill_t<8, 1, true, false>(p, stream)
+                   : launch_prefill_t<8, 1, false, false>(p, stream);
 }
 
 }  // namespace msa

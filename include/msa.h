@@ -143,9 +143,10 @@ typedef struct {
                              attended keys (z_j the logits of lse), -inf for an
                              empty row (msa_sparse_attention page, Parameters:
                              return_temperature_lse, lse_temperature_scale).
-                             Computed by the general kernel at every shape;
-                             bf16 / fp8 / E2M1 K/V; else MSA_ERR_UNSUPPORTED  */
-  float lse_temperature_scale; /* > 0 when lse_t is set (1 gives lse)        */
+                             Accumulated by the same decode and prefill
+                             kernels beside the row sum, every format        */
+  float lse_temperature_scale; /* finite and > 0 when lse_t is set (1 gives
+                             lse), else MSA_ERR_UNSUPPORTED                   */
   /* Causal positions of the queries (msa_sparse_attention page, Parameters:
      q_offset; the page calls it a per-query offset tensor and defines it no
      further).  Reading: q_offset_mode 0 (default): right-aligned, query iq
@@ -160,8 +161,9 @@ typedef struct {
 } msa_attn_args_t;
 
 /* Bytes of workspace msa_sparse_attention needs for these arguments: the
- * fp32 split-KV partials (O / l per row) and their LSE
- * (prepare_msa_nvfp4_sparse_decode page, Parameters: workspace_buffer), or,
+ * fp32 split-KV partials (O / l per row) and their LSE, and with lse_t
+ * their temperature LSE (prepare_msa_nvfp4_sparse_decode page, Parameters:
+ * workspace_buffer), or,
  * for fp8 / E2M1 K/V on the prefill route, the bf16 pages their blocks are
  * converted to: 2 * batch * S * Hkv * 32 KiB plus the page table and
  * lengths, with S = max_k_tiles (every visible block), or, when
@@ -191,9 +193,8 @@ msa_status_t msa_sparse_attention_plan(const msa_attn_args_t* args, int32_t* dec
  * ignored; rows must be ascending without duplicates (caller contract).
  * Route: the decode kernel when max_seqlen_q * G <= 64, or, with
  * G = Hq / Hkv in [16, 64], when max_seqlen_q <= 64 (one token per tile);
- * flat E2M1 and the temperature LSE always take prefill tiles.  A prefill
- * tile holds 256 query rows (128 with the temperature LSE): a larger G is
- * MSA_ERR_SHAPE.  `workspace` may be NULL when the size query returned 0. */
+ * flat E2M1 always takes prefill tiles.  A prefill tile holds 256 query
+ * rows: a larger G is MSA_ERR_SHAPE.  `workspace` may be NULL when the size query returned 0. */
 msa_status_t msa_sparse_attention(const msa_attn_args_t* args, void* workspace,
                                   size_t workspace_bytes, void* stream);
 

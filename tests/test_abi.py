@@ -120,15 +120,22 @@ def test_attention_e2m1_needs_scales_with_contiguous_rows():
     assert st == 5
 
 
-def test_temperature_lse_needs_positive_scale_and_a_supported_format():
-    st, msg = _call(_attn(lse_t=FAKE, lse_temperature_scale=0.0))
-    assert st == 5 and "lse_temperature_scale" in msg
-    st, msg = _call(_attn(lse_t=FAKE, lse_temperature_scale=1.0, kv_dtype=3))
-    assert st == 5 and "temperature" in msg
-    # the temperature route never splits: no workspace for a decode shape
-    a = _attn(lse_t=FAKE, lse_temperature_scale=2.0, total_q=2, max_seqlen_q=1,
-              max_k_tiles=512, splits=4)
-    assert _size(a) == (0, 0)
+def test_temperature_lse_needs_a_finite_positive_scale():
+    for tau in (0.0, -1.0, float("inf"), float("nan")):
+        st, msg = _call(_attn(lse_t=FAKE, lse_temperature_scale=tau))
+        assert st == 5 and "lse_temperature_scale" in msg
+    # the temperature LSE keeps the decode route and its split partials: the
+    # workspace grows by one partial per row and split
+    a = _attn(num_qo_heads=32, num_kv_heads=2, total_q=4, batch=4, max_seqlen_q=1,
+              max_k_tiles=64, topk=16, page_table=FAKE, seqused_k=FAKE, page_table_width=64,
+              splits=4)
+    a.cu_seqlens_k = None
+    st, n0 = _size(a)
+    assert _plan(a)[:2] == (0, 1)
+    a.lse_t, a.lse_temperature_scale = FAKE, 2.0
+    st, n1 = _size(a)
+    assert st == 0 and n1 > n0
+    assert _plan(a)[:2] == (0, 1)
 
 
 def test_workspace_sizing_and_enforcement():
@@ -316,7 +323,7 @@ def test_long_queries_take_the_prefill_route():
     assert _plan(a)[:2] == (0, 0)
 
 
-@pytest.mark.parametrize("hq,hkv,temp", [(512, 1, False), (256, 1, True), (1024, 2, False)])
+@pytest.mark.parametrize("hq,hkv,temp", [(512, 1, False), (512, 1, True), (1024, 2, False)])
 def test_group_larger_than_a_tile_is_rejected(hq, hkv, temp):
     kw = dict(num_qo_heads=hq, num_kv_heads=hkv, total_q=64, max_seqlen_q=32)
     if temp:

@@ -116,41 +116,68 @@ def test_decode_flat_e2m1(msa, splits):
 
 
 TEMPERATURE_CASES = [
-    # q_lens, k_lens, Hq, Hkv, paged, fmt, tau, selection
-    ([300, 77], [300, 500], 16, 2, False, synth.KV_BF16, 0.5, "general"),
-    ([260, 33], [400, 33], 8, 2, False, synth.KV_FP8, 2.0, "general"),
-    ([1, 1, 1], [2000, 129, 700], 16, 2, True, synth.KV_BF16, 1.5, "decode"),
-    ([1, 1], [3000, 900], 16, 1, True, synth.KV_E2M1, 0.7, "decode"),
-    ([4, 4], [2500, 600], 32, 2, True, synth.KV_FP8, 1.0, "decode"),
+    # q_lens, k_lens, Hq, Hkv, paged, fmt, tau, selection, splits, softmax_scale
+    ([300, 77], [300, 500], 16, 2, False, synth.KV_BF16, 0.5, "general", 0, None),
+    ([260, 33], [400, 33], 8, 2, False, synth.KV_FP8, 2.0, "general", 0, None),
+    ([1, 1, 1], [2000, 129, 700], 16, 2, True, synth.KV_BF16, 1.5, "decode", 0, None),
+    ([1, 1], [3000, 900], 16, 1, True, synth.KV_E2M1, 0.7, "decode", 0, None),
+    ([4, 4], [2500, 600], 32, 2, True, synth.KV_FP8, 1.0, "decode", 0, None),
+    # tau > 1 shrinks the rescale slack to 64 / tau; a large softmax scale
+    # spreads the logits so the reference max moves
+    ([300, 129], [700, 300], 8, 2, False, synth.KV_BF16, 10.0, "general", 0, 0.5),
+    ([200, 64], [500, 300], 8, 1, False, synth.KV_F16, 4.0, "general", 0, 0.3),
+    ([150, 40], [600, 300], 8, 2, True, synth.KV_E2M1, 0.1, "general", 0, None),
+    ([1, 1, 1, 1], [9000, 129, 3000, 700], 16, 1, True, synth.KV_E2M1, 3.0, "decode", 3, 0.8),
+    ([1, 1, 1], [5000, 300, 2000], 16, 2, True, synth.KV_BF16, 6.0, "decode", 2, 0.5),
+    ([2, 2], [3000, 900], 16, 2, True, synth.KV_F16, 2.5, "decode", 0, 0.25),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(TEMPERATURE_CASES)))
 def test_temperature_lse_matches_oracle(msa, case):
-    ql, kl, hq, hkv, paged, fmt, tau, selection = TEMPERATURE_CASES[case]
+    ql, kl, hq, hkv, paged, fmt, tau, selection, splits, scale = TEMPERATURE_CASES[case]
     print(f"temperature LSE case {case}", flush=True)
     kw = dict(k_global_scale=0.5, v_global_scale=2.0) if fmt == synth.KV_E2M1 else {}
     p = synth.make_problem("temp", q_lens=ql, k_lens=kl, num_qo_heads=hq, num_kv_heads=hkv,
                            topk=6, paged=paged, kv_dtype=fmt, seed=60 + case,
-                           selection=selection, **kw)
+                           selection=selection, softmax_scale=scale, **kw)
     d = _dev(p)
+    # the temperature LSE keeps the tuned routes: decode shapes the decode
+    # kernel (split as asked), prefill shapes the prefill tiles
+    route, nsplit = msa.attention_plan(
+        d.q, d.k, d.v, d.q2k, d.cu_seqlens_q, d.cu_seqlens_k, page_table=d.page_table,
+        seqused_k=d.seqused_k, k_scale=d.k_scale, v_scale=d.v_scale, max_seqlen_q=max(ql),
+        max_k_tiles=p.max_k_tiles, splits=splits, return_temperature_lse=True)
+    assert route == (1 if selection == "decode" else 0)
+    if splits:
+        assert nsplit == splits
     out, lse, lse_t = msa.sparse_attention(
         d.q, d.k, d.v, d.q2k, d.cu_seqlens_q, d.cu_seqlens_k, causal=p.causal,
-        page_table=d.page_table, seqused_k=d.seqused_k, k_scale=d.k_scale, v_scale=d.v_scale,
-        k_global_scale=p.k_global_scale, v_global_scale=p.v_global_scale,
+        softmax_scale=scale, page_table=d.page_table, seqused_k=d.seqused_k, k_scale=d.k_scale,
+        v_scale=d.v_scale, k_global_scale=p.k_global_scale, v_global_scale=p.v_global_scale,
         max_seqlen_q=max(ql), max_k_tiles=p.max_k_tiles, return_temperature_lse=True,
-        lse_temperature_scale=tau)
+        lse_temperature_scale=tau, splits=splits)
     torch.cuda.synchronize()
     ref_out, ref_lse, ref_lt = oracle.sparse_attention(
         p.q, p.k, p.v, p.q2k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k,
         page_table=p.page_table, seqused_k=p.seqused_k, causal=p.causal, kv_format=fmt,
-        k_scale=p.k_scale, v_scale=p.v_scale, k_global_scale=p.k_global_scale,
-        v_global_scale=p.v_global_scale, lse_temperature_scale=tau)
+        softmax_scale=scale, k_scale=p.k_scale, v_scale=p.v_scale,
+        k_global_scale=p.k_global_scale, v_global_scale=p.v_global_scale,
+        lse_temperature_scale=tau)
     assert_attention_close(out, lse, ref_out, ref_lse, f"temperature case {case}")
     lt = lse_t.cpu().double()
     fin = torch.isfinite(ref_lt)
     assert torch.equal(torch.isfinite(lt), fin)
-    assert float((lt[fin] - ref_lt[fin]).abs().max()) <= 1e-3 * max(1.0, tau)
+    assert float((lt[fin] - ref_lt[fin]).abs().max()) <= 1e-3
+    # the same call without lse_t gives the same out and lse, bit for bit
+    out2, lse2 = msa.sparse_attention(
+        d.q, d.k, d.v, d.q2k, d.cu_seqlens_q, d.cu_seqlens_k, causal=p.causal,
+        softmax_scale=scale, page_table=d.page_table, seqused_k=d.seqused_k, k_scale=d.k_scale,
+        v_scale=d.v_scale, k_global_scale=p.k_global_scale, v_global_scale=p.v_global_scale,
+        max_seqlen_q=max(ql), max_k_tiles=p.max_k_tiles, return_softmax_lse=True, splits=splits)
+    torch.cuda.synchronize()
+    if tau <= 1.0:   # (tau > 1 moves the reference max on its own slack)
+        assert torch.equal(out, out2) and torch.equal(lse, lse2)
 
 
 def test_prefill_without_lse_and_diagonal_selection(msa):
