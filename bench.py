@@ -294,11 +294,14 @@ def bench_decode(args, msa, synth, torch):
     out = torch.empty_like(p.q)
     lse = torch.empty(p.total_q, p.num_qo_heads, dtype=torch.float32, device="cuda")
     pipeline = p.q2k is None
-    scores = q2k = None
+    ws = q2k = None
     if pipeline:
-        scores = torch.empty(1 if p.reduce_heads else p.num_qo_heads, T, p.total_q,
-                             dtype=torch.float32, device="cuda")
+        # proxy -> head reduce -> top-K in one call (the running top-K)
         q2k = torch.empty(p.num_kv_heads, p.total_q, p.topk, dtype=torch.int32, device="cuda")
+        ws = msa.Workspace(msa.proxy_topk_workspace_size(
+            p.q, p.k, p.cu_seqlens_q, topk=p.topk, page_table=p.page_table,
+            seqused_k=p.seqused_k, causal=True, max_seqlen_q=mq, max_k_tiles=T,
+            reduce_heads=p.reduce_heads), "cuda")
     else:
         q2k = p.q2k
     scrub32 = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
@@ -306,12 +309,10 @@ def bench_decode(args, msa, synth, torch):
     def step(ev=None):
         if ev: ev[0].record()
         if pipeline:
-            msa.proxy_score(p.q, p.k, p.cu_seqlens_q, page_table=p.page_table,
-                            seqused_k=p.seqused_k, causal=True, max_seqlen_q=mq, max_k_tiles=T,
-                            output=scores, reduce_heads=p.reduce_heads)
+            msa.proxy_topk(p.q, p.k, p.cu_seqlens_q, topk=p.topk, page_table=p.page_table,
+                           seqused_k=p.seqused_k, causal=True, max_seqlen_q=mq, max_k_tiles=T,
+                           reduce_heads=p.reduce_heads, out=q2k, workspace=ws)
         if ev: ev[1].record()
-        if pipeline:
-            msa.topk_select(scores, p.topk, p.num_kv_heads, out=q2k)
         if ev: ev[2].record()
         msa.sparse_attention(p.q, p.k, p.v, q2k, p.cu_seqlens_q, causal=True,
                              page_table=p.page_table, seqused_k=p.seqused_k,
@@ -347,9 +348,8 @@ def bench_decode(args, msa, synth, torch):
         "config": {"workload": p.name, "batch": B, "seqlen_q": mq, "num_qo_heads": p.num_qo_heads,
                    "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "topk": p.topk,
                    "kv_format": fmt, "cold_cache": True},
-        "stages_ms": ({"proxy_score": round(st[0], 4), "topk_select": round(st[1], 4),
-                       "sparse_attention": round(st[2], 4)} if pipeline
-                      else {"sparse_attention": round(st[2], 4)}),
+        "stages_ms": ({"proxy_topk": round(st[0], 4), "sparse_attention": round(st[2], 4)}
+                      if pipeline else {"sparse_attention": round(st[2], 4)}),
         "work": {"kv_bytes": nbytes},
         **({"graph_ms_per_step": _graph_decode_ms(args, p, scrub32, sink, torch)}
            if args.graph else {}),

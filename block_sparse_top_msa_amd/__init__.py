@@ -23,7 +23,7 @@ from typing import Optional
 import torch
 
 __all__ = [
-    "attention_plan", "sparse_attention_noalloc",
+    "attention_plan", "sparse_attention_noalloc", "proxy_topk", "proxy_topk_workspace_size",
     "MsaError", "lib", "library_path", "sparse_attention", "validate_attention",
     "prepare_msa_nvfp4_sparse_decode", "MSANvfp4DecodeRunner", "proxy_score",
     "topk_select",
@@ -43,7 +43,8 @@ EXPORTED_SYMBOLS = (
     "msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
     "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward", "msa_qsa_bitmap_forward",
     "msa_validate_attention", "msa_sparse_attention_plan", "msa_sparse_attention_noalloc",
-    "msa_status_string", "msa_last_error", "msa_version",
+    "msa_proxy_topk_workspace_size", "msa_proxy_topk", "msa_status_string", "msa_last_error",
+    "msa_version",
 )
 
 _STATUS = {0: "MSA_OK", 1: "MSA_ERR_NULL", 2: "MSA_ERR_SHAPE", 3: "MSA_ERR_DTYPE",
@@ -126,6 +127,10 @@ def _load():
     L.msa_sparse_attention.argtypes = [ctypes.POINTER(AttnArgs), _P, ctypes.c_size_t, _P]
     L.msa_sparse_attention_noalloc.argtypes = [ctypes.POINTER(AttnArgs), _P]
     L.msa_proxy_score.argtypes = [ctypes.POINTER(ProxyArgs), _P]
+    L.msa_proxy_topk_workspace_size.argtypes = [ctypes.POINTER(ProxyArgs), ctypes.c_int32,
+                                                ctypes.POINTER(ctypes.c_size_t)]
+    L.msa_proxy_topk.argtypes = [ctypes.POINTER(ProxyArgs), ctypes.c_int32, _P, _P,
+                                 ctypes.c_size_t, _P]
     L.msa_topk_select.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]
     L.msa_tile_union.argtypes = [_P, _P, _P] + [ctypes.c_int32] * 8 + [_P, _P, _P, _P]
@@ -138,7 +143,8 @@ def _load():
     for fn in ("msa_sparse_attention_workspace_size", "msa_sparse_attention", "msa_proxy_score",
                "msa_topk_select", "msa_tile_union", "msa_qsa_indexed_forward",
                "msa_qsa_bitmap_forward", "msa_validate_attention",
-               "msa_sparse_attention_plan", "msa_sparse_attention_noalloc"):
+               "msa_sparse_attention_plan", "msa_sparse_attention_noalloc",
+               "msa_proxy_topk_workspace_size", "msa_proxy_topk"):
         getattr(L, fn).restype = ctypes.c_int
     L.msa_status_string.argtypes = [ctypes.c_int]
     L.msa_status_string.restype = ctypes.c_char_p
@@ -505,15 +511,9 @@ def prepare_msa_nvfp4_sparse_decode(q, k, v, q2k_indices, *, k_scale, v_scale, p
     return run
 
 
-def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, seqused_k=None,
-                causal=True, max_seqlen_q=None, max_k_tiles=None, output=None,
-                reduce_heads=False, q_offset=None):
-    """Stage-1 block max of unscaled masked QK^T (msa_proxy_score page).
-    reduce_heads: False (per query head), True (max over all heads) or
-    "group" (max over each KV head's query heads).  q_offset: None
-    (right-aligned), an int o (query iq at o + iq) or an int32 tensor of
-    per-row positions.  Returns fp32 (num_qo_heads | 1 | num_kv_heads,
-    max_k_tiles, total_q)."""
+def _proxy_args(q, k, cu_seqlens_q, cu_seqlens_k, page_table, seqused_k, causal, max_seqlen_q,
+                max_k_tiles, reduce_heads, q_offset):
+    """ProxyArgs for these tensors, and (score heads, max_k_tiles)."""
     for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k),
                     ("page_table", page_table), ("seqused_k", seqused_k)):
         _check_i32(name, t)
@@ -538,11 +538,6 @@ def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, sequs
         H = 1 if reduce_heads else q.shape[1]
     else:
         raise ValueError(f"reduce_heads must be False, True or 'group', got {reduce_heads!r}")
-    if output is None:
-        output = torch.empty(H, T, q.shape[0], dtype=torch.float32, device=q.device)
-    elif (output.shape != (H, T, q.shape[0]) or output.dtype != torch.float32
-          or not output.is_contiguous()):
-        raise ValueError(f"output must be contiguous fp32 {(H, T, q.shape[0])}")
     a = ProxyArgs()
     a.batch = cu_seqlens_q.numel() - 1
     a.total_q = q.shape[0]
@@ -561,10 +556,66 @@ def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, sequs
     a.cu_seqlens_k = _ptr(cu_seqlens_k)
     a.page_table = _ptr(page_table)
     a.seqused_k = _ptr(seqused_k)
-    a.out = _ptr(output)
     _set_q_offset(a, q_offset, q.shape[0])
+    return a, H, T
+
+
+def proxy_score(q, k, cu_seqlens_q, cu_seqlens_k=None, *, page_table=None, seqused_k=None,
+                causal=True, max_seqlen_q=None, max_k_tiles=None, output=None,
+                reduce_heads=False, q_offset=None):
+    """Stage-1 block max of unscaled masked QK^T (msa_proxy_score page).
+    reduce_heads: False (per query head), True (max over all heads) or
+    "group" (max over each KV head's query heads).  q_offset: None
+    (right-aligned), an int o (query iq at o + iq) or an int32 tensor of
+    per-row positions.  Returns fp32 (num_qo_heads | 1 | num_kv_heads,
+    max_k_tiles, total_q)."""
+    a, H, T = _proxy_args(q, k, cu_seqlens_q, cu_seqlens_k, page_table, seqused_k, causal,
+                          max_seqlen_q, max_k_tiles, reduce_heads, q_offset)
+    if output is None:
+        output = torch.empty(H, T, q.shape[0], dtype=torch.float32, device=q.device)
+    elif (output.shape != (H, T, q.shape[0]) or output.dtype != torch.float32
+          or not output.is_contiguous()):
+        raise ValueError(f"output must be contiguous fp32 {(H, T, q.shape[0])}")
+    a.out = _ptr(output)
     _check(lib.msa_proxy_score(ctypes.byref(a), _stream()))
     return output
+
+
+def proxy_topk(q, k, cu_seqlens_q, cu_seqlens_k=None, *, topk, page_table=None, seqused_k=None,
+               causal=True, max_seqlen_q=None, max_k_tiles=None, reduce_heads=False,
+               q_offset=None, out=None, workspace=None):
+    """Proxy score -> head reduction -> top-K select in one call
+    (msa_proxy_topk): q2k int32 (num_kv_heads, total_q, topk), equal to
+    topk_select(proxy_score(...), topk, num_kv_heads).  On decode shapes the
+    selection runs inside the proxy pass and no score buffer exists.
+    workspace: a Workspace of at least proxy_topk_workspace_size bytes, or
+    None (one is allocated)."""
+    a, _, _ = _proxy_args(q, k, cu_seqlens_q, cu_seqlens_k, page_table, seqused_k, causal,
+                          max_seqlen_q, max_k_tiles, reduce_heads, q_offset)
+    if out is None:
+        out = torch.empty(k.shape[1], q.shape[0], int(topk), dtype=torch.int32, device=q.device)
+    elif (out.shape != (k.shape[1], q.shape[0], int(topk)) or out.dtype != torch.int32
+          or not out.is_contiguous()):
+        raise ValueError(f"out must be contiguous int32 {(k.shape[1], q.shape[0], int(topk))}")
+    need = ctypes.c_size_t(0)
+    _check(lib.msa_proxy_topk_workspace_size(ctypes.byref(a), int(topk), ctypes.byref(need)))
+    if workspace is None:
+        workspace = Workspace(max(1, need.value), q.device)
+    elif workspace.nbytes < need.value:
+        raise MsaError(6, f"workspace of {need.value} bytes needed, got {workspace.nbytes}")
+    _check(lib.msa_proxy_topk(ctypes.byref(a), int(topk), _ptr(out), _ptr(workspace.view),
+                              workspace.nbytes, _stream()))
+    return out
+
+
+def proxy_topk_workspace_size(q, k, cu_seqlens_q, cu_seqlens_k=None, *, topk, page_table=None,
+                              seqused_k=None, causal=True, max_seqlen_q=None, max_k_tiles=None,
+                              reduce_heads=False) -> int:
+    a, _, _ = _proxy_args(q, k, cu_seqlens_q, cu_seqlens_k, page_table, seqused_k, causal,
+                          max_seqlen_q, max_k_tiles, reduce_heads, None)
+    need = ctypes.c_size_t(0)
+    _check(lib.msa_proxy_topk_workspace_size(ctypes.byref(a), int(topk), ctypes.byref(need)))
+    return int(need.value)
 
 
 def topk_select(max_score, topk, num_kv_heads, mode=None, out=None):

@@ -496,8 +496,18 @@ msa_status_t msa_sparse_attention_noalloc(const msa_attn_args_t* args, void* str
   return run_attention(args, r, ws, r.ws_bytes ? kScratchBytes : 0, stream);
 }
 
-msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks and launch parameters of a proxy call (the arguments of
+// msa_proxy_score; out is required only when need_out).  *empty: nothing to
+// compute.  *wide_out: the prefill-shaped kernel (> 64 rows per request and
+// KV head) rather than the decode-shaped one.
+msa_status_t resolve_proxy(const msa_proxy_args_t* a, bool need_out, msa::ProxyParams* pp,
+                           int* wide_out, bool* empty) {
   if (!a) return fail(MSA_ERR_NULL, "args is NULL");
+
   if (a->head_dim != 128) return fail(MSA_ERR_SHAPE, "head_dim must be 128 (got %d)", a->head_dim);
   if (a->batch < 0 || a->total_q < 0 || a->max_k_tiles < 0 || a->max_seqlen_q < 0)
     return fail(MSA_ERR_SHAPE, "sizes must be >= 0");
@@ -519,12 +529,13 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   } else if (a->seqused_k) {
     return fail(MSA_ERR_UNSUPPORTED, "seqused_k is read only with a page_table");
   }
-  if (a->total_q == 0 || a->batch == 0 || a->max_k_tiles == 0) return ok();
-  if (!a->q || !a->k || !a->cu_seqlens_q || !a->out)
-    return fail(MSA_ERR_NULL, "q, k, cu_seqlens_q and out must be non-NULL");
+  *empty = a->total_q == 0 || a->batch == 0 || a->max_k_tiles == 0;
+  if (*empty) return ok();
+  if (!a->q || !a->k || !a->cu_seqlens_q || (need_out && !a->out))
+    return fail(MSA_ERR_NULL, "q, k, cu_seqlens_q%s must be non-NULL", need_out ? " and out" : "");
   if (!aligned(a->q, 16) || !aligned(a->k, 16))
     return fail(MSA_ERR_UNSUPPORTED, "q and k must be 16-byte aligned");
-  msa::ProxyParams p;
+  msa::ProxyParams& p = *pp;
   std::memset(&p, 0, sizeof(p));
   msa_status_t st;
   const int rb = kv_row_bytes(a->kv_dtype);
@@ -555,6 +566,7 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   const int lqmax = std::max(1, a->max_seqlen_q);
   const int rows = lqmax * G;
   const int wide = rows > 64;
+  *wide_out = wide;
   p.rows_per_tile = wide ? 256 : (rows <= 32 ? 32 : 64);
   p.row_tiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
   // aim for >= ~2048 workgroups; at least 4 blocks per workgroup (a multiple
@@ -566,11 +578,108 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
   else bpw = std::min(64, std::max(bpw, 16));   // amortise the Q tile over >= 16 blocks
   p.blocks_per_wg = bpw;
   p.block_chunks = (a->max_k_tiles + bpw - 1) / bpw;
-  return hip_status(msa::launch_proxy(p, a->kv_dtype == MSA_KV_FP8_E4M3 ? msa::kFmtFp8
-                                      : a->kv_dtype == MSA_KV_F16    ? msa::kFmtF16
-                                                                     : msa::kFmtBf16,
-                                      wide, static_cast<hipStream_t>(stream)),
+  return MSA_OK;
+}
+
+int proxy_fmt(int kv_dtype) {
+  return kv_dtype == MSA_KV_FP8_E4M3 ? msa::kFmtFp8
+       : kv_dtype == MSA_KV_F16      ? msa::kFmtF16
+                                     : msa::kFmtBf16;
+}
+
+// Workspace of msa_proxy_topk: fused (decode shapes): [sel_rows, total_q, Hg,
+// chunks, topk] candidate scores then ids; else the score buffer
+// [H_s, max_k_tiles, total_q] fp32.
+size_t proxy_topk_bytes(const msa_proxy_args_t* a, const msa::ProxyParams& p, int wide,
+                        int topk) {
+  if (!wide) {
+    const int sel_rows = a->reduce_heads == 1 ? 1 : a->num_kv_heads;
+    const int hg = a->reduce_heads == 1 ? a->num_kv_heads : 1;
+    const size_t n = (size_t)sel_rows * a->total_q * hg * p.block_chunks * topk;
+    return round_up(n * 4, 256) * 2;
+  }
+  const int hs = a->reduce_heads == 1 ? 1 : (a->reduce_heads == 2 ? a->num_kv_heads
+                                                                    : a->num_qo_heads);
+  return round_up((size_t)hs * a->max_k_tiles * a->total_q * 4, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+msa_status_t msa_proxy_score(const msa_proxy_args_t* a, void* stream) {
+  msa::ProxyParams p;
+  int wide = 0;
+  bool empty = false;
+  msa_status_t st = resolve_proxy(a, true, &p, &wide, &empty);
+  if (st || empty) return st;
+  return hip_status(msa::launch_proxy(p, proxy_fmt(a->kv_dtype), wide,
+                                      static_cast<hipStream_t>(stream)),
                     "msa_proxy_score launch");
+}
+
+msa_status_t msa_proxy_topk_workspace_size(const msa_proxy_args_t* a, int32_t topk,
+                                           size_t* bytes) {
+  if (!bytes) return fail(MSA_ERR_NULL, "bytes is NULL");
+  if (topk < 1 || topk > msa::kMaxTopk)
+    return fail(MSA_ERR_SHAPE, "topk must be in [1, %d] (got %d)", msa::kMaxTopk, topk);
+  msa::ProxyParams p;
+  int wide = 0;
+  bool empty = false;
+  msa_status_t st = resolve_proxy(a, false, &p, &wide, &empty);
+  if (st) return st;
+  *bytes = empty ? 0 : proxy_topk_bytes(a, p, wide, topk);
+  return ok();
+}
+
+msa_status_t msa_proxy_topk(const msa_proxy_args_t* a, int32_t topk, int32_t* q2k,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (topk < 1 || topk > msa::kMaxTopk)
+    return fail(MSA_ERR_SHAPE, "topk must be in [1, %d] (got %d)", msa::kMaxTopk, topk);
+  msa::ProxyParams p;
+  int wide = 0;
+  bool empty = false;
+  msa_status_t st = resolve_proxy(a, false, &p, &wide, &empty);
+  if (st) return st;
+  if (a->total_q == 0 || a->batch == 0) return ok();
+  if (!q2k) return fail(MSA_ERR_NULL, "q2k must be non-NULL");
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (empty) {   // no blocks: every row is padding
+    return hip_status(msa::launch_topk(nullptr, 1, 0, a->total_q, topk, a->num_kv_heads, 1, q2k,
+                                       hs),
+                      "msa_proxy_topk launch");
+  }
+  const size_t need = proxy_topk_bytes(a, p, wide, topk);
+  if (!workspace || workspace_bytes < need)
+    return fail(MSA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need,
+                workspace_bytes, workspace);
+  if (!aligned(workspace, 256)) return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const int fmt = proxy_fmt(a->kv_dtype);
+  if (!wide) {
+    // running top-K in the proxy kernel, then the merge of the candidates
+    const int sel_rows = a->reduce_heads == 1 ? 1 : a->num_kv_heads;
+    const int hg = a->reduce_heads == 1 ? a->num_kv_heads : 1;
+    const size_t n = (size_t)sel_rows * a->total_q * hg * p.block_chunks * topk;
+    p.cand_s = static_cast<float*>(workspace);
+    p.cand_id = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + round_up(n * 4, 256));
+    p.topk = topk;
+    p.reduce = a->reduce_heads == 1 ? 1 : 2;
+    if ((st = hip_status(msa::launch_proxy_candidates(p, fmt, hs), "msa_proxy_topk launch")))
+      return st;
+    return hip_status(msa::launch_topk_merge(p.cand_s, p.cand_id, hg * p.block_chunks * topk,
+                                             a->max_k_tiles, a->total_q, topk, a->num_kv_heads,
+                                             a->reduce_heads == 1, q2k, hs),
+                      "msa_proxy_topk merge launch");
+  }
+  // prefill shapes: scores into the workspace, then the select
+  p.out = static_cast<float*>(workspace);
+  if ((st = hip_status(msa::launch_proxy(p, fmt, wide, hs), "msa_proxy_topk launch"))) return st;
+  const int sh = a->reduce_heads == 1 ? 1 : (a->reduce_heads == 2 ? a->num_kv_heads
+                                                                   : a->num_qo_heads);
+  const int mode = a->reduce_heads == 1 ? 1 : (sh == a->num_kv_heads ? 0 : 2);
+  return hip_status(msa::launch_topk(p.out, sh, a->max_k_tiles, a->total_q, topk,
+                                     a->num_kv_heads, mode, q2k, hs),
+                    "msa_proxy_topk select launch");
 }
 
 msa_status_t msa_topk_select(const float* scores, int32_t score_heads, int32_t max_k_tiles,

@@ -93,12 +93,27 @@ struct ProxyParams {
   int blocks_per_wg;          // KV blocks per workgroup
   int block_chunks;           // ceil(max_k_tiles / blocks_per_wg)
   QueryPos qpos;              // causal positions of the queries
+  // running top-K (decode shapes): each workgroup writes the top-K of its
+  // chunk per query instead of scores, [sel_rows, total_q, Hg, chunks, topk]
+  float* cand_s;
+  int32_t* cand_id;
+  int topk;
 };
 
 hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream);
+// decode-shaped proxy (<= 64 rows per request and KV head) writing per-chunk
+// top-K candidates (p.cand_s, p.cand_id) instead of scores
+hipError_t launch_proxy_candidates(const ProxyParams& p, int fmt, hipStream_t stream);
 
 hipError_t launch_topk(const float* scores, int score_heads, int T, int total_q, int topk,
                        int hkv, int mode, int32_t* q2k, hipStream_t stream);
+
+// q2k from per-chunk top-K candidates ([sel_rows, total_q, n_cand] scores
+// and block ids, -1 padded): ids folded by max score, then the top-K; shared:
+// one selection written to every KV head's row.
+hipError_t launch_topk_merge(const float* cand_s, const int32_t* cand_id, int n_cand, int T,
+                             int total_q, int topk, int hkv, int shared, int32_t* q2k,
+                             hipStream_t stream);
 
 struct QsaParams {
   const uint16_t* q;          // bf16 [total_q, hq, 256]

@@ -17,6 +17,7 @@
 #include "async_lds.hpp"
 #include "common.hpp"
 #include "internal.hpp"
+#include "topk.hpp"
 
 namespace msa {
 
@@ -135,7 +136,15 @@ __device__ __forceinline__ void g2lds16_px(const void* gaddr, uint32_t lds_base)
 
 // fp8 stages fit two workgroups per CU (256 VGPRs per wave); bf16 stages
 // take the LDS of one, whose waves may then use the whole register file.
-template <int NT, int FMT, bool REDUCE>
+//
+// FUSE (running top-K, msa_proxy_score page, Parameters: reduce_heads: the
+// reduction and the selection folded into the kernel): no score is written;
+// per query, the workgroup takes the maximum over its KV head's query heads
+// of each of its chunk's blocks and writes that chunk's top-K (score, block
+// id) candidates, ascending, -1 padded; the merge kernel then selects the
+// row's top-K from every chunk's (and, for a selection shared by all heads,
+// every KV head's) candidates.
+template <int NT, int FMT, bool REDUCE, bool FUSE = false>
 __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_kernel(ProxyParams p) {
   using Geo = RowsGeom<FMT>;
   constexpr int NST = Geo::kStages;
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_ke
   }
 
   // blocks of the chunk with no visible key: -inf (pre-filled when reducing)
-  if (!REDUCE && half == 0) {
+  if (!REDUCE && !FUSE && half == 0) {
     for (int t = t_act + wave; t < t_end; t += 4) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
@@ -372,6 +381,44 @@ __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_ke
       const float v = xor_max(bm[nt], 32);
       if (half == 0) lds.res[wave][i][32 * nt + col] = v;
     }
+  }
+
+  if constexpr (FUSE) {
+    // ---- the chunk's top-K per query: every wave's block maxima visible
+    __syncthreads();
+    const int K = p.topk;
+    const int nch = t_end - t_beg;                 // <= 32 blocks: lane = block
+    const int sel = p.reduce == 1 ? 0 : g;         // selection row
+    const int Hg = p.reduce == 1 ? p.hkv : 1;      // KV heads folded into it
+    const int hgi = p.reduce == 1 ? g : 0;
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+    for (int tk = wave; tk < lq; tk += 4) {
+      const int t = t_beg + lane;
+      float s = -INFINITY;
+      if (lane < nch && t < t_act) {
+        // block t = t_beg + w + 4 i was scored by wave w, slot i
+        const int w = lane & 3, i = lane >> 2;
+        for (int hh = 0; hh < G; ++hh) s = fmaxf(s, lds.res[w][i][tk * G + hh]);
+      }
+      uint32_t key[1];
+      bool valid[1], chosen[1];
+      valid[0] = lane < nch && (__float_as_uint(s) & 0x7F800000u) != 0x7F800000u;
+      key[0] = valid[0] ? ordered_f32(s) : 0u;
+      select_topk<1>(key, valid, K, lane, chosen);
+      const int64_t base =
+          (((int64_t)sel * p.total_q + q0 + tk) * Hg + hgi) * p.block_chunks * K + (int64_t)chunk * K;
+      const unsigned long long m = __ballot(chosen[0]);
+      if (chosen[0]) {
+        const int pos = popc64(m & below);
+        p.cand_s[base + pos] = s;
+        p.cand_id[base + pos] = t;
+      }
+      for (int k = popc64(m) + lane; k < K; k += kWave) {
+        p.cand_s[base + k] = -INFINITY;
+        p.cand_id[base + k] = -1;
+      }
+    }
+    return;
   }
 
   // ---- results of this wave's blocks (its own LDS rows: no barrier)
@@ -709,6 +756,25 @@ static hipError_t launch_proxy_rows_t(const ProxyParams& p, hipStream_t stream) 
     hipLaunchKernelGGL((msa_proxy_rows_kernel<NT, FMT, false>), dim3(n), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+// Running top-K on the decode-shaped path: candidates instead of scores.
+template <int NT, int FMT>
+static hipError_t launch_proxy_cand_t(const ProxyParams& p, hipStream_t stream) {
+  const int n = p.batch * p.hkv * p.block_chunks;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((msa_proxy_rows_kernel<NT, FMT, true, true>), dim3(n), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_proxy_candidates(const ProxyParams& p, int fmt, hipStream_t stream) {
+  if (p.rows_per_tile <= 32)
+    return fmt == kFmtFp8 ? launch_proxy_cand_t<1, kFmtFp8>(p, stream)
+         : fmt == kFmtF16 ? launch_proxy_cand_t<1, kFmtF16>(p, stream)
+                          : launch_proxy_cand_t<1, kFmtBf16>(p, stream);
+  return fmt == kFmtFp8 ? launch_proxy_cand_t<2, kFmtFp8>(p, stream)
+       : fmt == kFmtF16 ? launch_proxy_cand_t<2, kFmtF16>(p, stream)
+                        : launch_proxy_cand_t<2, kFmtBf16>(p, stream);
 }
 
 // wide_rows: 1 -> 256 rows per workgroup (msa_proxy_wide_kernel); 0 -> at

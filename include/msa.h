@@ -267,6 +267,27 @@ typedef struct {
  * never written (msa_proxy_score page, Parameters: reduce_heads). */
 msa_status_t msa_proxy_score(const msa_proxy_args_t* args, void* stream);
 
+/* Proxy score, head reduction and top-K block select in one call, with the
+ * selection kept running inside the proxy pass where the query is short
+ * (msa_proxy_score page, Parameters: reduce_heads, on folding the reduction
+ * into the kernel so that no score buffer is materialised).  Writes q2k int32
+ * [num_kv_heads, total_q, topk] exactly as msa_proxy_score followed by
+ * msa_topk_select would: reduce_heads 1 selects on the max over all query
+ * heads and writes that shared selection to every KV head's row; 0 and 2
+ * select per KV head on the max over its query heads.  args->out is not
+ * read (may be NULL).  Decode shapes (max_seqlen_q * G <= 64): each proxy
+ * workgroup writes, per query, the top-K (score, block id) of its own chunk
+ * of blocks over its KV head's head-group maximum, and a merge kernel folds
+ * every chunk's and KV head's candidates by block id (largest score) and
+ * selects the top-K; no score buffer exists.  Other shapes: the scores go to
+ * the workspace, then the select.  workspace: caller-owned, 256-byte
+ * aligned, msa_proxy_topk_workspace_size bytes, no initialisation or state.
+ * 1 <= topk <= 64; the other checks as msa_proxy_score. */
+msa_status_t msa_proxy_topk_workspace_size(const msa_proxy_args_t* args, int32_t topk,
+                                           size_t* bytes);
+msa_status_t msa_proxy_topk(const msa_proxy_args_t* args, int32_t topk, int32_t* q2k,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Top-K block select                                                        */
 /* ------------------------------------------------------------------------ */

@@ -24,7 +24,7 @@ def _declared_functions():
 
 def test_header_declarations_are_exported():
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     assert set(names) == set(msa.EXPORTED_SYMBOLS)
     for n in names:
         assert hasattr(msa.lib, n), n
@@ -372,3 +372,19 @@ def test_q_offset_modes_are_checked_on_the_host():
     p.q = p.k = p.out = p.cu_seqlens_q = p.cu_seqlens_k = FAKE
     p.q_offset_mode = 2
     assert msa.lib.msa_proxy_score(ctypes.byref(p), None) == 1
+
+
+def test_proxy_topk_host_checks():
+    p = msa.ProxyArgs()
+    p.batch, p.total_q, p.num_qo_heads, p.num_kv_heads = 2, 8, 32, 2
+    p.head_dim, p.max_seqlen_q, p.max_k_tiles, p.kv_dtype = 128, 4, 64, 1
+    p.q = p.k = p.cu_seqlens_q = p.page_table = p.seqused_k = FAKE
+    p.page_table_width, p.reduce_heads = 64, 1
+    n = ctypes.c_size_t(0)
+    assert msa.lib.msa_proxy_topk_workspace_size(ctypes.byref(p), 0, ctypes.byref(n)) == 2
+    assert msa.lib.msa_proxy_topk_workspace_size(ctypes.byref(p), 16, ctypes.byref(n)) == 0
+    # candidates: one shared selection x 8 queries x 2 KV heads x chunks x 16, score + id
+    assert n.value >= 2 * 8 * 2 * 16 * 4
+    assert msa.lib.msa_proxy_topk(ctypes.byref(p), 16, FAKE, None, 0, None) == 6
+    assert msa.lib.msa_proxy_topk(ctypes.byref(p), 16, None, FAKE, n.value, None) == 1
+    assert msa.lib.msa_proxy_topk(ctypes.byref(p), 16, FAKE, FAKE + 8, n.value, None) == 6
