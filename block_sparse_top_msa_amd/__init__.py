@@ -217,13 +217,15 @@ def _host_max_tiles(cu_k, seqused_k) -> int:
 
 
 class Workspace:
-    """Caller-owned split-KV workspace (the fp32 partials of every split and
-    their LSE; no state survives a launch).  Launches that may overlap need
-    separate workspaces."""
+    """Caller-owned workspace of sparse_attention (the fp32 partials of every
+    split and their LSE, or staged bf16 pages) and of proxy_topk.  Created
+    zero-filled: its last 64 KiB hold the split-KV arrival counters, which
+    the library keeps at zero between launches.  Launches that may overlap
+    need separate workspaces."""
 
     def __init__(self, nbytes: int, device):
         self.nbytes = int(nbytes)
-        self.buffer = torch.empty(max(self.nbytes, 256) + 256, dtype=torch.uint8, device=device)
+        self.buffer = torch.zeros(max(self.nbytes, 256) + 256, dtype=torch.uint8, device=device)
         off = (-self.buffer.data_ptr()) % 256
         self.view = self.buffer[off:off + max(self.nbytes, 256)]
 
@@ -505,6 +507,7 @@ def prepare_msa_nvfp4_sparse_decode(q, k, v, q2k_indices, *, k_scale, v_scale, p
             ws.nbytes = workspace_buffer.numel() - off
             ws.buffer = workspace_buffer
             ws.view = workspace_buffer[off:]
+            ws.view.zero_()   # the split counters start at zero (preparation, not the runner)
     keep = (q, k, v, q2k_indices, k_scale, v_scale, page_table, seqused_k, cu_q)
     run = MSANvfp4DecodeRunner(a, keep, out, lse, ws, int(splits.value))
     run.decode_route = int(route.value)

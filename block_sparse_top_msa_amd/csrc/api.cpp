@@ -287,6 +287,10 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     r->ws_bytes = msa::stage16_bytes(a->batch, a->max_k_tiles, a->num_kv_heads, r->stage_slots);
   }
   if (plan.splits > 1) {
+    if ((int64_t)a->batch * a->num_kv_heads * p.tiles_per_req > msa::kMaxCounterUnits)
+      return fail(MSA_ERR_SHAPE, "split-KV over %lld (request, KV head, token tile) units: at most "
+                  "%d are counted; use splits = 1", (long long)a->batch * a->num_kv_heads *
+                  p.tiles_per_req, msa::kMaxCounterUnits);
     // [partial LSE][partial O][partial temperature LSE (with lse_t)]
     const int rows = plan.tok_per_tile * G;
     const int rows_pad = (rows + 31) / 32 * 32;
@@ -297,6 +301,10 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
     r->ws_bytes = l_bytes + round_up(units * plan.splits * rows * 128 * sizeof(float), 256) +
                   (temp ? l_bytes : 0);
   }
+  // every nonzero workspace keeps the split counters' tail free: the data
+  // ends on a 256-byte boundary, and the counters take the last
+  // kCounterBytes of the (256-byte rounded-down) buffer, past any data
+  if (r->ws_bytes) r->ws_bytes = round_up(r->ws_bytes, 256) + msa::kCounterBytes;
   return MSA_OK;
 }
 
@@ -423,6 +431,9 @@ msa_status_t run_attention(const msa_attn_args_t* args, Resolved& r, void* works
     r.p.ws_lse = reinterpret_cast<float*>(base);
     r.p.ws_o = reinterpret_cast<float*>(base + l_bytes);
     r.p.ws_lse_t = args->lse_t ? reinterpret_cast<float*>(base + l_bytes + o_bytes) : nullptr;
+    // the counters: the last kCounterBytes of the caller's buffer
+    r.p.ws_count = reinterpret_cast<uint32_t*>(base + workspace_bytes / 256 * 256 -
+                                               msa::kCounterBytes);
   }
   if (args->total_q == 0 || args->batch == 0) return ok();
   if (r.stage16) {

@@ -22,11 +22,15 @@
 //    v_mfma_f32_16x16x32_bf16, 16-row tiles (one tile per token at G = 16).
 //  * The four waves' softmax states are merged through LDS at the end.  With
 //    one split the output is written directly; otherwise each split writes
-//    an fp32 partial (O / l and its LSE) and msa_decode_merge_kernel combines
-//    them by LSE (prepare_msa_nvfp4_sparse_decode page, Parameters:
-//    workspace_buffer).  A separate launch orders the partial writes before
-//    the merge without device-scope fences inside the kernel (each such
-//    fence writes back and invalidates the whole L2).
+//    an fp32 partial (O / l and its LSE) and counts its arrival on the unit's
+//    counter; the last split to arrive merges them by LSE and resets the
+//    counter (prepare_msa_nvfp4_sparse_decode page, Parameters:
+//    workspace_buffer).  The partials are written and read only as
+//    device-scope atomic accesses, which stay coherent across the XCDs' L2s
+//    without an L2 writeback or invalidate, and every writer waits for its
+//    stores to complete before it counts; a device-scope fence instead (an
+//    L2 writeback and invalidate on this chip) measured slower than the
+//    separate merge launch it replaces.
 #include "async_lds.hpp"
 #include "common.hpp"
 #include "internal.hpp"
@@ -68,6 +72,15 @@ __device__ __forceinline__ uint32_t pk_out(float lo, float hi) {
 namespace {
 
 constexpr float kLn2d = 0.69314718055994530942f;
+
+// Device-scope relaxed float store / load (the split partials): coherent
+// across the XCDs' L2s without a fence.
+__device__ __forceinline__ void st_dev(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* a) {
+  return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 constexpr int kPtCache = 1024;   // page-table entries read ahead into LDS
 
 // Per-wave staging geometry: wave w stages (and alone reads) key rows
@@ -317,6 +330,7 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
   static_assert(NWV == 4 || NWV == 8, "4 waves, or 8 taking alternate pages");
   static_assert(sizeof(MergeLds<NWV>) <= DecodeLds<FMT, NWV>::kRing, "merge buffer inside the ring");
   __shared__ __attribute__((aligned(16))) DecodeLds<FMT, NWV> lds;
+  __shared__ int s_last;   // this workgroup merges the unit's splits
 
   const int lid = blockIdx.x;
   const int split = lid % p.splits;
@@ -848,10 +862,11 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
         if (TEMP && d0 == 0) p.lse_t[orow] = lset_nat;
       } else {
         float* po = p.ws_o + ((int64_t)unit_split * p.ws_rows + row) * kHeadDim + d0;
-        *reinterpret_cast<f32x4*>(po) = f32x4{acc8[0], acc8[1], acc8[2], acc8[3]};
-        *reinterpret_cast<f32x4*>(po + 4) = f32x4{acc8[4], acc8[5], acc8[6], acc8[7]};
-        if (d0 == 0) p.ws_lse[(int64_t)unit_split * p.ws_lse_rows + row] = lse_nat;
-        if (TEMP && d0 == 0) p.ws_lse_t[(int64_t)unit_split * p.ws_lse_rows + row] = lset_nat;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) st_dev(po + k, acc8[k]);
+        if (d0 == 0) st_dev(p.ws_lse + (int64_t)unit_split * p.ws_lse_rows + row, lse_nat);
+        if (TEMP && d0 == 0)
+          st_dev(p.ws_lse_t + (int64_t)unit_split * p.ws_lse_rows + row, lset_nat);
       }
     }
     if (rt + 1 < RT && 16 * (rt + 1) < R) {   // the next tile rewrites the merge buffer
@@ -859,62 +874,54 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
       block_barrier();
     }
   }
-}
-
-// Combine the split partials of every (request, KV head) by their LSE:
-// lse = ln sum_s exp(lse_s), out = v_gs * sum_s exp(lse_s - lse) O_s.
-// Thread: one row, 8 head dims.
-__global__ __launch_bounds__(256) void msa_decode_merge_kernel(AttnParams p) {
-  const int per_unit = p.ws_rows * 16;
-  const int64_t task = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int unit = (int)(task / per_unit);    // (request, KV head, token tile)
-  const int rem = (int)(task % per_unit);
-  if (unit >= p.batch * p.hkv * p.tiles_per_req) return;
-  const int jt = unit % p.tiles_per_req;
-  const int g = (unit / p.tiles_per_req) % p.hkv, b = unit / p.tiles_per_req / p.hkv;
-  const int j0 = jt * p.tok_per_tile;
-  const int q0 = p.cu_q[b] + j0;
-  const int lq = min(p.cu_q[b + 1] - q0, p.tok_per_tile);
-  const int row = rem >> 4, d0 = 8 * (rem & 15);
-  if (row >= lq * p.group) return;
+  if (p.splits == 1) return;
+  // ---- split arrival: the partial stores of every thread have completed
+  // (device scope) before the unit's counter counts this split
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(p.ws_count + unit, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(p.splits - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // the last split merges: lse = ln sum_s exp(lse_s), out = v_gs * sum_s
+  // exp(lse_s - lse) O_s, then resets the counter for the next launch
   const int nsp = p.splits;
-  const float* lsep = p.ws_lse + (int64_t)unit * nsp * p.ws_lse_rows + row;
-  float M = -INFINITY;
-  for (int s = 0; s < nsp; ++s) M = fmaxf(M, lsep[(int64_t)s * p.ws_lse_rows]);
-  const float Mu = M == -INFINITY ? 0.f : M;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float W = 0.f;
-  for (int s = 0; s < nsp; ++s) {
-    const float w = __expf(lsep[(int64_t)s * p.ws_lse_rows] - Mu);
-    W += w;
-    const float* po = p.ws_o + (((int64_t)unit * nsp + s) * p.ws_rows + row) * kHeadDim + d0;
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(po);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(po + 4);
+  for (int task = tid; task < R * 16; task += NT) {
+    const int row = task >> 4, d0 = 8 * (task & 15);
+    const float* lsep = p.ws_lse + (int64_t)unit * nsp * p.ws_lse_rows + row;
+    float M = -INFINITY;
+    for (int s = 0; s < nsp; ++s) M = fmaxf(M, ld_dev(lsep + (int64_t)s * p.ws_lse_rows));
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    for (int s = 0; s < nsp; ++s) {
+      const float w = __builtin_amdgcn_exp2f((ld_dev(lsep + (int64_t)s * p.ws_lse_rows) - Mu) *
+                                             1.4426950408889634f);
+      W += w;
+      const float* po = p.ws_o + (((int64_t)unit * nsp + s) * p.ws_rows + row) * kHeadDim + d0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      acc[k] += w * a0[k];
-      acc[4 + k] += w * a1[k];
+      for (int k = 0; k < 8; ++k) acc8[k] += w * ld_dev(po + k);
+    }
+    const float sc = W > 0.f ? p.v_gs / W : 0.f;
+    const int64_t orow = (int64_t)(q0 + row / G) * p.hq + g * G + row % G;
+    u32x4 w4;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w4[k] = pk_out<FMT>(acc8[2 * k] * sc, acc8[2 * k + 1] * sc);
+    *reinterpret_cast<u32x4*>(p.out + orow * kHeadDim + d0) = w4;
+    if (p.lse && d0 == 0) p.lse[orow] = W > 0.f ? M + __logf(W) : -INFINITY;
+    if (TEMP && d0 == 0) {
+      const float* ltp = p.ws_lse_t + (int64_t)unit * nsp * p.ws_lse_rows + row;
+      float Mt = -INFINITY;
+      for (int s = 0; s < nsp; ++s) Mt = fmaxf(Mt, ld_dev(ltp + (int64_t)s * p.ws_lse_rows));
+      float St = 0.f;
+      if (Mt > -INFINITY)
+        for (int s = 0; s < nsp; ++s) St += __expf(ld_dev(ltp + (int64_t)s * p.ws_lse_rows) - Mt);
+      p.lse_t[orow] = St > 0.f ? Mt + __logf(St) : -INFINITY;
     }
   }
-  const float sc = W > 0.f ? p.v_gs / W : 0.f;
-  const int64_t orow = (int64_t)(q0 + row / p.group) * p.hq + g * p.group + row % p.group;
-  if (p.lse_t && d0 == 0) {
-    // lse_t = ln sum_s exp(lse_t_s)
-    const float* ltp = p.ws_lse_t + (int64_t)unit * nsp * p.ws_lse_rows + row;
-    float Mt = -INFINITY;
-    for (int s = 0; s < nsp; ++s) Mt = fmaxf(Mt, ltp[(int64_t)s * p.ws_lse_rows]);
-    float St = 0.f;
-    if (Mt > -INFINITY)
-      for (int s = 0; s < nsp; ++s) St += __expf(ltp[(int64_t)s * p.ws_lse_rows] - Mt);
-    p.lse_t[orow] = St > 0.f ? Mt + __logf(St) : -INFINITY;
-  }
-  u32x4 w4;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    w4[k] = p.out_f16 ? pack_f16x2(acc[2 * k] * sc, acc[2 * k + 1] * sc)
-                      : pack_bf16x2(acc[2 * k] * sc, acc[2 * k + 1] * sc);
-  *reinterpret_cast<u32x4*>(p.out + orow * kHeadDim + d0) = w4;
-  if (p.lse && d0 == 0) p.lse[orow] = W > 0.f ? M + __logf(W) : -INFINITY;
+  if (tid == 0) __hip_atomic_store(p.ws_count + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
 }
 
 template <int FMT, int RT, int NWV = 4>
@@ -925,11 +932,6 @@ static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, true>), dim3(n), dim3(NWV * 64), 0, stream, p);
   else
     hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, false>), dim3(n), dim3(NWV * 64), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t tasks = (int64_t)p.batch * p.hkv * p.tiles_per_req * p.ws_rows * 16;
-  hipLaunchKernelGGL(msa_decode_merge_kernel, dim3((unsigned)((tasks + 255) / 256)), dim3(256), 0,
-                     stream, p);
   return hipGetLastError();
 }
 

@@ -60,7 +60,15 @@ struct AttnParams {
   float tau;                  // lse_temperature_scale
   float tslack;               // rescale slack (log2 units) keeping 2^(tau (x - m)) <= 2^64
   float* ws_lse_t;            // [units, splits, rows_pad] split partials of lse_t
+  uint32_t* ws_count;         // [units] split arrival counters, zero between launches
 };
+
+// Split-KV arrival counters sit in the last kCounterBytes of the caller's
+// workspace (every workspace size the library reports reserves them, and
+// nothing else writes there): zero-filled before first use, each unit's
+// counter is reset by the workgroup that merges it.
+constexpr size_t kCounterBytes = 64 * 1024;
+constexpr int kMaxCounterUnits = (int)(kCounterBytes / 4);
 
 // Kernel family selection for one attention call.
 struct AttnPlan {

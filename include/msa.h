@@ -161,19 +161,25 @@ typedef struct {
 } msa_attn_args_t;
 
 /* Bytes of workspace msa_sparse_attention needs for these arguments: the
- * fp32 split-KV partials (O / l per row) and their LSE, and with lse_t
- * their temperature LSE (prepare_msa_nvfp4_sparse_decode page, Parameters:
- * workspace_buffer), or,
- * for fp8 / E2M1 K/V on the prefill route, the bf16 pages their blocks are
- * converted to: 2 * batch * S * Hkv * 32 KiB plus the page table and
- * lengths, with S = max_k_tiles (every visible block), or, when
- * max_seqlen_q * Hkv * topk <= 2048, S = min(that product, max_k_tiles)
- * (only the blocks some query of the request selected).  0 for bf16 / fp16 K/V on the prefill route and
- * for decode shapes whose plan uses one split.  The buffer is 256-byte
- * aligned, owned by the caller, needs no initialisation and carries no
- * state between launches: every launch writes what it reads later on the
- * same stream.  Launches that may run concurrently need separate
- * workspaces. */
+ * fp32 split-KV partials (O / l per row) and their LSE, and with lse_t their
+ * temperature LSE (prepare_msa_nvfp4_sparse_decode page, Parameters:
+ * workspace_buffer), or, for fp8 / E2M1 K/V on the prefill route, the bf16
+ * pages their blocks are converted to: 2 * batch * S * Hkv * 32 KiB plus the
+ * page table and lengths, with S = max_k_tiles (every visible block), or,
+ * when max_seqlen_q * Hkv * topk <= 2048, S = min(that product,
+ * max_k_tiles) (only the blocks some query of the request selected).  0 for
+ * bf16 / fp16 K/V on the prefill route and for decode shapes whose plan uses
+ * one split.  Every nonzero size includes 64 KiB at the end of the buffer
+ * for the split-KV arrival counters: each split's workgroup counts its
+ * arrival there, and the last of a (request, KV head, token tile) merges
+ * the partials and resets its counter (the page's runner likewise resets its
+ * completion counters after every merge).  So the buffer must be zero-filled
+ * before its first use; the library keeps the last 64 KiB of any buffer it
+ * is given at zero between launches and writes nothing else there.  At most
+ * 16384 units can be split (MSA_ERR_SHAPE beyond).  The buffer is 256-byte
+ * aligned and owned by the caller; apart from the counters every launch
+ * writes what it reads later on the same stream.  Launches that may run
+ * concurrently need separate workspaces. */
 msa_status_t msa_sparse_attention_workspace_size(const msa_attn_args_t* args,
                                                  size_t* bytes);
 
@@ -281,7 +287,7 @@ msa_status_t msa_proxy_score(const msa_proxy_args_t* args, void* stream);
  * every chunk's and KV head's candidates by block id (largest score) and
  * selects the top-K; no score buffer exists.  Other shapes: the scores go to
  * the workspace, then the select.  workspace: caller-owned, 256-byte
- * aligned, msa_proxy_topk_workspace_size bytes, no initialisation or state.
+ * aligned, msa_proxy_topk_workspace_size bytes, no initialisation needed.
  * 1 <= topk <= 64; the other checks as msa_proxy_score. */
 msa_status_t msa_proxy_topk_workspace_size(const msa_proxy_args_t* args, int32_t topk,
                                            size_t* bytes);

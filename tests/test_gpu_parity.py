@@ -275,14 +275,45 @@ def test_decode_single_token_rows_out_of_order_and_repeated(msa):
     assert_attention_close(out, lse, ref_out, ref_lse, "unsorted one-token rows")
 
 
+COUNTER_BYTES = 64 * 1024   # the split arrival counters at the end of a workspace
+
+
+def test_split_merge_in_kernel_many_launches(msa):
+    # the last split of every unit merges the others' partials (device-scope
+    # stores and loads, no fence): many launches with new queries each time,
+    # split factors 2..5, and a staged fp8 prefill through the same cached
+    # workspace in between, against the unsplit launch
+    p = synth.make_problem("merge", q_lens=[1] * 40, k_lens=[int(x) for x in
+                           torch.randint(300, 20000, (40,), generator=torch.Generator().manual_seed(3))],
+                           num_qo_heads=16, num_kv_heads=1, topk=16, paged=True,
+                           kv_dtype=synth.KV_E2M1, seed=33, selection="decode",
+                           k_global_scale=0.5, v_global_scale=2.0)
+    d = _dev(p)
+    pf = _dev(synth.make_problem("merge_pf", q_lens=[300], k_lens=[700], num_qo_heads=8,
+                                 num_kv_heads=2, topk=3, kv_dtype=synth.KV_FP8, seed=34,
+                                 selection="general"))
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for it in range(24):
+        d.q.copy_(torch.randn(d.q.shape, generator=g, device="cuda").to(d.q.dtype))
+        splits = 2 + it % 4
+        a = gpu_attention(msa, d, splits=splits)
+        ref = gpu_attention(msa, d, splits=1)
+        if it % 6 == 0:
+            gpu_attention(msa, pf)            # fp8 prefill: staged pages in the workspace
+        torch.cuda.synchronize()
+        assert (a[0].float() - ref[0].float()).abs().max() <= 2e-2, it
+        assert (a[1] - ref[1]).abs().max() <= 1e-3, it
+
+
 def test_decode_is_deterministic_and_workspace_carries_no_state(msa):
+    # (apart from the split counters in the last 64 KiB, kept at zero)
     p = _dev(synth.make_problem("det", q_lens=[4] * 6, k_lens=[5000, 3000, 900, 4000, 128, 2000],
                                 num_qo_heads=32, num_kv_heads=2, topk=16, paged=True,
                                 kv_dtype=synth.KV_FP8, seed=11, selection="decode"))
     ws = msa.Workspace(msa.workspace_size(p.q, p.k, p.v, p.q2k, p.cu_seqlens_q, page_table=p.page_table,
                                           seqused_k=p.seqused_k, max_seqlen_q=4,
                                           max_k_tiles=p.max_k_tiles, splits=4), "cuda")
-    ws.view.fill_(0xFF)   # NaN bytes: nothing may be read before it is written
+    ws.view[:-COUNTER_BYTES].fill_(0xFF)   # NaN bytes: nothing may be read before it is written
     a = gpu_attention(msa, p, splits=4, workspace=ws)
     # a different shape through the same workspace in between
     small = _dev(synth.make_problem("det2", q_lens=[1, 1], k_lens=[700, 300], num_qo_heads=16,
@@ -296,6 +327,7 @@ def test_decode_is_deterministic_and_workspace_carries_no_state(msa):
     assert torch.equal(a[1], b[1]) and torch.equal(a[1], c[1])
     ref_out, ref_lse = oracle_attention(p.to("cpu"))
     assert_attention_close(a[0], a[1], ref_out, ref_lse, "decode splits=4")
+    assert not ws.view[-COUNTER_BYTES:].any()   # every merge reset its counter
     # split factors agree with each other within tolerance
     one = gpu_attention(msa, p, splits=1)
     assert float((one[0].float() - a[0].float()).abs().max()) <= 2e-2
