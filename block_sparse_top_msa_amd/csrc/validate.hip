@@ -5,6 +5,7 @@
 // atomic minimum of (kind << 48 | position), so the report names the first
 // kind and, within it, the first position, whatever the thread order.
 #include <algorithm>
+#include <mutex>
 
 #include "validate.hpp"
 
@@ -68,7 +69,14 @@ __global__ __launch_bounds__(256) void msa_validate_kernel(ValidateParams p) {
 
 }  // namespace
 
+// The result word is one per process and device: checks are serialised
+// (each holds the lock from the reset to the copy back and waits for its
+// stream), so concurrent callers on different threads or streams do not
+// interleave their reset, minimum and read.
+std::mutex g_validate_mu;
+
 hipError_t run_validate(const ValidateParams& p, hipStream_t stream, unsigned long long* word) {
+  std::lock_guard<std::mutex> lock(g_validate_mu);
   void* dev = nullptr;
   hipError_t e = hipGetSymbolAddress(&dev, HIP_SYMBOL(g_violation));
   if (e != hipSuccess) return e;

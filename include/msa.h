@@ -227,7 +227,8 @@ msa_status_t msa_sparse_attention_noalloc(const msa_attn_args_t* args, void* str
  * ascend without repeats and -1 padding is trailing.  Page ids are not
  * bounded above (the pool size is not an argument).  Runs the host checks of
  * msa_sparse_attention, then one small kernel on `stream`, and waits for it
- * (synchronises the stream).  Returns MSA_ERR_CONTRACT, with the first
+ * (synchronises the stream); concurrent checks in one process are
+ * serialised (they share one result word per device).  Returns MSA_ERR_CONTRACT, with the first
  * violation (kind, then position) in msa_last_error(), or MSA_OK; never
  * launches the attention. */
 msa_status_t msa_validate_attention(const msa_attn_args_t* args, void* stream);
