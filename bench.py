@@ -61,6 +61,10 @@ def _args():
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run plain copies of BYTES bytes (profiler counter scaling)")
+    ap.add_argument("--traffic-from", default=None, metavar="DIR",
+                    help="no GPU: write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / "
+                         "WRITE_SIZE runs under DIR (pmc_<counter>_<workload>/ and "
+                         "pmc_<counter>_copy/ for a 1 GiB copy)")
     return ap.parse_args()
 
 
@@ -91,6 +95,73 @@ def _traffic_for(kernel: str):
         with open(os.path.join(ROOT, "block_sparse_top_msa_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return ent["bytes_per_launch"] if h.hexdigest()[:16] == ent.get("sources_sha256_16") else None
+
+
+# kernel -> the sources its machine code is built from (the stored traffic
+# is used only while they hash as they did when the counters were taken)
+TRAFFIC_KERNELS = {
+    "msa_prefill_kernel": ["prefill.hip", "async_lds.hpp", "common.hpp", "tile_union.hpp",
+                           "internal.hpp"],
+    "msa_decode_kernel": ["decode.hip", "async_lds.hpp", "common.hpp", "tile_union.hpp",
+                          "internal.hpp"],
+    "msa_qsa_kernel": ["qsa.hip", "async_lds.hpp", "common.hpp", "internal.hpp"],
+}
+
+
+def write_traffic(src_dir: str, copy_bytes: int = 1 << 30):
+    """profiles/traffic.json from rocprofv3 counter CSVs: per workload, the
+    roofline kernel's FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged),
+    each scaled by the factor that makes a plain copy of copy_bytes read and
+    write copy_bytes."""
+    import collections
+    import csv
+    import glob
+    import hashlib
+
+    def pmc(counter, tag):
+        files = glob.glob(os.path.join(src_dir, f"pmc_{counter}_{tag}", "**",
+                                       "*counter_collection.csv"), recursive=True)
+        acc = collections.defaultdict(list)
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return acc
+
+    def mean(v):
+        return sum(v) / len(v)
+
+    cf = pmc("FETCH_SIZE", "copy")
+    cw = pmc("WRITE_SIZE", "copy")
+    kf = [v for k, v in cf.items() if "copyBuffer" in k][0]
+    kw = [v for k, v in cw.items() if "copyBuffer" in k][0]
+    fs = copy_bytes / 1024 / mean(kf)
+    ws = copy_bytes / 1024 / mean(kw)
+    out = {"_about": "HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                     "dispatch), each scaled by the factor that makes a plain 1 GiB device copy "
+                     "read 1 GiB and write 1 GiB; valid only while the listed kernel sources "
+                     "hash to sources_sha256_16; written by bench.py --traffic-from"}
+    for d in sorted(glob.glob(os.path.join(src_dir, "pmc_FETCH_SIZE_*"))):
+        wl = os.path.basename(d)[len("pmc_FETCH_SIZE_"):]
+        if wl == "copy":
+            continue
+        f, w = pmc("FETCH_SIZE", wl), pmc("WRITE_SIZE", wl)
+        for kern, srcs in TRAFFIC_KERNELS.items():
+            names = [k for k in f if kern + "<" in k or kern + "(" in k]
+            if not names:
+                continue
+            fk = mean(sum((f[k] for k in names), []))
+            wk = mean(sum((w[k] for k in names), []))
+            h = hashlib.sha256()
+            for n in srcs:
+                with open(os.path.join(ROOT, "block_sparse_top_msa_amd", "csrc", n), "rb") as fh:
+                    h.update(fh.read())
+            out[f"{kern}:{wl}"] = {"sources": srcs, "sources_sha256_16": h.hexdigest()[:16],
+                                   "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                                   "fetch_scale": round(fs, 5), "write_scale": round(ws, 5),
+                                   "bytes_per_launch": int(round((fk * fs + wk * ws) * 1024))}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def calibrate_copy(nbytes: int, reps: int):
@@ -455,6 +526,9 @@ def cpu_baseline_qsa(p, rows_n):
 
 def main():
     args = _args()
+    if args.traffic_from:
+        write_traffic(args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the MSA hot path here runs on a single MI355X and "
               f"has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)

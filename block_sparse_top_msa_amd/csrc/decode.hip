@@ -75,11 +75,23 @@ constexpr float kLn2d = 0.69314718055994530942f;
 
 // Device-scope relaxed float store / load (the split partials): coherent
 // across the XCDs' L2s without a fence.
+typedef float f32x2_dev __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void st_dev(float* a, float v) {
   __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_dev(const float* a) {
   return __hip_atomic_load(const_cast<float*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// four floats at a 16-byte aligned address, stored with the device-scope
+// coherence bit (sc1) that the 32- and 64-bit device-scope atomic stores
+// carry, as one 16-byte write
+__device__ __forceinline__ void st_dev4(float* a, f32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ f32x2_dev ld_dev2(const float* a) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(a)),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return f32x2_dev{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
 }
 constexpr int kPtCache = 1024;   // page-table entries read ahead into LDS
 
@@ -862,8 +874,8 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
         if (TEMP && d0 == 0) p.lse_t[orow] = lset_nat;
       } else {
         float* po = p.ws_o + ((int64_t)unit_split * p.ws_rows + row) * kHeadDim + d0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) st_dev(po + k, acc8[k]);
+        st_dev4(po, f32x4{acc8[0], acc8[1], acc8[2], acc8[3]});
+        st_dev4(po + 4, f32x4{acc8[4], acc8[5], acc8[6], acc8[7]});
         if (d0 == 0) st_dev(p.ws_lse + (int64_t)unit_split * p.ws_lse_rows + row, lse_nat);
         if (TEMP && d0 == 0)
           st_dev(p.ws_lse_t + (int64_t)unit_split * p.ws_lse_rows + row, lset_nat);
@@ -901,7 +913,11 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
       W += w;
       const float* po = p.ws_o + (((int64_t)unit * nsp + s) * p.ws_rows + row) * kHeadDim + d0;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc8[k] += w * ld_dev(po + k);
+      for (int k = 0; k < 4; ++k) {
+        const f32x2_dev x = ld_dev2(po + 2 * k);
+        acc8[2 * k] += w * x[0];
+        acc8[2 * k + 1] += w * x[1];
+      }
     }
     const float sc = W > 0.f ? p.v_gs / W : 0.f;
     const int64_t orow = (int64_t)(q0 + row / G) * p.hq + g * G + row % G;
