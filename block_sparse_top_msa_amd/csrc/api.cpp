@@ -580,10 +580,13 @@ msa_status_t resolve_proxy(const msa_proxy_args_t* a, bool need_out, msa::ProxyP
   *wide_out = wide;
   p.rows_per_tile = wide ? 256 : (rows <= 32 ? 32 : 64);
   p.row_tiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
-  // aim for >= ~2048 workgroups; at least 4 blocks per workgroup (a multiple
-  // of 4 on the register path, whose 4 waves take every 4th block)
+  // aim for >= ~2048 workgroups (~3072 on the decode-shaped path, where
+  // 24-block chunks measured 3.5 % faster than 32 on the MTP decode proxy
+  // and 16 slower); at least 4 blocks per workgroup (a multiple of 4 on the
+  // decode-shaped path, whose 4 waves take every 4th block)
   const int base = std::max(1, a->batch * a->num_kv_heads * p.row_tiles);
-  int chunks = std::max(1, (2048 + base - 1) / base);
+  const int target_wg = wide ? 2048 : 3072;
+  int chunks = std::max(1, (target_wg + base - 1) / base);
   int bpw = std::max(4, (a->max_k_tiles + chunks - 1) / chunks);
   if (!wide) bpw = std::min(32, (bpw + 3) / 4 * 4);
   else bpw = std::min(64, std::max(bpw, 16));   // amortise the Q tile over >= 16 blocks
