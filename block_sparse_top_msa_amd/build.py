@@ -44,6 +44,7 @@ FLAGS = [
 PER_FILE = {
     "prefill.hip": ["-fno-honor-nans"],
     "decode.hip": ["-fno-honor-nans"],
+    "proxy.hip": ["-fno-honor-nans"],
     "qsa.hip": ["-fno-honor-nans"],
 }
 

@@ -580,18 +580,27 @@ msa_status_t resolve_proxy(const msa_proxy_args_t* a, bool need_out, msa::ProxyP
   *wide_out = wide;
   p.rows_per_tile = wide ? 256 : (rows <= 32 ? 32 : 64);
   p.row_tiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
-  // aim for >= ~2048 workgroups (~3072 on the decode-shaped path, where
-  // 24-block chunks measured 3.5 % faster than 32 on the MTP decode proxy
-  // and 16 slower); at least 4 blocks per workgroup (a multiple of 4 on the
-  // decode-shaped path, whose 4 waves take every 4th block)
   const int base = std::max(1, a->batch * a->num_kv_heads * p.row_tiles);
-  const int target_wg = wide ? 2048 : 3072;
-  int chunks = std::max(1, (target_wg + base - 1) / base);
+  if (wide) {
+    // pieces per row-tile pair: about two workgroups per CU in all, each
+    // piece at most kWideMaxSeg blocks of a row tile
+    const int pairs = std::max(1, a->batch * a->num_kv_heads * ((p.row_tiles + 1) / 2));
+    p.pieces = std::max((512 + pairs - 1) / pairs,
+                        (2 * a->max_k_tiles + msa::kWideMaxSeg - 1) / msa::kWideMaxSeg);
+    p.pieces = std::max(1, p.pieces);
+    p.blocks_per_wg = 0;
+    p.block_chunks = 0;
+    return MSA_OK;
+  }
+  // aim for ~3072 workgroups (24-block chunks measured 3.5 % faster than 32
+  // on the MTP decode proxy and 16 slower), a multiple of 4 blocks each (the
+  // 4 waves take every 4th block)
+  const int chunks = std::max(1, (3072 + base - 1) / base);
   int bpw = std::max(4, (a->max_k_tiles + chunks - 1) / chunks);
-  if (!wide) bpw = std::min(32, (bpw + 3) / 4 * 4);
-  else bpw = std::min(64, std::max(bpw, 16));   // amortise the Q tile over >= 16 blocks
+  bpw = std::min(32, (bpw + 3) / 4 * 4);
   p.blocks_per_wg = bpw;
   p.block_chunks = (a->max_k_tiles + bpw - 1) / bpw;
+  p.pieces = 0;
   return MSA_OK;
 }
 

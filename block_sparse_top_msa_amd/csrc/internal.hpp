@@ -98,8 +98,9 @@ struct ProxyParams {
   int max_k_tiles;
   int rows_per_tile;          // query rows (token x head) per workgroup
   int row_tiles;              // ceil(max_seqlen_q * group / rows_per_tile)
-  int blocks_per_wg;          // KV blocks per workgroup
+  int blocks_per_wg;          // KV blocks per workgroup (decode-shaped path)
   int block_chunks;           // ceil(max_k_tiles / blocks_per_wg)
+  int pieces;                 // prefill-shaped path: workgroups per row-tile pair
   QueryPos qpos;              // causal positions of the queries
   // running top-K (decode shapes): each workgroup writes the top-K of its
   // chunk per query instead of scores, [sel_rows, total_q, Hg, chunks, topk]
@@ -107,6 +108,9 @@ struct ProxyParams {
   int32_t* cand_id;
   int topk;
 };
+
+// Most KV blocks of one row tile a prefill-shaped proxy workgroup scores.
+constexpr int kWideMaxSeg = 64;
 
 hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream);
 // decode-shaped proxy (<= 64 rows per request and KV head) writing per-chunk

@@ -13,6 +13,7 @@
 // a wave across the G heads of a token, then across KV heads with an exact
 // order-independent atomic max into an output pre-filled with -inf.
 #include <climits>
+#include <type_traits>
 
 #include "async_lds.hpp"
 #include "common.hpp"
@@ -26,8 +27,10 @@ namespace msa {
 // a few MTP tokens x G heads): HBM-bound, every K page is read once.  Each
 // wave scores whole blocks (t_beg + wave, + 4, ...) on its own, without
 // barriers: the blocks stream global -> LDS (global_load_lds, raw bytes)
-// through a per-wave ring of NST stages, so NST blocks per wave are in
-// flight.  Lane (key l % 32, half l / 32) then reads its key row's bytes for
+// through a per-wave stage of one block, refilled 32 keys at a time: as soon
+// as a 32-key chunk has been read into registers the same chunk of the
+// wave's next block is requested, so close to a block's worth of loads stays
+// in flight through the scoring.  Lane (key l % 32, half l / 32) then reads its key row's bytes for
 // head dims 64 half .. 64 half + 63; with the same permutation of the head
 // dimension on Q that is exactly the A operand of S^T = K Q^T on 32x32x16
 // MFMA (k-step s covers dims 64 half + 8 s ..).  fp8 K is converted in
@@ -39,7 +42,6 @@ template <>
 struct RowsGeom<kFmtFp8> {
   static constexpr int kRow = 128;
   static constexpr int kStage = kBlock * kRow;   // 16 KiB
-  static constexpr int kStages = 1;
   static constexpr int kLoads = kStage / 1024;
   static constexpr int kLaneBytes = 64;          // per lane and 32-key chunk
 };
@@ -47,20 +49,18 @@ template <>
 struct RowsGeom<kFmtBf16> {
   static constexpr int kRow = 256;
   static constexpr int kStage = kBlock * kRow;   // 32 KiB
-  static constexpr int kStages = 1;
   static constexpr int kLoads = kStage / 1024;
   static constexpr int kLaneBytes = 128;
 };
 
 constexpr int kRowsMaxBpw = 32;   // blocks per workgroup on this path
-constexpr int kWideMaxBpw = 64;   // ... and on the prefill-shaped path
 
 template <>
 struct RowsGeom<kFmtF16> : RowsGeom<kFmtBf16> {};   // fp16 rows: same bytes as bf16
 
 template <int FMT>
 struct RowsLds {
-  uint8_t ring[4 * RowsGeom<FMT>::kStages * RowsGeom<FMT>::kStage];   // [wave][stage]
+  uint8_t ring[4 * RowsGeom<FMT>::kStage];   // [wave]: one block
   int32_t page[kRowsMaxBpw];
   // block maxima per wave, block and row: written out after the block loop,
   // so that no global store or atomic (counted by vmcnt like the staging
@@ -113,25 +113,23 @@ __device__ __forceinline__ void lds_rd4_issue(u32x4 (&k)[4], const uint32_t (&a)
       : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));
 }
+// Same, at a[j] + OFF (the instruction's immediate offset).
+template <int OFF>
+__device__ __forceinline__ void lds_rd4_issue_at(u32x4 (&k)[4], const uint32_t (&a)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%8\n\t"
+      "ds_read_b128 %1, %5 offset:%8\n\t"
+      "ds_read_b128 %2, %6 offset:%8\n\t"
+      "ds_read_b128 %3, %7 offset:%8"
+      : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "n"(OFF));
+}
 __device__ __forceinline__ void lds_wait4(u32x4 (&k)[4]) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(k[0]), "+v"(k[1]), "+v"(k[2]), "+v"(k[3]));
 }
 
 __device__ __forceinline__ uint32_t lds_addr32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// (M0 restored afterwards, as in g2lds16)
-__device__ __forceinline__ void g2lds16_px(const void* gaddr, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\t"
-               "s_mov_b32 m0, %2\n\t"
-               "s_nop 0\n\t"
-               "global_load_lds_dwordx4 %1, off\n\t"
-               "s_mov_b32 m0, %0"
-               : "=&s"(saved)
-               : "v"(gaddr), "s"(lds_base)
-               : "memory");
 }
 
 // fp8 stages fit two workgroups per CU (256 VGPRs per wave); bf16 stages
@@ -147,8 +145,8 @@ __device__ __forceinline__ void g2lds16_px(const void* gaddr, uint32_t lds_base)
 template <int NT, int FMT, bool REDUCE, bool FUSE = false>
 __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_kernel(ProxyParams p) {
   using Geo = RowsGeom<FMT>;
-  constexpr int NST = Geo::kStages;
   constexpr int LOADS = Geo::kLoads;
+  constexpr int QL = LOADS / 4;   // loads per 32-key chunk
   __shared__ __attribute__((aligned(16))) RowsLds<FMT> lds;
 
   const int chunk = blockIdx.x % p.block_chunks;
@@ -236,146 +234,127 @@ __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_ke
 
   const int64_t kst = p.k_st.token;
   const uint32_t wring = __builtin_amdgcn_readfirstlane(lds_addr32(lds.ring)) +
-                         wave * NST * Geo::kStage;
+                         wave * Geo::kStage;
   // this wave's blocks: t_beg + wave + 4 i, i < nb
   const int nb = t_act - t_beg > wave ? (t_act - t_beg - wave + 3) / 4 : 0;
 
-  // stage block i of this wave: load nn writes LDS bytes [1024 nn, +1024);
-  // rows XOR-swizzled in 16-byte chunks (conflict-free operand reads)
-  // Per-lane byte offsets within a block of the staged rows: row = RPL nn +
-  // lane / LPR (RPL rows per load, LPR lanes per row); the XOR swizzle of a
-  // row depends on nn only through (RPL nn) mod SW, so VAR offsets suffice
-  // and the rest of the row offset goes into the scalar base.
+  // stage block i of this wave: load nn writes LDS bytes [1024 nn, +1024),
+  // rows RPL nn .. (RPL rows per load, LPR lanes per row), XOR-swizzled in
+  // 16-byte chunks (conflict-free operand reads)
   constexpr int LPR = Geo::kRow / 16;          // lanes per row
   constexpr int RPL = 64 / LPR;                // rows per load
   constexpr int SW = FMT == kFmtFp8 ? 8 : 16;  // swizzle period (rows)
-  constexpr int VAR = SW / RPL;                // distinct lane offsets
-  uint32_t loff[VAR];
-#pragma unroll
-  for (int v = 0; v < VAR; ++v) {
-    const int row = RPL * v + lane / LPR;
-    loff[v] = (uint32_t)((lane / LPR) * kst) + 16u * (uint32_t)((lane % LPR) ^ (row % SW));
-  }
-  auto issue = [&](int i, int stage) {
+  // chunk c (keys 32 c .. 32 c + 31) of block i of this wave: loads
+  // QL c .. QL c + QL - 1 (scalar block base + 32-bit lane offsets; token
+  // strides are at most 16 MiB); rows past the sequence end load row 0
+  // (masked)
+  auto issue = [&](int i, int c) {
     const int t = t_beg + wave + 4 * i;
     const int pg = __builtin_amdgcn_readfirstlane(lds.page[t - t_beg]);
     const int nvalid = min(kBlock, lk - kBlock * t);
-    const uint8_t* base = p.paged ? p.k + (int64_t)pg * p.k_st.page + g * p.k_st.head
-                                  : p.k + (int64_t)pg * kst + g * p.k_st.head;
-    const uint32_t dst = wring + stage * Geo::kStage;
-    if (nvalid == kBlock) {
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(uniform64((unsigned long long)(
+        p.paged ? p.k + (int64_t)pg * p.k_st.page + g * p.k_st.head
+                : p.k + (int64_t)pg * kst + g * p.k_st.head)));
 #pragma unroll
-      for (int nn = 0; nn < LOADS; ++nn)
-        g2lds16_sv(base + (int64_t)(RPL * nn) * kst, loff[nn % VAR], dst + 1024 * nn);
-    } else {
-#pragma unroll
-      for (int nn = 0; nn < LOADS; ++nn) {
-        const int row = RPL * nn + lane / LPR;
-        const int c = (lane % LPR) ^ (row % SW);
-        const int rr = row < nvalid ? row : 0;   // past the end: row 0 (masked)
-        g2lds16_px(base + rr * kst + 16 * c, dst + 1024 * nn);
-      }
+    for (int n2 = 0; n2 < QL; ++n2) {
+      const int nn = QL * c + n2;
+      const int row = RPL * nn + lane / LPR;
+      const int c = (lane % LPR) ^ (row % SW);
+      const int rr = row < nvalid ? row : 0;
+      g2lds16_sv(base, (uint32_t)(rr * kst) + 16u * (uint32_t)c, wring + 1024 * nn);
     }
   };
 
   constexpr int LB = Geo::kLaneBytes / 16;   // 16-byte pieces per lane and chunk
-  // lane's key rows 32 c + col of chunks c0, c0 + 1: bytes of head dims
-  // 64 half .. 64 half + 63
-  auto read_pair = [&](uint32_t sb, int c0, u32x4 (&kr)[2][LB]) {
+  // lane's key row 32 c + col of chunk c: bytes of head dims 64 half ..
+  // 64 half + 63
+  auto read_chunk = [&](uint32_t sb, int c, u32x4 (&kr)[LB]) {
+    const int row = 32 * c + col;
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int row = 32 * (c0 + cc) + col;
+    for (int j0 = 0; j0 < LB; j0 += 4) {
+      uint32_t a[4];
 #pragma unroll
-      for (int j0 = 0; j0 < LB; j0 += 4) {
-        uint32_t a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int lc = LB * half + j0 + j;   // logical 16-byte chunk of the row
-          const int pc = FMT == kFmtFp8 ? (lc ^ (row & 7)) : (lc ^ (row & 15));
-          a[j] = sb + row * Geo::kRow + 16 * pc;
-        }
-        u32x4 w[4];
-        lds_rd4(w, a);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kr[cc][j0 + j] = w[j];
+      for (int j = 0; j < 4; ++j) {
+        const int lc = LB * half + j0 + j;   // logical 16-byte chunk of the row
+        const int pc = FMT == kFmtFp8 ? (lc ^ (row & 7)) : (lc ^ (row & 15));
+        a[j] = sb + row * Geo::kRow + 16 * pc;
       }
+      u32x4 w[4];
+      lds_rd4(w, a);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kr[j0 + j] = w[j];
     }
   };
 
-  // block max of chunks c0, c0 + 1 into bm: 2 x NT independent accumulator
-  // chains keep the MFMA pipe busy
-  auto score_pair = [&](int t, int c0, const u32x4 (&kr)[2][LB], float (&bm)[NT]) {
+  // block max of chunk c into bm: NT independent accumulator chains
+  auto score_chunk = [&](int t, int c, const u32x4 (&kr)[LB], float (&bm)[NT]) {
     const int nvalid = min(kBlock, lk - kBlock * t);
     const bool full = nvalid == kBlock && (!p.causal || pos_min >= kBlock * t + kBlock - 1);
-    f32x16 acc[2][NT];
+    f32x16 acc[NT];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
+      bf16x8 a;
+      if constexpr (FMT == kFmtFp8) {
+        const u32x4 w = kr[s >> 1];
+        a = (s & 1) ? fp8x8_bf16(w[2], w[3]) : fp8x8_bf16(w[0], w[1]);
+      } else {
+        a = as_bf16x8(kr[s]);
+      }
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        bf16x8 a;
-        if constexpr (FMT == kFmtFp8) {
-          const u32x4 w = kr[cc][s >> 1];
-          a = (s & 1) ? fp8x8_bf16(w[2], w[3]) : fp8x8_bf16(w[0], w[1]);
+      for (int nt = 0; nt < NT; ++nt) {
+        if (s == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) z[r] = 0.f;
+          acc[nt] = mm32<FMT>(a, qf[nt][s], z);
         } else {
-          a = as_bf16x8(kr[cc][s]);
-        }
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          if (s == 0) {
-            f32x16 z;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = 0.f;
-            acc[cc][nt] = mm32<FMT>(a, qf[nt][s], z);
-          } else {
-            acc[cc][nt] = mm32<FMT>(a, qf[nt][s], acc[cc][nt]);
-          }
+          acc[nt] = mm32<FMT>(a, qf[nt][s], acc[nt]);
         }
       }
     }
-    if (full) {
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+    for (int nt = 0; nt < NT; ++nt) {
+      if (!full) {
+        int lim = nvalid - 1;
+        if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) bm[nt] = fmaxf(bm[nt], max16(acc[cc][nt]));
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int c = c0 + cc;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          int lim = nvalid - 1;
-          if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * c + 8 * (r >> 2) + 4 * half + (r & 3);
-            acc[cc][nt][r] = key <= lim ? acc[cc][nt][r] : -INFINITY;
-          }
-          bm[nt] = fmaxf(bm[nt], max16(acc[cc][nt]));
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * c + 8 * (r >> 2) + 4 * half + (r & 3);
+          acc[nt][r] = key <= lim ? acc[nt][r] : -INFINITY;
         }
       }
+      bm[nt] = fmaxf(bm[nt], max16(acc[nt]));
     }
   };
 
-#pragma unroll
-  for (int s = 0; s < NST; ++s)
-    if (s < nb) issue(s, s);
-  for (int i = 0; i < nb; ++i) {
-    const int stage = i % NST;
-    const int later = min(NST - 1, nb - 1 - i);
-    if (later >= 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LOADS) : "memory");
+  // wait until at most `left` quarters of this wave's loads are outstanding
+  auto wait_left = [&](int left) {
+    if (left >= 3) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * QL) : "memory");
+    else if (left == 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * QL) : "memory");
+    else if (left == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(QL) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  };
+
+  if (nb > 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) issue(0, c);
+  }
+  for (int i = 0; i < nb; ++i) {
+    const bool next = i + 1 < nb;
     const int t = t_beg + wave + 4 * i;
-    const uint32_t sb = wring + stage * Geo::kStage;
     float bm[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) bm[nt] = -INFINITY;
-    u32x4 kr[2][LB];
-    read_pair(sb, 0, kr);
-    score_pair(t, 0, kr, bm);
-    read_pair(sb, 2, kr);
-    // the stage has been read: it takes the block NST ahead
-    if (i + NST < nb) issue(i + NST, stage);
-    score_pair(t, 2, kr, bm);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // chunk c landed: behind it in flight are the block's later chunks
+      // and the next block's chunks requested so far (three in all)
+      wait_left(next ? 3 : 3 - c);
+      u32x4 kr[LB];
+      read_chunk(wring, c, kr);
+      if (next) issue(i + 1, c);   // read: the chunk's rows take the next block's
+      score_chunk(t, c, kr, bm);
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float v = xor_max(bm[nt], 32);
@@ -448,15 +427,17 @@ __global__ __launch_bounds__(256, FMT == kFmtFp8 ? 2 : 1) void msa_proxy_rows_ke
 }
 
 // ---------------------------------------------------------------------------
-// Prefill-shaped proxy (many query rows): MFMA-bound.  A workgroup owns 256
-// query rows (4 waves x 64, token x head of one KV head) and a range of KV
-// blocks.  Each block's K streams global -> LDS with global_load_lds (raw
-// bytes, XOR-swizzled rows, double buffered, one barrier per block); lane
-// (key l % 32, half l / 32) reads its key row's bytes for head dims
-// 64 half .. 64 half + 63 in the A-operand layout of 32x32x16 MFMA (Q uses
-// the same head-dim permutation), fp8 converted in registers.  Per block and
-// wave: 4 key subtiles x 2 row tiles x 8 k-steps, the two row tiles' chains
-// interleaved; block maxima go out as coalesced rows.
+// Prefill-shaped proxy (many query rows): MFMA-bound.  A workgroup scores
+// tiles of 256 query rows (4 waves x 64, token x head of one KV head)
+// against an equal share of a row-tile pair's visible KV blocks (see the
+// work mapping below).  Each block's K streams global -> LDS with
+// global_load_lds (raw bytes, XOR-swizzled rows, double buffered, one
+// barrier per block); lane (key l % 32, half l / 32) reads its key row's
+// bytes for head dims 64 half .. 64 half + 63 in the A-operand layout of
+// 32x32x16 MFMA (Q uses the same head-dim permutation), fp8 converted in
+// registers.  Per block and wave: 4 key subtiles x 2 row tiles x 8 k-steps,
+// the two row tiles' chains interleaved, and the previous subtile's row
+// maxima issued between them; block maxima go out as coalesced rows.
 // ---------------------------------------------------------------------------
 template <int FMT, bool REDUCE>
 __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
@@ -465,39 +446,35 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   constexpr int LOADS = Geo::kStage / 4096;  // 1 KiB loads per wave per block
   constexpr int SW = FMT == kFmtFp8 ? 8 : 16;
   __shared__ __attribute__((aligned(16))) uint8_t ring[2][Geo::kStage];
-  __shared__ int64_t kbase[kWideMaxBpw];
+  __shared__ int64_t kbase[kWideMaxSeg];
 
-  const int n = p.batch * p.hkv * p.row_tiles * p.block_chunks;
-  int lid;
-  if (p.causal && (p.row_tiles & 1) == 0 && n % 512 == 0) {
-    // Passes of two workgroups per CU (256 CUs): within each run of 512,
-    // blockIdx b and b + 256 land on the same CU (XCD b % 8, CU (b / 8) %
-    // 32).  Under the causal mask row tile rt sees about 2 rt + 2 blocks, so
-    // (rt, chunk c) and its reflection (R - 1 - rt, C - 1 - c) together hold
-    // an almost constant amount of work: give them the same CU.
-    const int b2 = blockIdx.x;
-    if (b2 >= n) return;
-    const int half_rt = p.row_tiles / 2;
-    // representative (b, g, rt < R / 2, c)
-    const int k = (b2 / 512) * 256 + b2 % 256;
-    const int c = k % p.block_chunks;
-    int r2 = k / p.block_chunks;
-    const int rtr = r2 % half_rt;
-    const int bg = r2 / half_rt;
-    const bool mirror = b2 % 512 >= 256;
-    const int rt_sel = mirror ? p.row_tiles - 1 - rtr : rtr;
-    const int c_sel = mirror ? p.block_chunks - 1 - c : c;
-    lid = (bg * p.row_tiles + rt_sel) * p.block_chunks + c_sel;
+  // Workgroup -> (request, KV head, row-tile pair, piece).  Row tile rt is
+  // paired with its reflection R - 1 - rt: under the causal mask their
+  // visible blocks add up to about the same count for every pair, so cutting
+  // each pair's blocks into P equal pieces gives every workgroup the same
+  // work (two per CU, both busy to the end).  A pair's pieces run on one XCD,
+  // so its Q tiles and K blocks are fetched into that L2 once.
+  const int pairs = (p.row_tiles + 1) / 2;
+  const int P = p.pieces;
+  const int units = p.batch * p.hkv;
+  int unit, pi, piece;
+  if (units <= 8 && 8 % units == 0) {
+    // each (request, KV head) keeps to 8 / units XCDs
+    const int xpu = 8 / units;
+    const int x = blockIdx.x % 8, k = blockIdx.x / 8;
+    unit = x / xpu;
+    pi = (k / P) * xpu + x % xpu;
+    piece = k % P;
+    if (pi >= pairs) return;
   } else {
-    lid = xcd_remap(blockIdx.x, n);
+    const int lid = xcd_remap(blockIdx.x, units * pairs * P);
     if (lid < 0) return;
+    piece = lid % P;
+    pi = (lid / P) % pairs;
+    unit = lid / P / pairs;
   }
-  const int chunk = lid % p.block_chunks;
-  int rest = lid / p.block_chunks;
-  const int rt = rest % p.row_tiles;
-  rest /= p.row_tiles;
-  const int g = rest % p.hkv;
-  const int b = rest / p.hkv;
+  const int g = unit % p.hkv;
+  const int b = unit / p.hkv;
 
   const int G = p.group;
   // reduced output row block: all heads -> row 0, group of KV head g -> row g
@@ -505,22 +482,26 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   const int q0 = p.cu_q[b];
   const int lq = p.cu_q[b + 1] - q0;
   const int nrows = lq * G;
-  const int r0 = rt * 256;
-  if (r0 >= nrows) return;
   const int lk = p.paged ? p.seqused_k[b] : (p.cu_k[b + 1] - p.cu_k[b]);
   const int nblk = max(0, (lk + kBlock - 1) / kBlock);
-  const int t_beg = chunk * p.blocks_per_wg;
-  const int t_end = min(t_beg + p.blocks_per_wg, p.max_k_tiles);
-  if (t_beg >= t_end) return;
-  const int r_last = min(r0 + 256, nrows) - 1;
   const bool rowpos = p.qpos.mode == 2;
   const int pos0 = query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0, 0, lq, lk);
-  const int pos_min = rowpos ? INT_MIN : pos0 + r0 / G;
-  const int pos_max = rowpos ? INT_MAX : pos0 + r_last / G;
-  int t_act = min(t_end, nblk);
-  if (p.paged) t_act = min(t_act, p.pt_width);
-  if (p.causal) t_act = min(t_act, pos_max < 0 ? 0 : pos_max / kBlock + 1);
-  t_act = max(t_act, t_beg);
+  // blocks 0 .. visible(rt) - 1 hold a key some row of tile rt may see;
+  // per-row positions have no order, so they bound nothing
+  auto visible = [&](int rt) {
+    const int r0 = rt * 256;
+    if (r0 >= nrows) return 0;
+    const int pos_max = rowpos ? INT_MAX : pos0 + (min(r0 + 256, nrows) - 1) / G;
+    int v = min(nblk, p.max_k_tiles);
+    if (p.paged) v = min(v, p.pt_width);
+    if (p.causal) v = min(v, pos_max < 0 ? 0 : pos_max / kBlock + 1);
+    return max(v, 0);
+  };
+  const int rta = pi, rtb = p.row_tiles - 1 - pi;
+  const int va = visible(rta);
+  const int vb = rtb != rta ? visible(rtb) : 0;
+  const int64_t cost = (int64_t)va + vb;
+  const int s_lo = (int)(cost * piece / P), s_hi = (int)(cost * (piece + 1) / P);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -528,6 +509,32 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   const int col = lane & 31;
   const int half = lane >> 5;
   const int64_t kst = p.k_st.token;
+
+  // blocks with no visible key: -inf (pre-filled when reducing), written by
+  // the pair's first piece
+  if (!REDUCE && piece == 0 && half == 0) {
+    for (int h2 = 0; h2 < (rtb != rta ? 2 : 1); ++h2) {
+      const int r0 = (h2 ? rtb : rta) * 256;
+      for (int t = h2 ? vb : va; t < p.max_k_tiles; ++t) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int r = r0 + 64 * wave + 32 * nt + col;
+          if (r < nrows)
+            p.out[((int64_t)(g * G + r % G) * p.max_k_tiles + t) * p.total_q + q0 + r / G] = -INFINITY;
+        }
+      }
+    }
+  }
+
+  // the piece's blocks: [s_lo, s_hi) of tile rta's visible blocks followed
+  // by tile rtb's
+  for (int seg = 0; seg < 2; ++seg) {
+  const int rt = seg ? rtb : rta;
+  const int t_beg = seg ? max(s_lo - va, 0) : s_lo;
+  const int t_act = seg ? s_hi - va : min(s_hi, va);
+  if (t_beg >= t_act) continue;
+  const int r0 = rt * 256;
+  const int pos_min = rowpos ? INT_MIN : pos0 + r0 / G;
 
   for (int i = tid; i < t_act - t_beg; i += 256) {
     const int t = t_beg + i;
@@ -558,17 +565,6 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
       for (int s = 0; s < 8; ++s) qf[nt][s] = as_bf16x8(u32x4{0, 0, 0, 0});
     }
   }
-  // blocks of the chunk with no visible key: -inf (pre-filled when reducing)
-  if (!REDUCE && half == 0) {
-    for (int t = t_act; t < t_end; ++t) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int r = row_[nt];
-        if (r < nrows)
-          p.out[((int64_t)(g * G + r % G) * p.max_k_tiles + t) * p.total_q + q0 + r / G] = -INFINITY;
-      }
-    }
-  }
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -586,6 +582,7 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   const uint32_t ring0 = __builtin_amdgcn_readfirstlane(lds_addr32(&ring[0][0]));
   // (scalar block base + 32-bit lane offsets; token strides are at most
   // 16 MiB)
+  static_assert((4 * RPL) % SW == 0, "a wave's staged rows keep one swizzle phase");
   auto issue = [&](int t, int buf) {
     const int i = t - t_beg;
     const int nvalid = min(kBlock, lk - kBlock * t);
@@ -595,13 +592,26 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
     // would hold registers through the MFMAs
     int ln;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    if (nvalid == kBlock) {
+      // load nn of wave w stages rows RPL (4 nn + w) + l / LPR: their
+      // swizzle phase is the same for every nn, so one lane offset serves
+      // all loads and the row step goes into the scalar base
+      const int row0 = RPL * wave + ln / LPR;
+      const uint32_t voff = (uint32_t)((ln / LPR) * kst) + 16u * (uint32_t)((ln % LPR) ^ (row0 % SW));
 #pragma unroll
-    for (int nn = 0; nn < LOADS; ++nn) {
-      const int ld = 4 * nn + wave;
-      const int row = RPL * ld + ln / LPR;
-      const int c = (ln % LPR) ^ (row % SW);
-      const int rr = row < nvalid ? row : 0;   // past the end: row 0 (masked)
-      g2lds16_sv(base, (uint32_t)(rr * kst) + 16 * c, ring0 + buf * Geo::kStage + 1024 * ld);
+      for (int nn = 0; nn < LOADS; ++nn) {
+        const int ld = 4 * nn + wave;
+        g2lds16_sv(base + (int64_t)(RPL * ld) * kst, voff, ring0 + buf * Geo::kStage + 1024 * ld);
+      }
+    } else {
+#pragma unroll
+      for (int nn = 0; nn < LOADS; ++nn) {
+        const int ld = 4 * nn + wave;
+        const int row = RPL * ld + ln / LPR;
+        const int c = (ln % LPR) ^ (row % SW);
+        const int rr = row < nvalid ? row : 0;   // past the end: row 0 (masked)
+        g2lds16_sv(base, (uint32_t)(rr * kst) + 16 * c, ring0 + buf * Geo::kStage + 1024 * ld);
+      }
     }
   };
 
@@ -624,15 +634,24 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
     // Software pipeline over the 4 key subtiles: the LDS reads of subtile
     // kt + 1 and the row maxima of subtile kt - 1 overlap the MFMAs of kt.
     u32x4 kr[2][LB];
+    // lane's row col of subtile 0; subtile kt is 32 kt rows further, with
+    // the same swizzle phase (32 is a multiple of SW), so its reads take
+    // the same addresses plus an immediate offset
+    uint32_t ka[LB];
+#pragma unroll
+    for (int j = 0; j < LB; ++j) ka[j] = sb + col * Geo::kRow + 16 * ((LB * half + j) ^ (col % SW));
+    // (kt is a constant once the subtile loop is unrolled)
     auto kread = [&](int kt, u32x4 (&dst)[LB]) {
-      const int row = 32 * kt + col;
 #pragma unroll
       for (int j0 = 0; j0 < LB; j0 += 4) {
-        uint32_t a[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[j] = sb + row * Geo::kRow + 16 * ((LB * half + j0 + j) ^ (row % SW));
+        const uint32_t a[4] = {ka[j0], ka[j0 + 1], ka[j0 + 2], ka[j0 + 3]};
         u32x4 w[4];
-        lds_rd4_issue(w, a);
+        switch (kt) {
+          case 0: lds_rd4_issue_at<0>(w, a); break;
+          case 1: lds_rd4_issue_at<32 * Geo::kRow>(w, a); break;
+          case 2: lds_rd4_issue_at<64 * Geo::kRow>(w, a); break;
+          default: lds_rd4_issue_at<96 * Geo::kRow>(w, a); break;
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) dst[j0 + j] = w[j];
       }
@@ -646,53 +665,73 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
         for (int j = 0; j < 4; ++j) dst[j0 + j] = w[j];
       }
     };
-    auto reduce = [&](int kt, f32x16 (&acc)[2]) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        if (!full) {
-          int lim = nvalid - 1;
-          if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
-            acc[nt][r] = key <= lim ? acc[nt][r] : -INFINITY;
-          }
-        }
-        bm[nt] = fmaxf(bm[nt], max16(acc[nt]));
-      }
-    };
-    f32x16 acc[2][2];
-    kread(0, kr[0]);
-    kwait(kr[0]);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int cur = kt & 1;
-      if (kt < 3) kread(kt + 1, kr[cur ^ 1]);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        bf16x8 a;
-        if constexpr (FMT == kFmtFp8) {
-          const u32x4 w = kr[cur][s >> 1];
-          a = (s & 1) ? fp8x8_bf16(w[2], w[3]) : fp8x8_bf16(w[0], w[1]);
-        } else {
-          a = as_bf16x8(kr[cur][s]);
-        }
+    // Whole blocks (no key masked) and the others take separate copies of
+    // the subtile loop, so that the whole-block copy is straight-line code
+    // whose MFMAs, row maxima and LDS reads can be interleaved.
+    auto body = [&](auto full_c) {
+      constexpr bool FULL = decltype(full_c)::value;
+      auto reduce = [&](int kt, f32x16 (&acc)[2]) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          if (s == 0) {
-            f32x16 z;
+          if constexpr (!FULL) {
+            int lim = nvalid - 1;
+            if (p.causal) lim = min(lim, pos_[nt] - kBlock * t);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) z[r] = 0.f;
-            acc[cur][nt] = mm32<FMT>(a, qf[nt][s], z);
+            for (int r = 0; r < 16; ++r) {
+              const int key = 32 * kt + 8 * (r >> 2) + 4 * half + (r & 3);
+              acc[nt][r] = key <= lim ? acc[nt][r] : -INFINITY;
+            }
+          }
+          bm[nt] = fmaxf(bm[nt], max16(acc[nt]));
+        }
+      };
+      f32x16 acc[2][2];
+      kread(0, kr[0]);
+      kwait(kr[0]);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int cur = kt & 1;
+        if (kt < 3) kread(kt + 1, kr[cur ^ 1]);
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          bf16x8 a;
+          if constexpr (FMT == kFmtFp8) {
+            const u32x4 w = kr[cur][s >> 1];
+            a = (s & 1) ? fp8x8_bf16(w[2], w[3]) : fp8x8_bf16(w[0], w[1]);
           } else {
-            acc[cur][nt] = mm32<FMT>(a, qf[nt][s], acc[cur][nt]);
+            a = as_bf16x8(kr[cur][s]);
+          }
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            if (s == 0) {
+              f32x16 z;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) z[r] = 0.f;
+              acc[cur][nt] = mm32<FMT>(a, qf[nt][s], z);
+            } else {
+              acc[cur][nt] = mm32<FMT>(a, qf[nt][s], acc[cur][nt]);
+            }
           }
         }
+        if (kt > 0) reduce(kt - 1, acc[cur ^ 1]);
+        if constexpr (FULL) {
+          if (kt > 0) {
+            // the previous subtile's row maxima between this one's MFMAs
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt < 3) kwait(kr[cur ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      if (kt > 0) reduce(kt - 1, acc[cur ^ 1]);
-      if (kt < 3) kwait(kr[cur ^ 1]);
-    }
-    reduce(3, acc[1]);
+      reduce(3, acc[1]);
+    };
+    if (full) body(std::true_type{});
+    else body(std::false_type{});
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float v = xor_max(bm[nt], 32);
@@ -715,6 +754,7 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   }
+  }  // segments
 }
 
 __global__ void msa_fill_kernel(float* __restrict__ out, int64_t n, float v) {
@@ -725,9 +765,13 @@ __global__ void msa_fill_kernel(float* __restrict__ out, int64_t n, float v) {
 
 template <int FMT>
 static hipError_t launch_proxy_wide_t(const ProxyParams& p, hipStream_t stream) {
-  const int n = p.batch * p.hkv * p.row_tiles * p.block_chunks;
+  const int units = p.batch * p.hkv;
+  const int pairs = (p.row_tiles + 1) / 2;
+  const int n = units * pairs * p.pieces;
   if (n <= 0) return hipSuccess;
-  const int grid = 8 * ((n + 7) / 8);
+  const int grid = units <= 8 && 8 % units == 0
+                       ? 8 * ((pairs + 8 / units - 1) / (8 / units)) * p.pieces
+                       : 8 * ((n + 7) / 8);
   if (p.reduce) {
     const int64_t total = (int64_t)(p.reduce == 2 ? p.hkv : 1) * p.max_k_tiles * p.total_q;
     if (total > 0) {

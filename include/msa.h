@@ -271,7 +271,8 @@ typedef struct {
  * the block is visible or the block is past the sequence (msa_proxy_score
  * page, summary).  With reduce_heads the max over h (all heads, or the heads
  * of each KV head's group) is taken in-kernel, so the per-head scores are
- * never written (msa_proxy_score page, Parameters: reduce_heads). */
+ * never written (msa_proxy_score page, Parameters: reduce_heads).  q and k
+ * hold finite values (NaN or infinite inputs leave the scores unspecified). */
 msa_status_t msa_proxy_score(const msa_proxy_args_t* args, void* stream);
 
 /* Proxy score, head reduction and top-K block select in one call, with the
