@@ -391,6 +391,41 @@ def test_proxy_matches_oracle(msa, case):
     assert_proxy_close(got, ref, f"proxy case {case}")
 
 
+# Prefill-shaped proxy: every workgroup scores an equal piece of a reflected
+# row-tile pair's visible blocks (pieces may span both tiles of the pair).
+WIDE_PROXY_CASES = [
+    # q_lens, k_lens, Hq, Hkv, paged, fmt, causal, reduce, extra columns
+    ([1280], [1280], 1, 1, False, synth.KV_BF16, True, False, 0),        # 5 row tiles: the middle one alone
+    ([600, 1100], [600, 1500], 2, 2, False, synth.KV_FP8, True, False, 3),   # fp8 K, ragged
+    ([520, 260], [900, 700], 16, 2, True, synth.KV_BF16, True, "group", 1),  # paged, G = 8 reduced
+    ([300, 300, 300, 129, 700], [300, 800, 301, 129, 700], 4, 2, False, synth.KV_BF16, True, True, 0),  # 10 (request, KV head) units
+    ([700], [5000], 2, 1, True, synth.KV_FP8, False, False, 2),           # non-causal, 40 blocks per row
+    ([2048], [2048], 1, 1, False, synth.KV_F16, True, False, 0),          # fp16 Q and K, 8 row tiles
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE_PROXY_CASES)))
+def test_wide_proxy_pieces_match_oracle(msa, case):
+    ql, kl, hq, hkv, paged, fmt, causal, reduce, extra = WIDE_PROXY_CASES[case]
+    p = synth.make_problem("wide_proxy", q_lens=ql, k_lens=kl, num_qo_heads=hq,
+                           num_kv_heads=hkv, paged=paged, kv_dtype=fmt, causal=causal,
+                           seed=430 + case, selection="proxy",
+                           reduce_heads=reduce is True)
+    print(f"wide proxy case {case}", flush=True)
+    d = _dev(p)
+    T = p.max_k_tiles + extra
+    got = msa.proxy_score(d.q, d.k, d.cu_seqlens_q, d.cu_seqlens_k, page_table=d.page_table,
+                          seqused_k=d.seqused_k, causal=causal, max_seqlen_q=max(ql),
+                          max_k_tiles=T, reduce_heads=reduce)
+    torch.cuda.synchronize()
+    ref = oracle.proxy_score(p.q, p.k, p.cu_seqlens_q, cu_seqlens_k=p.cu_seqlens_k,
+                             page_table=p.page_table, seqused_k=p.seqused_k, causal=causal,
+                             max_k_tiles=T, reduce_heads=reduce is True, kv_format=fmt)
+    if reduce == "group":
+        ref = ref.view(hkv, hq // hkv, T, -1).amax(dim=1)
+    assert_proxy_close(got, ref, f"wide proxy case {case}")
+
+
 # ---------------------------------------------------------------------------
 # top-K select
 # ---------------------------------------------------------------------------
