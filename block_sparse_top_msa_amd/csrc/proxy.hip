@@ -503,16 +503,21 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   const int64_t cost = (int64_t)va + vb;
   const int s_lo = (int)(cost * piece / P), s_hi = (int)(cost * (piece + 1) / P);
 
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int lane = tid & (kWave - 1);
-  const int col = lane & 31;
-  const int half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int64_t kst = p.k_st.token;
+  // lane quantities are recomputed from the lane id where they are used
+  // (read through a volatile asm, so not hoisted): kept from the prologue
+  // they would hold registers through the block loop
+  auto lane_id = [] {
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    return ln;
+  };
 
   // blocks with no visible key: -inf (pre-filled when reducing), written by
   // the pair's first piece
-  if (!REDUCE && piece == 0 && half == 0) {
+  if (!REDUCE && piece == 0 && lane_id() < 32) {
+    const int col = lane_id() & 31;
     for (int h2 = 0; h2 < (rtb != rta ? 2 : 1); ++h2) {
       const int r0 = (h2 ? rtb : rta) * 256;
       for (int t = h2 ? vb : va; t < p.max_k_tiles; ++t) {
@@ -535,6 +540,10 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   if (t_beg >= t_act) continue;
   const int r0 = rt * 256;
   const int pos_min = rowpos ? INT_MIN : pos0 + r0 / G;
+  const int lane = lane_id();
+  const int tid = wave * kWave + lane;
+  const int col = lane & 31;
+  const int half = lane >> 5;
 
   for (int i = tid; i < t_act - t_beg; i += 256) {
     const int t = t_beg + i;
@@ -547,12 +556,11 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   }
 
   // rows of this wave: r0 + 64 wave + 32 nt + col
-  int row_[2], pos_[2];
+  int pos_[2];
   bf16x8 qf[2][8];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt) {
     const int r = r0 + 64 * wave + 32 * nt + col;
-    row_[nt] = r;
     const int tk = r / G, hh = r % G;
     pos_[nt] = r < nrows ? query_pos(p.qpos.rows, p.qpos.mode, p.qpos.base, q0 + tk, tk, lq, lk) : 0;
     if (r < nrows) {
@@ -735,7 +743,7 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       float v = xor_max(bm[nt], 32);
-      const int r = row_[nt];
+      const int r = r0 + 64 * wave + 32 * nt + (lane_id() & 31);
       const int tk = r / G, hh = r % G;
       if constexpr (!REDUCE) {
         if (half == 0 && r < nrows)
