@@ -5,8 +5,8 @@ Serving loops run the same decode shapes every step; capturing the step
 pipeline of the msa_proxy_score and msa_sparse_attention pages) removes the
 per-launch host work and gaps.  The library never allocates, never
 synchronises and clears nothing with memset (its fills are kernels), so the
-step captures as it is: this module only binds the buffers (outputs,
-selection scores, q2k, the split-KV workspace) before capture and passes
+step captures as it is: this module only binds the buffers (outputs, q2k,
+the proxy/top-K and split-KV workspaces) before capture and passes
 every size explicitly, so that no call inside the graph reads a device
 value on the host.
 
@@ -19,7 +19,8 @@ from __future__ import annotations
 
 import torch
 
-from . import (Workspace, proxy_score, sparse_attention, topk_select, workspace_size)
+from . import (Workspace, proxy_topk, proxy_topk_workspace_size, sparse_attention,
+               workspace_size)
 
 
 class DecodeGraph:
@@ -28,9 +29,10 @@ class DecodeGraph:
     With `q2k` given, the step is the sparse attention over those rows; with
     `q2k=None` it first scores every block with the proxy pass (`proxy_q`,
     default `q`, against `k`; `reduce_heads` as in proxy_score) and selects
-    the top-`topk` blocks into `self.q2k`.  `max_seqlen_q` and `max_k_tiles`
-    are required (no host reads of device lengths).  `replay()` returns
-    (out, lse); lse is None unless `return_lse`."""
+    the top-`topk` blocks into `self.q2k` in the same call (proxy_topk: on
+    decode shapes the selection runs inside the proxy pass).  `max_seqlen_q`
+    and `max_k_tiles` are required (no host reads of device lengths).
+    `replay()` returns (out, lse); lse is None unless `return_lse`."""
 
     def __init__(self, q, k, v, cu_seqlens_q, *, max_seqlen_q, max_k_tiles, topk,
                  page_table=None, seqused_k=None, cu_seqlens_k=None, q2k=None, proxy_q=None,
@@ -51,11 +53,11 @@ class DecodeGraph:
         if self.select:
             self.proxy_q = q if proxy_q is None else proxy_q
             self.reduce_heads = reduce_heads
-            hs = (1 if reduce_heads is True else
-                  hkv if reduce_heads == "group" else self.proxy_q.shape[1])
-            self.scores = torch.empty(hs, self.max_k_tiles, total_q, dtype=torch.float32,
-                                      device=dev)
             self.q2k = torch.empty(hkv, total_q, topk, dtype=torch.int32, device=dev)
+            self.select_workspace = Workspace(max(1, proxy_topk_workspace_size(
+                self.proxy_q, k, cu_seqlens_q, cu_seqlens_k, topk=topk, page_table=page_table,
+                seqused_k=seqused_k, causal=causal, max_seqlen_q=self.max_seqlen_q,
+                max_k_tiles=self.max_k_tiles, reduce_heads=reduce_heads)), dev)
         else:
             self.q2k = q2k
         need = workspace_size(q, k, v, self.q2k, cu_seqlens_q, cu_seqlens_k,
@@ -81,11 +83,11 @@ class DecodeGraph:
     def step(self):
         """The step itself, launched eagerly on the current stream."""
         if self.select:
-            proxy_score(self.proxy_q, self.k, self.cu_seqlens_q, self.cu_seqlens_k,
-                        page_table=self.page_table, seqused_k=self.seqused_k, causal=self.causal,
-                        max_seqlen_q=self.max_seqlen_q, max_k_tiles=self.max_k_tiles,
-                        output=self.scores, reduce_heads=self.reduce_heads)
-            topk_select(self.scores, self.topk, self.k.shape[1], out=self.q2k)
+            proxy_topk(self.proxy_q, self.k, self.cu_seqlens_q, self.cu_seqlens_k,
+                       topk=self.topk, page_table=self.page_table, seqused_k=self.seqused_k,
+                       causal=self.causal, max_seqlen_q=self.max_seqlen_q,
+                       max_k_tiles=self.max_k_tiles, reduce_heads=self.reduce_heads,
+                       out=self.q2k, workspace=self.select_workspace)
         return sparse_attention(
             self.q, self.k, self.v, self.q2k, self.cu_seqlens_q, self.cu_seqlens_k,
             causal=self.causal, softmax_scale=self.softmax_scale, page_table=self.page_table,

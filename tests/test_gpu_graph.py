@@ -54,6 +54,14 @@ def test_fp8_mtp_pipeline_graph(msa):
                            reduce_heads=True).to("cuda")
     g = _graph(msa, p, reduce_heads=True)
     _replays_match_eager(g, q_new=True)
+    # the captured selection (proxy and top-K in one call) equals the proxy
+    # scores followed by the separate select
+    scores = msa.proxy_score(g.q, p.k, p.cu_seqlens_q, page_table=p.page_table,
+                             seqused_k=p.seqused_k, causal=True, max_seqlen_q=max(p.q_lens),
+                             max_k_tiles=p.max_k_tiles, reduce_heads=True)
+    ref = msa.topk_select(scores, p.topk, p.num_kv_heads)
+    torch.cuda.synchronize()
+    assert torch.equal(g.q2k, ref)
 
 
 @pytest.mark.parametrize("fmt,splits", [(synth.KV_BF16, 0), (synth.KV_E2M1, 3)])
