@@ -455,6 +455,26 @@ def test_topk_bit_exact(msa, T, topk, hs, hkv, mode):
     assert torch.equal(got.cpu(), ref)
 
 
+@pytest.mark.parametrize("T", [64, 200])
+def test_topk_shared_prefix_rows(msa, T):
+    # rows whose finite scores agree in their leading bits (the search starts
+    # below that prefix) or whose top-K is settled before the last bit
+    rows = [
+        torch.full((T,), 1.5),                                        # all equal
+        torch.tensor([1.0 + i * 2.0 ** -23 for i in range(T)]),       # last bits only
+        torch.where(torch.arange(T) % 4 == 1, 3.0, 2.0),              # exactly T/4 at the top
+        torch.where(torch.arange(T) < 20, 7.0, -7.0),                 # 20 tied at the max
+        torch.linspace(-1.0, 1.0, T),                                 # both signs
+        torch.where(torch.arange(T) % 7 == 0, 0.25, float("-inf")),   # few finite
+        torch.tensor([2.0 ** -(i % 30) for i in range(T)]),           # exponents only
+    ]
+    s = torch.stack(rows, dim=1).unsqueeze(0).contiguous()            # (1, T, rows)
+    for topk in (1, 16, 17):
+        got = msa.topk_select(s.cuda(), topk, 1, mode=0)
+        ref = oracle.topk_select(s, topk, 1, mode="none")
+        assert torch.equal(got.cpu(), ref), topk
+
+
 # ---------------------------------------------------------------------------
 # tile union
 # ---------------------------------------------------------------------------
