@@ -455,6 +455,17 @@ def test_topk_bit_exact(msa, T, topk, hs, hkv, mode):
     assert torch.equal(got.cpu(), ref)
 
 
+@pytest.mark.parametrize("T,topk,hs,hkv,mode", [
+    (64, 16, 2, 2, 0), (50, 16, 3, 1, 1), (64, 8, 4, 2, 2),
+])
+def test_topk_many_rows(msa, T, topk, hs, hkv, mode):
+    # a full-size row count (16387 queries) with the adversarial score mix
+    s = _adversarial_scores(hs, T, 16387, seed=3 * T + mode)
+    got = msa.topk_select(s.cuda(), topk, hkv, mode=mode)
+    ref = oracle.topk_select(s, topk, hkv, mode={0: "none", 1: "all", 2: "group"}[mode])
+    assert torch.equal(got.cpu(), ref)
+
+
 @pytest.mark.parametrize("T", [64, 200])
 def test_topk_shared_prefix_rows(msa, T):
     # rows whose finite scores agree in their leading bits (the search starts
