@@ -298,6 +298,10 @@ def bench_prefill_pipeline(args, msa, synth, torch):
     lens = p.cu_seqlens_k[1:] - p.cu_seqlens_k[:-1]
     flops = accounting.attention_flops(q2k, p.cu_seqlens_q, lens, p.num_qo_heads)
     pflops = accounting.proxy_flops(p.cu_seqlens_q, lens, p.proxy_q.shape[1]) if pipeline else 0
+    # MFMA work the tile kernel executes (whole 32-row slots over union blocks)
+    exe_flops = accounting.prefill_executed_flops(
+        q2k, p.cu_seqlens_q, lens, p.num_qo_heads,
+        accounting.prefill_tile_tokens(p.num_qo_heads, p.num_kv_heads, p.topk))
 
     evs = [_events(4) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -332,7 +336,16 @@ def bench_prefill_pipeline(args, msa, synth, torch):
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
                      "traffic": (None if temp or args.kv_format == "fp8"
-                                 else _traffic_for("msa_prefill_kernel:" + p.name))},
+                                 else _traffic_for("msa_prefill_kernel:" + p.name)),
+                     "executed": {
+                         "flops": exe_flops,
+                         "tflops": round(exe_flops / (attn_ms * 1e-3) / 1e12, 3),
+                         "frac": round(exe_flops / (attn_ms * 1e-3) / 1e12
+                                       / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "selected_share": round(flops / exe_flops, 4) if exe_flops else None,
+                         "what": "MFMA FLOPs of the tile kernel: every 32-row slot x union "
+                                 "block it computes (S^T and O^T += V^T P^T), counted on the "
+                                 "host from q2k; diagnostic, not the metric"}},
     }
     return res, p
 

@@ -89,3 +89,65 @@ def proxy_flops(cu_seqlens_q, lengths_k, num_qo_heads, head_dim=128, causal=True
         else:
             pairs += lq * lk
     return pairs * num_qo_heads * 2 * head_dim
+
+
+# ---------------------------------------------------------------------------
+# Executed MFMA work of the prefill tile kernel (a diagnostic beside the
+# selected-work count above, not part of it)
+# ---------------------------------------------------------------------------
+
+SLOT_ROWS = 32
+TILE_ROWS = 256
+
+
+def prefill_tile_tokens(num_qo_heads, num_kv_heads, topk, max_union=512):
+    """Query tokens per tile on the prefill route: 256 token-major rows of G
+    heads each, at most 64 tokens (the per-block token masks) and at most
+    `max_union` / topk tokens (the union list)."""
+    G = num_qo_heads // num_kv_heads
+    t = max(1, min(64, TILE_ROWS // G))
+    if t * topk > max_union:
+        t = max(1, max_union // topk)
+    return t
+
+
+def prefill_slot_blocks(q2k, cu_seqlens_q, lengths_k, num_qo_heads, tile_tokens):
+    """Number of (32-row slot, KV block) pairs the prefill kernel computes.
+
+    Tiles hold `tile_tokens` consecutive queries of one request and one KV
+    head; their rows are token-major (row = G t + head), cut into 32-row
+    slots.  A slot computes a block of its tile's union when a token with a
+    row in the slot selected it (ids outside [0, ceil(Lk / 128)) are not in
+    the union)."""
+    hkv, total_q, topk = q2k.shape
+    G = num_qo_heads // hkv
+    dev = q2k.device
+    b, _, iq, lk = _row_geometry(cu_seqlens_q, lengths_k, total_q, dev)
+    B = cu_seqlens_q.numel() - 1
+    t = q2k.to(torch.int64)
+    nblk = ((lk + BLOCK - 1) // BLOCK).view(1, -1, 1)
+    ok = (t >= 0) & (t < nblk)
+    max_blk = int(nblk.max()) + 1 if nblk.numel() else 1
+    tile = (iq // tile_tokens).view(1, -1, 1)
+    tin = (iq % tile_tokens).view(1, -1, 1)
+    s_lo = (G * tin) // SLOT_ROWS
+    s_hi = (G * tin + G - 1) // SLOT_ROWS
+    n_tiles = int(tile.max()) + 1 if tile.numel() else 1
+    n_slots = (tile_tokens * G + SLOT_ROWS - 1) // SLOT_ROWS
+    gg = torch.arange(hkv, device=dev).view(-1, 1, 1)
+    bb = b.view(1, -1, 1)
+    keys = []
+    for k in range((G + SLOT_ROWS - 1) // SLOT_ROWS + 1):
+        slot = s_lo + k
+        use = ok & (slot <= s_hi)
+        key = (((gg * B + bb) * n_tiles + tile) * n_slots + slot) * max_blk + t
+        keys.append(key.expand_as(t)[use])
+    return int(torch.unique(torch.cat(keys)).numel()) if keys else 0
+
+
+def prefill_executed_flops(q2k, cu_seqlens_q, lengths_k, num_qo_heads, tile_tokens,
+                           head_dim=128):
+    """MFMA FLOPs of the prefill kernel: per computed (slot, block), S^T of
+    32 rows x 128 keys and O^T += V^T P^T of the same size."""
+    n = prefill_slot_blocks(q2k, cu_seqlens_q, lengths_k, num_qo_heads, tile_tokens)
+    return n * SLOT_ROWS * BLOCK * head_dim * 4

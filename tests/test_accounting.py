@@ -1,0 +1,108 @@
+"""Host-side work accounting used by bench.py, against brute-force counts on
+small random problems (CPU only)."""
+import random
+
+import pytest
+import torch
+
+from block_sparse_top_msa_amd import accounting as acc
+
+
+def _problem(seed, q_lens, k_lens, hkv, topk):
+    rng = random.Random(seed)
+    rows = []
+    for g in range(hkv):
+        for lq, lk in zip(q_lens, k_lens):
+            nblk = (lk + 127) // 128
+            for _ in range(lq):
+                # some ids past the last block and some -1 padding
+                n = rng.randint(0, topk)
+                ids = sorted(rng.sample(range(nblk + 2), min(n, nblk + 2)))
+                rows.append(ids + [-1] * (topk - len(ids)))
+    q2k = torch.tensor(rows, dtype=torch.int32).view(hkv, sum(q_lens), topk)
+    cu = torch.tensor([0] + list(torch.cumsum(torch.tensor(q_lens), 0).tolist()))
+    return q2k, cu, torch.tensor(k_lens)
+
+
+def _brute_slot_blocks(q2k, q_lens, k_lens, G, tile_tokens):
+    hkv = q2k.shape[0]
+    n = 0
+    for g in range(hkv):
+        q0 = 0
+        for lq, lk in zip(q_lens, k_lens):
+            nblk = (lk + 127) // 128
+            for j in range(0, lq, tile_tokens):
+                toks = range(j, min(lq, j + tile_tokens))
+                n_slots = (tile_tokens * G + 31) // 32
+                for s in range(n_slots):
+                    blocks = set()
+                    for t in toks:
+                        t_in = t - j
+                        if G * t_in <= 32 * s + 31 and G * t_in + G - 1 >= 32 * s:
+                            blocks |= {x for x in q2k[g, q0 + t].tolist() if 0 <= x < nblk}
+                    n += len(blocks)
+            q0 += lq
+    return n
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (16, 2), (4, 4), (32, 2), (64, 1), (6, 3), (128, 1)])
+def test_prefill_slot_blocks_match_brute_force(hq, hkv):
+    q_lens, k_lens = [70, 5, 129], [900, 130, 2000]
+    q2k, cu, lk = _problem(hq + hkv, q_lens, k_lens, hkv, 6)
+    G = hq // hkv
+    tt = acc.prefill_tile_tokens(hq, hkv, 6)
+    assert tt == max(1, min(64, 256 // G))
+    got = acc.prefill_slot_blocks(q2k, cu, lk, hq, tt)
+    assert got == _brute_slot_blocks(q2k, q_lens, k_lens, G, tt)
+
+
+def test_prefill_slot_blocks_closed_forms():
+    # every token of a request selects the same 5 blocks: each used slot of
+    # each tile computes exactly those 5
+    hq, hkv, lq = 16, 2, 100                       # G = 8: 4 tokens per slot, 32 per tile
+    q2k = torch.tensor([0, 3, 4, 7, 9, -1], dtype=torch.int32).repeat(hkv, lq, 1)
+    cu, lk = torch.tensor([0, lq]), torch.tensor([1280])
+    slots = sum((min(32, lq - j) + 3) // 4 for j in range(0, lq, 32))   # 8 + 8 + 8 + 1
+    assert acc.prefill_slot_blocks(q2k, cu, lk, hq, 32) == hkv * slots * 5
+    assert acc.prefill_executed_flops(q2k, cu, lk, hq, 32) == hkv * slots * 5 * 32 * 128 * 128 * 4
+    # a union never holds blocks past the request's last one
+    assert acc.prefill_slot_blocks(q2k, cu, torch.tensor([700]), hq, 32) == hkv * slots * 3
+    # the tile width shrinks when tokens x topk passes the union list
+    assert acc.prefill_tile_tokens(16, 2, 64) == 8
+    assert acc.prefill_tile_tokens(2, 2, 16) == 32
+
+
+def test_attended_keys_and_flops_match_brute_force():
+    q_lens, k_lens, hkv, hq = [40, 3, 90], [300, 129, 1000], 2, 8
+    q2k, cu, lk = _problem(5, q_lens, k_lens, hkv, 5)
+    got = acc.attended_keys(q2k, cu, lk, causal=True)
+    ref = torch.zeros_like(got)
+    q0 = 0
+    for lq, L in zip(q_lens, k_lens):
+        nblk = (L + 127) // 128
+        for i in range(lq):
+            pos = L - lq + i
+            for g in range(hkv):
+                n = 0
+                for x in q2k[g, q0 + i].tolist():
+                    if 0 <= x < nblk:
+                        n += max(0, min(128 * x + 128, L, pos + 1) - 128 * x)
+                ref[g, q0 + i] = n
+        q0 += lq
+    assert torch.equal(got, ref)
+    assert acc.attention_flops(q2k, cu, lk, hq) == int(ref.sum()) * (hq // hkv) * 4 * 128
+
+
+def test_decode_kv_bytes_match_brute_force():
+    q_lens, k_lens, hkv, T = [1, 4, 2], [300, 129, 5000], 2, 40
+    q2k, cu, lk = _problem(9, q_lens, k_lens, hkv, 7)
+    ref = 0
+    for g in range(hkv):
+        q0 = 0
+        for lq, L in zip(q_lens, k_lens):
+            nblk = (L + 127) // 128
+            used = {x for i in range(lq) for x in q2k[g, q0 + i].tolist() if 0 <= x < nblk}
+            ref += sum(min(128, L - 128 * x) for x in used)
+            q0 += lq
+    for fmt, per in acc.BYTES_PER_TOKEN_SIDE.items():
+        assert acc.decode_kv_bytes(q2k, cu, lk, fmt, T) == ref * 2 * per
