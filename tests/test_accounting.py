@@ -106,3 +106,13 @@ def test_decode_kv_bytes_match_brute_force():
             q0 += lq
     for fmt, per in acc.BYTES_PER_TOKEN_SIDE.items():
         assert acc.decode_kv_bytes(q2k, cu, lk, fmt, T) == ref * 2 * per
+
+
+def test_proxy_flops_match_brute_force():
+    cu, lk = torch.tensor([0, 5, 5, 12]), torch.tensor([9, 4, 7])
+    pairs = 0
+    for b, (lq, L) in enumerate(zip([5, 0, 7], [9, 4, 7])):
+        for i in range(lq):
+            pairs += sum(1 for j in range(L) if j <= L - lq + i)
+    assert acc.proxy_flops(cu, lk, 3, head_dim=128) == pairs * 3 * 2 * 128
+    assert acc.proxy_flops(cu, lk, 3, head_dim=128, causal=False) == (5 * 9 + 7 * 7) * 3 * 2 * 128
