@@ -344,7 +344,11 @@ __global__ __launch_bounds__(NWV * 64) void msa_decode_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) DecodeLds<FMT, NWV> lds;
   __shared__ int s_last;   // this workgroup merges the unit's splits
 
-  const int lid = blockIdx.x;
+  // Consecutive logical workgroups (the splits and token tiles of one
+  // request and KV head) run on one XCD, so the pages their selections share
+  // are fetched into that XCD's L2 once.
+  const int lid = xcd_remap(blockIdx.x, p.batch * p.hkv * p.tiles_per_req * p.splits);
+  if (lid < 0) return;
   const int split = lid % p.splits;
   const int unit = lid / p.splits;           // (request, KV head, token tile)
   const int jt = unit % p.tiles_per_req;
@@ -944,10 +948,11 @@ template <int FMT, int RT, int NWV = 4>
 static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
   const int n = p.batch * p.hkv * p.tiles_per_req * p.splits;
   if (n <= 0) return hipSuccess;
+  const dim3 grid(8 * ((n + 7) / 8));
   if (p.lse_t)
-    hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, true>), dim3(n), dim3(NWV * 64), 0, stream, p);
+    hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, true>), grid, dim3(NWV * 64), 0, stream, p);
   else
-    hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, false>), dim3(n), dim3(NWV * 64), 0, stream, p);
+    hipLaunchKernelGGL((msa_decode_kernel<FMT, RT, NWV, false>), grid, dim3(NWV * 64), 0, stream, p);
   return hipGetLastError();
 }
 
