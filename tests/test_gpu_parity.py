@@ -54,6 +54,32 @@ def test_prefill_bf16_matches_oracle(msa, case):
     assert_attention_close(out, lse, ref_out, ref_lse, f"prefill case {case}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(6, 2), (10, 2), (12, 2), (24, 2), (40, 8)])
+def test_prefill_groups_not_dividing_a_slot(msa, hq, hkv):
+    # G = 3, 5, 6, 12: a token's heads straddle two 32-row slots (and the
+    # tile's last slot is partly empty)
+    p = synth.make_problem("prefill_odd_g", q_lens=[200, 61], k_lens=[700, 61], num_qo_heads=hq,
+                           num_kv_heads=hkv, topk=5, seed=200 + hq, selection="general")
+    print(f"prefill G {hq // hkv}", flush=True)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, f"prefill G {hq // hkv}")
+
+
+@pytest.mark.parametrize("hq,hkv,lq,fmt", [(6, 2, 4, synth.KV_BF16), (10, 2, 4, synth.KV_FP8),
+                                          (12, 1, 4, synth.KV_E2M1), (40, 8, 1, synth.KV_BF16)])
+def test_decode_groups_not_dividing_a_row_tile(msa, hq, hkv, lq, fmt):
+    # a token's heads straddle two 16-row tiles of the decode kernel
+    kw = dict(k_global_scale=0.5, v_global_scale=2.0) if fmt == synth.KV_E2M1 else {}
+    p = synth.make_problem("decode_odd_g", q_lens=[lq] * 3, k_lens=[3000, 129, 900],
+                           num_qo_heads=hq, num_kv_heads=hkv, topk=6, paged=True, kv_dtype=fmt,
+                           seed=210 + hq, selection="decode", **kw)
+    print(f"decode G {hq // hkv} x {lq} tokens, {fmt}", flush=True)
+    out, lse = gpu_attention(msa, _dev(p))
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, f"decode G {hq // hkv}")
+
+
 def test_prefill_fp8_and_scales(msa):
     p = synth.make_problem("prefill_fp8", q_lens=[260, 33], k_lens=[400, 33], num_qo_heads=8,
                            num_kv_heads=2, topk=3, kv_dtype=synth.KV_FP8, seed=7,
