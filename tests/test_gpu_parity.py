@@ -396,6 +396,7 @@ PROXY_CASES = [
     ([4, 4], [700, 1300], 32, 2, True, synth.KV_FP8, True, False),
     ([1, 1, 1], [900, 128, 2000], 16, 1, True, synth.KV_BF16, True, True),
     ([3, 2], [1000, 500], 6, 2, True, synth.KV_BF16, True, True),  # G = 3 (atomic path)
+    ([150, 90], [400, 300], 10, 2, False, synth.KV_BF16, True, True),  # wide, G = 5, all heads
 ]
 
 
@@ -567,6 +568,8 @@ def test_decode_per_token_tiles_with_uneven_query_lengths(msa, fmt, hq, hkv, spl
     ([300, 200], [300, 456], 16, 2, False, synth.KV_BF16),     # > 64 rows: wide kernel
     ([4, 4, 4], [3000, 700, 129], 32, 2, True, synth.KV_FP8),   # <= 64 rows: rows kernel
     ([2, 1], [1000, 2000], 8, 1, True, synth.KV_BF16),
+    ([150, 90], [400, 300], 10, 2, False, synth.KV_BF16),    # G = 5 (not a power of 2), wide
+    ([4, 4], [2000, 700], 12, 2, True, synth.KV_FP8),         # G = 6, rows kernel
 ])
 def test_proxy_group_reduction_in_kernel(msa, ql, kl, hq, hkv, paged, fmt):
     # reduce_heads="group": the max over each KV head's G query heads is taken
