@@ -40,6 +40,7 @@ PREFILL_CASES = [
     ([129, 64, 1], [129, 640, 200], 32, 2, 3, True),  # G = 16
     ([90], [400], 2, 2, 4, True),                 # MHA, G = 1
     ([150, 40], [150, 300], 6, 3, 4, True),       # G = 2
+    ([300, 50], [200, 50], 8, 2, 4, True),        # Lq > Lk: the first 100 queries see no key
 ]
 
 
@@ -397,6 +398,7 @@ PROXY_CASES = [
     ([1, 1, 1], [900, 128, 2000], 16, 1, True, synth.KV_BF16, True, True),
     ([3, 2], [1000, 500], 6, 2, True, synth.KV_BF16, True, True),  # G = 3 (atomic path)
     ([150, 90], [400, 300], 10, 2, False, synth.KV_BF16, True, True),  # wide, G = 5, all heads
+    ([300, 50], [200, 50], 2, 2, False, synth.KV_BF16, True, False),   # Lq > Lk
 ]
 
 
