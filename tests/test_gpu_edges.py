@@ -1,6 +1,7 @@
 """Edge cases of the HIP path against the fp64 oracle (GPU).
 
-Largest top-K, the widest GQA group, requests with no queries or no keys,
+Largest top-K, the widest GQA group, requests with no queries or no keys
+(and multi-token decode against fewer keys than queries),
 a million-token paged context (page ids past the LDS read-ahead), the flat
 layout on the decode-shaped kernel, non-causal multi-token decode and empty
 batches.  Every call goes through the C ABI (via the ctypes binding).
@@ -88,3 +89,16 @@ def test_empty_batches(msa):
                                     max_seqlen_q=0, max_k_tiles=0)
     torch.cuda.synchronize()
     assert out.shape == (0, 8, 128) and lse.shape == (0, 8)
+
+
+@pytest.mark.parametrize("fmt", [synth.KV_BF16, synth.KV_FP8, synth.KV_E2M1])
+def test_mtp_decode_with_fewer_keys_than_queries(msa, fmt):
+    # 4 query tokens against 2, 3 and 0 keys: the leading tokens see no key
+    # (0 / -inf), the rest a partial first page
+    kw = dict(k_global_scale=0.5, v_global_scale=2.0) if fmt == synth.KV_E2M1 else {}
+    d = synth.make_problem("short_kv_decode", q_lens=[4] * 4, k_lens=[2, 3, 0, 1000],
+                           num_qo_heads=16, num_kv_heads=1, topk=4, paged=True, kv_dtype=fmt,
+                           seed=39, selection="decode", **kw)
+    out, lse = _check(msa, d, f"MTP decode with short KV, {fmt}")
+    assert (out[:2].float() == 0).all() and torch.isneginf(lse[:2]).all()
+    assert (out[8:12].float() == 0).all() and torch.isneginf(lse[8:12]).all()
