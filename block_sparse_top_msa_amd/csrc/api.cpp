@@ -583,10 +583,12 @@ msa_status_t resolve_proxy(const msa_proxy_args_t* a, bool need_out, msa::ProxyP
   const int base = std::max(1, a->batch * a->num_kv_heads * p.row_tiles);
   if (wide) {
     // pieces per row-tile pair: about two workgroups per CU in all, each
-    // piece at most kWideMaxSeg blocks of a row tile
+    // piece at most kWideMaxSeg blocks of a row tile (a pair's blocks plus
+    // the tile-switch charge, cut into equal pieces)
     const int pairs = std::max(1, a->batch * a->num_kv_heads * ((p.row_tiles + 1) / 2));
     p.pieces = std::max((512 + pairs - 1) / pairs,
-                        (2 * a->max_k_tiles + msa::kWideMaxSeg - 1) / msa::kWideMaxSeg);
+                        (2 * a->max_k_tiles + msa::kSegSwitch + msa::kWideMaxSeg - 1) /
+                            msa::kWideMaxSeg);
     p.pieces = std::max(1, p.pieces);
     p.blocks_per_wg = 0;
     p.block_chunks = 0;

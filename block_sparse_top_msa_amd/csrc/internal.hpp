@@ -111,6 +111,9 @@ struct ProxyParams {
 
 // Most KV blocks of one row tile a prefill-shaped proxy workgroup scores.
 constexpr int kWideMaxSeg = 64;
+// Blocks a prefill-shaped proxy piece is charged for running over from one
+// row tile into the next (a second start: Q rows, first K block).
+constexpr int kSegSwitch = 2;
 
 hipError_t launch_proxy(const ProxyParams& p, int fmt, int wide_rows, hipStream_t stream);
 // decode-shaped proxy (<= 64 rows per request and KV head) writing per-chunk

@@ -501,7 +501,14 @@ __global__ __launch_bounds__(256, 2) void msa_proxy_wide_kernel(ProxyParams p) {
   const int va = visible(rta);
   const int vb = rtb != rta ? visible(rtb) : 0;
   const int64_t cost = (int64_t)va + vb;
-  const int s_lo = (int)(cost * piece / P), s_hi = (int)(cost * (piece + 1) / P);
+  // The piece that runs over from tile rta into rtb pays a second start (its
+  // Q rows and first K block): it is counted as kSegSwitch blocks more, so
+  // that piece takes fewer blocks (the cut points move over a virtual gap at
+  // the tile boundary; every block still falls in exactly one piece).
+  const int pen = (va > 0 && vb > 0) ? kSegSwitch : 0;
+  const int64_t ext = cost + pen;
+  auto cut = [&](int64_t x) { return (int)(x < va ? x : (x < va + pen ? va : x - pen)); };
+  const int s_lo = cut(ext * piece / P), s_hi = cut(ext * (piece + 1) / P);
 
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
   const int64_t kst = p.k_st.token;
