@@ -235,7 +235,10 @@ msa_status_t resolve_attention(const msa_attn_args_t* a, Resolved* r, bool need_
   // their row tiles), with less state per workgroup.
   const bool per_token = G >= 16 && G <= 64 && lqmax > 1 && lqmax <= kDecodeMaxTokens;
   const int dec_rows = per_token ? G : rows_req;
-  if (dec_rows <= 64 && !flat_e2m1) {
+  // a decode tile holds all of a request's tokens: their selections must fit
+  // the union list, else the prefill tiles (which shrink to fit) take them
+  const bool dec_union_fits = (per_token ? 1 : lqmax) * a->topk <= msa::kMaxUnion;
+  if (dec_rows <= 64 && !flat_e2m1 && dec_union_fits) {
     // decode shape: one workgroup per (request, KV head, token tile, split);
     // its waves split every page's keys
     plan.decode = 1;

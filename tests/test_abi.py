@@ -323,6 +323,17 @@ def test_long_queries_take_the_prefill_route():
     assert _plan(a)[:2] == (0, 0)
 
 
+@pytest.mark.parametrize("seqlen_q,topk,route", [(32, 16, 1), (33, 16, 0), (8, 64, 1), (9, 64, 0)])
+def test_short_queries_whose_union_overflows_take_the_prefill_route(seqlen_q, topk, route):
+    # G = 1: seqlen_q rows fit one decode tile, but seqlen_q x topk selections
+    # must also fit its 512-entry union; past that the prefill tiles take them
+    a = _attn(batch=2, total_q=2 * seqlen_q, num_qo_heads=2, num_kv_heads=2, topk=topk,
+              max_seqlen_q=seqlen_q, max_k_tiles=64)
+    st, r, _ = _plan(a)
+    assert st == 0 and r == route
+    assert _size(a)[0] == 0
+
+
 @pytest.mark.parametrize("hq,hkv,temp", [(512, 1, False), (512, 1, True), (1024, 2, False)])
 def test_group_larger_than_a_tile_is_rejected(hq, hkv, temp):
     kw = dict(num_qo_heads=hq, num_kv_heads=hkv, total_q=64, max_seqlen_q=32)

@@ -81,6 +81,31 @@ def test_decode_groups_not_dividing_a_row_tile(msa, hq, hkv, lq, fmt):
     assert_attention_close(out, lse, ref_out, ref_lse, f"decode G {hq // hkv}")
 
 
+@pytest.mark.parametrize("q_lens,k_lens,hq,hkv,topk,fmt,paged", [
+    ([33, 15], [214, 15], 8, 8, 16, synth.KV_E2M1, True),
+    ([32], [32], 2, 2, 33, synth.KV_F16, False),
+    ([33, 0], [589, 64], 1, 1, 64, synth.KV_BF16, True),
+    ([40, 40], [700, 300], 2, 1, 16, synth.KV_FP8, True),
+])
+def test_short_queries_past_the_decode_union(msa, q_lens, k_lens, hq, hkv, topk, fmt, paged):
+    # few enough rows for a decode tile, too many selections for its union:
+    # the prefill tiles take the call
+    kw = dict(k_global_scale=0.5, v_global_scale=2.0) if fmt == synth.KV_E2M1 else {}
+    p = synth.make_problem("short_q_union", q_lens=q_lens, k_lens=k_lens, num_qo_heads=hq,
+                           num_kv_heads=hkv, topk=topk, paged=paged, kv_dtype=fmt, seed=230 + hq,
+                           selection="general", **kw)
+    d = _dev(p)
+    route, _ = msa.attention_plan(d.q, d.k, d.v, d.q2k, d.cu_seqlens_q, d.cu_seqlens_k,
+                                  page_table=d.page_table, seqused_k=d.seqused_k,
+                                  k_scale=d.k_scale, v_scale=d.v_scale, max_seqlen_q=max(q_lens),
+                                  max_k_tiles=p.max_k_tiles)
+    assert route == 0
+    print(f"short queries past the decode union: {q_lens} topk {topk} {fmt}", flush=True)
+    out, lse = gpu_attention(msa, d)
+    ref_out, ref_lse = oracle_attention(p)
+    assert_attention_close(out, lse, ref_out, ref_lse, "short queries past the decode union")
+
+
 def test_prefill_fp8_and_scales(msa):
     p = synth.make_problem("prefill_fp8", q_lens=[260, 33], k_lens=[400, 33], num_qo_heads=8,
                            num_kv_heads=2, topk=3, kv_dtype=synth.KV_FP8, seed=7,
