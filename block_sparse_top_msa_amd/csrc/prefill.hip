@@ -193,7 +193,10 @@ __device__ __forceinline__ float exp_pair(const f32x16& acc, int r, float cs, fl
 }
 
 // The chunk's 16 exponentials, their row sum and P^T, without scheduling
-// constraints (rare path).
+// constraints (rare path).  The sum runs in the common path's order (pair
+// sums added one after another), so a row whose reference max did not move
+// gets bitwise the same sum whether or not another row of its wave took the
+// rare path: a row's result does not depend on the other tokens of its slot.
 template <bool F16>
 __device__ __forceinline__ float exp_all(const f32x16& acc, float cs, float mu, u32x4& q0, u32x4& q1) {
   float ps[8];
@@ -204,7 +207,10 @@ __device__ __forceinline__ float exp_all(const f32x16& acc, float cs, float mu, 
     if (i < 4) q0[i] = w;
     else q1[i - 4] = w;
   }
-  return ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+  float l = ps[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) l += ps[i];
+  return l;
 }
 
 // One 32-key chunk C of a block, software pipelined as groups of one MFMA,

@@ -8,6 +8,7 @@ limit.  Every call goes through the C ABI (via the ctypes binding).
 import pytest
 import torch
 
+import gpu_helpers
 import oracle
 import synth
 from gpu_helpers import (assert_attention_close, assert_proxy_close, gpu_attention,
@@ -754,3 +755,44 @@ def test_e2m1_every_scale_byte(msa, route):
     assert bool(((out[fin] - ref_out[fin]).abs() <= ref_out[fin].abs() * 2.0 ** -8).all())
     f = ~torch.isnan(ref_lse)
     assert float((lse[f] - ref_lse[f]).abs().max()) <= 1e-3
+
+
+@pytest.mark.parametrize("hq,hkv,lq,lk,topk,scale,seed,paged", [
+    (4, 1, 200, 3000, 4, None, 4, False),    # G = 4: a row's LSE here moved with its slot mates
+    (8, 1, 130, 1500, 6, 1.5, 248, False),   # large logit spread: the rescale path
+    (16, 2, 64, 1500, 6, 1.5, 256, True),
+    (32, 2, 4, 1500, 6, 1.5, 272, True),     # decode tiles
+])
+def test_row_result_does_not_depend_on_its_slot_mates(msa, hq, hkv, lq, lk, topk, scale, seed,
+                                                      paged):
+    # the tokens that share a query row's MFMA tile (its slot, or a decode
+    # tile) get other selections; every row of the other tokens must come out
+    # bitwise unchanged (the first block of a row, and any move of its
+    # reference max, send its whole wave down the rescale path)
+    p = synth.make_problem("slot_mates", q_lens=[lq], k_lens=[lk], num_qo_heads=hq,
+                           num_kv_heads=hkv, topk=topk, paged=paged, seed=seed,
+                           softmax_scale=scale, selection="general")
+    d = _dev(p)
+    out_a, lse_a = gpu_attention(msa, d)
+    q2k = p.q2k.clone()
+    g = torch.Generator().manual_seed(7)
+    nblk = (lk + 127) // 128
+    changed = torch.arange(lq) % 2 == 1
+    for h in range(hkv):
+        for i in torch.nonzero(changed).flatten().tolist():
+            ids = sorted(torch.randperm(nblk, generator=g)[:topk].tolist())
+            q2k[h, i] = torch.tensor(ids, dtype=torch.int32)
+    out_b, lse_b = gpu_attention(msa, d, q2k=q2k.cuda())
+    torch.cuda.synchronize()
+    keep = ~changed
+    assert torch.equal(out_a[keep].cpu(), out_b[keep].cpu())
+    assert torch.equal(lse_a[keep].cpu(), lse_b[keep].cpu())
+    # outputs near a single V row reach |out| ~ 4 here, where bf16's spacing
+    # is 1/32: the tolerance grows by 2^-8 of the largest |out|
+    ref_out, ref_lse = oracle_attention(p, q2k=q2k)
+    saved = gpu_helpers.OUT_TOL
+    gpu_helpers.OUT_TOL = 2e-2 + 2.0 ** -8 * float(ref_out.abs().max())
+    try:
+        assert_attention_close(out_b, lse_b, ref_out, ref_lse, "changed slot mates")
+    finally:
+        gpu_helpers.OUT_TOL = saved
