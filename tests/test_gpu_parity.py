@@ -796,3 +796,47 @@ def test_row_result_does_not_depend_on_its_slot_mates(msa, hq, hkv, lq, lk, topk
         assert_attention_close(out_b, lse_b, ref_out, ref_lse, "changed slot mates")
     finally:
         gpu_helpers.OUT_TOL = saved
+
+
+def _sub_problem(p, reqs):
+    """The requests `reqs` of p (flat layout) as a problem of their own, with
+    the same Q, K, V rows and selections."""
+    cq = p.cu_seqlens_q.tolist()
+    ck = p.cu_seqlens_k.tolist()
+    qi = torch.cat([torch.arange(cq[r], cq[r + 1]) for r in reqs])
+    ki = torch.cat([torch.arange(ck[r], ck[r + 1]) for r in reqs])
+    ql = [cq[r + 1] - cq[r] for r in reqs]
+    kl = [ck[r + 1] - ck[r] for r in reqs]
+    cu = lambda lens: torch.tensor([0] + torch.cumsum(torch.tensor(lens), 0).tolist(),
+                                   dtype=torch.int32)
+    return dict(q=p.q[qi], k=p.k[ki], v=p.v[ki], q2k=p.q2k[:, qi].contiguous(),
+                cu_q=cu(ql), cu_k=cu(kl), lq=max(ql), T=max((L + 127) // 128 for L in kl)), qi
+
+
+@pytest.mark.parametrize("fmt,hq,hkv,q_lens,k_lens,splits", [
+    (synth.KV_BF16, 16, 2, [100, 50, 7], [700, 300, 900], 0),   # prefill tiles
+    (synth.KV_FP8, 8, 2, [100, 50, 7], [700, 300, 900], 0),     # staged fp8 prefill
+    (synth.KV_BF16, 16, 1, [1, 1, 1], [3000, 129, 5000], 2),     # decode, fixed split count
+    (synth.KV_FP8, 32, 2, [4, 4, 4], [2000, 700, 4000], 1),      # MTP decode
+])
+def test_request_result_does_not_depend_on_its_batch(msa, fmt, hq, hkv, q_lens, k_lens, splits):
+    # a request computed alone, or in another order with other requests,
+    # gives bitwise the same rows (decode at a fixed split count)
+    p = synth.make_problem("batch_inv", q_lens=q_lens, k_lens=k_lens, num_qo_heads=hq,
+                           num_kv_heads=hkv, topk=6, kv_dtype=fmt, seed=250 + hq,
+                           selection="decode" if len(set(q_lens)) == 1 else "general")
+    outs = {}
+    for order in ([0, 1, 2], [0], [2, 0]):
+        s, qi = _sub_problem(p, order)
+        d = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in s.items()}
+        out, lse = msa.sparse_attention(d["q"], d["k"], d["v"], d["q2k"], d["cu_q"], d["cu_k"],
+                                        causal=True, return_softmax_lse=True,
+                                        max_seqlen_q=d["lq"], max_k_tiles=d["T"], splits=splits)
+        torch.cuda.synchronize()
+        n0 = q_lens[0]
+        start = order.index(0)
+        first = sum(q_lens[r] for r in order[:start])
+        outs[tuple(order)] = (out[first:first + n0].cpu(), lse[first:first + n0].cpu())
+    a = outs[(0, 1, 2)]
+    for key in ((0,), (2, 0)):
+        assert torch.equal(a[0], outs[key][0]) and torch.equal(a[1], outs[key][1]), key
