@@ -197,7 +197,8 @@ msa_status_t msa_sparse_attention_plan(const msa_attn_args_t* args, int32_t* dec
  * and write out (and lse) directly, or through split-KV partials merged by
  * LSE on the decode route.  q2k entries outside [0, ceil(Lk/128)) and -1 are
  * ignored; rows must be ascending without duplicates (caller contract).
- * Route: the decode kernel when max_seqlen_q * G <= 64, or, with
+ * Route: the decode kernel when max_seqlen_q * G <= 64 and the tile's
+ * selections fit its union (max_seqlen_q * topk <= 512), or, with
  * G = Hq / Hkv in [16, 64], when max_seqlen_q <= 64 (one token per tile);
  * flat E2M1 always takes prefill tiles.  A prefill tile holds 256 query
  * rows: a larger G is MSA_ERR_SHAPE.  `workspace` may be NULL when the size query returned 0. */
