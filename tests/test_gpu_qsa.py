@@ -105,10 +105,14 @@ def test_qsa_bitmap_matches_oracle(msa, lens, hq, hkv, density, mode):
     _check(p, out, out_f32, lse, f"qsa bitmap {lens} {hq}/{hkv}", rows=_bitmap_rows(p))
 
 
-def test_qsa_bitmap_hand_rows_and_indexed_equivalence(msa):
-    # rows that exercise the device compaction: exactly 8 and 9 selected
-    # blocks, hits at window edges (63, 64, 127), an empty row, one block
-    T, tk = 12, 517                            # 130 blocks, the last one token long
+@pytest.mark.parametrize("tk", [517, 17000])
+def test_qsa_bitmap_hand_rows_and_indexed_equivalence(msa, tk):
+    # rows that exercise the block compaction: exactly 8 and 9 selected
+    # blocks, hits at window edges (63, 64, 127), an empty row, one block.
+    # Tk = 517 (130 blocks, the last one token long): shared-key tiles;
+    # Tk = 17000: both tiles' keys span more than 16384 tokens (row 7 takes
+    # every block, row 11 the last one), so every token scans its own row
+    T = 12
     p = synth.make_qsa_bitmap_problem("qsa_bm_hand", [T], 12, 1, 0.0, seed=3)
     k = synth._randn_cast((tk, 1, 256), synth._gen(4, "cpu"), "cpu", torch.bfloat16)
     v = synth._randn_cast((tk, 1, 256), synth._gen(5, "cpu"), "cpu", torch.bfloat16)
@@ -124,12 +128,16 @@ def test_qsa_bitmap_hand_rows_and_indexed_equivalence(msa):
     bm[9, 120:] = 1
     bm[10, 64] = 1
     bm[11, [5, 70, 100]] = 1
+    if tk > 16384:
+        bm[11, -1] = 1
     p = synth.QsaProblem("qsa_bm_hand", p.q, k, v, None, [T], bm)
     d = p.to("cuda")
     out, out_f32, lse = msa.qsa_bitmap_forward(d.q, d.k, d.v, d.bitmap)
     torch.cuda.synchronize()
     _check(p, out, out_f32, lse, "qsa bitmap hand rows", rows=_bitmap_rows(p))
     assert torch.isneginf(lse[:, 3]).all() and (out[3].float() == 0).all()
+    if tk > 2052:
+        return   # rows longer than the indexed entry point's widest
     # the indexed entry point over the same key lists (ascending, -1 padded)
     # consumes the same 32-token chunks: bitwise equal results
     ind = oracle.qsa_bitmap_indices(bm, tk).cuda()
@@ -165,3 +173,91 @@ def test_qsa_bitmap_without_kv_tokens(msa):
     out, out_f32, lse = msa.qsa_bitmap_forward(q, k, k, bm)
     torch.cuda.synchronize()
     assert (out.float() == 0).all() and (out_f32 == 0).all() and torch.isneginf(lse).all()
+
+
+def _qsa_routes(rows, G):
+    """The route each tile takes by the kernel's rule: tiles of
+    min(16, 128 // G) consecutive tokens; the shared-key route unless the
+    tile's listed keys span more than 16384 tokens or
+    5 * union * ceil(live 16-row slots / 4) > 8 * listed entries."""
+    tt = min(16, 128 // G)
+    routes = []
+    for t0 in range(0, len(rows), tt):
+        tile = rows[t0:t0 + tt]
+        keys = [k for r in tile for k in r if k >= 0]
+        if not keys:
+            routes.append("shared")
+        elif max(keys) - min(keys) >= 16384:
+            routes.append("token")
+        else:
+            slots = (len(tile) * G + 15) // 16
+            ok = 5 * len(set(keys)) * ((slots + 3) // 4) <= 8 * len(keys)
+            routes.append("shared" if ok else "token")
+    return routes
+
+
+def _mixed_rows(tk, seed):
+    # 10-token tiles (G = 12): tile 0 lists 48 of the same 64 keys per token
+    # (shared keys), tile 1 eight random keys of 8000 per token (sparse: per
+    # token), tile 2 64 keys spread over all tk rows (a range past 16384 keys)
+    g = torch.Generator().manual_seed(seed)
+    rows = [sorted(torch.randperm(64, generator=g)[:48].tolist()) for _ in range(10)]
+    rows += [torch.randperm(8000, generator=g)[:8].tolist() for _ in range(10)]
+    rows += [torch.randperm(tk, generator=g)[:64].tolist() for _ in range(7)]
+    return rows
+
+
+@pytest.mark.parametrize("hq,hkv", [(12, 1), (24, 2)])
+def test_qsa_shared_and_per_token_tiles_in_one_launch(msa, hq, hkv):
+    tk = 20000
+    rows = _mixed_rows(tk, seed=11 + hkv)
+    assert _qsa_routes(rows, hq // hkv) == ["shared", "token", "token"]
+    ind = torch.full((len(rows), 64), -1, dtype=torch.int32)
+    for i, r in enumerate(rows):
+        ind[i, :len(r)] = torch.tensor(r, dtype=torch.int32)
+    g = synth._gen(21, "cpu")
+    q = synth._randn_cast((len(rows), hq, 256), g, "cpu", torch.bfloat16)
+    k = synth._randn_cast((tk, hkv, 256), g, "cpu", torch.bfloat16)
+    v = synth._randn_cast((tk, hkv, 256), g, "cpu", torch.bfloat16)
+    p = synth.QsaProblem("qsa_mixed", q, k, v, ind, [len(rows)])
+    print(f"qsa mixed routes {hq}/{hkv} Tk {tk}", flush=True)
+    d = p.to("cuda")
+    a = msa.qsa_indexed_forward(d.q, d.k, d.v, d.indices)
+    b = msa.qsa_indexed_forward(d.q, d.k, d.v, d.indices)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    _check(p, *a, f"qsa mixed routes {hq}/{hkv}")
+
+
+def test_qsa_bitmap_shared_and_per_token_tiles(msa):
+    # the same three kinds of tile through the bitmap entry point (Tk = 20001:
+    # the last block one token long), then the indexed entry point over the
+    # equivalent ascending rows: the same routes and chunks, bitwise equal
+    tk, T = 20001, 27
+    g = torch.Generator().manual_seed(5)
+    nb = (tk + 3) // 4
+    bm = torch.zeros(T, nb, dtype=torch.uint8)
+    for i in range(10):
+        bm[i, torch.randperm(16, generator=g)[:12]] = 1
+    for i in range(10, 20):
+        bm[i, torch.randperm(2000, generator=g)[:2]] = 1
+    for i in range(20, T):
+        bm[i, torch.randperm(nb, generator=g)[:16]] = 1
+    bm[26, nb - 1] = 1
+    full = oracle.qsa_bitmap_indices(bm, tk)
+    rows = [[int(x) for x in r if x >= 0] for r in full]
+    assert _qsa_routes(rows, 12) == ["shared", "token", "token"]
+    gq = synth._gen(22, "cpu")
+    q = synth._randn_cast((T, 12, 256), gq, "cpu", torch.bfloat16)
+    k = synth._randn_cast((tk, 1, 256), gq, "cpu", torch.bfloat16)
+    v = synth._randn_cast((tk, 1, 256), gq, "cpu", torch.bfloat16)
+    p = synth.QsaProblem("qsa_bm_mixed", q, k, v, None, [T], bm)
+    print("qsa bitmap mixed routes", flush=True)
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_bitmap_forward(d.q, d.k, d.v, d.bitmap)
+    torch.cuda.synchronize()
+    _check(p, out, out_f32, lse, "qsa bitmap mixed routes", rows=_bitmap_rows(p))
+    w = (max(len(r) for r in rows) + 3) // 4 * 4
+    b = msa.qsa_indexed_forward(d.q, d.k, d.v, full[:, :w].contiguous().cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(out, b[0]) and torch.equal(out_f32, b[1]) and torch.equal(lse, b[2])
