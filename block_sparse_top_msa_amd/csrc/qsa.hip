@@ -47,7 +47,6 @@ constexpr int kQsaTileRows = 16 * kQsaWaves;      // query rows of a tile
 constexpr int kQsaMaxTokens = 16;                 // token bits of a key's mask word
 constexpr int kQsaChunkBytes = 32 * kQsaRowBytes; // 32 K (or V) rows: 16 KiB
 constexpr int kQsaWin = 16384;                    // key range the shared route covers
-constexpr float kQsaSlack = 64.0f;                // p = 2^(s - m) <= 2^64 between rescales
 // Shared route when kTileCost * union * (slot rounds) <= kTokenCost * listed
 // entries: per union key a round of four 16-row slots costs about 5/8 of one
 // per-token key gather (1 KiB per key and token, measured rates).
@@ -80,17 +79,29 @@ struct QsaTokLds {
   int32_t blk[8];                 // bitmap source: the chunk's selected blocks
 };
 
-// Workgroup LDS (bytes).  Shared route: [2 buffers][K | V] chunk ring, the
-// key-mask words of the tile's key range (then the compacted union), and a
-// few words of reduction scratch.  Per-token route: one QsaTokLds per wave
-// over the same bytes.
-constexpr int kRingBytes = 2 * 2 * kQsaChunkBytes;
-constexpr int kMaskOff = kRingBytes;
-constexpr int kMiscOff = kMaskOff + 4 * kQsaWin;
-constexpr int kSharedLds = kMiscOff + 256;
-constexpr int kTokenLds = kQsaWaves * (int)sizeof(QsaTokLds);
-constexpr int kQsaLds = kSharedLds > kTokenLds ? kSharedLds : kTokenLds;
+// Workgroup LDS (bytes), all 160 KiB.  Shared route: the key-mask words of
+// the tile's key range from offset 0 (at most 64 KiB), compacted in place
+// into the union list; then a ring of [K | V] chunk buffers right after the
+// list (four when the union has at most 8192 keys, else three), and a few
+// words of reduction scratch at the top (read only before the ring is
+// filled).  Per-token route: one QsaTokLds per wave from offset 0.
+constexpr int kQsaLds = 160 * 1024;
+constexpr int kMiscOff = kQsaLds - 256;
+// Ring rows are padded so that every operand read is conflict-free with the
+// lane's part of the address fixed for the whole loop: K rows 528 bytes apart
+// (16 keys x 16 bytes of one k-step cover all 64 banks), V rows 544 bytes
+// (the transposing reads of 8 rows x 32 bytes cover all 64 banks).
+constexpr int kKPitch = kQsaRowBytes + 16;
+constexpr int kVPitch = kQsaRowBytes + 32;
+constexpr int kKChunk = 32 * kKPitch;
+constexpr int kPairBytes = kKChunk + 32 * kVPitch;   // one ring buffer: K and V of a chunk
+constexpr int kQsaMaxBuf = 4;
+// A lane's eight exponentials of a chunk sum to at most 8 * 2^64 while every
+// score is within 64 (log2 units) of the row's reference max.
+constexpr float kQsaSumLimit = 0x1p68f;
 static_assert(sizeof(QsaTokLds) % 16 == 0, "per-wave regions stay 16-byte aligned");
+static_assert(kQsaWaves * (int)sizeof(QsaTokLds) <= kMiscOff, "per-wave regions fit below the scratch");
+static_assert(4 * kQsaWin + 2 * kPairBytes <= kQsaLds, "two ring buffers fit after the widest list");
 
 // Per-token route: one wave computes query token `tok` against KV head g,
 // its G <= 16 query heads as the 16 rows of the MFMA tile, the token's keys
@@ -257,6 +268,42 @@ __device__ __forceinline__ void qsa_token(const QsaParams& p, int tok, int g, Qs
     p.lse[(int64_t)hrow * p.total_q + tok] = lsum > 0.f ? (m + __log2f(lsum)) * kQsaLn2 : -INFINITY;
 }
 
+// Index entries e0 + tid + 512 i (i < 4) of the tile's rows j < 16, all
+// loads in flight together; rows past the tile re-read its last row and
+// entries past the row its last entry (the caller skips both).
+__device__ __forceinline__ void index_batch(const QsaParams& p, int t0, int nt, int e0,
+                                            int (&id)[kQsaMaxTokens][4]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kQsaMaxTokens; ++j) {
+    const int32_t* row = p.indices + (int64_t)(t0 + min(j, nt - 1)) * p.width;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) id[j][i] = row[min(e0 + tid + kQsaThreads * i, p.width - 1)];
+  }
+}
+
+// Token bits of blocks b0 + tid + 512 i (i < 4): bit j set when the tile's
+// token j selects the block (bitmap byte non-zero); blocks past the map read
+// its last block (the caller skips them).
+__device__ __forceinline__ void block_masks(const QsaParams& p, int t0, int nt, int b0,
+                                            uint32_t (&mk)[4]) {
+  const int tid = threadIdx.x;
+  uint8_t v[kQsaMaxTokens][4];
+#pragma unroll
+  for (int j = 0; j < kQsaMaxTokens; ++j) {
+    const uint8_t* row = p.bitmap + (int64_t)(t0 + min(j, nt - 1)) * p.num_blocks;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[j][i] = row[min(b0 + tid + kQsaThreads * i, p.num_blocks - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < kQsaMaxTokens; ++j) m |= (j < nt && v[j][i] != 0 ? 1u : 0u) << j;
+    mk[i] = m;
+  }
+}
+
 }  // namespace
 
 // BITMAP: the keys come from a uint8 [T, num_blocks] block bitmap instead of
@@ -278,35 +325,52 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
   const int lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.group;
-  uint32_t* M = reinterpret_cast<uint32_t*>(smem + kMaskOff);
+  uint32_t* M = reinterpret_cast<uint32_t*>(smem);
   int* misc = reinterpret_cast<int*>(smem + kMiscOff);
 
   // ---- pass 1: listed entries (saturated: only compared with the union
-  // below) and the lowest and highest listed key of the tile ----
+  // below) and the lowest and highest listed key of the tile.  Loads go out
+  // 16 rows x 4 entries per thread at a time (rows past the tile re-read its
+  // last row, entries past the row its last entry; neither is counted).  A
+  // bitmap over at most 16384 keys also writes every key's token bits here,
+  // at key offset 0 (base 0). ----
+  const bool direct = BITMAP && p.num_kv_tokens <= kQsaWin;
   int cnt = 0, lo = INT32_MAX, hi = -1;
   if constexpr (BITMAP) {
-    for (int j = 0; j < nt; ++j) {
-      const uint8_t* row = p.bitmap + (int64_t)(t0 + j) * p.num_blocks;
-      for (int b = tid; b < p.num_blocks; b += kQsaThreads) {
-        if (row[b]) {
-          const int last = min(4 * b + 3, p.num_kv_tokens - 1);
-          cnt += last - 4 * b + 1;
+    const int nb = p.num_blocks;
+    for (int b0 = 0; b0 < nb; b0 += 4 * kQsaThreads) {
+      uint32_t mk[4];
+      block_masks(p, t0, nt, b0, mk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = b0 + tid + kQsaThreads * i;
+        if (b >= nb) continue;
+        const int last = min(4 * b + 3, p.num_kv_tokens - 1);
+        if (mk[i]) {
+          cnt += __popc(mk[i]) * (last - 4 * b + 1);
           lo = min(lo, 4 * b);
           hi = max(hi, last);
+        }
+        if (direct) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * b + e <= last) M[4 * b + e] = mk[i];
         }
       }
     }
   } else {
-    for (int j = 0; j < nt; ++j) {
-      const int32_t* row = p.indices + (int64_t)(t0 + j) * p.width;
-      for (int e = tid; e < p.width; e += kQsaThreads) {
-        const int id = row[e];
-        if (id >= 0) {
-          ++cnt;
-          lo = min(lo, id);
-          hi = max(hi, id);
-        }
-      }
+    for (int e0 = 0; e0 < p.width; e0 += 4 * kQsaThreads) {
+      int id[kQsaMaxTokens][4];
+      index_batch(p, t0, nt, e0, id);
+#pragma unroll
+      for (int j = 0; j < kQsaMaxTokens; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (j < nt && e0 + tid + kQsaThreads * i < p.width && id[j][i] >= 0) {
+            ++cnt;
+            lo = min(lo, id[j][i]);
+            hi = max(hi, id[j][i]);
+          }
     }
   }
   cnt = min(cnt, 1 << 20);
@@ -335,36 +399,44 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
   const int live_waves = (nt * G + 15) >> 4;
   bool shared = true;   // nothing listed: the shared route writes 0 / -inf
   int U = 0;            // union size
-  const int base = hi >= 0 ? lo : 0;
-  if (hi >= 0 && hi - lo >= kQsaWin) {
+  const int base = hi < 0 || direct ? 0 : lo;
+  if (hi >= 0 && hi - base >= kQsaWin) {
     shared = false;
   } else if (hi >= 0) {
-    const int range = hi - lo + 1;
-    // ---- pass 2: token bits of every key in [lo, hi] ----
-    if (32 * tid < range) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x4*>(M + 32 * tid + 4 * i) = u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
+    const int range = hi - base + 1;
+    // ---- pass 2: token bits of every key in [base, hi] ----
     if constexpr (BITMAP) {
-      for (int b = (lo >> 2) + tid; b <= (hi >> 2); b += kQsaThreads) {
-        uint32_t mk = 0;
-        for (int j = 0; j < nt; ++j)
-          mk |= (p.bitmap[(int64_t)(t0 + j) * p.num_blocks + b] != 0 ? 1u : 0u) << j;
-        if (mk) {
+      if (!direct) {
+        // every block of the range written, selected or not
+        for (int b0 = lo >> 2; b0 <= (hi >> 2); b0 += 4 * kQsaThreads) {
+          uint32_t mk[4];
+          block_masks(p, t0, nt, b0, mk);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (4 * b + e <= hi) M[4 * b + e - base] = mk;
+          for (int i = 0; i < 4; ++i) {
+            const int b = b0 + tid + kQsaThreads * i;
+            if (b > (hi >> 2)) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * b + e <= hi) M[4 * b + e - base] = mk[i];
+          }
         }
       }
     } else {
-      for (int j = 0; j < nt; ++j) {
-        const int32_t* row = p.indices + (int64_t)(t0 + j) * p.width;
-        for (int e = tid; e < p.width; e += kQsaThreads) {
-          const int id = row[e];
-          if (id >= 0) atomicOr(M + (id - base), 1u << j);
-        }
+      if (32 * tid < range) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          *reinterpret_cast<u32x4*>(M + 32 * tid + 4 * i) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+      for (int e0 = 0; e0 < p.width; e0 += 4 * kQsaThreads) {
+        int id[kQsaMaxTokens][4];
+        index_batch(p, t0, nt, e0, id);
+#pragma unroll
+        for (int j = 0; j < kQsaMaxTokens; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (j < nt && e0 + tid + kQsaThreads * i < p.width && id[j][i] >= 0)
+              atomicOr(M + (id[j][i] - base), 1u << j);
       }
     }
     __syncthreads();
@@ -377,8 +449,9 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
                                        : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        vals[4 * i + k] = x[k];
-        c += x[k] != 0u;
+        // words past the range were never written
+        vals[4 * i + k] = 32 * tid + 4 * i + k < range ? x[k] : 0u;
+        c += vals[4 * i + k] != 0u;
       }
     }
     int x = c;   // inclusive scan over the wave
@@ -400,9 +473,10 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
 #pragma unroll
     for (int i = 0; i < 32; ++i)
       if (vals[i]) M[rank++] = (uint32_t)(32 * tid + i) << 16 | vals[i];
-    // the last chunk's padding: no token, key offset 0 (a listed key)
-    if (U + tid < ((U + 31) & ~31)) M[U + tid] = 0u;
+    // the last chunk's padding: no token, the lowest listed key
+    if (U + tid < ((U + 31) & ~31)) M[U + tid] = (uint32_t)(lo - base) << 16;
     __syncthreads();
+    U = __builtin_amdgcn_readfirstlane(U);
     shared = (int64_t)kTileCost * U * ((live_waves + 3) >> 2) <= (int64_t)kTokenCost * listed;
   }
 
@@ -436,100 +510,133 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
 
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k) + (int64_t)g * p.k_head_stride;
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.v) + (int64_t)g * p.v_head_stride;
-  const uint32_t ring = __builtin_amdgcn_readfirstlane(lds_addr(smem));
-  const uint32_t mlds = __builtin_amdgcn_readfirstlane(lds_addr(M));
   const float C = p.scale_log2;
   const int nch = (U + 31) >> 5;
+  const uint32_t mlds = __builtin_amdgcn_readfirstlane(lds_addr(M));
+  const uint32_t ring = mlds + 128 * nch;   // right after the union list
+  const int nbuf = min(kQsaMaxBuf, (kQsaLds - 128 * nch) / kPairBytes);
 
-  // chunk c's K and V rows into buffer c & 1: wave w stages keys 4 w .. 4 w + 3,
-  // two rows per load (lane l: row 4 w + 2 i + l / 32, 16-byte unit l % 32,
-  // read from its swizzled source unit)
-  auto stage = [&](int c) {
-    const uint32_t kb = ring + (c & 1) * 2 * kQsaChunkBytes;
+  // chunk K and V rows into ring buffer b: wave w stages keys 4 w .. 4 w + 3,
+  // whose union entries `ent` it has read beforehand, one padded row per
+  // load (lanes 0..31, 16 bytes each, the row's address in scalar
+  // registers); eight loads per wave
+  auto entries = [&](int c) { return lds_b128(mlds + 128 * c + 16 * w); };
+  auto stage = [&](int b, u32x4 ent) {
+    const uint32_t kb = ring + b * kPairBytes;
+    if (lane < 32) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 4 * w + 2 * i + (lane >> 5);
-      const uint32_t ent = M[32 * c + r];
-      const int64_t id = base + (int)(ent >> 16);
-      const int u = lane & 31;
-      const uint32_t dst = kb + (4 * w + 2 * i) * kQsaRowBytes;
-      g2lds16(kg + id * p.k_row_stride + 16 * (u ^ (r & 15)), dst);
-      g2lds16(vg + id * p.v_row_stride + 16 * (u ^ ((r & 7) << 1)), dst + kQsaChunkBytes);
+      for (int i = 0; i < 4; ++i) {
+        const int64_t id = base + (int)(__builtin_amdgcn_readfirstlane(ent[i]) >> 16);
+        const int r = 4 * w + i;
+        g2lds16_sv(kg + id * p.k_row_stride, 16 * lane, kb + r * kKPitch);
+        g2lds16_sv(vg + id * p.v_row_stride, 16 * lane, kb + kKChunk + r * kVPitch);
+      }
     }
   };
 
+  // reference max m (log2 units; -inf until the row's first listed key) and
+  // the row sum: p = 2^(s - m), m moved (rescaling O and l) only when a
+  // lane's chunk sum reveals a score past it by the slack, or the row meets
+  // its first listed key
   float m = -INFINITY, l = 0.f;
   f32x4 o[16];
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t bit = live ? 1u << tl : 0u;   // the row's token bit in a key's mask
+  // K fragment (key 16 kt + l % 16, k-step s): kofs + kt * 16 * kKPitch + 64 s;
+  // V^T fragment (head dims 16 dt + l % 16, rows 4 q + e and 16 + 4 q + e
+  // via the transposing read): vofs + 32 dt (+ 16 * kVPitch)
+  const uint32_t kofs = l16 * kKPitch + 16 * q;
+  const uint32_t vofs = kKChunk + (4 * q + (l16 >> 2)) * kVPitch + 8 * (l16 & 3);
 
-  if (nch > 0) stage(0);
+  // chunks 0 .. nbuf - 2 in flight before the first one is computed
+  for (int c = 0; c < min(nbuf - 1, nch); ++c) stage(c, entries(c));
+  int bc = 0;   // ring buffer of chunk c
   for (int c = 0; c < nch; ++c) {
-    // chunk c has landed for every wave, and every wave is done with chunk
-    // c - 1, whose buffer chunk c + 1 now refills
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const int cn = c + nbuf - 1;   // the chunk staged in this step
+    const u32x4 ent = entries(cn < nch ? cn : c);
+    // chunk c has landed for every wave (the later chunks staged so far may
+    // still be in flight: eight loads each), and every wave is done with
+    // chunk c - 1, whose buffer chunk cn now refills
+    const int ahead = min(nbuf - 2, nch - 1 - c);
+    if (ahead >= 2)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (ahead == 1)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     block_barrier();
-    if (c + 1 < nch) stage(c + 1);
+    if (cn < nch) stage(bc == 0 ? nbuf - 1 : bc - 1, ent);
+    const int b = bc;
+    bc = bc + 1 == nbuf ? 0 : bc + 1;
     if (!wave_live) continue;
-    const uint32_t kb = ring + (c & 1) * 2 * kQsaChunkBytes;
-    const uint32_t vb = kb + kQsaChunkBytes;
+    const uint32_t kb = ring + b * kPairBytes;
 
-    f32x4 acc[2];
+    // every K fragment and the token masks of the lane's eight keys in
+    // flight at once, then S^T = K Q^T
+    u32x4 kf[2][8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint32_t ka = kb + (16 * kt + l16) * kQsaRowBytes;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        acc[kt] = mfma16(as_bf16x8(lds_b128(ka + 16 * ((4 * s + q) ^ l16))), qf[s], acc[kt]);
+      for (int s = 0; s < 8; ++s) kf[kt][s] = lds_b128(kb + kofs + kt * 16 * kKPitch + 64 * s);
+    const uint32_t mrow = mlds + 128 * c;
+    const u32x4 ma = lds_b128(mrow + 16 * q);
+    const u32x4 mb = lds_b128(mrow + 64 + 16 * q);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma16(as_bf16x8(kf[kt][s]), qf[s], acc[kt]);
+    __builtin_amdgcn_sched_barrier(0);
+    // V^T fragments, read while the softmax below runs
+    u32x4 vt[16];
+#pragma unroll
+    for (int dt = 0; dt < 16; ++dt) {
+      const u32x2 lo2 = lds_tr16(kb + vofs + 32 * dt);
+      const u32x2 hi2 = lds_tr16(kb + vofs + 32 * dt + 16 * kVPitch);
+      vt[dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
     }
-    // token masks of the eight keys whose scores this lane holds
-    const u32x4 ma = lds_b128(mlds + 128 * c + 16 * q);
-    const u32x4 mb = lds_b128(mlds + 128 * c + 64 + 16 * q);
+    __builtin_amdgcn_sched_barrier(0);
+
     const uint32_t mk[8] = {ma[0], ma[1], ma[2], ma[3], mb[0], mb[1], mb[2], mb[3]};
-    float sc[8];
+    bool vis[8];
+    float e[8], ps = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float s = acc[j >> 2][j & 3] * C;
-      sc[j] = live && ((mk[j] >> tl) & 1u) ? s : -INFINITY;
+      vis[j] = (mk[j] & bit) != 0u;
+      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j >> 2][j & 3], C, -m));
+      e[j] = vis[j] ? x : 0.f;
+      ps += e[j];
     }
-    float cm = sc[0];
+    if (__ballot(!(ps <= kQsaSumLimit))) {
+      // rows whose chunk passed the reference (or met their first listed
+      // key) move it to their max; other rows keep theirs (alpha 1, the
+      // same exponentials), so a row's result does not depend on its mates
+      const float trig = xmax_16_32(!(ps <= kQsaSumLimit) ? 1.f : 0.f);
+      float cm = -INFINITY;
 #pragma unroll
-    for (int j = 1; j < 8; ++j) cm = fmaxf(cm, sc[j]);
-    cm = xmax_16_32(cm);
-    // move the reference max only when a score passes it by the slack (or
-    // the row sees its first listed key)
-    const bool move = cm > m + kQsaSlack;
-    if (__ballot(move)) {
-      const float alpha = move ? __builtin_amdgcn_exp2f(m - cm) : 1.f;
-      m = move ? cm : m;
+      for (int j = 0; j < 8; ++j) cm = fmaxf(cm, vis[j] ? acc[j >> 2][j & 3] * C : -INFINITY);
+      cm = xmax_16_32(cm);
+      const float mn = trig > 0.f ? fmaxf(m, cm) : m;
+      const float alpha = mn == m ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+      m = mn;
       l *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
-    }
-    const float mu = m == -INFINITY ? 0.f : m;   // no listed key yet: p = 0
-    float e[8];
+      ps = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      e[j] = __builtin_amdgcn_exp2f(sc[j] - mu);
-      l += e[j];
+      for (int j = 0; j < 8; ++j) {
+        const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j >> 2][j & 3], C, -m));
+        e[j] = vis[j] ? x : 0.f;
+        ps += e[j];
+      }
     }
+    l += ps;
     const bf16x8 pf = as_bf16x8(u32x4{cvt_pk_bf16(e[0], e[1]), cvt_pk_bf16(e[2], e[3]),
                                       cvt_pk_bf16(e[4], e[5]), cvt_pk_bf16(e[6], e[7])});
-
-    // V^T fragments: head dims 16 dt + l % 16; lane 4 e + a of a 16-lane
-    // group reads 8 bytes (head dims 16 dt + 4 a ..) of rows 4 q + e and
-    // 16 + 4 q + e, found at their swizzled 16-byte units
-    const int vrow = 4 * q + (l16 >> 2);
-    const int vsw = (vrow & 7) << 1;
-    const uint32_t va0 = vb + vrow * kQsaRowBytes + 8 * (l16 & 1);
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const uint32_t a = va0 + 16 * ((2 * dt + ((l16 & 3) >> 1)) ^ vsw);
-      const u32x2 lo2 = lds_tr16(a);
-      const u32x2 hi2 = lds_tr16(a + 16 * kQsaRowBytes);
-      o[dt] = mfma16(as_bf16x8(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}), pf, o[dt]);
-    }
+    for (int dt = 0; dt < 16; ++dt) o[dt] = mfma16(as_bf16x8(vt[dt]), pf, o[dt]);
   }
 
   if (!wave_live) return;
