@@ -11,17 +11,18 @@
 //    the key), then compacted, in ascending key order, into (key offset,
 //    token mask) words.  The keys are consumed 32 at a time: every chunk's K
 //    and V rows (512 bytes each) are staged global -> LDS with
-//    global_load_lds by all eight waves, double buffered with one barrier
-//    per chunk, so a key listed by several tokens of the tile is read once
-//    per tile rather than once per token.  Every slot computes the whole
-//    chunk and masks the keys its row's token did not list.
-//  * S^T = K Q^T (keys on M, query rows on N), K fragments from LDS with the
-//    rows XOR-swizzled in 16-byte units (conflict-free operand reads at a
-//    512-byte pitch); online softmax in log2 units against a per-row
-//    reference max that moves (rescaling O and l) only when a chunk's max
-//    passes it by more than 64; O^T += V^T P^T with V^T from
-//    ds_read_b64_tr_b16 and P straight from the S^T registers (keys 4 q ..
-//    4 q + 3 and 16 + 4 q .. 16 + 4 q + 3 of lane group q).
+//    global_load_lds by all eight waves into a ring of 2-4 chunk buffers
+//    (one barrier per chunk), so a key listed by several tokens of the tile
+//    is read once per tile rather than once per token.  Every slot computes
+//    the whole chunk and masks the keys its row's token did not list.
+//  * S^T = K Q^T (keys on M, query rows on N), K fragments from LDS (ring
+//    rows padded so that operand reads are conflict-free and each lane's
+//    addresses are one register plus instruction offsets); online softmax
+//    in log2 units against a per-row reference max that moves (rescaling O
+//    and l) only when the row meets its first listed key or a chunk's
+//    partial sum reveals a score past it by more than 64; O^T += V^T P^T
+//    with V^T from ds_read_b64_tr_b16 and P straight from the S^T registers
+//    (keys 4 q .. 4 q + 3 and 16 + 4 q .. 16 + 4 q + 3 of lane group q).
 //  * Per-token keys.  When the tile's keys span more than 16384 tokens, or
 //    the union is large against what its tokens listed (masking would then
 //    compute far more scores than gathering each token's own keys), the

@@ -376,19 +376,27 @@ typedef struct {
  * -inf LSE (qsa page: the indexed API, outputs and LSE, empty selections).
  * Causality is the caller's, carried by the indices.  Index values are a
  * caller contract (distinct, < Tk), not validated on the device; k and v
- * must hold at least one row (-1 padding entries read row 0, with weight
- * 0).  Host-side checks return MSA_ERR_SHAPE / MSA_ERR_NULL /
+ * must hold at least one row (-1 padding entries may read row 0, with
+ * weight 0).  Host-side checks return MSA_ERR_SHAPE / MSA_ERR_NULL /
  * MSA_ERR_UNSUPPORTED (head_dim != 256, Hq / Hkv > 16, misaligned pointers)
- * before any launch.  Every (query, head) is computed in index order by one
- * wave: results are bitwise repeatable. */
+ * before any launch.
+ * Work split: one workgroup per tile of min(16, 128 / G) consecutive query
+ * tokens and KV head.  A tile whose listed keys span at most 16384 tokens
+ * and whose key union is at most 4/5 of its listed entries reads each
+ * union key once and computes its rows over the union in ascending key
+ * order, masking the keys a row's token did not list; any other tile
+ * computes each token over its own keys in index order.  Results are
+ * bitwise repeatable. */
 msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* args, void* stream);
 
 /* The same attention with the key set of query i given by row i of a block
  * bitmap over the packed K/V (qsa page: the bitmap API over 4-token blocks):
  * keys are the tokens of the selected blocks, in ascending order, the last
- * block cut at Tk.  The selected blocks are compacted on the device, 32
- * tokens per step, so nothing is allocated and no index scratch is written;
- * width and indices are ignored, any number of blocks may be selected.
+ * block cut at Tk.  The selected blocks are compacted on the device (per
+ * tile or per token, as for the indexed entry point, which gives bitwise
+ * equal results on the equivalent ascending index rows), so nothing is
+ * allocated and no index scratch is written; width and indices are
+ * ignored, any number of blocks may be selected.
  * Host-side checks as for the indexed entry point, plus bitmap non-NULL
  * (when T > 0 and Tk > 0; with Tk == 0 nothing is selected and k, v and
  * bitmap may be NULL) and 0 <= Tk < 2^31 - 4 (MSA_ERR_SHAPE). */
