@@ -16,11 +16,11 @@
 //    is read once per tile rather than once per token.  Every slot computes
 //    the whole chunk and masks the keys its row's token did not list.
 //  * S^T = K Q^T (keys on M, query rows on N), K fragments from LDS (ring
-//    rows padded so that operand reads are conflict-free and each lane's
-//    addresses are one register plus instruction offsets); online softmax
-//    in log2 units against a per-row reference max that moves (rescaling O
-//    and l) only when the row meets its first listed key or a chunk's
-//    partial sum reveals a score past it by more than 64; O^T += V^T P^T
+//    rows XOR-swizzled in 16-byte units so that operand reads are
+//    conflict-free); online softmax in log2 units against a per-row
+//    reference max that moves (rescaling O and l) only when the row meets
+//    its first listed key or a chunk's partial sum reveals a score past it
+//    by more than 64; O^T += V^T P^T
 //    with V^T from ds_read_b64_tr_b16 and P straight from the S^T registers
 //    (keys 4 q .. 4 q + 3 and 16 + 4 q .. 16 + 4 q + 3 of lane group q).
 //  * Per-token keys.  When the tile's keys span more than 16384 tokens, or
@@ -88,12 +88,14 @@ struct QsaTokLds {
 // filled).  Per-token route: one QsaTokLds per wave from offset 0.
 constexpr int kQsaLds = 160 * 1024;
 constexpr int kMiscOff = kQsaLds - 256;
-// Ring rows are padded so that every operand read is conflict-free with the
-// lane's part of the address fixed for the whole loop: K rows 528 bytes apart
-// (16 keys x 16 bytes of one k-step cover all 64 banks), V rows 544 bytes
-// (the transposing reads of 8 rows x 32 bytes cover all 64 banks).
-constexpr int kKPitch = kQsaRowBytes + 16;
-constexpr int kVPitch = kQsaRowBytes + 32;
+// Ring rows are unpadded (512 bytes) and XOR-swizzled in 16-byte units:
+// unit u of K row r sits at u ^ (r % 16), of V row r at u ^ 2 (r % 8), so the
+// 16 keys one K operand read touches and the rows one transposing V read
+// touches fall on distinct banks.  (Rows padded to 528 / 544 bytes instead,
+// with per-row loads, measured 16x the bank-conflict cycles and 12 % more
+// time.)
+constexpr int kKPitch = kQsaRowBytes;
+constexpr int kVPitch = kQsaRowBytes;
 constexpr int kKChunk = 32 * kKPitch;
 constexpr int kPairBytes = kKChunk + 32 * kVPitch;   // one ring buffer: K and V of a chunk
 constexpr int kQsaMaxBuf = 4;
@@ -518,20 +520,21 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
   const int nbuf = min(kQsaMaxBuf, (kQsaLds - 128 * nch) / kPairBytes);
 
   // chunk K and V rows into ring buffer b: wave w stages keys 4 w .. 4 w + 3,
-  // whose union entries `ent` it has read beforehand, one padded row per
-  // load (lanes 0..31, 16 bytes each, the row's address in scalar
-  // registers); eight loads per wave
+  // whose union entries `ent` it has read beforehand, two rows per load
+  // (lane l: row 4 w + 2 i + l / 32, 16-byte unit l % 32, read from its
+  // swizzled source unit); four loads per wave
   auto entries = [&](int c) { return lds_b128(mlds + 128 * c + 16 * w); };
   auto stage = [&](int b, u32x4 ent) {
     const uint32_t kb = ring + b * kPairBytes;
-    if (lane < 32) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t id = base + (int)(__builtin_amdgcn_readfirstlane(ent[i]) >> 16);
-        const int r = 4 * w + i;
-        g2lds16_sv(kg + id * p.k_row_stride, 16 * lane, kb + r * kKPitch);
-        g2lds16_sv(vg + id * p.v_row_stride, 16 * lane, kb + kKChunk + r * kVPitch);
-      }
+    for (int i = 0; i < 2; ++i) {
+      const int r = 4 * w + 2 * i + (lane >> 5);
+      const uint32_t e = (lane >> 5) ? ent[2 * i + 1] : ent[2 * i];
+      const int64_t id = base + (int)(e >> 16);
+      const int u = lane & 31;
+      const uint32_t dst = kb + (4 * w + 2 * i) * kQsaRowBytes;
+      g2lds16(kg + id * p.k_row_stride + 16 * (u ^ (r & 15)), dst);
+      g2lds16(vg + id * p.v_row_stride + 16 * (u ^ ((r & 7) << 1)), dst + kKChunk);
     }
   };
 
@@ -544,11 +547,13 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
 #pragma unroll
   for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t bit = live ? 1u << tl : 0u;   // the row's token bit in a key's mask
-  // K fragment (key 16 kt + l % 16, k-step s): kofs + kt * 16 * kKPitch + 64 s;
-  // V^T fragment (head dims 16 dt + l % 16, rows 4 q + e and 16 + 4 q + e
-  // via the transposing read): vofs + 32 dt (+ 16 * kVPitch)
-  const uint32_t kofs = l16 * kKPitch + 16 * q;
-  const uint32_t vofs = kKChunk + (4 * q + (l16 >> 2)) * kVPitch + 8 * (l16 & 3);
+  // K fragment (key 16 kt + l % 16, k-step s): unit 4 s + q of the key's row;
+  // V^T fragment (head dims 16 dt + l % 16): lane 4 e + a of a 16-lane group
+  // reads 8 bytes (head dims 16 dt + 4 a ..) of rows 4 q + e and
+  // 16 + 4 q + e, each at its swizzled unit
+  const int vrow = 4 * q + (l16 >> 2);
+  const int vsw = (vrow & 7) << 1;
+  const uint32_t vofs = kKChunk + vrow * kVPitch + 8 * (l16 & 1);
 
   // chunks 0 .. nbuf - 2 in flight before the first one is computed
   for (int c = 0; c < min(nbuf - 1, nch); ++c) stage(c, entries(c));
@@ -557,13 +562,13 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
     const int cn = c + nbuf - 1;   // the chunk staged in this step
     const u32x4 ent = entries(cn < nch ? cn : c);
     // chunk c has landed for every wave (the later chunks staged so far may
-    // still be in flight: eight loads each), and every wave is done with
+    // still be in flight: four loads each), and every wave is done with
     // chunk c - 1, whose buffer chunk cn now refills
     const int ahead = min(nbuf - 2, nch - 1 - c);
     if (ahead >= 2)
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (ahead == 1)
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (ahead == 1)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     block_barrier();
@@ -579,7 +584,8 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int s = 0; s < 8; ++s) kf[kt][s] = lds_b128(kb + kofs + kt * 16 * kKPitch + 64 * s);
+      for (int s = 0; s < 8; ++s)
+        kf[kt][s] = lds_b128(kb + (16 * kt + l16) * kKPitch + 16 * ((4 * s + q) ^ l16));
     const uint32_t mrow = mlds + 128 * c;
     const u32x4 ma = lds_b128(mrow + 16 * q);
     const u32x4 mb = lds_b128(mrow + 64 + 16 * q);
@@ -594,8 +600,9 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
     u32x4 vt[16];
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
-      const u32x2 lo2 = lds_tr16(kb + vofs + 32 * dt);
-      const u32x2 hi2 = lds_tr16(kb + vofs + 32 * dt + 16 * kVPitch);
+      const uint32_t a = kb + vofs + 16 * ((2 * dt + ((l16 & 3) >> 1)) ^ vsw);
+      const u32x2 lo2 = lds_tr16(a);
+      const u32x2 hi2 = lds_tr16(a + 16 * kVPitch);
       vt[dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
     }
     __builtin_amdgcn_sched_barrier(0);
