@@ -46,7 +46,6 @@ constexpr int kQsaWaves = 8;
 constexpr int kQsaThreads = kQsaWaves * kWave;
 constexpr int kQsaTileRows = 16 * kQsaWaves;      // query rows of a tile
 constexpr int kQsaMaxTokens = 16;                 // token bits of a key's mask word
-constexpr int kQsaChunkBytes = 32 * kQsaRowBytes; // 32 K (or V) rows: 16 KiB
 constexpr int kQsaWin = 16384;                    // key range the shared route covers
 // Shared route when kTileCost * union * (slot rounds) <= kTokenCost * listed
 // entries: per union key a round of four 16-row slots costs about 5/8 of one

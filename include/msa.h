@@ -382,9 +382,10 @@ typedef struct {
  * before any launch.
  * Work split: one workgroup per tile of min(16, 128 / G) consecutive query
  * tokens and KV head.  A tile whose listed keys span at most 16384 tokens
- * and whose key union is at most 4/5 of its listed entries reads each
- * union key once and computes its rows over the union in ascending key
- * order, masking the keys a row's token did not list; any other tile
+ * and whose key union U is small against its L listed entries
+ * (5 * U * ceil(S / 4) <= 8 * L, S = ceil(tokens * G / 16) row slots) reads
+ * each union key once and computes its rows over the union in ascending
+ * key order, masking the keys a row's token did not list; any other tile
  * computes each token over its own keys in index order.  Results are
  * bitwise repeatable. */
 msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* args, void* stream);
