@@ -469,6 +469,10 @@ def bench_qsa(args, msa, synth, torch):
     lse = torch.empty(hq, T, dtype=torch.float32, device="cuda")
     keys = _qsa_keys(p)
     flops = 4 * d * hq * keys
+    from block_sparse_top_msa_amd import accounting
+    exe_flops, exe_shared, exe_token = accounting.qsa_executed(
+        hq, p.k.shape[1], indices=None if bitmap else p.indices,
+        bitmap=p.bitmap if bitmap else None, num_kv_tokens=p.k.shape[0], head_dim=d)
 
     def step():
         if bitmap:
@@ -505,7 +509,16 @@ def bench_qsa(args, msa, synth, torch):
         "roofline": {"kernel": "msa_qsa_kernel", "bound": "mfma",
                      "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": _traffic_for("msa_qsa_kernel:" + p.name)},
+                     "traffic": _traffic_for("msa_qsa_kernel:" + p.name),
+                     "executed": {
+                         "flops": exe_flops,
+                         "tflops": round(exe_flops / (kern_ms * 1e-3) / 1e12, 3),
+                         "frac": round(exe_flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "selected_share": round(flops / exe_flops, 4) if exe_flops else None,
+                         "tiles_shared": exe_shared, "tiles_per_token": exe_token,
+                         "what": "MFMA FLOPs of the QSA kernel: each shared-key tile's live 16-row "
+                                 "slots over its whole key union, each per-token tile's tokens over "
+                                 "their own chunks, counted on the host; diagnostic, not the metric"}},
     }
     return res, p
 

@@ -151,3 +151,77 @@ def prefill_executed_flops(q2k, cu_seqlens_q, lengths_k, num_qo_heads, tile_toke
     32 rows x 128 keys and O^T += V^T P^T of the same size."""
     n = prefill_slot_blocks(q2k, cu_seqlens_q, lengths_k, num_qo_heads, tile_tokens)
     return n * SLOT_ROWS * BLOCK * head_dim * 4
+
+
+# ---------------------------------------------------------------------------
+# Executed MFMA work of the QSA tile kernel (a diagnostic beside the
+# selected-token count, not part of it)
+# ---------------------------------------------------------------------------
+
+QSA_TILE_ROWS = 128      # eight 16-row slots
+QSA_MAX_TOKENS = 16      # token bits of a key's mask word
+QSA_WIN = 16384          # key range of a shared-route tile
+QSA_SLOT_ROWS = 16
+
+
+def qsa_tile_tokens(num_qo_heads, num_kv_heads):
+    """Consecutive query tokens per QSA tile: 128 token-major rows of G heads,
+    at most 16 tokens."""
+    return min(QSA_MAX_TOKENS, QSA_TILE_ROWS // (num_qo_heads // num_kv_heads))
+
+
+def qsa_executed(num_qo_heads, num_kv_heads, indices=None, bitmap=None, num_kv_tokens=None,
+                 head_dim=256):
+    """(MFMA FLOPs, shared tiles, per-token tiles) of the QSA kernel on index
+    rows ([T, W] int32, negative = padding) or a block bitmap ([T, NB] uint8
+    over num_kv_tokens keys).
+
+    A tile of `qsa_tile_tokens` queries takes the shared route when its
+    listed keys span fewer than 16384 tokens (a bitmap over at most 16384
+    keys always does) and 5 * U * ceil(S / 4) <= 8 * L, with U its key union,
+    L its listed entries and S = ceil(tokens * G / 16) its live 16-row
+    slots; then every live slot computes 32-key chunks over the whole union
+    (ceil(U / 32) chunks).  Otherwise each token takes its own 16-row tile
+    over its own keys: ceil(W / 32) chunks of index entries, or one chunk
+    per eight selected blocks.  A 16-row slot's chunk costs 16 x 32 keys x
+    head_dim x 4 FLOPs (S^T and O^T += V^T P^T), for every KV head."""
+    G = num_qo_heads // num_kv_heads
+    tt = qsa_tile_tokens(num_qo_heads, num_kv_heads)
+    chunk = QSA_SLOT_ROWS * 32 * head_dim * 4
+    if bitmap is not None:
+        bm = bitmap.cpu() != 0
+        T, nb = bm.shape
+        blk = torch.arange(nb)
+        size = torch.clamp(num_kv_tokens - 4 * blk, max=4)   # tokens per block
+    else:
+        ind = indices.cpu().to(torch.int64)
+        T, W = ind.shape
+    flops = shared = token = 0
+    for t0 in range(0, T, tt):
+        nt = min(tt, T - t0)
+        slots = (nt * G + QSA_SLOT_ROWS - 1) // QSA_SLOT_ROWS
+        if bitmap is not None:
+            rows = bm[t0:t0 + nt]
+            listed = int((rows.to(torch.int64) * size).sum())
+            ub = rows.any(0)
+            U = int(size[ub].sum())
+            if U:
+                lo, hi = 4 * int(blk[ub][0]), min(4 * int(blk[ub][-1]) + 3, num_kv_tokens - 1)
+                base = 0 if num_kv_tokens <= QSA_WIN else lo
+            per_token = [(int(r.sum()) + 7) // 8 for r in rows]
+        else:
+            keys = ind[t0:t0 + nt]
+            keys = keys[keys >= 0]
+            listed = int(keys.numel())
+            U = int(torch.unique(keys).numel())
+            if U:
+                lo, hi = int(keys.min()), int(keys.max())
+                base = lo
+            per_token = [(W + 31) // 32] * nt
+        if U and (hi - base >= QSA_WIN or 5 * U * ((slots + 3) // 4) > 8 * listed):
+            token += 1
+            flops += sum(per_token) * chunk
+        else:
+            shared += 1
+            flops += slots * ((U + 31) // 32) * chunk
+    return flops * num_kv_heads, shared, token

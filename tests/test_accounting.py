@@ -116,3 +116,75 @@ def test_proxy_flops_match_brute_force():
             pairs += sum(1 for j in range(L) if j <= L - lq + i)
     assert acc.proxy_flops(cu, lk, 3, head_dim=128) == pairs * 3 * 2 * 128
     assert acc.proxy_flops(cu, lk, 3, head_dim=128, causal=False) == (5 * 9 + 7 * 7) * 3 * 2 * 128
+
+
+def _qsa_brute(G, hkv, rows, chunks_per_token, bitmap_direct=False):
+    """The QSA kernel's work by enumeration: rows = per-token sets of keys."""
+    tt = min(16, 128 // G)
+    total = 0
+    for t0 in range(0, len(rows), tt):
+        tile = rows[t0:t0 + tt]
+        union = set().union(*tile)
+        listed = sum(len(r) for r in tile)
+        slots = -(-len(tile) * G // 16)
+        wide = bool(union) and not bitmap_direct and max(union) - min(union) >= 16384
+        if union and (wide or 5 * len(union) * -(-slots // 4) > 8 * listed):
+            total += sum(chunks_per_token(i) for i in range(t0, t0 + len(tile))) * 16 * 32
+        else:
+            total += slots * -(-len(union) // 32) * 16 * 32
+    return total * 256 * 4 * hkv
+
+
+@pytest.mark.parametrize("hq,hkv", [(12, 1), (24, 2), (16, 1), (4, 1), (5, 1)])
+def test_qsa_executed_matches_enumeration(hq, hkv):
+    rng = random.Random(hq * 10 + hkv)
+    G = hq // hkv
+    T, W = 45, 64
+    rows, ind = [], torch.full((T, W), -1, dtype=torch.int32)
+    for i in range(T):
+        kind = rng.random()
+        if kind < 0.1:
+            r = []                                                 # empty row
+        elif kind < 0.4:
+            r = rng.sample(range(0, 20000), rng.randint(1, W))     # wide, sparse
+        else:
+            r = rng.sample(range(0, 80), rng.randint(1, W))        # dense, shared
+        rows.append(set(r))
+        ind[i, :len(r)] = torch.tensor(r, dtype=torch.int32)
+    flops, shared, token = acc.qsa_executed(hq, hkv, indices=ind)
+    assert flops == _qsa_brute(G, hkv, rows, lambda i: -(-W // 32))
+    assert shared + token == -(-T // min(16, 128 // G))
+
+
+def test_qsa_executed_bitmap_matches_enumeration():
+    rng = random.Random(7)
+    for tk in (517, 16384, 20001):
+        nb = (tk + 3) // 4
+        T = 33
+        bm = torch.zeros(T, nb, dtype=torch.uint8)
+        for i in range(T):
+            pick = rng.sample(range(nb), rng.choice([0, 2, 40])) if i % 3 else list(range(min(12, nb)))
+            bm[i, pick] = 1
+        rows = [set(t for b in torch.nonzero(bm[i]).flatten().tolist()
+                    for t in range(4 * b, min(4 * b + 4, tk))) for i in range(T)]
+        nblocks = [int(bm[i].sum()) for i in range(T)]
+        flops, _, _ = acc.qsa_executed(12, 1, bitmap=bm, num_kv_tokens=tk)
+        assert flops == _qsa_brute(12, 1, rows, lambda i: -(-nblocks[i] // 8),
+                                   bitmap_direct=tk <= 16384)
+
+
+def test_qsa_executed_closed_forms():
+    # ten tokens (G = 12: 120 rows, eight live 16-row slots) listing the same
+    # 40 keys: one shared tile, 2 chunks x 8 slots
+    ind = torch.arange(40, dtype=torch.int32).repeat(10, 1)
+    assert acc.qsa_executed(12, 1, indices=ind) == (8 * 2 * 16 * 32 * 256 * 4, 1, 0)
+    # ten tokens each listing one different key: U = 10 > 0.8 x 10 listed, so
+    # each token runs ceil(W / 32) = 1 chunk of its own
+    ind = torch.full((10, 4), -1, dtype=torch.int32)
+    ind[:, 0] = torch.arange(10) * 100
+    assert acc.qsa_executed(12, 1, indices=ind) == (10 * 16 * 32 * 256 * 4, 0, 1)
+    # keys 0 and 16384 in one tile: past the shared range
+    ind = torch.tensor([[0, 16384, 1, 2]] * 10, dtype=torch.int32)
+    assert acc.qsa_executed(12, 1, indices=ind)[2] == 1
+    # nothing listed: a shared tile with no chunks
+    assert acc.qsa_executed(12, 1, indices=torch.full((3, 4), -1, dtype=torch.int32)) == (0, 1, 0)
