@@ -261,3 +261,24 @@ def test_qsa_bitmap_shared_and_per_token_tiles(msa):
     b = msa.qsa_indexed_forward(d.q, d.k, d.v, full[:, :w].contiguous().cuda())
     torch.cuda.synchronize()
     assert torch.equal(out, b[0]) and torch.equal(out_f32, b[1]) and torch.equal(lse, b[2])
+
+
+def test_qsa_24_2_full_size_sampled_rows(msa):
+    # the page's other head configuration at the workload's size: 8192
+    # packed tokens in two sequences, 24 query / 2 KV heads, 2048-wide random
+    # rows; every 8th token (all 24 heads) against the oracle
+    p = synth.make_qsa_problem("qsa_24_2", [5000, 3192], 24, 2, 2048, seed=31)
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_indexed_forward(d.q, d.k, d.v, d.indices)
+    torch.cuda.synchronize()
+    rows = list(range(0, 8192, 8))
+    print("qsa 24/2 full size, sampled rows", flush=True)
+    ref_out, ref_lse = oracle.qsa_indexed_attention(p.q[rows], p.k, p.v, p.indices[rows])
+    o = out.float().cpu().double()[rows]
+    f = out_f32.cpu().double()[rows]
+    l = lse.cpu().double()[:, rows]
+    assert float((o - ref_out).abs().max()) <= 2e-2
+    assert float((f - ref_out).abs().max()) <= 2e-2
+    fin = torch.isfinite(ref_lse)
+    assert torch.equal(torch.isfinite(l), fin)
+    assert float((l[fin] - ref_lse[fin]).abs().max()) <= 1e-3
