@@ -160,7 +160,8 @@ def prefill_executed_flops(q2k, cu_seqlens_q, lengths_k, num_qo_heads, tile_toke
 
 QSA_TILE_ROWS = 128      # eight 16-row slots
 QSA_MAX_TOKENS = 16      # token bits of a key's mask word
-QSA_WIN = 16384          # key range of a shared-route tile
+QSA_WIN = 16384          # keys of one window of a tile's key range
+QSA_MAX_WIN = 64         # windows a shared-route tile may span
 QSA_SLOT_ROWS = 16
 
 
@@ -177,11 +178,12 @@ def qsa_executed(num_qo_heads, num_kv_heads, indices=None, bitmap=None, num_kv_t
     over num_kv_tokens keys).
 
     A tile of `qsa_tile_tokens` queries takes the shared route when its
-    listed keys span fewer than 16384 tokens (a bitmap over at most 16384
-    keys always does) and 5 * U * ceil(S / 4) <= 8 * L, with U its key union,
-    L its listed entries and S = ceil(tokens * G / 16) its live 16-row
-    slots; then every live slot computes 32-key chunks over the whole union
-    (ceil(U / 32) chunks).  Otherwise each token takes its own 16-row tile
+    listed keys fall in at most 64 windows of 16384 keys (from its lowest
+    key; a bitmap over at most 16384 keys is one window from key 0) and
+    5 * U * ceil(S / 4) <= 8 * L, with U its key union, L its listed entries
+    and S = ceil(tokens * G / 16) its live 16-row slots; then every live
+    slot computes 32-key chunks over each window's union (ceil(U_w / 32)
+    chunks per window).  Otherwise each token takes its own 16-row tile
     over its own keys: ceil(W / 32) chunks of index entries, or one chunk
     per eight selected blocks.  A 16-row slot's chunk costs 16 x 32 keys x
     head_dim x 4 FLOPs (S^T and O^T += V^T P^T), for every KV head."""
@@ -208,20 +210,26 @@ def qsa_executed(num_qo_heads, num_kv_heads, indices=None, bitmap=None, num_kv_t
             if U:
                 lo, hi = 4 * int(blk[ub][0]), min(4 * int(blk[ub][-1]) + 3, num_kv_tokens - 1)
                 base = 0 if num_kv_tokens <= QSA_WIN else lo
+                tok = torch.arange(4 * nb).view(nb, 4)[ub].flatten()
+                ukeys = tok[tok < num_kv_tokens]
             per_token = [(int(r.sum()) + 7) // 8 for r in rows]
         else:
             keys = ind[t0:t0 + nt]
             keys = keys[keys >= 0]
             listed = int(keys.numel())
-            U = int(torch.unique(keys).numel())
+            ukeys = torch.unique(keys)
+            U = int(ukeys.numel())
             if U:
                 lo, hi = int(keys.min()), int(keys.max())
                 base = lo
             per_token = [(W + 31) // 32] * nt
-        if U and (hi - base >= QSA_WIN or 5 * U * ((slots + 3) // 4) > 8 * listed):
+        if U and ((hi - base) // QSA_WIN + 1 > QSA_MAX_WIN or
+                  5 * U * ((slots + 3) // 4) > 8 * listed):
             token += 1
             flops += sum(per_token) * chunk
         else:
             shared += 1
-            flops += slots * ((U + 31) // 32) * chunk
+            if U:
+                per_win = torch.bincount((ukeys - base) // QSA_WIN)
+                flops += slots * int(((per_win + 31) // 32).sum()) * chunk
     return flops * num_kv_heads, shared, token

@@ -7,9 +7,9 @@
 // query rows (token-major) are cut into 16-row slots, one per wave, on
 // v_mfma_f32_16x16x32_bf16.
 //  * Shared keys.  The tile's selections are folded into one 32-bit word per
-//    key of the tile's key range in LDS (bit j: token j of the tile lists
-//    the key), then compacted, in ascending key order, into (key offset,
-//    token mask) words.  The keys are consumed 32 at a time: every chunk's K
+//    key in LDS (bit j: token j of the tile lists the key), one window of
+//    16384 keys of the tile's key range at a time, then compacted, in
+//    ascending key order, into (key offset, token mask) words.  The keys are consumed 32 at a time: every chunk's K
 //    and V rows (512 bytes each) are staged global -> LDS with
 //    global_load_lds by all eight waves into a ring of 2-4 chunk buffers
 //    (one barrier per chunk), so a key listed by several tokens of the tile
@@ -23,7 +23,8 @@
 //    by more than 64; O^T += V^T P^T
 //    with V^T from ds_read_b64_tr_b16 and P straight from the S^T registers
 //    (keys 4 q .. 4 q + 3 and 16 + 4 q .. 16 + 4 q + 3 of lane group q).
-//  * Per-token keys.  When the tile's keys span more than 16384 tokens, or
+//    The softmax state carries over from window to window.
+//  * Per-token keys.  When the tile's keys span more than 64 windows, or
 //    the union is large against what its tokens listed (masking would then
 //    compute far more scores than gathering each token's own keys), the
 //    eight waves take the tile's tokens one at a time instead: one wave per
@@ -46,7 +47,8 @@ constexpr int kQsaWaves = 8;
 constexpr int kQsaThreads = kQsaWaves * kWave;
 constexpr int kQsaTileRows = 16 * kQsaWaves;      // query rows of a tile
 constexpr int kQsaMaxTokens = 16;                 // token bits of a key's mask word
-constexpr int kQsaWin = 16384;                    // key range the shared route covers
+constexpr int kQsaWin = 16384;                    // keys of one window of a tile's key range
+constexpr int kQsaMaxWin = 64;                    // windows the shared route takes (1 Mi keys)
 // Shared route when kTileCost * union * (slot rounds) <= kTokenCost * listed
 // entries: per union key a round of four 16-row slots costs about 5/8 of one
 // per-token key gather (1 KiB per key and token, measured rates).
@@ -270,17 +272,18 @@ __device__ __forceinline__ void qsa_token(const QsaParams& p, int tok, int g, Qs
     p.lse[(int64_t)hrow * p.total_q + tok] = lsum > 0.f ? (m + __log2f(lsum)) * kQsaLn2 : -INFINITY;
 }
 
-// Index entries e0 + tid + 512 i (i < 4) of the tile's rows j < 16, all
+// Index entries e0 + tid + 512 i (i < NI) of the tile's rows j < 16, all
 // loads in flight together; rows past the tile re-read its last row and
 // entries past the row its last entry (the caller skips both).
+template <int NI>
 __device__ __forceinline__ void index_batch(const QsaParams& p, int t0, int nt, int e0,
-                                            int (&id)[kQsaMaxTokens][4]) {
+                                            int (&id)[kQsaMaxTokens][NI]) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int j = 0; j < kQsaMaxTokens; ++j) {
     const int32_t* row = p.indices + (int64_t)(t0 + min(j, nt - 1)) * p.width;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) id[j][i] = row[min(e0 + tid + kQsaThreads * i, p.width - 1)];
+    for (int i = 0; i < NI; ++i) id[j][i] = row[min(e0 + tid + kQsaThreads * i, p.width - 1)];
   }
 }
 
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
   } else {
     for (int e0 = 0; e0 < p.width; e0 += 4 * kQsaThreads) {
       int id[kQsaMaxTokens][4];
-      index_batch(p, t0, nt, e0, id);
+      index_batch<4>(p, t0, nt, e0, id);
 #pragma unroll
       for (int j = 0; j < kQsaMaxTokens; ++j)
 #pragma unroll
@@ -399,27 +402,32 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
   }
 
   const int live_waves = (nt * G + 15) >> 4;
-  bool shared = true;   // nothing listed: the shared route writes 0 / -inf
-  int U = 0;            // union size
+  // The tile's key range [base, hi] in windows of kQsaWin keys; the key
+  // union is built, compacted and consumed one window at a time.
   const int base = hi < 0 || direct ? 0 : lo;
-  if (hi >= 0 && hi - base >= kQsaWin) {
-    shared = false;
-  } else if (hi >= 0) {
-    const int range = hi - base + 1;
-    // ---- pass 2: token bits of every key in [base, hi] ----
+  const int nwin = hi < 0 ? 0 : (hi - base) / kQsaWin + 1;
+
+  // Token bits of the keys in [wb, wb + kQsaWin) (and <= hi) in M, compacted
+  // ascending into (key offset from wb << 16 | token mask) entries, the last
+  // chunk padded with the window's lowest listed key (no token); returns the
+  // window's union size (uniform).  Every thread calls it.
+  auto build = [&](int wb) -> int {
+    const int whi = hi - wb < kQsaWin ? hi : wb + kQsaWin - 1;
+    const int range = whi - wb + 1;
     if constexpr (BITMAP) {
       if (!direct) {
-        // every block of the range written, selected or not
-        for (int b0 = lo >> 2; b0 <= (hi >> 2); b0 += 4 * kQsaThreads) {
+        // every block of the window written, selected or not (wb and the
+        // window length are multiples of 4)
+        for (int b0 = wb >> 2; b0 <= (whi >> 2); b0 += 4 * kQsaThreads) {
           uint32_t mk[4];
           block_masks(p, t0, nt, b0, mk);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int b = b0 + tid + kQsaThreads * i;
-            if (b > (hi >> 2)) continue;
+            if (b > (whi >> 2)) continue;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (4 * b + e <= hi) M[4 * b + e - base] = mk[i];
+              if (4 * b + e <= whi) M[4 * b + e - wb] = mk[i];
           }
         }
       }
@@ -430,19 +438,21 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
           *reinterpret_cast<u32x4*>(M + 32 * tid + 4 * i) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
-      for (int e0 = 0; e0 < p.width; e0 += 4 * kQsaThreads) {
-        int id[kQsaMaxTokens][4];
-        index_batch(p, t0, nt, e0, id);
+      // two entries per row in flight (the softmax state may be live here)
+      for (int e0 = 0; e0 < p.width; e0 += 2 * kQsaThreads) {
+        int id[kQsaMaxTokens][2];
+        index_batch<2>(p, t0, nt, e0, id);
 #pragma unroll
         for (int j = 0; j < kQsaMaxTokens; ++j)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (j < nt && e0 + tid + kQsaThreads * i < p.width && id[j][i] >= 0)
-              atomicOr(M + (id[j][i] - base), 1u << j);
+          for (int i = 0; i < 2; ++i)
+            if (j < nt && e0 + tid + kQsaThreads * i < p.width && id[j][i] >= wb &&
+                id[j][i] <= whi)
+              atomicOr(M + (id[j][i] - wb), 1u << j);
       }
     }
     __syncthreads();
-    // ---- compaction, ascending: (key offset << 16 | token mask) ----
+    // compaction, ascending
     uint32_t vals[32];
     int c = 0;
 #pragma unroll
@@ -464,23 +474,34 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
     }
     if (lane == kWave - 1) misc[32 + w] = x;
     __syncthreads();
-    int before = 0;
+    int before = 0, u = 0;
 #pragma unroll
     for (int i = 0; i < kQsaWaves; ++i) {
-      const int s = misc[32 + i];
-      before += i < w ? s : 0;
-      U += s;
+      const int sw = misc[32 + i];
+      before += i < w ? sw : 0;
+      u += sw;
     }
     int rank = before + x - c;
 #pragma unroll
     for (int i = 0; i < 32; ++i)
       if (vals[i]) M[rank++] = (uint32_t)(32 * tid + i) << 16 | vals[i];
-    // the last chunk's padding: no token, the lowest listed key
-    if (U + tid < ((U + 31) & ~31)) M[U + tid] = (uint32_t)(lo - base) << 16;
     __syncthreads();
-    U = __builtin_amdgcn_readfirstlane(U);
-    shared = (int64_t)kTileCost * U * ((live_waves + 3) >> 2) <= (int64_t)kTokenCost * listed;
-  }
+    // the last chunk's padding: no token, the window's lowest listed key
+    // (entry 0); every thread has read the scan words before a later call
+    // writes them again
+    if (u > 0 && u + tid < ((u + 31) & ~31)) M[u + tid] = M[0] & 0xffff0000u;
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(u);
+  };
+
+  // The whole union first (every window built and counted), for the route;
+  // with one window its list stays in M for the shared route.  Nothing
+  // listed: the shared route writes 0 / -inf.
+  int U = 0;
+  const int ncount = nwin <= kQsaMaxWin ? nwin : 0;
+  for (int wi = 0; wi < ncount; ++wi) U += build(base + wi * kQsaWin);
+  const bool shared = nwin <= kQsaMaxWin && (int64_t)kTileCost * U * ((live_waves + 3) >> 2) <=
+                                                (int64_t)kTokenCost * listed;
 
   if (!shared) {
     // every thread has read the scratch words the per-wave regions cover
@@ -499,43 +520,13 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
   const int hh = live ? row - tl * G : 0;
   const bool wave_live = w < live_waves;
 
-  bf16x8 qf[8];
-  {
-    const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) +
-                        ((int64_t)(t0 + tl) * p.hq + g * G + hh) * kQsaRowBytes + 16 * q;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 64 * s);
-      qf[s] = as_bf16x8(live ? v : u32x4{0, 0, 0, 0});
-    }
-  }
+  const uint8_t* qp = reinterpret_cast<const uint8_t*>(p.q) +
+                      ((int64_t)(t0 + tl) * p.hq + g * G + hh) * kQsaRowBytes + 16 * q;
 
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k) + (int64_t)g * p.k_head_stride;
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.v) + (int64_t)g * p.v_head_stride;
   const float C = p.scale_log2;
-  const int nch = (U + 31) >> 5;
   const uint32_t mlds = __builtin_amdgcn_readfirstlane(lds_addr(M));
-  const uint32_t ring = mlds + 128 * nch;   // right after the union list
-  const int nbuf = min(kQsaMaxBuf, (kQsaLds - 128 * nch) / kPairBytes);
-
-  // chunk K and V rows into ring buffer b: wave w stages keys 4 w .. 4 w + 3,
-  // whose union entries `ent` it has read beforehand, two rows per load
-  // (lane l: row 4 w + 2 i + l / 32, 16-byte unit l % 32, read from its
-  // swizzled source unit); four loads per wave
-  auto entries = [&](int c) { return lds_b128(mlds + 128 * c + 16 * w); };
-  auto stage = [&](int b, u32x4 ent) {
-    const uint32_t kb = ring + b * kPairBytes;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 4 * w + 2 * i + (lane >> 5);
-      const uint32_t e = (lane >> 5) ? ent[2 * i + 1] : ent[2 * i];
-      const int64_t id = base + (int)(e >> 16);
-      const int u = lane & 31;
-      const uint32_t dst = kb + (4 * w + 2 * i) * kQsaRowBytes;
-      g2lds16(kg + id * p.k_row_stride + 16 * (u ^ (r & 15)), dst);
-      g2lds16(vg + id * p.v_row_stride + 16 * (u ^ ((r & 7) << 1)), dst + kKChunk);
-    }
-  };
 
   // reference max m (log2 units; -inf until the row's first listed key) and
   // the row sum: p = 2^(s - m), m moved (rescaling O and l) only when a
@@ -554,96 +545,141 @@ __global__ __launch_bounds__(kQsaThreads, 1) void msa_qsa_kernel(QsaParams p, in
   const int vsw = (vrow & 7) << 1;
   const uint32_t vofs = kKChunk + vrow * kVPitch + 8 * (l16 & 1);
 
-  // chunks 0 .. nbuf - 2 in flight before the first one is computed
-  for (int c = 0; c < min(nbuf - 1, nch); ++c) stage(c, entries(c));
-  int bc = 0;   // ring buffer of chunk c
-  for (int c = 0; c < nch; ++c) {
-    const int cn = c + nbuf - 1;   // the chunk staged in this step
-    const u32x4 ent = entries(cn < nch ? cn : c);
-    // chunk c has landed for every wave (the later chunks staged so far may
-    // still be in flight: four loads each), and every wave is done with
-    // chunk c - 1, whose buffer chunk cn now refills
-    const int ahead = min(nbuf - 2, nch - 1 - c);
-    if (ahead >= 2)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (ahead == 1)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    block_barrier();
-    if (cn < nch) stage(bc == 0 ? nbuf - 1 : bc - 1, ent);
-    const int b = bc;
-    bc = bc + 1 == nbuf ? 0 : bc + 1;
-    if (!wave_live) continue;
-    const uint32_t kb = ring + b * kPairBytes;
-
-    // every K fragment and the token masks of the lane's eight keys in
-    // flight at once, then S^T = K Q^T
-    u32x4 kf[2][8];
+  // one window: its Uw union keys (listed from M, offsets from wb) in
+  // 32-key chunks; the softmax state carries over from window to window
+  auto run = [&](int Uw, int wb) {
+    // query fragments (re-read per window, so that they are not held while
+    // a window's union is built)
+    bf16x8 qf[8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 64 * s);
+      qf[s] = as_bf16x8(live ? v : u32x4{0, 0, 0, 0});
+    }
+    const int nch = (Uw + 31) >> 5;
+    const uint32_t ring = mlds + 128 * nch;   // right after the union list
+    const int nbuf = min(kQsaMaxBuf, (kQsaLds - 128 * nch) / kPairBytes);
+
+    // chunk K and V rows into ring buffer b: wave w stages keys 4 w .. 4 w + 3,
+    // whose union entries `ent` it has read beforehand, two rows per load
+    // (lane l: row 4 w + 2 i + l / 32, 16-byte unit l % 32, read from its
+    // swizzled source unit); four loads per wave
+    auto entries = [&](int c) { return lds_b128(mlds + 128 * c + 16 * w); };
+    auto stage = [&](int b, u32x4 ent) {
+      const uint32_t kb = ring + b * kPairBytes;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = 4 * w + 2 * i + (lane >> 5);
+        const uint32_t e = (lane >> 5) ? ent[2 * i + 1] : ent[2 * i];
+        const int64_t id = wb + (int)(e >> 16);
+        const int u = lane & 31;
+        const uint32_t dst = kb + (4 * w + 2 * i) * kQsaRowBytes;
+        g2lds16(kg + id * p.k_row_stride + 16 * (u ^ (r & 15)), dst);
+        g2lds16(vg + id * p.v_row_stride + 16 * (u ^ ((r & 7) << 1)), dst + kKChunk);
+      }
+    };
+
+    // chunks 0 .. nbuf - 2 in flight before the first one is computed
+    for (int c = 0; c < min(nbuf - 1, nch); ++c) stage(c, entries(c));
+    int bc = 0;   // ring buffer of chunk c
+    for (int c = 0; c < nch; ++c) {
+      const int cn = c + nbuf - 1;   // the chunk staged in this step
+      const u32x4 ent = entries(cn < nch ? cn : c);
+      // chunk c has landed for every wave (the later chunks staged so far may
+      // still be in flight: four loads each), and every wave is done with
+      // chunk c - 1, whose buffer chunk cn now refills
+      const int ahead = min(nbuf - 2, nch - 1 - c);
+      if (ahead >= 2)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (ahead == 1)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      block_barrier();
+      if (cn < nch) stage(bc == 0 ? nbuf - 1 : bc - 1, ent);
+      const int b = bc;
+      bc = bc + 1 == nbuf ? 0 : bc + 1;
+      if (!wave_live) continue;
+      const uint32_t kb = ring + b * kPairBytes;
+
+      // every K fragment and the token masks of the lane's eight keys in
+      // flight at once, then S^T = K Q^T
+      u32x4 kf[2][8];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          kf[kt][s] = lds_b128(kb + (16 * kt + l16) * kKPitch + 16 * ((4 * s + q) ^ l16));
+      const uint32_t mrow = mlds + 128 * c;
+      const u32x4 ma = lds_b128(mrow + 16 * q);
+      const u32x4 mb = lds_b128(mrow + 64 + 16 * q);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        kf[kt][s] = lds_b128(kb + (16 * kt + l16) * kKPitch + 16 * ((4 * s + q) ^ l16));
-    const uint32_t mrow = mlds + 128 * c;
-    const u32x4 ma = lds_b128(mrow + 16 * q);
-    const u32x4 mb = lds_b128(mrow + 64 + 16 * q);
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+        for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma16(as_bf16x8(kf[kt][s]), qf[s], acc[kt]);
+      __builtin_amdgcn_sched_barrier(0);
+      // V^T fragments, read while the softmax below runs
+      u32x4 vt[16];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma16(as_bf16x8(kf[kt][s]), qf[s], acc[kt]);
-    __builtin_amdgcn_sched_barrier(0);
-    // V^T fragments, read while the softmax below runs
-    u32x4 vt[16];
-#pragma unroll
-    for (int dt = 0; dt < 16; ++dt) {
-      const uint32_t a = kb + vofs + 16 * ((2 * dt + ((l16 & 3) >> 1)) ^ vsw);
-      const u32x2 lo2 = lds_tr16(a);
-      const u32x2 hi2 = lds_tr16(a + 16 * kVPitch);
-      vt[dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int dt = 0; dt < 16; ++dt) {
+        const uint32_t a = kb + vofs + 16 * ((2 * dt + ((l16 & 3) >> 1)) ^ vsw);
+        const u32x2 lo2 = lds_tr16(a);
+        const u32x2 hi2 = lds_tr16(a + 16 * kVPitch);
+        vt[dt] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
+      __builtin_amdgcn_sched_barrier(0);
 
-    const uint32_t mk[8] = {ma[0], ma[1], ma[2], ma[3], mb[0], mb[1], mb[2], mb[3]};
-    bool vis[8];
-    float e[8], ps = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      vis[j] = (mk[j] & bit) != 0u;
-      const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j >> 2][j & 3], C, -m));
-      e[j] = vis[j] ? x : 0.f;
-      ps += e[j];
-    }
-    if (__ballot(!(ps <= kQsaSumLimit))) {
-      // rows whose chunk passed the reference (or met their first listed
-      // key) move it to their max; other rows keep theirs (alpha 1, the
-      // same exponentials), so a row's result does not depend on its mates
-      const float trig = xmax_16_32(!(ps <= kQsaSumLimit) ? 1.f : 0.f);
-      float cm = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) cm = fmaxf(cm, vis[j] ? acc[j >> 2][j & 3] * C : -INFINITY);
-      cm = xmax_16_32(cm);
-      const float mn = trig > 0.f ? fmaxf(m, cm) : m;
-      const float alpha = mn == m ? 1.f : __builtin_amdgcn_exp2f(m - mn);
-      m = mn;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
-      ps = 0.f;
+      const uint32_t mk[8] = {ma[0], ma[1], ma[2], ma[3], mb[0], mb[1], mb[2], mb[3]};
+      bool vis[8];
+      float e[8], ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
+        vis[j] = (mk[j] & bit) != 0u;
         const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j >> 2][j & 3], C, -m));
         e[j] = vis[j] ? x : 0.f;
         ps += e[j];
       }
-    }
-    l += ps;
-    const bf16x8 pf = as_bf16x8(u32x4{cvt_pk_bf16(e[0], e[1]), cvt_pk_bf16(e[2], e[3]),
-                                      cvt_pk_bf16(e[4], e[5]), cvt_pk_bf16(e[6], e[7])});
+      if (__ballot(!(ps <= kQsaSumLimit))) {
+        // rows whose chunk passed the reference (or met their first listed
+        // key) move it to their max; other rows keep theirs (alpha 1, the
+        // same exponentials), so a row's result does not depend on its mates
+        const float trig = xmax_16_32(!(ps <= kQsaSumLimit) ? 1.f : 0.f);
+        float cm = -INFINITY;
 #pragma unroll
-    for (int dt = 0; dt < 16; ++dt) o[dt] = mfma16(as_bf16x8(vt[dt]), pf, o[dt]);
+        for (int j = 0; j < 8; ++j) cm = fmaxf(cm, vis[j] ? acc[j >> 2][j & 3] * C : -INFINITY);
+        cm = xmax_16_32(cm);
+        const float mn = trig > 0.f ? fmaxf(m, cm) : m;
+        const float alpha = mn == m ? 1.f : __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 16; ++dt) o[dt] *= alpha;
+        ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[j >> 2][j & 3], C, -m));
+          e[j] = vis[j] ? x : 0.f;
+          ps += e[j];
+        }
+      }
+      l += ps;
+      const bf16x8 pf = as_bf16x8(u32x4{cvt_pk_bf16(e[0], e[1]), cvt_pk_bf16(e[2], e[3]),
+                                        cvt_pk_bf16(e[4], e[5]), cvt_pk_bf16(e[6], e[7])});
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) o[dt] = mfma16(as_bf16x8(vt[dt]), pf, o[dt]);
+    }
+
+  };
+  for (int wi = 0; wi < nwin; ++wi) {
+    const int wb = base + wi * kQsaWin;
+    // one window: still listed from the route decision; several: rebuilt
+    run(nwin == 1 ? U : build(wb), wb);
+    // every wave is done with this window's list and ring before the next
+    // window is built over them (no load is in flight: the last chunk
+    // waited for every one)
+    if (nwin > 1) __syncthreads();
   }
 
   if (!wave_live) return;

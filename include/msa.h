@@ -381,11 +381,12 @@ typedef struct {
  * MSA_ERR_UNSUPPORTED (head_dim != 256, Hq / Hkv > 16, misaligned pointers)
  * before any launch.
  * Work split: one workgroup per tile of min(16, 128 / G) consecutive query
- * tokens and KV head.  A tile whose listed keys span at most 16384 tokens
- * and whose key union U is small against its L listed entries
+ * tokens and KV head.  A tile whose listed keys fall in at most 64 windows
+ * of 16384 keys and whose key union U is small against its L listed entries
  * (5 * U * ceil(S / 4) <= 8 * L, S = ceil(tokens * G / 16) row slots) reads
  * each union key once and computes its rows over the union in ascending
- * key order, masking the keys a row's token did not list; any other tile
+ * key order (window by window), masking the keys a row's token did not
+ * list; any other tile
  * computes each token over its own keys in index order.  Results are
  * bitwise repeatable. */
 msa_status_t msa_qsa_indexed_forward(const msa_qsa_args_t* args, void* stream);

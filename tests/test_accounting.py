@@ -127,11 +127,15 @@ def _qsa_brute(G, hkv, rows, chunks_per_token, bitmap_direct=False):
         union = set().union(*tile)
         listed = sum(len(r) for r in tile)
         slots = -(-len(tile) * G // 16)
-        wide = bool(union) and not bitmap_direct and max(union) - min(union) >= 16384
+        base = 0 if bitmap_direct or not union else min(union)
+        windows = {}
+        for k in union:
+            windows[(k - base) // 16384] = windows.get((k - base) // 16384, 0) + 1
+        wide = bool(union) and (max(union) - base) // 16384 + 1 > 64
         if union and (wide or 5 * len(union) * -(-slots // 4) > 8 * listed):
             total += sum(chunks_per_token(i) for i in range(t0, t0 + len(tile))) * 16 * 32
         else:
-            total += slots * -(-len(union) // 32) * 16 * 32
+            total += slots * sum(-(-n // 32) for n in windows.values()) * 16 * 32
     return total * 256 * 4 * hkv
 
 
@@ -146,7 +150,7 @@ def test_qsa_executed_matches_enumeration(hq, hkv):
         if kind < 0.1:
             r = []                                                 # empty row
         elif kind < 0.4:
-            r = rng.sample(range(0, 20000), rng.randint(1, W))     # wide, sparse
+            r = rng.sample(range(0, 20000 if i % 2 else 2000000), rng.randint(1, W))   # wide
         else:
             r = rng.sample(range(0, 80), rng.randint(1, W))        # dense, shared
         rows.append(set(r))
@@ -183,8 +187,11 @@ def test_qsa_executed_closed_forms():
     ind = torch.full((10, 4), -1, dtype=torch.int32)
     ind[:, 0] = torch.arange(10) * 100
     assert acc.qsa_executed(12, 1, indices=ind) == (10 * 16 * 32 * 256 * 4, 0, 1)
-    # keys 0 and 16384 in one tile: past the shared range
+    # keys 0, 1, 2 and 16384 in one tile: two windows of one chunk each
     ind = torch.tensor([[0, 16384, 1, 2]] * 10, dtype=torch.int32)
+    assert acc.qsa_executed(12, 1, indices=ind) == (8 * 2 * 16 * 32 * 256 * 4, 1, 0)
+    # keys 0 and 64 * 16384: 65 windows, past the shared route's 64
+    ind = torch.tensor([[0, 64 * 16384, 1, 2]] * 10, dtype=torch.int32)
     assert acc.qsa_executed(12, 1, indices=ind)[2] == 1
     # nothing listed: a shared tile with no chunks
     assert acc.qsa_executed(12, 1, indices=torch.full((3, 4), -1, dtype=torch.int32)) == (0, 1, 0)

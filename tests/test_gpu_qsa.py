@@ -105,13 +105,15 @@ def test_qsa_bitmap_matches_oracle(msa, lens, hq, hkv, density, mode):
     _check(p, out, out_f32, lse, f"qsa bitmap {lens} {hq}/{hkv}", rows=_bitmap_rows(p))
 
 
-@pytest.mark.parametrize("tk", [517, 17000])
-def test_qsa_bitmap_hand_rows_and_indexed_equivalence(msa, tk):
+@pytest.mark.parametrize("tk,spread", [(517, False), (17000, False), (17000, True)])
+def test_qsa_bitmap_hand_rows_and_indexed_equivalence(msa, tk, spread):
     # rows that exercise the block compaction: exactly 8 and 9 selected
-    # blocks, hits at window edges (63, 64, 127), an empty row, one block.
-    # Tk = 517 (130 blocks, the last one token long): shared-key tiles;
-    # Tk = 17000: both tiles' keys span more than 16384 tokens (row 7 takes
-    # every block, row 11 the last one), so every token scans its own row
+    # blocks, hits at scan-window edges (63, 64, 127), an empty row, one
+    # block.  Tk = 517 (130 blocks, the last one token long): shared-key
+    # tiles; Tk = 17000: the tiles' keys fall in two 16384-key windows (row
+    # 7 takes every block, row 11 the last one), still shared; spread: each
+    # hand row alone in its 10-token tile (the others empty), so every tile
+    # takes the per-token route and each token scans its own row
     T = 12
     p = synth.make_qsa_bitmap_problem("qsa_bm_hand", [T], 12, 1, 0.0, seed=3)
     k = synth._randn_cast((tk, 1, 256), synth._gen(4, "cpu"), "cpu", torch.bfloat16)
@@ -130,12 +132,23 @@ def test_qsa_bitmap_hand_rows_and_indexed_equivalence(msa, tk):
     bm[11, [5, 70, 100]] = 1
     if tk > 16384:
         bm[11, -1] = 1
-    p = synth.QsaProblem("qsa_bm_hand", p.q, k, v, None, [T], bm)
+    q = p.q
+    if spread:
+        wide = torch.zeros(10 * T, bm.shape[1], dtype=torch.uint8)
+        wide[::10] = bm
+        bm = wide
+        q = synth._randn_cast((10 * T, 12, 256), synth._gen(6, "cpu"), "cpu", torch.bfloat16)
+        rows = [[int(x) for x in r if x >= 0] for r in oracle.qsa_bitmap_indices(bm, tk)]
+        # (the empty row's tile lists nothing: the shared route's 0 / -inf)
+        assert _qsa_routes(rows, 12) == ["token" if rows[10 * i] else "shared" for i in range(T)]
+    T = bm.shape[0]
+    p = synth.QsaProblem("qsa_bm_hand", q, k, v, None, [T], bm)
     d = p.to("cuda")
     out, out_f32, lse = msa.qsa_bitmap_forward(d.q, d.k, d.v, d.bitmap)
     torch.cuda.synchronize()
     _check(p, out, out_f32, lse, "qsa bitmap hand rows", rows=_bitmap_rows(p))
-    assert torch.isneginf(lse[:, 3]).all() and (out[3].float() == 0).all()
+    empty = 30 if spread else 3
+    assert torch.isneginf(lse[:, empty]).all() and (out[empty].float() == 0).all()
     if tk > 2052:
         return   # rows longer than the indexed entry point's widest
     # the indexed entry point over the same key lists (ascending, -1 padded)
@@ -178,8 +191,9 @@ def test_qsa_bitmap_without_kv_tokens(msa):
 def _qsa_routes(rows, G):
     """The route each tile takes by the kernel's rule: tiles of
     min(16, 128 // G) consecutive tokens; the shared-key route unless the
-    tile's listed keys span more than 16384 tokens or
-    5 * union * ceil(live 16-row slots / 4) > 8 * listed entries."""
+    tile's listed keys fall in more than 64 windows of 16384 keys (from its
+    lowest key) or 5 * union * ceil(live 16-row slots / 4) > 8 * listed
+    entries."""
     tt = min(16, 128 // G)
     routes = []
     for t0 in range(0, len(rows), tt):
@@ -187,7 +201,7 @@ def _qsa_routes(rows, G):
         keys = [k for r in tile for k in r if k >= 0]
         if not keys:
             routes.append("shared")
-        elif max(keys) - min(keys) >= 16384:
+        elif (max(keys) - min(keys)) // 16384 + 1 > 64:
             routes.append("token")
         else:
             slots = (len(tile) * G + 15) // 16
@@ -199,7 +213,7 @@ def _qsa_routes(rows, G):
 def _mixed_rows(tk, seed):
     # 10-token tiles (G = 12): tile 0 lists 48 of the same 64 keys per token
     # (shared keys), tile 1 eight random keys of 8000 per token (sparse: per
-    # token), tile 2 64 keys spread over all tk rows (a range past 16384 keys)
+    # token), tile 2 64 keys spread over all tk rows (sparse over two key windows)
     g = torch.Generator().manual_seed(seed)
     rows = [sorted(torch.randperm(64, generator=g)[:48].tolist()) for _ in range(10)]
     rows += [torch.randperm(8000, generator=g)[:8].tolist() for _ in range(10)]
@@ -282,3 +296,59 @@ def test_qsa_24_2_full_size_sampled_rows(msa):
     fin = torch.isfinite(ref_lse)
     assert torch.equal(torch.isfinite(l), fin)
     assert float((l[fin] - ref_lse[fin]).abs().max()) <= 1e-3
+
+
+@pytest.mark.parametrize("hq,hkv", [(12, 1), (24, 2)])
+def test_qsa_shared_tiles_over_several_key_windows(msa, hq, hkv):
+    # keys over 40 000 tokens, three 16384-key windows per tile: tile 0
+    # lists the same 1500 keys spread over every window, tile 1 the same 600
+    # keys in the first and last windows only (the middle one empty), tile 2
+    # a dense run in the first window; all three share keys
+    tk = 40000
+    g = torch.Generator().manual_seed(hkv)
+    spread = torch.randperm(tk, generator=g)[:1500]
+    ends = torch.cat([torch.randperm(300, generator=g), tk - 1 - torch.randperm(300, generator=g)])
+    rows = [torch.sort(spread).values.tolist()] * 10
+    rows += [ends.tolist()] * 10
+    rows += [list(range(i, 512 + i, 2)) for i in range(7)]
+    assert _qsa_routes(rows, hq // hkv) == ["shared"] * 3
+    ind = torch.full((len(rows), 1500), -1, dtype=torch.int32)
+    for i, r in enumerate(rows):
+        ind[i, :len(r)] = torch.tensor(r, dtype=torch.int32)
+    gq = synth._gen(40 + hkv, "cpu")
+    q = synth._randn_cast((len(rows), hq, 256), gq, "cpu", torch.bfloat16)
+    k = synth._randn_cast((tk, hkv, 256), gq, "cpu", torch.bfloat16)
+    v = synth._randn_cast((tk, hkv, 256), gq, "cpu", torch.bfloat16)
+    p = synth.QsaProblem("qsa_windows", q, k, v, ind, [len(rows)])
+    print(f"qsa shared windows {hq}/{hkv} Tk {tk}", flush=True)
+    d = p.to("cuda")
+    a = msa.qsa_indexed_forward(d.q, d.k, d.v, d.indices)
+    b = msa.qsa_indexed_forward(d.q, d.k, d.v, d.indices)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    _check(p, *a, f"qsa shared windows {hq}/{hkv}")
+
+
+def test_qsa_bitmap_dense_map_over_several_windows(msa):
+    # a half-density random map over 40 001 tokens (10 001 blocks, the last
+    # one token long): three windows per tile, shared keys; an empty row
+    tk, T = 40001, 25
+    g = torch.Generator().manual_seed(9)
+    nb = (tk + 3) // 4
+    bm = (torch.rand(T, nb, generator=g) < 0.5).to(torch.uint8)
+    bm[4] = 0
+    bm[5, nb - 1] = 1
+    full = oracle.qsa_bitmap_indices(bm, tk)
+    rows = [[int(x) for x in r if x >= 0] for r in full]
+    assert _qsa_routes(rows, 12) == ["shared"] * 3
+    gq = synth._gen(23, "cpu")
+    q = synth._randn_cast((T, 12, 256), gq, "cpu", torch.bfloat16)
+    k = synth._randn_cast((tk, 1, 256), gq, "cpu", torch.bfloat16)
+    v = synth._randn_cast((tk, 1, 256), gq, "cpu", torch.bfloat16)
+    p = synth.QsaProblem("qsa_bm_windows", q, k, v, None, [T], bm)
+    print("qsa bitmap windows", flush=True)
+    d = p.to("cuda")
+    out, out_f32, lse = msa.qsa_bitmap_forward(d.q, d.k, d.v, d.bitmap)
+    torch.cuda.synchronize()
+    _check(p, out, out_f32, lse, "qsa bitmap windows", rows=_bitmap_rows(p))
+    assert torch.isneginf(lse[:, 4]).all() and (out[4].float() == 0).all()
